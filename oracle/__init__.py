@@ -1,0 +1,35 @@
+"""CPU oracle for the paged decode-attention path.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the entry module's smoke
+check and the benchmark's CPU-baseline leg may import or run anything in
+this package; the GPU library and its Python binding never do.  The oracle
+shares no code with the GPU path: it is plain float64 numpy, written from
+the definition of paged attention, and every function is pinned by CPU tests
+to closed forms, invariants, a library routine, brute force on tiny inputs
+and the pages' own block-table layouts.
+"""
+from .paged_attention import (
+    attention,
+    blocks_held,
+    copy_blocks,
+    logical_kv,
+    merge_partials,
+    paged_decode,
+    partial_attention,
+    reshape_and_cache,
+    token_location,
+    widen,
+)
+
+__all__ = [
+    "attention",
+    "blocks_held",
+    "copy_blocks",
+    "logical_kv",
+    "merge_partials",
+    "paged_decode",
+    "partial_attention",
+    "reshape_and_cache",
+    "token_location",
+    "widen",
+]

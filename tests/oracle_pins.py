@@ -1,0 +1,410 @@
+"""Pins for the CPU oracle: checks against facts that do not come from the oracle.
+
+Each ``pin_*`` function takes the oracle module and raises AssertionError if
+the oracle disagrees with an independent fact: brute force over the
+per-token definition, a library attention routine, closed forms, invariants,
+the block-table layouts the pages draw, and round trips.  They are shared by
+``test_oracle_pins.py`` (the real oracle must pass all of them) and
+``test_oracle_mutations.py`` (an oracle with a planted mistake must fail at
+least one of them).
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------------------
+# Independent helpers (never call the oracle)
+# ---------------------------------------------------------------------------
+
+
+def torch_widen(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Float64 value of stored elements, decoded by torch's own casts."""
+    a = np.ascontiguousarray(a)
+    if dtype == "bf16":
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(a)
+    return t.double().numpy()
+
+
+def brute_decode(q, kc, vc, bt, ctx, scale, dtype) -> np.ndarray:
+    """Per-token loops over the definition: for each query, each context
+    token t is found at physical block bt[s][t // B], offset t % B; score =
+    scale * sum_d q_d k_d (math.fsum); softmax with math.exp; weighted V sum
+    with math.fsum.  Slow, tiny inputs only."""
+    qw, kw, vw = torch_widen(q, dtype), torch_widen(kc, dtype), torch_widen(vc, dtype)
+    S, H, D = q.shape
+    B = kc.shape[2]
+    out = np.zeros((S, H, D))
+    for s in range(S):
+        n = int(ctx[s])
+        if n <= 0:
+            continue
+        loc = [(int(bt[s][t // B]), t % B) for t in range(n)]
+        for h in range(H):
+            sc = [scale * math.fsum(float(qw[s, h, d]) * float(kw[b, h, o, d]) for d in range(D)) for b, o in loc]
+            mx = max(sc)
+            e = [math.exp(x - mx) for x in sc]
+            z = math.fsum(e)
+            for d in range(D):
+                out[s, h, d] = math.fsum(e[t] * float(vw[b, h, o, d]) for t, (b, o) in enumerate(loc)) / z
+    return out
+
+
+def scatter_contiguous(K: np.ndarray, table, B: int, N: int, dtype: str):
+    """Build an [N, H, B, D] pool holding contiguous K [H, n, D] at the blocks
+    named by ``table`` (token t -> block table[t // B], slot t % B), by loops.
+    Unused slots hold canaries."""
+    H, n, D = K.shape
+    pool = wl.canary_fill((N, H, B, D), dtype)
+    for t in range(n):
+        b, o = table[t // B], t % B
+        for h in range(H):
+            pool[b, h, o, :] = K[h, t, :]
+    return pool
+
+
+def _decode(orc, case: wl.Case, q=None, kc=None, vc=None, bt=None, ctx=None, scale=None):
+    return orc.paged_decode(
+        case.q if q is None else q,
+        case.k_cache if kc is None else kc,
+        case.v_cache if vc is None else vc,
+        case.block_tables if bt is None else bt,
+        case.context_lens if ctx is None else ctx,
+        case.scale if scale is None else scale,
+        case.dtype,
+    )
+
+
+def _small_cases():
+    yield wl.config1()
+    yield wl.random_case(1, 4, 2, 8, 4, "f32", ctx_range=(1, 21))
+    yield wl.random_case(2, 3, 2, 4, 2, "f16", ctx_range=(1, 13))
+    yield wl.random_case(3, 3, 1, 8, 3, "bf16", ctx_range=(1, 17))
+    yield wl.random_case(4, 2, 2, 8, 1, "f32", ctx=[1, 9])
+    yield wl.random_case(5, 3, 2, 8, 4, "bf16", ctx=[0, 4, 11])
+
+
+# ---------------------------------------------------------------------------
+# Pins
+# ---------------------------------------------------------------------------
+
+
+def pin_widen(orc):
+    """Stored f16/bf16/f32 values widen exactly as torch decodes them."""
+    rng = np.random.default_rng(11)
+    for dtype in wl.DTYPES:
+        bits = rng.integers(0, 2 ** (8 * wl.ELEM_BYTES[dtype]), 4096, dtype=np.uint64)
+        a = bits.astype(wl.NP_BITS[dtype]).view(wl.NP_STORAGE[dtype])
+        ref = torch_widen(a, dtype)
+        got = orc.widen(a, dtype)
+        fin = np.isfinite(ref)
+        assert np.array_equal(got[fin], ref[fin]), dtype
+        assert np.array_equal(np.isnan(got), np.isnan(ref)), dtype
+
+
+def pin_bruteforce(orc):
+    """Vectorised oracle == per-token brute force on tiny cases (<= 1e-12)."""
+    for case in _small_cases():
+        got = _decode(orc, case)
+        ref = brute_decode(case.q, case.k_cache, case.v_cache, case.block_tables, case.context_lens, case.scale, case.dtype)
+        err = np.abs(got - ref).max()
+        assert err <= 1e-12, (case.name, err)
+
+
+def pin_library_attention(orc):
+    """With K/V scattered into a pool by explicit loops, the paged result
+    equals torch's scaled_dot_product_attention on the contiguous tensors."""
+    rng = np.random.default_rng(12)
+    for dtype, H, D, B, n in (("f32", 3, 16, 8, 37), ("f16", 2, 32, 4, 29), ("bf16", 4, 8, 16, 16), ("f32", 2, 8, 2, 1)):
+        nb = -(-n // B)
+        N = nb + 4
+        table = rng.permutation(N)[:nb]
+        K = wl.to_storage(rng.standard_normal((H, n, D), dtype=np.float32), dtype)
+        V = wl.to_storage(rng.standard_normal((H, n, D), dtype=np.float32), dtype)
+        q = wl.to_storage(rng.standard_normal((1, H, D), dtype=np.float32), dtype)
+        kc = scatter_contiguous(K, table, B, N, dtype)
+        vc = scatter_contiguous(V, table, B, N, dtype)
+        bt = np.full((1, nb + 2), -1, dtype=np.int32)
+        bt[0, :nb] = table
+        scale = 1.0 / math.sqrt(D)
+        got = orc.paged_decode(q, kc, vc, bt, np.array([n], np.int32), scale, dtype)
+        tq = torch.from_numpy(torch_widen(q, dtype)).reshape(1, H, 1, D)
+        tk = torch.from_numpy(torch_widen(K, dtype)).unsqueeze(0)
+        tv = torch.from_numpy(torch_widen(V, dtype)).unsqueeze(0)
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=scale).reshape(1, H, D).numpy()
+        err = np.abs(got - ref).max()
+        assert err <= 1e-12, (dtype, err)
+        # Plain softmax attention written with torch ops, too.
+        w = torch.softmax(scale * (tk[0] @ tq[0].transpose(1, 2)).squeeze(-1), dim=-1)
+        ref2 = (w.unsqueeze(1) @ tv[0]).squeeze(1).numpy()
+        assert np.abs(got[0] - ref2).max() <= 1e-12
+
+
+def pin_permutation(orc):
+    """Relabelling physical blocks (moving them and rewriting the tables)
+    leaves the result bit-for-bit unchanged."""
+    rng = np.random.default_rng(13)
+    for case in (wl.config1(), wl.random_case(6, 4, 2, 8, 4, "f16", ctx_range=(1, 30)), wl.random_case(7, 3, 2, 8, 2, "bf16")):
+        base = _decode(orc, case)
+        pi = rng.permutation(case.num_blocks)
+        kc = np.empty_like(case.k_cache)
+        vc = np.empty_like(case.v_cache)
+        kc[pi] = case.k_cache
+        vc[pi] = case.v_cache
+        bt = np.where(case.block_tables >= 0, pi[np.maximum(case.block_tables, 0)], -1).astype(np.int32)
+        got = _decode(orc, case, kc=kc, vc=vc, bt=bt)
+        assert np.array_equal(got, base), case.name
+
+
+def pin_single_token(orc):
+    """A context of one token returns that token's V row exactly."""
+    for dtype in wl.DTYPES:
+        case = wl.random_case(8, 3, 2, 8, 4, dtype, ctx=[1, 1, 1])
+        got = _decode(orc, case)
+        for s in range(3):
+            b = case.block_tables[s, 0]
+            assert np.array_equal(got[s], torch_widen(case.v_cache[b, :, 0, :], dtype)), dtype
+
+
+def pin_closed_forms(orc):
+    """scale 0 or K = 0 -> mean of V rows; equal V rows -> that row;
+    two tokens -> logistic weights; empty context -> zeros."""
+    case = wl.random_case(9, 2, 2, 8, 4, "f32", ctx=[7, 13])
+    vmean = []
+    for s in range(2):
+        n = int(case.context_lens[s])
+        rows = [case.v_cache[case.block_tables[s][t // 4], :, t % 4, :].astype(np.float64) for t in range(n)]
+        vmean.append(np.array([[math.fsum(r[h, d] for r in rows) / n for d in range(8)] for h in range(2)]))
+    vmean = np.stack(vmean)
+    assert np.abs(_decode(orc, case, scale=0.0) - vmean).max() <= 1e-14
+    kz = np.where(np.isnan(case.k_cache), case.k_cache, np.float32(0))
+    assert np.abs(_decode(orc, case, kc=kz) - vmean).max() <= 1e-14
+    # Every token of a (sequence, head) has the same V row c -> output c.
+    vconst = case.v_cache.copy()
+    c = np.arange(1, 9, dtype=np.float32) / 8
+    for s in range(2):
+        for t in range(int(case.context_lens[s])):
+            vconst[case.block_tables[s][t // 4], :, t % 4, :] = c * (1 + s)
+    got = _decode(orc, case, vc=vconst)
+    for s in range(2):
+        assert np.abs(got[s] - (c * (1 + s)).astype(np.float64)).max() <= 1e-14
+    # Two tokens: weight of token 0 is the logistic function of the score gap.
+    two = wl.random_case(10, 1, 3, 8, 4, "f32", ctx=[2], scale=0.7)
+    qv = two.q[0].astype(np.float64)
+    b = two.block_tables[0, 0]
+    k0, k1 = two.k_cache[b, :, 0, :].astype(np.float64), two.k_cache[b, :, 1, :].astype(np.float64)
+    v0, v1 = two.v_cache[b, :, 0, :].astype(np.float64), two.v_cache[b, :, 1, :].astype(np.float64)
+    gap = 0.7 * (np.sum(qv * k0, axis=1) - np.sum(qv * k1, axis=1))
+    w0 = 1.0 / (1.0 + np.exp(-gap))
+    ref = w0[:, None] * v0 + (1.0 - w0)[:, None] * v1
+    assert np.abs(_decode(orc, two)[0] - ref).max() <= 1e-13
+    # Empty context (reading: zero output).
+    empty = wl.random_case(11, 2, 1, 8, 4, "f16", ctx=[0, 3])
+    assert np.array_equal(_decode(orc, empty)[0], np.zeros((1, 8)))
+
+
+def _marker_pool(N, B):
+    """Pool whose slot (block b, offset o) holds the vector [b, o, 0, 0]."""
+    kc = np.zeros((N, 1, B, 4), dtype=np.float32)
+    for b in range(N):
+        for o in range(B):
+            kc[b, 0, o, 0] = b
+            kc[b, 0, o, 1] = o
+    return kc
+
+
+def pin_page_layouts(orc):
+    """The block tables drawn on the pages resolve tokens to the drawn blocks."""
+    g = _golden("digest_flowchart_layout.json")
+    B, N = g["block_size"], g["pool_blocks"]
+    pool = _marker_pool(N, B)
+    for seq, n_list in g["lengths"].items():
+        table = np.array(g["tables"][seq], dtype=np.int32)
+        for n in n_list:
+            assert orc.blocks_held(n, B) == g["blocks_held"][seq]
+            kv = orc.logical_kv(pool, table, n)
+            for j, (lo, hi) in enumerate(g["logical_block_token_ranges"][seq]):
+                hi = n - 1 if hi is None else hi
+                for t in range(lo, hi + 1):
+                    assert kv[0, t, 0] == table[j] and kv[0, t, 1] == t - lo
+    for loc in g["token_locations"]:
+        table = np.array(g["tables"][loc["seq"]], dtype=np.int32)
+        assert orc.token_location(table, loc["token"], B) == (loc["block"], loc["offset"])
+        kv = orc.logical_kv(pool, table, loc["token"] + 1)
+        assert (kv[0, loc["token"], 0], kv[0, loc["token"], 1]) == (loc["block"], loc["offset"])
+
+    # Copy-on-write of the shared block P3 into the free P9.
+    rng = np.random.default_rng(14)
+    H, D = 2, 8
+    kc = wl.canary_fill((N, H, B, D), "f32")
+    vc = wl.canary_fill((N, H, B, D), "f32")
+    lens = {"seq1": 33, "seq2": 17}
+    for seq, n in lens.items():
+        for t in range(n):
+            b = g["tables"][seq][t // B]
+            kc[b, :, t % B, :] = rng.standard_normal((H, D))
+            vc[b, :, t % B, :] = rng.standard_normal((H, D))
+    q = rng.standard_normal((2, H, D)).astype(np.float32)
+    bt = np.full((2, 3), -1, dtype=np.int32)
+    bt[0, :3] = g["tables"]["seq1"]
+    bt[1, :2] = g["tables"]["seq2"]
+    ctx = np.array([lens["seq1"], lens["seq2"]], dtype=np.int32)
+    before = orc.paged_decode(q, kc, vc, bt, ctx, 0.5, "f32")
+    src, dst = g["cow"]["src"], g["cow"]["dst"]
+    kc2, vc2 = orc.copy_blocks(kc, vc, [(src, dst)])
+    assert np.array_equal(kc2[dst].view(np.uint32), kc[src].view(np.uint32))
+    assert np.array_equal(vc2[dst].view(np.uint32), vc[src].view(np.uint32))
+    bt2 = bt.copy()
+    bt2[1, 0] = dst
+    after = orc.paged_decode(q, kc2, vc2, bt2, ctx, 0.5, "f32")
+    assert np.array_equal(before, after)
+    # A divergent write into sequence 2's private copy leaves sequence 1 alone.
+    kn = rng.standard_normal((1, H, D)).astype(np.float32)
+    vn = rng.standard_normal((1, H, D)).astype(np.float32)
+    kc3, vc3 = orc.reshape_and_cache(kn, vn, kc2, vc2, np.array([dst * B + 5], dtype=np.int64))
+    div = orc.paged_decode(q, kc3, vc3, bt2, ctx, 0.5, "f32")
+    assert np.array_equal(div[0], before[0])
+    assert not np.array_equal(div[1], before[1])
+
+    v = _golden("velog_block_table.json")
+    pool = _marker_pool(v["pool_blocks"], v["block_size"])
+    kv = orc.logical_kv(pool, np.array(v["table"], dtype=np.int32), len(v["table"]) * v["block_size"])
+    for t in range(kv.shape[1]):
+        assert kv[0, t, 0] == v["table"][t // v["block_size"]] and kv[0, t, 1] == t % v["block_size"]
+
+    for c in _golden("blocks_needed.json")["cases"]:
+        nb = orc.blocks_held(c["tokens"], c["block_size"])
+        assert nb == c["blocks"]
+        assert nb * c["block_size"] - c["tokens"] == c["last_block_free_slots"]
+
+
+def pin_append(orc):
+    """Appending writes each token's rows exactly where the block table says,
+    reading the sequence back returns them bit-exactly, and nothing else in
+    the pool changes; negative slots are skipped."""
+    for dtype in wl.DTYPES:
+        case = wl.random_case(15, 4, 3, 8, 4, dtype, ctx_range=(3, 23), n_append=3, spare_blocks=5)
+        st = case.steps[0]
+        slots = st.slot_mapping.copy()
+        slots[1] = -1  # padding token
+        kc, vc = orc.reshape_and_cache(st.key, st.value, case.k_cache, case.v_cache, slots)
+        B = case.block_size
+        written = np.zeros(case.k_cache.shape[:1] + case.k_cache.shape[2:3], dtype=bool)
+        for i, sl in enumerate(slots):
+            if sl < 0:
+                continue
+            b, o = int(sl) // B, int(sl) % B
+            written[b, o] = True
+            assert np.array_equal(wl.bits_view(kc[b, :, o, :]), wl.bits_view(st.key[i]))
+            assert np.array_equal(wl.bits_view(vc[b, :, o, :]), wl.bits_view(st.value[i]))
+        keep = ~written
+        assert np.array_equal(wl.bits_view(kc).transpose(0, 2, 1, 3)[keep], wl.bits_view(case.k_cache).transpose(0, 2, 1, 3)[keep])
+        assert np.array_equal(wl.bits_view(vc).transpose(0, 2, 1, 3)[keep], wl.bits_view(case.v_cache).transpose(0, 2, 1, 3)[keep])
+        # Read back through the block table: the new tokens are the last ones.
+        n_new = 3
+        for s in range(case.num_seqs):
+            n = int(case.context_lens[s])
+            kv = orc.logical_kv(kc, case.block_tables[s], n)
+            for r in range(n_new):
+                i = s * n_new + r
+                if slots[i] < 0:
+                    continue
+                assert np.array_equal(wl.bits_view(kv[:, n - n_new + r, :]), wl.bits_view(st.key[i]))
+
+
+def pin_cow(orc):
+    """Block copies: destination equals source bit-for-bit, other blocks are
+    untouched, reading through a copy gives the same attention as through the
+    original, and a write into one sample's block does not reach the others."""
+    case = wl.config4(block_size=4, num_prompts=3, samples=4, prompt_len=10, num_heads=2, head_dim=8, pool_tokens=4096)
+    ap0, cp, ap1 = case.steps
+    kc, vc = orc.reshape_and_cache(ap0.key, ap0.value, case.k_cache, case.v_cache, ap0.slot_mapping)
+    kc2, vc2 = orc.copy_blocks(kc, vc, cp.pairs)
+    assert cp.pairs.shape == (9, 2)
+    moved = np.zeros(case.num_blocks, dtype=bool)
+    for src, dst in cp.pairs:
+        moved[dst] = True
+        assert np.array_equal(wl.bits_view(kc2[dst]), wl.bits_view(kc[src]))
+        assert np.array_equal(wl.bits_view(vc2[dst]), wl.bits_view(vc[src]))
+    assert np.array_equal(wl.bits_view(kc2[~moved]), wl.bits_view(kc[~moved]))
+    assert np.array_equal(wl.bits_view(vc2[~moved]), wl.bits_view(vc[~moved]))
+    # Before any suffix write, every sample (copy or original) sees the prompt.
+    pre_ctx = np.full(case.num_seqs, 10, dtype=np.int32)
+    fork_out = orc.paged_decode(case.q, kc2, vc2, case.block_tables, pre_ctx, case.scale, case.dtype)
+    orig_bt = case.block_tables.copy()
+    for g in range(3):
+        orig_bt[4 * g : 4 * g + 4] = case.block_tables[4 * g + 3]
+    base_out = orc.paged_decode(case.q, kc2, vc2, orig_bt, pre_ctx, case.scale, case.dtype)
+    assert np.array_equal(fork_out, base_out)
+    # After the suffix writes, samples 0..2 still read the unchanged prompt
+    # tokens; sample 3 wrote into the original last block in place.
+    kc3, vc3 = orc.reshape_and_cache(ap1.key, ap1.value, kc2, vc2, ap1.slot_mapping)
+    for g in range(3):
+        last = 10 // 4
+        orig = case.block_tables[4 * g + 3, last]
+        for i in range(3):
+            mine = case.block_tables[4 * g + i, last]
+            assert mine != orig
+            for o in range(10 % 4):
+                assert np.array_equal(wl.bits_view(kc3[mine, :, o]), wl.bits_view(kc[orig, :, o]))
+    out = orc.paged_decode(case.q, kc3, vc3, case.block_tables, case.context_lens, case.scale, case.dtype)
+    ref = brute_decode(case.q, kc3, vc3, case.block_tables, case.context_lens, case.scale, case.dtype)
+    assert np.abs(out - ref).max() <= 1e-12
+
+
+def pin_split_merge(orc):
+    """Merging the partials of any split of the context reproduces the
+    unsplit attention, and one slice's o / l is its own attention."""
+    rng = np.random.default_rng(16)
+    for n in (1, 5, 64, 333):
+        q = rng.standard_normal(16)
+        K = rng.standard_normal((n, 16)) * 2
+        V = rng.standard_normal((n, 16))
+        full = orc.attention(q, K, V, 0.3)
+        # Independent reference: softmax with math.fsum.
+        sc = [0.3 * math.fsum(q * K[t]) for t in range(n)]
+        mx = max(sc)
+        e = [math.exp(x - mx) for x in sc]
+        ref = np.array([math.fsum(e[t] * V[t, d] for t in range(n)) for d in range(16)]) / math.fsum(e)
+        assert np.abs(full - ref).max() <= 1e-13
+        for _ in range(3):
+            cuts = sorted(set(rng.integers(1, n, size=min(4, max(0, n - 1))).tolist())) if n > 1 else []
+            bounds = [0] + cuts + [n]
+            parts = [orc.partial_attention(q, K[a:b], V[a:b], 0.3) for a, b in zip(bounds[:-1], bounds[1:])]
+            assert np.abs(orc.merge_partials(parts) - ref).max() <= 1e-13
+            m, l, o = parts[0]
+            a, b = bounds[0], bounds[1]
+            assert np.abs(o / l - orc.attention(q, K[a:b], V[a:b], 0.3)).max() <= 1e-13
+        # A slice whose scores are far below the others contributes ~nothing.
+        parts = [orc.partial_attention(q, K, V, 0.3), (-1e4, 1.0, np.full(16, 7.0))]
+        assert np.abs(orc.merge_partials(parts) - ref).max() <= 1e-13
+
+
+ALL_PINS = [
+    pin_widen,
+    pin_bruteforce,
+    pin_library_attention,
+    pin_permutation,
+    pin_single_token,
+    pin_closed_forms,
+    pin_page_layouts,
+    pin_append,
+    pin_cow,
+    pin_split_merge,
+]

@@ -1,0 +1,129 @@
+"""Planted mistakes in the oracle are caught by the pins.
+
+Each mutant replaces one oracle function (on the CPU, inside this process
+only) with a plausible wrong version: a dropped term, a flipped sign, a
+wrong index or a transposed operand.  The test passes only if at least one
+pin of ``oracle_pins.ALL_PINS`` rejects the mutant, which shows the pins are
+strong enough to catch that class of mistake in the real oracle.
+"""
+import numpy as np
+import pytest
+
+import oracle.paged_attention as opa
+from oracle_pins import ALL_PINS
+
+_real = {name: getattr(opa, name) for name in dir(opa) if not name.startswith("_")}
+
+
+def _attention_no_scale(q, K, V, scale):
+    return _real["attention"](q, K, V, 1.0)
+
+
+def _attention_flipped(q, K, V, scale):
+    s = scale * (K @ q)
+    w = np.exp(s.max() - s)
+    return (w / w.sum()) @ V
+
+
+def _attention_unnormalised(q, K, V, scale):
+    s = scale * (K @ q)
+    return np.exp(s - s.max()) @ V
+
+
+def _attention_weights_on_k(q, K, V, scale):
+    s = scale * (K @ q)
+    w = np.exp(s - s.max())
+    return (w / w.sum()) @ K
+
+
+def _logical_kv_no_transpose(cache, table_row, ctx):
+    _, H, B, D = cache.shape
+    nb = _real["blocks_held"](ctx, B)
+    blocks = cache[np.asarray(table_row[:nb], dtype=np.int64)]
+    return blocks.reshape(H, nb * B, D)[:, :ctx, :] if nb else blocks.reshape(H, 0, D)
+
+
+def _logical_kv_reversed(cache, table_row, ctx):
+    _, H, B, D = cache.shape
+    nb = _real["blocks_held"](ctx, B)
+    rev = np.asarray(table_row[:nb])[::-1]
+    return _real["logical_kv"](cache, np.concatenate([rev, table_row[nb:]]), ctx)
+
+
+def _logical_kv_drop_last(cache, table_row, ctx):
+    full = _real["logical_kv"](cache, table_row, ctx)
+    return full[:, : max(1, ctx - 1), :]
+
+
+def _blocks_floor(n, B):
+    return int(n) // int(B)
+
+
+def _widen_bf16_wrong(a, dtype):
+    if dtype == "bf16":
+        return (np.asarray(a).astype(np.uint32) << np.uint32(8)).view(np.float32).astype(np.float64)
+    return _real["widen"](a, dtype)
+
+
+def _reshape_swapped(key, value, k_cache, v_cache, slot_mapping):
+    kc, vc = k_cache.copy(), v_cache.copy()
+    B = kc.shape[2]
+    for i, slot in enumerate(slot_mapping):
+        if slot < 0:
+            continue
+        off, b = divmod(int(slot), B)
+        if off < B and b < kc.shape[0]:
+            kc[b, :, off, :] = key[i]
+            vc[b, :, off, :] = value[i]
+    return kc, vc
+
+
+def _copy_k_only(k_cache, v_cache, pairs):
+    kc, _ = _real["copy_blocks"](k_cache, v_cache, pairs)
+    return kc, v_cache.copy()
+
+
+def _merge_no_rescale(parts):
+    return sum(o for _, _, o in parts) / sum(l for _, l, _ in parts)
+
+
+def _decode_wrong_head(q, k_cache, v_cache, block_tables, context_lens, scale, dtype):
+    out = _real["paged_decode"](q, k_cache, v_cache, block_tables, context_lens, scale, dtype)
+    return out[:, ::-1, :].copy()
+
+
+def _partial_no_max(q, K, V, scale):
+    s = scale * (K @ q)
+    w = np.exp(s - s.min())
+    return s.max(), w.sum(), w @ V
+
+
+MUTANTS = {
+    "attention drops the scale": ("attention", _attention_no_scale),
+    "softmax exponent sign flipped": ("attention", _attention_flipped),
+    "softmax not normalised": ("attention", _attention_unnormalised),
+    "weights applied to K instead of V": ("attention", _attention_weights_on_k),
+    "block layout not transposed": ("logical_kv", _logical_kv_no_transpose),
+    "block table walked backwards": ("logical_kv", _logical_kv_reversed),
+    "last context token dropped": ("logical_kv", _logical_kv_drop_last),
+    "blocks held rounds down": ("blocks_held", _blocks_floor),
+    "bf16 widened with the wrong shift": ("widen", _widen_bf16_wrong),
+    "slot split into (offset, block)": ("reshape_and_cache", _reshape_swapped),
+    "block copy skips V": ("copy_blocks", _copy_k_only),
+    "partials merged without rescaling": ("merge_partials", _merge_no_rescale),
+    "heads transposed in the output": ("paged_decode", _decode_wrong_head),
+    "partial stats use the wrong reference": ("partial_attention", _partial_no_max),
+}
+
+
+@pytest.mark.parametrize("name", list(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(opa, attr, fn)
+    failures = []
+    for pin in ALL_PINS:
+        try:
+            pin(opa)
+        except Exception as e:  # a pin rejecting the mutant, by assertion or otherwise
+            failures.append((pin.__name__, type(e).__name__))
+    assert failures, f"no pin caught the planted mistake: {name}"

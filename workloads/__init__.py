@@ -1,0 +1,24 @@
+"""Seeded synthetic inputs for paged decode attention.
+
+Shared by the CPU oracle tests and the GPU path's tests and benchmark.  It
+holds input generation and host-side block bookkeeping only: no step of the
+attention, cache-write or block-copy computation lives here.
+"""
+from .blockpool import BlockPool, PoolExhausted, SeqBlocks, append_tokens, cow_last_block, fork, tables_array
+from .cases import (
+    CONFIG_NAMES,
+    AppendStep,
+    Case,
+    CopyStep,
+    config,
+    config1,
+    config2,
+    config3,
+    config3_lengths,
+    config4,
+    config5,
+    normal_storage,
+    random_case,
+)
+from .rng import normal_f32
+from .storage import CANARY_BITS, DTYPES, ELEM_BYTES, NP_BITS, NP_STORAGE, bits_view, canary_fill, f32_to_bf16_bits, to_storage

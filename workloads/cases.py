@@ -1,0 +1,325 @@
+"""Seeded synthetic workloads for paged decode attention.
+
+Each ``Case`` holds, in storage encoding (see ``storage.py``):
+
+* ``q``            [S, H, D]      one query token per sequence
+* ``k_cache``      [N, H, B, D]   physical key blocks (state before ``steps``)
+* ``v_cache``      [N, H, B, D]   physical value blocks
+* ``block_tables`` int32 [S, W]   logical -> physical block, padded with -1
+* ``context_lens`` int32 [S]      tokens each query attends to (after steps)
+* ``steps``        cache updates to apply, in order, before the decode:
+  ``AppendStep`` (new K/V rows written at slot-mapped positions) and
+  ``CopyStep`` (copy-on-write block duplication).
+
+Pool slots that hold no valid token carry NaN canaries.  The recipes follow
+the workload shapes of the PagedAttention pages: LLaMA-7B / OPT-13B /
+OPT-175B-shaped decode layers, chat-like length mixes standing in for the
+ShareGPT traces (which are not available), and parallel sampling with a
+shared prompt.  No attention arithmetic happens here.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import List, Optional, Sequence, Union
+
+import numpy as np
+
+from .blockpool import BlockPool, SeqBlocks, append_tokens, cow_last_block, fork, tables_array
+from .rng import normal_encoded
+from .storage import NP_STORAGE, canary_fill, to_storage
+
+BASE_SEED = 322
+
+
+@dataclass
+class AppendStep:
+    key: np.ndarray  # [T, H, D] storage
+    value: np.ndarray  # [T, H, D] storage
+    slot_mapping: np.ndarray  # int64 [T]
+
+
+@dataclass
+class CopyStep:
+    pairs: np.ndarray  # int64 [n, 2] of (src, dst)
+
+
+Step = Union[AppendStep, CopyStep]
+
+
+@dataclass
+class Case:
+    name: str
+    dtype: str
+    num_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    q: np.ndarray
+    k_cache: np.ndarray
+    v_cache: np.ndarray
+    block_tables: np.ndarray
+    context_lens: np.ndarray
+    scale: float
+    steps: List[Step] = field(default_factory=list)
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def max_context_len(self) -> int:
+        return int(self.context_lens.max()) if self.context_lens.size else 0
+
+    @property
+    def elem_bytes(self) -> int:
+        return int(self.q.dtype.itemsize)
+
+
+def normal_storage(seed: int, tag: str, shape, dtype: str) -> np.ndarray:
+    n = int(np.prod(shape))
+    return normal_encoded(seed, tag, n, NP_STORAGE[dtype], lambda x: to_storage(x, dtype)).reshape(shape)
+
+
+def _fill_history(cache: np.ndarray, seqs: Sequence[SeqBlocks], hist: Sequence[int], seed: int, tag: str, dtype: str) -> None:
+    """Write N(0, 1) values into the first ``hist[i]`` token slots of every sequence.
+
+    Full blocks are filled in chunks of whole blocks; each sequence's final
+    partially filled block gets only its filled slots, the rest keep their
+    canaries.  Values are drawn per physical block in allocation order.
+    """
+    _, H, B, D = cache.shape
+    full: List[int] = []
+    partial: List[tuple] = []
+    for s, n in zip(seqs, hist):
+        nfull, rem = divmod(int(n), B)
+        full.extend(s.table[:nfull])
+        if rem:
+            partial.append((s.table[nfull], rem))
+    chunk = max(1, (1 << 26) // (H * B * D))
+    for c0 in range(0, len(full), chunk):
+        ids = np.asarray(full[c0 : c0 + chunk], dtype=np.int64)
+        cache[ids] = normal_storage(seed, f"{tag}/full/{c0}", (len(ids), H, B, D), dtype)
+    if partial:
+        total = sum(r for _, r in partial)
+        vals = normal_storage(seed, f"{tag}/partial", (H, total, D), dtype)
+        o = 0
+        for b, r in partial:
+            cache[b, :, :r, :] = vals[:, o : o + r, :]
+            o += r
+
+
+def _paged_case(name, dtype, H, D, B, N, ctx, seed, perm, n_append: int, scale=None) -> Case:
+    """Sequences with ``ctx[i] - n_append`` history tokens in a permuted pool and
+    ``n_append`` new tokens per sequence written by an append step."""
+    pool = BlockPool(N, B, perm)
+    seqs = [SeqBlocks() for _ in ctx]
+    hist = [int(c) - n_append for c in ctx]
+    assert min(hist) >= 0
+    for s, h in zip(seqs, hist):
+        append_tokens(pool, s, h)
+    k_cache = canary_fill((N, H, B, D), dtype)
+    v_cache = canary_fill((N, H, B, D), dtype)
+    _fill_history(k_cache, seqs, hist, seed, "k", dtype)
+    _fill_history(v_cache, seqs, hist, seed, "v", dtype)
+    steps: List[Step] = []
+    if n_append:
+        slots: List[int] = []
+        for s in seqs:
+            sl, pairs = append_tokens(pool, s, n_append)
+            assert not pairs
+            slots.extend(sl)
+        T = len(slots)
+        steps.append(
+            AppendStep(
+                normal_storage(seed, "k_new", (T, H, D), dtype),
+                normal_storage(seed, "v_new", (T, H, D), dtype),
+                np.asarray(slots, dtype=np.int64),
+            )
+        )
+    q = normal_storage(seed, "q", (len(ctx), H, D), dtype)
+    return Case(
+        name=name,
+        dtype=dtype,
+        num_heads=H,
+        head_dim=D,
+        block_size=B,
+        num_blocks=N,
+        q=q,
+        k_cache=k_cache,
+        v_cache=v_cache,
+        block_tables=tables_array(seqs),
+        context_lens=np.asarray(ctx, dtype=np.int32),
+        scale=(1.0 / math.sqrt(D)) if scale is None else scale,
+        steps=steps,
+        meta={"blocks_used": pool.used},
+    )
+
+
+# --------------------------------------------------------------------------
+# The five workload configurations.
+# --------------------------------------------------------------------------
+
+CONFIG_NAMES = {
+    1: "tiny-f32: 3 seqs ctx 5/16/37, H=1, D=8, B=4",
+    2: "llama7b-decode: 64 seqs ctx U[128,2048], H=32, D=128, f16, B=16",
+    3: "opt13b-decode: 256 seqs lognormal(300, 0.9) ctx, H=40, D=128, f16, B=16, +1 appended token",
+    4: "parallel-sampling-cow: 64 prompts x 4 samples, prompt 500, suffix U[0,256], H=40, D=128, f16",
+    5: "opt175b-decode: 128 seqs ctx U[1024,2048], H=96, D=128, bf16, B=16",
+}
+
+
+def config1() -> Case:
+    seed = BASE_SEED + 1
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(16)
+    return _paged_case("config1", "f32", 1, 8, 4, 16, [5, 16, 37], seed, perm, 0, scale=1.0 / math.sqrt(8.0))
+
+
+def config2(num_seqs: int = 64) -> Case:
+    seed = BASE_SEED + 2
+    rng = np.random.default_rng(seed)
+    ctx = rng.integers(128, 2049, 64)[:num_seqs]
+    perm = rng.permutation(8192)
+    return _paged_case("config2", "f16", 32, 128, 16, 8192, ctx, seed, perm, 0)
+
+
+def config3_lengths() -> np.ndarray:
+    rng = np.random.default_rng(BASE_SEED + 3)
+    return np.clip(np.round(rng.lognormal(math.log(300.0), 0.9, 256)), 16, 2048).astype(np.int64)
+
+
+def config3() -> Case:
+    seed = BASE_SEED + 3
+    ctx = config3_lengths()
+    rng = np.random.default_rng([seed, 1])
+    perm = rng.permutation(16384)
+    return _paged_case("config3", "f16", 40, 128, 16, 16384, ctx, seed, perm, 1)
+
+
+def config5(num_heads: int = 96) -> Case:
+    seed = BASE_SEED + 5
+    rng = np.random.default_rng(seed)
+    ctx = rng.integers(1024, 2049, 128)
+    perm = rng.permutation(16384)
+    return _paged_case("config5", "bf16", num_heads, 128, 16, 16384, ctx, seed, perm, 0)
+
+
+def config4(
+    block_size: int = 16,
+    num_prompts: int = 64,
+    samples: int = 4,
+    prompt_len: int = 500,
+    num_heads: int = 40,
+    head_dim: int = 128,
+    pool_tokens: int = 262144,
+) -> Case:
+    """Parallel sampling with copy-on-write of the shared partial prompt block.
+
+    Order of cache updates: the prompt K/V of every prompt is appended once;
+    each prompt forks into ``samples`` sequences that share all prompt blocks;
+    samples 0..n-2 take private copies of the partially filled last prompt
+    block (one batched block copy), sample n-1 keeps the original; each sample
+    then appends its own suffix tokens; decode attends to prompt + suffix.
+    """
+    seed = BASE_SEED + 4
+    D, dtype, B = head_dim, "f16", block_size
+    H = num_heads
+    rng = np.random.default_rng(seed)
+    suffix = rng.integers(0, 257, (64, 4))[:num_prompts, :samples]
+    N = pool_tokens // B
+    perm = np.random.default_rng([seed, B]).permutation(N)
+    pool = BlockPool(N, B, perm)
+    prompts = [SeqBlocks() for _ in range(num_prompts)]
+    prompt_slots: List[int] = []
+    for p in prompts:
+        sl, pairs = append_tokens(pool, p, prompt_len)
+        assert not pairs
+        prompt_slots.extend(sl)
+    prompt_blocks = pool.used
+    kids: List[SeqBlocks] = []
+    pairs: List[tuple] = []
+    for p in prompts:
+        ks = fork(pool, p, samples)
+        for k in ks[:-1]:
+            pairs.extend(cow_last_block(pool, k))
+        kids.extend(ks)
+    suffix_slots: List[int] = []
+    for i, k in enumerate(kids):
+        sl, pr = append_tokens(pool, k, int(suffix.reshape(-1)[i]))
+        assert not pr  # the only shared block was copied at the fork
+        suffix_slots.extend(sl)
+    ctx = np.asarray([k.length for k in kids], dtype=np.int32)
+    no_share = sum(math.ceil(int(c) / B) for c in ctx)
+    T0, T1 = len(prompt_slots), len(suffix_slots)
+    steps: List[Step] = [
+        AppendStep(
+            normal_storage(seed, f"kp/{B}", (T0, H, D), dtype),
+            normal_storage(seed, f"vp/{B}", (T0, H, D), dtype),
+            np.asarray(prompt_slots, dtype=np.int64),
+        ),
+        CopyStep(np.asarray(pairs, dtype=np.int64).reshape(-1, 2)),
+        AppendStep(
+            normal_storage(seed, f"ks/{B}", (T1, H, D), dtype),
+            normal_storage(seed, f"vs/{B}", (T1, H, D), dtype),
+            np.asarray(suffix_slots, dtype=np.int64),
+        ),
+    ]
+    return Case(
+        name=f"config4-B{B}",
+        dtype=dtype,
+        num_heads=H,
+        head_dim=D,
+        block_size=B,
+        num_blocks=N,
+        q=normal_storage(seed, f"q/{B}", (len(kids), H, D), dtype),
+        k_cache=canary_fill((N, H, B, D), dtype),
+        v_cache=canary_fill((N, H, B, D), dtype),
+        block_tables=tables_array(kids),
+        context_lens=ctx,
+        scale=1.0 / math.sqrt(D),
+        steps=steps,
+        meta={
+            "blocks_used": pool.used,
+            "prompt_blocks": prompt_blocks,
+            "blocks_without_sharing": no_share,
+            "kv_memory_saved": 1.0 - pool.used / no_share,
+            "samples": samples,
+        },
+    )
+
+
+def config(n: int, **kw) -> Case:
+    return {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}[n](**kw)
+
+
+# --------------------------------------------------------------------------
+# Random small cases for parity sweeps.
+# --------------------------------------------------------------------------
+
+
+def random_case(
+    seed: int,
+    num_seqs: int,
+    num_heads: int,
+    head_dim: int,
+    block_size: int,
+    dtype: str,
+    ctx: Optional[Sequence[int]] = None,
+    ctx_range=(1, 64),
+    spare_blocks: int = 3,
+    n_append: int = 0,
+    scale: Optional[float] = None,
+) -> Case:
+    """A small paged case with a seeded random physical placement."""
+    rng = np.random.default_rng([BASE_SEED, seed])
+    if ctx is None:
+        ctx = rng.integers(ctx_range[0], ctx_range[1] + 1, num_seqs)
+    ctx = [int(c) for c in ctx]
+    need = sum(max(0, math.ceil(c / block_size)) for c in ctx)
+    N = need + spare_blocks
+    perm = rng.permutation(N)
+    return _paged_case(
+        f"random-{seed}", dtype, num_heads, head_dim, block_size, N, ctx, seed * 7919 + 17, perm, n_append, scale=scale
+    )
