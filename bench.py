@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""Paged decode attention benchmark on one MI355X.
+
+One step = one serving decode step of a whole batch through the hot path:
+``pa_reshape_and_cache`` stores every sequence's newest K/V row into its
+slot, then ``pa_decode`` attends each sequence's query over its paged
+context (partition kernel, plus the merge kernel for contexts longer than a
+partition).  The default workload is the LLaMA-7B-shaped decode layer: 64
+sequences, context lengths uniform in [128, 2048], 32 heads, head_dim 128,
+fp16, 16-token blocks in an 8192-block pool with random physical placement.
+The workload has no shared blocks, so copy-on-write has nothing to copy in
+the step; ``pa_copy_blocks`` is timed beside it on a batch of block pairs.
+
+Reported (one JSON line on stdout):
+  value       algorithmic bytes of the step / step time (GB/s), with
+              bytes = 2*e*H*D*sum(ctx) (K and V) + 2*S*H*D*e (q, out)
+                      + 4*sum(ceil(ctx/B)) (block ids) + 4*S (lengths)
+                      + 4*T*H*D*e + 8*T (append: read k/v, write k/v, slots)
+  roofline    pa_decode alone: its algorithmic bytes / its event-timed
+              duration, against the 8 TB/s HBM3E peak
+  cpu_baseline the float64 CPU oracle on the same batch, on this host
+
+Inputs are resident in HBM before timing.  Consecutive steps alternate
+between ``--rotate`` independent copies of the KV pools so no step finds the
+previous step's blocks in the 256 MB last-level cache.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, vendor figure
+METRIC = "paged decode attention: KV-read GB/s and % of HBM peak; decode tokens/s"
+WORKLOADS = {
+    2: "llama7b-decode-layer: 64 seqs, ctx U[128,2048], H=32, D=128, f16, B=16, 8192-block pool",
+    3: "opt13b-decode-layer: 256 seqs, ctx lognormal(median 300, sigma 0.9) in [16,2048], H=40, D=128, f16, B=16",
+    5: "opt175b-decode-layer: 128 seqs, ctx U[1024,2048], H=96, D=128, bf16, B=16, 16384-block pool",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, choices=sorted(WORKLOADS))
+    ap.add_argument("--partition", type=int, default=0, help="KV partition tokens (0 = library default)")
+    ap.add_argument("--rotate", type=int, default=2, help="independent pool copies cycled across steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle baseline")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def make_case(cfg):
+    import workloads as wl
+
+    if cfg == 2:
+        return wl.config2(n_append=1)
+    if cfg == 3:
+        return wl.config3()
+    return wl.config5(n_append=1)
+
+
+def algorithmic_bytes(case):
+    e = case.elem_bytes
+    S, H, D, B = case.num_seqs, case.num_heads, case.head_dim, case.block_size
+    ctx = case.context_lens.astype(np.int64)
+    decode = 2 * e * H * D * int(ctx.sum()) + 2 * S * H * D * e + 4 * int(np.ceil(ctx / B).sum()) + 4 * S
+    T = sum(st.slot_mapping.size for st in case.steps)
+    append = 4 * T * H * D * e + 8 * T
+    return decode, append
+
+
+def traffic_from_profiles(kernel_src_sha):
+    """HBM bytes per decode launch from the committed counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "decode_llama7b_counters.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256") != kernel_src_sha:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def kernel_source_sha():
+    import hashlib
+
+    root = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_cache_322_amd", "csrc")
+    h = hashlib.sha256()
+    for name in ("pa_decode.hip", "pa_device.h", "pa_internal.h"):
+        h.update(open(os.path.join(root, name), "rb").read())
+    return h.hexdigest()
+
+
+def cpu_baseline(case, target_s, step_bytes):
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    st = case.steps[0]
+    best, total, reps = math.inf, 0.0, 0
+    while reps < 3 and (reps == 0 or total < target_s):
+        t0 = time.perf_counter()
+        kc, vc = oracle.reshape_and_cache(st.key, st.value, case.k_cache, case.v_cache, st.slot_mapping)
+        oracle.paged_decode(case.q, kc, vc, case.block_tables, case.context_lens, case.scale, case.dtype)
+        dt = time.perf_counter() - t0
+        best, total, reps = min(best, dt), total + dt, reps + 1
+        del kc, vc
+    return {
+        "value": round(step_bytes / best / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": f"whole batch (all {case.num_seqs} sequences, append + decode), best of {reps} "
+                  f"({best:.2f} s each, float64 numpy; host has {len(os.sched_getaffinity(0))} cpus)",
+        "seconds_per_step": round(best, 4),
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): the paged "
+              "decode path has no cross-GPU step; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import paged_kv_cache_322_amd as pa
+    from workloads import to_storage  # noqa: F401  (imported for side-effect-free check)
+
+    dev = torch.device("cuda:0")
+    log(f"building workload config {args.config}")
+    case = make_case(args.config)
+    dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[case.dtype]
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if case.dtype == "bf16" and a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    S, H, D, B = case.num_seqs, case.num_heads, case.head_dim, case.block_size
+    st = case.steps[0]
+    q, bt, ctx = up(case.q), up(case.block_tables), up(case.context_lens)
+    k_new, v_new, slots = up(st.key), up(st.value), up(st.slot_mapping)
+    pools = [(up(case.k_cache), up(case.v_cache)) for _ in range(max(1, args.rotate))]
+    out = torch.empty_like(q)
+    max_ctx = case.max_context_len
+    ws_bytes = pa.decode_workspace_size(S, H, D, max_ctx, args.partition)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        kc, vc = pools[i % len(pools)]
+        if ev is not None:
+            ev[0].record()
+        pa.reshape_and_cache(k_new, v_new, kc, vc, slots)
+        if ev is not None:
+            ev[1].record()
+        pa.decode(out, q, kc, vc, bt, ctx, case.scale, max_ctx, partition_size=args.partition, workspace=ws)
+        if ev is not None:
+            ev[2].record()
+
+    log(f"warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        step(i, evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    append_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    decode_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    log(f"timed {args.steps} steps: {ms_step*1e3:.1f} us/step (append {append_ms*1e3:.1f} us, decode {decode_ms*1e3:.1f} us)")
+
+    # Copy-on-write block copies, timed beside the step on the first pool:
+    # a fork-sized batch (192 pairs) and a large batch used as the HBM copy probe.
+    used = np.unique(case.block_tables[case.block_tables >= 0])
+    free = np.setdiff1d(np.arange(case.num_blocks), used)
+    block_bytes = H * B * D * case.elem_bytes
+
+    def time_copies(n, reps=20):
+        n = int(min(n, used.size, free.size))
+        pairs = up(np.stack([used[:n], free[:n]], axis=1).astype(np.int64))
+        kc, vc = pools[0]
+        pa.copy_blocks(kc, vc, pairs)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            pa.copy_blocks(kc, vc, pairs)
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) / reps * 1e3
+        moved = 2 * 2 * n * block_bytes  # K and V, read and write
+        return {"pairs": n, "us": round(us, 2), "GB/s": round(moved / us / 1e3, 1)}
+
+    cow = time_copies(192)
+    probe = time_copies(4096)
+    log(f"copy_blocks: {cow}; copy probe: {probe}")
+
+    decode_bytes, append_bytes = algorithmic_bytes(case)
+    step_bytes = decode_bytes + append_bytes
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    achieved = decode_bytes / (decode_ms * 1e-3) / 1e9
+    traffic = traffic_from_profiles(kernel_source_sha())
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": case.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": WORKLOADS[args.config],
+            "step": "reshape_and_cache (1 new token per sequence) + pa_decode",
+            "num_seqs": S,
+            "num_heads": H,
+            "head_dim": D,
+            "block_size": B,
+            "num_blocks": case.num_blocks,
+            "sum_context_len": int(case.context_lens.sum()),
+            "max_context_len": max_ctx,
+            "partition_tokens": args.partition or pa.DEFAULT_PARTITION_TOKENS,
+            "pool_copies_rotated": len(pools),
+        },
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "decode_tokens_per_s": round(S / (ms_step * 1e-3), 1),
+        "step_bytes": int(step_bytes),
+        "roofline": {
+            "kernel": "pa_decode (partition kernel + merge kernel), event-timed",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": int(decode_bytes),
+            "avg_launch_us": round(decode_ms * 1e3, 2),
+        },
+        "append_us": round(append_ms * 1e3, 2),
+        "copy_blocks": cow,
+        "hbm_copy_probe": probe,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on the same batch")
+        result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds, step_bytes)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,163 @@
+/*
+ * pa.h - C ABI of libpa, paged decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * Three operations on a KV cache that is cut into fixed-size physical blocks
+ * of B tokens and addressed through per-sequence block tables:
+ *
+ *   pa_decode             single-query (decode) attention over the blocks
+ *   pa_reshape_and_cache  write new tokens' K/V rows into slot-mapped blocks
+ *   pa_copy_blocks        copy-on-write duplication of whole blocks
+ *
+ * Memory layout (every array dense, row-major, no padding):
+ *   query, out          [num_seqs, num_heads, head_dim]              element type `dtype`
+ *   k_cache, v_cache    [num_blocks, num_heads, block_size, head_dim] element type `dtype`
+ *   block_tables        int32 [num_seqs, max_blocks_per_seq]; entry j of row s
+ *                       is the physical block holding tokens j*B .. j*B+B-1 of
+ *                       sequence s; entries at j >= ceil(ctx_s / B) are never read
+ *   context_lens        int32 [num_seqs]
+ *   slot_mapping        int64 [num_tokens]; slot = block * B + offset, < 0 = skip
+ *   block_pairs         int64 [num_pairs, 2]; (src, dst) physical block ids
+ * bf16 is the upper half of an IEEE binary32; f16 is IEEE binary16.
+ *
+ * Ownership and execution: every pointer argument other than the scalars is
+ * device memory owned by the caller (query, caches, tables, lengths, slot
+ * mapping, pairs, out, workspace).  The library allocates nothing, frees
+ * nothing and never synchronises: each call validates its arguments on the
+ * host, enqueues its kernels on `stream` (a hipStream_t; NULL is the null
+ * stream) and returns.  The library keeps no global state, so calls are
+ * re-entrant; calls on one stream execute in order.
+ *
+ * Errors: the return value is a pa_status.  Argument errors are detected on
+ * the host before anything is enqueued.  PA_ERR_HIP reports a failed launch.
+ * Contents of device memory are the caller's contract and are not checked on
+ * the host (the kernels guard their own reads and writes, see each call).
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PA_F32 = 0,  /* IEEE binary32 */
+    PA_F16 = 1,  /* IEEE binary16 */
+    PA_BF16 = 2  /* bfloat16 */
+} pa_dtype;
+
+typedef enum {
+    PA_OK = 0,
+    PA_ERR_NULL = 1,        /* a required pointer is NULL */
+    PA_ERR_UNSUPPORTED = 2, /* dtype, head_dim or block_size outside the built kernels */
+    PA_ERR_INVALID = 3,     /* sizes, alignment, scale or workspace out of range */
+    PA_ERR_HIP = 4          /* the HIP runtime rejected a launch */
+} pa_status;
+
+/* Supported shapes: head_dim in {8, 16, 32, 64, 128, 256}; block_size a power
+ * of two in [1, 256]; num_seqs and num_heads at most 65535. */
+
+/*
+ * pa_decode_workspace_size - bytes of device scratch pa_decode needs.
+ *
+ * Long contexts are split into KV partitions of `partition_size` tokens (0
+ * selects the library default); each partition's unnormalised partial result
+ * goes to the workspace and a second kernel merges them.  Returns 0 when no
+ * sequence can span two partitions (then pa_decode accepts a NULL workspace),
+ * and 0 for invalid sizes.
+ */
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                int32_t max_context_len, int32_t partition_size);
+
+/*
+ * pa_decode - paged single-query attention.
+ *
+ * Defined by the page "PagedAttention - Efficient Memory Management for LLM
+ * Serving with vLLM" (irregular6612.github.io), section "Method": the KV cache
+ * is split into fixed-size blocks of B tokens, attention follows the block
+ * table to gather a sequence's non-contiguous blocks and evaluates
+ * softmax(Q K^T) V.  For every sequence s and head h:
+ *
+ *   out[s,h,:] = sum_t softmax_t( scale * <query[s,h,:], K_s[t,h,:]> ) * V_s[t,h,:]
+ *
+ * over t = 0 .. context_lens[s]-1, where token t of sequence s is stored in
+ * physical block block_tables[s][t / B] at offset t % B.  Arithmetic is fp32
+ * (fp32 accumulation of products of widened inputs); out is rounded to
+ * `dtype` with round-to-nearest-even.
+ *
+ *   out            [S, H, D] written
+ *   query          [S, H, D] read
+ *   k_cache, v_cache  [N, H, B, D] read
+ *   block_tables   int32 [S, max_blocks_per_seq] read
+ *   context_lens   int32 [S] read
+ *   max_context_len  host upper bound of context_lens (sizes the grid without
+ *                  a device-to-host copy); must be <= max_blocks_per_seq * B
+ *   num_blocks     N, the number of physical blocks in each cache
+ *   scale          finite softmax scale (1/sqrt(D) for standard attention)
+ *   partition_size tokens per KV partition, 0 = default (512)
+ *   workspace      device scratch of at least pa_decode_workspace_size(...)
+ *                  bytes, 4-byte aligned; contents need no initialisation
+ *
+ * query, out and both caches must be 16-byte aligned.  Device-side guards:
+ * a context length of 0 yields zeros; a context length below 0 or above
+ * max_context_len, or a needed block id outside [0, N), yields NaN for that
+ * (sequence, head) without reading outside the caches.
+ */
+int pa_decode(void* out, const void* query, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, const int32_t* context_lens,
+              int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t block_size,
+              int32_t max_blocks_per_seq, int32_t max_context_len, int64_t num_blocks,
+              float scale, int32_t dtype, int32_t partition_size,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_reshape_and_cache - store new tokens' keys and values in their slots.
+ *
+ * Page "LLM Inference 8: PagedAttention" (velog.io), section on how
+ * PagedAttention works: each new token's key and value go into the
+ * sequence's current physical block, and a fresh block is taken only when
+ * that block is full (the caller's allocator does this and encodes the
+ * result as the slot mapping).  For every i with slot = slot_mapping[i] >= 0:
+ *
+ *   k_cache[slot / B, h, slot % B, :] = key[i, h, :]    for every head h
+ *   v_cache[slot / B, h, slot % B, :] = value[i, h, :]
+ *
+ * A bit-exact copy (no arithmetic).  key, value [num_tokens, H, D] read;
+ * caches written in place.  key, value and the caches must be 16-byte
+ * aligned.  Slots must be distinct (duplicates race); a slot at or beyond
+ * num_blocks * B is skipped by the kernel.
+ */
+int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                         const int64_t* slot_mapping, int32_t num_tokens, int32_t num_heads,
+                         int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                         int32_t dtype, void* stream);
+
+/*
+ * pa_copy_blocks - copy-on-write block duplication.
+ *
+ * PagedAttention digest (irregular6612.github.io), section "Method": samples
+ * of parallel sampling or beam search share the prompt's physical blocks,
+ * and when a shared block is written at the branch point only that block is
+ * copied.  For every pair (src, dst) in block_pairs:
+ *
+ *   k_cache[dst] = k_cache[src];  v_cache[dst] = v_cache[src]
+ *
+ * whole blocks (all heads, slots and channels), bit-exact.  Destinations must
+ * be distinct and disjoint from the sources (otherwise the result depends on
+ * execution order); a pair with an id outside [0, num_blocks) is skipped by
+ * the kernel.  The caches must be 16-byte aligned.
+ */
+int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pairs, int32_t num_pairs,
+                   int32_t num_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                   int32_t dtype, void* stream);
+
+/* Human-readable name of a pa_status value (static storage; never NULL). */
+const char* pa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

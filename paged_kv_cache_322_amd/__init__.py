@@ -1,0 +1,189 @@
+"""Paged decode attention for AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding over ``libpa.so`` (C ABI declared in ``include/pa.h``).
+The functions here only check tensor shapes and types, turn torch tensors
+into device pointers plus the current HIP stream, and call the library;
+every step of the computation runs in the library's HIP kernels.  PyTorch
+supplies device memory and streams only.
+
+If ``libpa.so`` has not been built, importing this package raises
+ImportError: there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "PagedAttentionError",
+    "LIB_PATH",
+    "lib",
+    "decode",
+    "decode_workspace_size",
+    "reshape_and_cache",
+    "copy_blocks",
+    "status_string",
+    "DEFAULT_PARTITION_TOKENS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
+DEFAULT_PARTITION_TOKENS = 512
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run `python -m paged_kv_cache_322_amd.build` "
+        "(or __graft_entry__.build()) first"
+    )
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+
+lib.pa_status_string.restype = ctypes.c_char_p
+lib.pa_status_string.argtypes = [ctypes.c_int]
+lib.pa_decode_workspace_size.restype = ctypes.c_size_t
+lib.pa_decode_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32]
+lib.pa_decode.restype = ctypes.c_int
+lib.pa_decode.argtypes = [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i64,
+                          ctypes.c_float, _i32, _i32, _p, ctypes.c_size_t, _p]
+lib.pa_reshape_and_cache.restype = ctypes.c_int
+lib.pa_reshape_and_cache.argtypes = [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i64, _i32, _p]
+lib.pa_copy_blocks.restype = ctypes.c_int
+lib.pa_copy_blocks.argtypes = [_p, _p, _p, _i32, _i32, _i32, _i32, _i64, _i32, _p]
+
+_DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+
+
+class PagedAttentionError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)}")
+        self.status = status
+
+
+def status_string(status: int) -> str:
+    return lib.pa_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise PagedAttentionError(status, what)
+
+
+def _stream_handle(device: torch.device, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, ndim=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+
+
+def _code(dtype: torch.dtype) -> int:
+    try:
+        return _DTYPE_CODE[dtype]
+    except KeyError:
+        raise TypeError(f"unsupported element type {dtype}; use float32, float16 or bfloat16") from None
+
+
+def decode_workspace_size(num_seqs: int, num_heads: int, head_dim: int, max_context_len: int,
+                          partition_size: int = 0) -> int:
+    """Bytes of scratch ``decode`` needs (0 if no sequence spans two partitions)."""
+    return int(lib.pa_decode_workspace_size(num_seqs, num_heads, head_dim, max_context_len, partition_size))
+
+
+def decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+           block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float, max_context_len: int,
+           partition_size: int = 0, workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Paged single-query attention (``pa_decode``); writes and returns ``out``.
+
+    out, query [S, H, D]; key_cache, value_cache [N, H, B, D]; block_tables
+    int32 [S, W]; context_lens int32 [S]; ``max_context_len`` a host bound on
+    context_lens.  ``workspace`` (uint8, >= decode_workspace_size bytes) is
+    allocated from torch's caching allocator when not given.
+    """
+    _dev(query, "query", ndim=3)
+    dt = query.dtype
+    _dev(out, "out", dt, 3)
+    _dev(key_cache, "key_cache", dt, 4)
+    _dev(value_cache, "value_cache", dt, 4)
+    _dev(block_tables, "block_tables", torch.int32, 2)
+    _dev(context_lens, "context_lens", torch.int32, 1)
+    S, H, D = query.shape
+    N, Hk, B, Dk = key_cache.shape
+    if tuple(out.shape) != (S, H, D) or tuple(value_cache.shape) != tuple(key_cache.shape):
+        raise ValueError("out/value_cache shapes do not match query/key_cache")
+    if Hk != H or Dk != D:
+        raise ValueError(f"key_cache heads/head_dim {Hk}/{Dk} != query {H}/{D}")
+    if block_tables.shape[0] != S or context_lens.shape[0] != S:
+        raise ValueError("block_tables / context_lens must have one row per sequence")
+    need = decode_workspace_size(S, H, D, max_context_len, partition_size)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+    ws_ptr, ws_bytes = 0, 0
+    if workspace is not None:
+        _dev(workspace, "workspace")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    st = lib.pa_decode(
+        out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+        block_tables.data_ptr(), context_lens.data_ptr(), S, H, D, B, block_tables.shape[1],
+        int(max_context_len), N, float(scale), _code(dt), int(partition_size), ws_ptr, ws_bytes,
+        _stream_handle(query.device, stream),
+    )
+    _check(st, "pa_decode")
+    return out
+
+
+def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
+                      value_cache: torch.Tensor, slot_mapping: torch.Tensor, stream=None) -> None:
+    """Write key/value [T, H, D] into the slots named by ``slot_mapping`` (int64 [T])."""
+    _dev(key, "key", ndim=3)
+    dt = key.dtype
+    _dev(value, "value", dt, 3)
+    _dev(key_cache, "key_cache", dt, 4)
+    _dev(value_cache, "value_cache", dt, 4)
+    _dev(slot_mapping, "slot_mapping", torch.int64, 1)
+    T, H, D = key.shape
+    N, Hk, B, Dk = key_cache.shape
+    if tuple(value.shape) != (T, H, D) or tuple(value_cache.shape) != tuple(key_cache.shape):
+        raise ValueError("value/value_cache shapes do not match key/key_cache")
+    if Hk != H or Dk != D or slot_mapping.shape[0] != T:
+        raise ValueError("key, caches and slot_mapping disagree on tokens/heads/head_dim")
+    st = lib.pa_reshape_and_cache(
+        key.data_ptr(), value.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+        slot_mapping.data_ptr(), T, H, D, B, N, _code(dt), _stream_handle(key.device, stream),
+    )
+    _check(st, "pa_reshape_and_cache")
+
+
+def copy_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor, block_pairs: torch.Tensor,
+                stream=None) -> None:
+    """Copy whole blocks: cache[dst] = cache[src] for each (src, dst) row of int64 ``block_pairs``."""
+    _dev(key_cache, "key_cache", ndim=4)
+    dt = key_cache.dtype
+    _dev(value_cache, "value_cache", dt, 4)
+    _dev(block_pairs, "block_pairs", torch.int64)
+    if block_pairs.numel() % 2:
+        raise ValueError("block_pairs must have shape [n, 2]")
+    N, H, B, D = key_cache.shape
+    if tuple(value_cache.shape) != tuple(key_cache.shape):
+        raise ValueError("value_cache shape differs from key_cache")
+    st = lib.pa_copy_blocks(
+        key_cache.data_ptr(), value_cache.data_ptr(), block_pairs.data_ptr(), block_pairs.numel() // 2,
+        H, D, B, N, _code(dt), _stream_handle(key_cache.device, stream),
+    )
+    _check(st, "pa_copy_blocks")

@@ -1,0 +1,145 @@
+// C ABI of libpa: host-side validation, launch geometry and workspace sizing.
+// Every check happens before anything is enqueued; nothing here allocates,
+// frees or synchronises.
+#include <math.h>
+
+#include "../../include/pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+bool supported_dtype(int32_t d) { return d == PA_F32 || d == PA_F16 || d == PA_BF16; }
+
+int elem_bytes(int32_t d) { return d == PA_F32 ? 4 : 2; }
+
+bool supported_head_dim(int32_t d) {
+    return d == 8 || d == 16 || d == 32 || d == 64 || d == 128 || d == 256;
+}
+
+bool supported_block_size(int32_t b) { return b >= 1 && b <= 256 && (b & (b - 1)) == 0; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int resolve_partition(int32_t partition_size) {
+    return partition_size == 0 ? pa::kDefaultPartitionTokens : partition_size;
+}
+
+int64_t parts_for(int32_t max_context_len, int part) {
+    return max_context_len <= 0 ? 1 : (static_cast<int64_t>(max_context_len) + part - 1) / part;
+}
+
+// Workspace bytes for the split path, or 0 when one partition always suffices.
+size_t workspace_bytes_for(int64_t num_seqs, int64_t num_heads, int64_t head_dim, int64_t parts) {
+    if (parts <= 1) return 0;
+    return static_cast<size_t>(num_seqs * num_heads * parts * (head_dim + 2)) * sizeof(float);
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(int status) {
+    switch (status) {
+        case PA_OK: return "PA_OK";
+        case PA_ERR_NULL: return "PA_ERR_NULL: a required pointer is NULL";
+        case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: dtype, head_dim or block_size not built";
+        case PA_ERR_INVALID: return "PA_ERR_INVALID: size, alignment, scale or workspace out of range";
+        case PA_ERR_HIP: return "PA_ERR_HIP: the HIP runtime rejected a launch";
+        default: return "PA_ERR_UNKNOWN";
+    }
+}
+
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                int32_t max_context_len, int32_t partition_size) {
+    if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || max_context_len < 0 || partition_size < 0)
+        return 0;
+    const int part = resolve_partition(partition_size);
+    return workspace_bytes_for(num_seqs, num_heads, head_dim, parts_for(max_context_len, part));
+}
+
+int pa_decode(void* out, const void* query, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+              int32_t num_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+              int32_t max_context_len, int64_t num_blocks, float scale, int32_t dtype,
+              int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!supported_dtype(dtype) || !supported_head_dim(head_dim) || !supported_block_size(block_size))
+        return PA_ERR_UNSUPPORTED;
+    if (num_seqs == 0) return PA_OK;  // nothing to read or write
+    if (!out || !query || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
+    if (num_seqs < 0 || num_seqs > 65535 || num_heads <= 0 || num_heads > 65535 ||
+        max_blocks_per_seq <= 0 || max_context_len < 0 || num_blocks <= 0 || partition_size < 0)
+        return PA_ERR_INVALID;
+    if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
+        return PA_ERR_INVALID;
+    if (!isfinite(scale)) return PA_ERR_INVALID;
+    if (!aligned16(out) || !aligned16(query) || !aligned16(k_cache) || !aligned16(v_cache))
+        return PA_ERR_INVALID;
+    const int part = resolve_partition(partition_size);
+    // A partition may start mid-block, so it touches at most ceil(P/B) + 1 blocks.
+    if ((static_cast<int64_t>(part) + block_size - 1) / block_size + 1 > pa::kMaxPartitionBlocks)
+        return PA_ERR_INVALID;
+    const int64_t parts = parts_for(max_context_len, part);
+    if (parts > 0x7FFFFFFF) return PA_ERR_INVALID;
+    const size_t need = workspace_bytes_for(num_seqs, num_heads, head_dim, parts);
+    if (need) {
+        if (!workspace) return PA_ERR_NULL;
+        if (workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 3u)) return PA_ERR_INVALID;
+    }
+
+    pa::DecodeArgs a;
+    a.out = out;
+    a.query = query;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.num_seqs = num_seqs;
+    a.num_heads = num_heads;
+    a.head_dim = head_dim;
+    a.block_size = block_size;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.max_context_len = max_context_len;
+    a.num_blocks = num_blocks;
+    a.scale = scale;
+    a.dtype = dtype;
+    a.part_tokens = part;
+    a.max_parts = static_cast<int>(parts);
+    a.workspace = need ? workspace : nullptr;
+    a.stream = static_cast<hipStream_t>(stream);
+    return hip_status(pa::launch_decode(a));
+}
+
+int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                         const int64_t* slot_mapping, int32_t num_tokens, int32_t num_heads,
+                         int32_t head_dim, int32_t block_size, int64_t num_blocks, int32_t dtype,
+                         void* stream) {
+    if (!supported_dtype(dtype) || !supported_head_dim(head_dim) || !supported_block_size(block_size))
+        return PA_ERR_UNSUPPORTED;
+    if (num_tokens < 0 || num_heads <= 0 || num_blocks <= 0) return PA_ERR_INVALID;
+    if (num_tokens == 0) return PA_OK;  // nothing to read or write
+    if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PA_ERR_NULL;
+    if (!aligned16(key) || !aligned16(value) || !aligned16(k_cache) || !aligned16(v_cache))
+        return PA_ERR_INVALID;
+    return hip_status(pa::launch_reshape_and_cache(
+        key, value, k_cache, v_cache, slot_mapping, num_tokens, num_heads,
+        head_dim * elem_bytes(dtype), block_size, num_blocks, static_cast<hipStream_t>(stream)));
+}
+
+int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pairs, int32_t num_pairs,
+                   int32_t num_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                   int32_t dtype, void* stream) {
+    if (!supported_dtype(dtype) || !supported_head_dim(head_dim) || !supported_block_size(block_size))
+        return PA_ERR_UNSUPPORTED;
+    if (num_pairs < 0 || num_pairs > 65535 || num_heads <= 0 || num_blocks <= 0) return PA_ERR_INVALID;
+    if (num_pairs == 0) return PA_OK;  // nothing to copy
+    if (!k_cache || !v_cache || !block_pairs) return PA_ERR_NULL;
+    if (!aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_INVALID;
+    const int64_t block_bytes =
+        static_cast<int64_t>(num_heads) * block_size * head_dim * elem_bytes(dtype);
+    return hip_status(pa::launch_copy_blocks(k_cache, v_cache, block_pairs, num_pairs, block_bytes,
+                                             num_blocks, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

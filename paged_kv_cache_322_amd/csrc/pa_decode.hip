@@ -1,0 +1,275 @@
+// Paged decode attention for gfx950.
+//
+// Operation (PagedAttention digest, irregular6612.github.io, section
+// "Method"): for each sequence s and head h, attention of the single query
+// q[s,h,:] over the sequence's context, whose K/V rows live in fixed-size
+// physical blocks found through the sequence's block table.
+//
+// Work decomposition.  The context of every (sequence, head) is cut into KV
+// partitions of P tokens; one workgroup of four wavefronts handles one
+// (partition, head, sequence).  Decode attention is a matrix-vector product:
+// each K and V byte is used once, so the kernel is bound by HBM bandwidth and
+// uses no matrix cores.  Inside a workgroup:
+//
+//   * the partition's physical block ids are staged in LDS once;
+//   * a wavefront processes U tokens per step.  A token's row of D elements
+//     is spread over LPR = D / (16 / elem) lanes, each lane loading 16 bytes,
+//     so one wave-wide load instruction covers 64 / LPR whole token rows and
+//     every lane issues NL loads of K and NL loads of V per step, all before
+//     using any of them;
+//   * q.k partial dots are summed across a row's lanes with DPP permutes, the
+//     running maximum is shared across rows, and each lane keeps its own
+//     running sum and fp32 accumulators for its slice of D (online softmax,
+//     exponentials taken base 2 with log2(e) folded into the query);
+//   * wavefronts interleave steps, then merge their (max, sum, accumulators)
+//     through LDS.
+//
+// A sequence that fits one partition has its output written directly.  For
+// longer ones each partition writes its unnormalised accumulator, its
+// maximum and its sum to the workspace and a second kernel merges them.
+#include <math.h>
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+
+template <class T, int D>
+struct DecodeShape {
+    static constexpr int VEC = kVec<T>;
+    static constexpr int LPR = D / VEC;         // lanes per token row
+    static constexpr int TPL = kWave / LPR;     // token rows per wave-wide load
+    static constexpr int NL = (16 / TPL) < 1 ? 1 : ((16 / TPL) > 8 ? 8 : (16 / TPL));
+    static constexpr int U = NL * TPL;          // tokens per wavefront step
+    static_assert(LPR >= 1 && LPR <= kWave && (kWave % LPR) == 0, "unsupported head_dim");
+};
+
+template <class T, int D>
+__global__ __launch_bounds__(kThreads) void decode_partition_kernel(
+    typename T::bits* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_m,
+    float* __restrict__ ws_l, const typename T::bits* __restrict__ q,
+    const typename T::bits* __restrict__ kc, const typename T::bits* __restrict__ vc,
+    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
+    int num_heads, int log2_bs, int max_blocks_per_seq, int max_context_len, int64_t num_blocks,
+    int part_tokens, int max_parts, float qscale) {
+    using Sh = DecodeShape<T, D>;
+    constexpr int VEC = Sh::VEC, LPR = Sh::LPR, TPL = Sh::TPL, NL = Sh::NL, U = Sh::U;
+
+    __shared__ int s_blk[kMaxPartitionBlocks];
+    __shared__ float s_m[kWaves], s_l[kWaves];
+    __shared__ float s_o[kWaves][D];
+
+    const int part = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int row = lane / LPR, col = lane % LPR;
+    const int64_t sh = static_cast<int64_t>(s) * num_heads + h;
+    const int ctx = context_lens[s];
+
+    if (ctx <= 0 || ctx > max_context_len) {
+        // Empty context -> zeros; impossible length -> NaN.  Partition 0 writes.
+        if (part == 0) {
+            const float v = (ctx == 0) ? 0.0f : __builtin_nanf("");
+            for (int d = tid; d < D; d += kThreads) out[sh * D + d] = narrow<T>(v);
+        }
+        return;
+    }
+    const int t_begin = part * part_tokens;
+    if (t_begin >= ctx) return;
+    const int t_end = min(ctx, t_begin + part_tokens);
+    const int bmask = (1 << log2_bs) - 1;
+    const int j0 = t_begin >> log2_bs;
+    const int nblk = ((t_end - 1) >> log2_bs) - j0 + 1;  // <= kMaxPartitionBlocks (host check)
+
+    // Stage this partition's physical block ids; flag ids outside the pool.
+    const int32_t* bt = block_tables + static_cast<int64_t>(s) * max_blocks_per_seq;
+    for (int i = tid; i < nblk; i += kThreads) {
+        const int b = bt[j0 + i];
+        s_blk[i] = (b >= 0 && b < num_blocks) ? b : -1;
+    }
+
+    // This lane's slice of the query, scaled by scale * log2(e).
+    float qf[VEC];
+    widen16<T>(load16(q + sh * D + col * VEC), qf);
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) qf[v] *= qscale;
+    __syncthreads();
+
+    const int64_t blk_stride = (static_cast<int64_t>(num_heads) << log2_bs) * D;
+    const int64_t head_off = (static_cast<int64_t>(h) << log2_bs) * D + col * VEC;
+
+    float m = -INFINITY;  // running max of base-2 scores (wave-uniform)
+    float l = 0.0f;       // running sum of exp2(score - m) over this lane's row
+    float acc[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[v] = 0.0f;
+    int bad = 0;
+
+    const int niter = (t_end - t_begin + U - 1) / U;
+    for (int it = wave; it < niter; it += kWaves) {
+        const int tb = t_begin + it * U;
+        uint4 kr[NL], vr[NL];
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            // Tokens past the partition re-read the last valid token (always
+            // in bounds) and are masked out of the softmax below.
+            const int t = min(tb + i * TPL + row, t_end - 1);
+            int b = s_blk[(t >> log2_bs) - j0];
+            bad |= (b < 0);
+            b = max(b, 0);
+            const int64_t e = b * blk_stride + head_off + static_cast<int64_t>(t & bmask) * D;
+            kr[i] = load16(kc + e);
+            vr[i] = load16(vc + e);
+        }
+        float sc[NL];
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            float kf[VEC];
+            widen16<T>(kr[i], kf);
+            float d = 0.0f;
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) d = fmaf(qf[v], kf[v], d);
+            d = group_reduce<1, LPR>(d, OpAdd{});
+            sc[i] = (tb + i * TPL + row < t_end) ? d : -INFINITY;
+        }
+        float mx = sc[0];
+#pragma unroll
+        for (int i = 1; i < NL; ++i) mx = fmaxf(mx, sc[i]);
+        mx = group_reduce<LPR, kWave>(mx, OpMax{});
+        const float m_new = fmaxf(m, mx);  // finite: token tb is always valid
+        const float alpha = exp2f(m - m_new);
+        l *= alpha;
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) acc[v] *= alpha;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const float p = exp2f(sc[i] - m_new);
+            l += p;
+            float vf[VEC];
+            widen16<T>(vr[i], vf);
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) acc[v] = fmaf(p, vf[v], acc[v]);
+        }
+        m = m_new;
+    }
+
+    // Combine the rows of each wavefront: rows hold disjoint tokens.
+    l = group_reduce<LPR, kWave>(l, OpAdd{});
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[v] = xor_sum_from<LPR>(acc[v]);
+    if (row == 0) {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) s_o[wave][col * VEC + v] = acc[v];
+    }
+    if (lane == 0) {
+        s_m[wave] = m;
+        s_l[wave] = l;
+    }
+    bad = __syncthreads_or(bad);
+
+    // Combine the wavefronts.  Wave 0 always processed token t_begin.
+    float M = s_m[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w]);
+    float f[kWaves];
+    float L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        f[w] = (s_m[w] == -INFINITY) ? 0.0f : exp2f(s_m[w] - M);
+        L = fmaf(f[w], s_l[w], L);
+    }
+    const bool single = ctx <= part_tokens;
+    for (int d = tid; d < D; d += kThreads) {
+        float O = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) O = fmaf(f[w], s_o[w][d], O);
+        if (bad) O = __builtin_nanf("");
+        if (single) {
+            out[sh * D + d] = narrow<T>(O / L);
+        } else {
+            ws_o[(sh * max_parts + part) * D + d] = O;
+        }
+    }
+    if (!single && tid == 0) {
+        ws_m[sh * max_parts + part] = M;
+        ws_l[sh * max_parts + part] = L;
+    }
+}
+
+// Merge the partitions of every (sequence, head) whose context spans more
+// than one partition: with M the largest partition maximum, each partition's
+// sum and accumulator are rescaled by exp2(m_p - M) and added.
+template <class T, int D>
+__global__ __launch_bounds__(kWave) void decode_merge_kernel(
+    typename T::bits* __restrict__ out, const float* __restrict__ ws_o,
+    const float* __restrict__ ws_m, const float* __restrict__ ws_l,
+    const int32_t* __restrict__ context_lens, int num_heads, int max_context_len, int part_tokens,
+    int max_parts) {
+    const int h = blockIdx.x, s = blockIdx.y;
+    const int ctx = context_lens[s];
+    if (ctx <= part_tokens || ctx > max_context_len) return;  // written by the partition kernel
+    const int np = (ctx + part_tokens - 1) / part_tokens;
+    const int64_t sh = static_cast<int64_t>(s) * num_heads + h;
+    const float* wm = ws_m + sh * max_parts;
+    const float* wl = ws_l + sh * max_parts;
+    float M = -INFINITY;
+    for (int p = 0; p < np; ++p) M = fmaxf(M, wm[p]);
+    float L = 0.0f;
+    for (int p = 0; p < np; ++p) L = fmaf(exp2f(wm[p] - M), wl[p], L);
+    const float* wo = ws_o + sh * max_parts * D;
+    for (int d = threadIdx.x; d < D; d += kWave) {
+        float O = 0.0f;
+        for (int p = 0; p < np; ++p) O = fmaf(exp2f(wm[p] - M), wo[p * D + d], O);
+        out[sh * D + d] = narrow<T>(O / L);
+    }
+}
+
+template <class T, int D>
+static hipError_t launch_decode_t(const DecodeArgs& a) {
+    const int log2_bs = __builtin_ctz(static_cast<unsigned>(a.block_size));
+    const float qscale = a.scale * 1.4426950408889634f;  // log2(e)
+    using bits = typename T::bits;
+    auto* out = static_cast<bits*>(a.out);
+    float* ws_o = static_cast<float*>(a.workspace);
+    const size_t n_sh = static_cast<size_t>(a.num_seqs) * a.num_heads * a.max_parts;
+    float* ws_m = ws_o ? ws_o + n_sh * D : nullptr;
+    float* ws_l = ws_o ? ws_m + n_sh : nullptr;
+    dim3 grid(a.max_parts, a.num_heads, a.num_seqs);
+    hipLaunchKernelGGL((decode_partition_kernel<T, D>), grid, dim3(kThreads), 0, a.stream, out, ws_o,
+                       ws_m, ws_l, static_cast<const bits*>(a.query),
+                       static_cast<const bits*>(a.k_cache), static_cast<const bits*>(a.v_cache),
+                       a.block_tables, a.context_lens, a.num_heads, log2_bs, a.max_blocks_per_seq,
+                       a.max_context_len, a.num_blocks, a.part_tokens, a.max_parts, qscale);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || a.max_parts <= 1) return err;
+    hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(a.num_heads, a.num_seqs), dim3(kWave), 0,
+                       a.stream, out, ws_o, ws_m, ws_l, a.context_lens, a.num_heads,
+                       a.max_context_len, a.part_tokens, a.max_parts);
+    return hipGetLastError();
+}
+
+template <class T>
+static hipError_t launch_decode_dim(const DecodeArgs& a) {
+    switch (a.head_dim) {
+        case 8: return launch_decode_t<T, 8>(a);
+        case 16: return launch_decode_t<T, 16>(a);
+        case 32: return launch_decode_t<T, 32>(a);
+        case 64: return launch_decode_t<T, 64>(a);
+        case 128: return launch_decode_t<T, 128>(a);
+        case 256: return launch_decode_t<T, 256>(a);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_decode(const DecodeArgs& a) {
+    switch (a.dtype) {
+        case 0: return launch_decode_dim<F32>(a);
+        case 1: return launch_decode_dim<F16>(a);
+        case 2: return launch_decode_dim<BF16>(a);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace pa

@@ -1,0 +1,118 @@
+"""The C-ABI library loads, exports every declared entry point, and its host
+checks return the documented statuses (CPU only: no call here reaches a
+kernel launch)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+pa = pytest.importorskip("paged_kv_cache_322_amd", reason="libpa.so not built")
+
+OK, NULL, UNSUP, INVALID, HIP = 0, 1, 2, 3, 4
+P = 0x10000  # a 16-byte-aligned fake device address; never dereferenced here
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(pa_[a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert {"pa_decode", "pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_workspace_size",
+            "pa_status_string"} <= set(names)
+    lib = ctypes.CDLL(pa.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for code in (OK, NULL, UNSUP, INVALID, HIP):
+        assert pa.status_string(code).startswith("PA_")
+    assert pa.status_string(99) == "PA_ERR_UNKNOWN"
+
+
+def test_workspace_size():
+    assert pa.decode_workspace_size(64, 32, 128, 512) == 0  # one partition suffices
+    assert pa.decode_workspace_size(64, 32, 128, 513) == 64 * 32 * 2 * 130 * 4
+    assert pa.decode_workspace_size(128, 96, 128, 2048, 256) == 128 * 96 * 8 * 130 * 4
+    assert pa.decode_workspace_size(3, 1, 8, 37, 16) == 3 * 1 * 3 * 10 * 4
+    assert pa.decode_workspace_size(-1, 1, 8, 37, 16) == 0
+
+
+def dec(**kw):
+    a = dict(out=P, query=P, k=P, v=P, bt=P, ctx=P, S=2, H=4, D=128, B=16, W=8, maxc=100, N=64,
+             scale=0.1, dtype=1, part=0, ws=0, wsb=0)
+    a.update(kw)
+    return pa.lib.pa_decode(a["out"], a["query"], a["k"], a["v"], a["bt"], a["ctx"], a["S"], a["H"], a["D"],
+                            a["B"], a["W"], a["maxc"], a["N"], a["scale"], a["dtype"], a["part"], a["ws"],
+                            a["wsb"], None)
+
+
+def test_decode_host_checks():
+    assert dec(S=0, out=0, query=0) == OK  # empty batch: nothing enqueued
+    assert dec(out=0) == NULL
+    assert dec(bt=0) == NULL
+    assert dec(dtype=3) == UNSUP
+    assert dec(D=96) == UNSUP
+    assert dec(B=12) == UNSUP
+    assert dec(B=512) == UNSUP
+    assert dec(H=0) == INVALID
+    assert dec(S=70000) == INVALID
+    assert dec(maxc=8 * 16 + 1) == INVALID  # more tokens than the table can name
+    assert dec(scale=math.nan) == INVALID
+    assert dec(scale=math.inf) == INVALID
+    assert dec(query=P + 8) == INVALID  # misaligned
+    assert dec(part=-1) == INVALID
+    assert dec(B=1, part=600, maxc=8) == INVALID  # partition spans too many blocks for LDS staging
+    assert dec(maxc=100, part=16) == NULL  # split needs a workspace
+    need = pa.decode_workspace_size(2, 4, 128, 100, 16)
+    assert dec(maxc=100, part=16, ws=P, wsb=need - 1) == INVALID
+    assert dec(maxc=100, part=16, ws=P + 2, wsb=need) == INVALID
+
+
+def cache(**kw):
+    a = dict(key=P, value=P, k=P, v=P, slots=P, T=5, H=4, D=128, B=16, N=64, dtype=2)
+    a.update(kw)
+    return pa.lib.pa_reshape_and_cache(a["key"], a["value"], a["k"], a["v"], a["slots"], a["T"], a["H"],
+                                       a["D"], a["B"], a["N"], a["dtype"], None)
+
+
+def test_reshape_and_cache_host_checks():
+    assert cache(T=0, slots=0, key=0) == OK
+    assert cache(slots=0) == NULL
+    assert cache(dtype=-1) == UNSUP
+    assert cache(D=100) == UNSUP
+    assert cache(T=-1) == INVALID
+    assert cache(N=0) == INVALID
+    assert cache(key=P + 4) == INVALID
+
+
+def copy(**kw):
+    a = dict(k=P, v=P, pairs=P, n=3, H=4, D=128, B=16, N=64, dtype=0)
+    a.update(kw)
+    return pa.lib.pa_copy_blocks(a["k"], a["v"], a["pairs"], a["n"], a["H"], a["D"], a["B"], a["N"],
+                                 a["dtype"], None)
+
+
+def test_copy_blocks_host_checks():
+    assert copy(n=0, pairs=0) == OK
+    assert copy(pairs=0) == NULL
+    assert copy(B=3) == UNSUP
+    assert copy(n=70000) == INVALID
+    assert copy(v=P + 1) == INVALID
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+
+    t = torch.zeros(2, 4, 128, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        pa.decode(t, t, t.view(2, 4, 1, 128), t.view(2, 4, 1, 128), torch.zeros(2, 1, dtype=torch.int32),
+                  torch.ones(2, dtype=torch.int32), 0.1, 1)

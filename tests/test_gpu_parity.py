@@ -1,0 +1,202 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Tolerances: max-abs 2e-3 for f16/bf16 inputs and 1e-5 for f32 inputs on the
+attention output; cache writes and block copies bit-exact over the whole
+pool (compared as integers, so NaN canaries compare too).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from gpu_helpers import (GpuCase, assert_close, assert_pool_equal, log, oracle_decode, oracle_steps, pa,
+                         to_gpu)
+
+pytestmark = pytest.mark.gpu
+
+
+def full_parity(case: wl.Case, partitions=(0,), seqs=None, strict=True):
+    g = GpuCase(case)
+    kc, vc = case.k_cache, case.v_cache
+    for i, (kc, vc) in enumerate(oracle_steps(case)):
+        log(f"{case.name}: step {i}")
+        g.run_step(i)
+        assert_pool_equal(g.kc, kc, case.dtype, f"{case.name} K after step {i}")
+        assert_pool_equal(g.vc, vc, case.dtype, f"{case.name} V after step {i}")
+    ref = oracle_decode(case, kc, vc, seqs)
+    for p in partitions:
+        log(f"{case.name}: decode partition={p}")
+        out = g.decode(partition=p)
+        torch.cuda.synchronize()
+        assert_close(out, ref, case.dtype, f"{case.name} partition={p}", seqs=seqs, strict=strict)
+    return g, ref
+
+
+def test_config1_tiny_f32():
+    full_parity(wl.config1(), partitions=(0, 4, 8, 12, 37))
+
+
+def test_config2_llama7b_shape():
+    full_parity(wl.config2(), partitions=(0, 256))
+
+
+def test_config3_append_then_decode():
+    full_parity(wl.config3())
+
+
+@pytest.mark.parametrize("B", [8, 16, 32])
+def test_config4_parallel_sampling_cow(B):
+    full_parity(wl.config4(block_size=B))
+
+
+def test_config5_opt175b_shape_sampled():
+    case = wl.config5()
+    order = np.argsort(case.context_lens)
+    seqs = sorted(set(order[:: max(1, case.num_seqs // 12)].tolist() + [int(order[-1]), int(order[0])]))
+    full_parity(case, partitions=(0,), seqs=seqs)
+
+
+SWEEP = [
+    # dtype, head_dim, block_size, ctx, partition
+    ("f32", 128, 16, [1, 17, 300, 1299], 0),
+    ("f16", 128, 16, [1, 15, 16, 17, 513, 1300], 64),
+    ("bf16", 128, 32, [2, 33, 700, 1025], 0),
+    ("f16", 64, 8, [5, 100, 900], 100),
+    ("bf16", 256, 16, [3, 64, 511, 512, 777], 128),
+    ("f32", 256, 4, [7, 260], 32),
+    ("f16", 8, 1, [1, 2, 3, 64, 129], 16),
+    ("f32", 8, 4, [5, 16, 37], 0),
+    ("f16", 16, 2, [9, 40], 8),
+    ("bf16", 32, 64, [65, 200], 0),
+    ("f16", 128, 256, [1, 257, 600], 0),
+]
+
+
+@pytest.mark.parametrize("dtype,D,B,ctx,part", SWEEP, ids=[f"{s[0]}-D{s[1]}-B{s[2]}-P{s[4]}" for s in SWEEP])
+def test_shape_sweep(dtype, D, B, ctx, part):
+    case = wl.random_case(100 + D + B, len(ctx), 3, D, B, dtype, ctx=ctx, spare_blocks=7)
+    # Short contexts give |out| near 1-3, where f16/bf16 rounding alone
+    # exceeds 2e-3: the bound here is 2e-3 or one output ulp.
+    full_parity(case, partitions=(part,), strict=False)
+
+
+def test_append_sweep():
+    for dtype, D, B in (("f32", 64, 4), ("bf16", 128, 16), ("f16", 256, 32)):
+        case = wl.random_case(200 + D, 5, 4, D, B, dtype, ctx_range=(3, 90), n_append=3, spare_blocks=6)
+        st = case.steps[0]
+        # An extra padding row (slot -1) that belongs to no sequence is skipped.
+        pad = np.zeros((1,) + st.key.shape[1:], dtype=st.key.dtype)
+        st.key = np.concatenate([st.key[:2], pad, st.key[2:]])
+        st.value = np.concatenate([st.value[:2], pad, st.value[2:]])
+        st.slot_mapping = np.concatenate([st.slot_mapping[:2], [-1], st.slot_mapping[2:]]).astype(np.int64)
+        full_parity(case, strict=False)
+
+
+def test_context_len_zero_and_one():
+    for dtype in wl.DTYPES:
+        case = wl.random_case(300, 4, 2, 128, 16, dtype, ctx=[0, 1, 1, 0])
+        g = GpuCase(case)
+        out = g.decode()
+        torch.cuda.synchronize()
+        got = out.double().cpu().numpy()
+        assert (got[0] == 0).all() and (got[3] == 0).all()
+        for s in (1, 2):
+            b = case.block_tables[s, 0]
+            v = g.vc[b, :, 0, :]
+            assert torch.equal(out[s].view(torch.int16 if dtype != "f32" else torch.int32),
+                               v.view(torch.int16 if dtype != "f32" else torch.int32)), dtype
+
+
+def test_longest_context_and_full_table():
+    # A context that uses every entry of its table row, 8192 tokens long.
+    case = wl.random_case(301, 2, 2, 128, 16, "f16", ctx=[8192, 4097], spare_blocks=2)
+    assert case.block_tables.shape[1] * 16 == 8192
+    full_parity(case, partitions=(0, 2048))
+
+
+def test_empty_calls_are_no_ops():
+    case = wl.random_case(302, 2, 2, 64, 8, "f16", ctx=[3, 9])
+    g = GpuCase(case)
+    before_k = g.kc.clone()
+    e16 = torch.empty(0, 2, 64, dtype=torch.float16, device="cuda")
+    pa().reshape_and_cache(e16, e16, g.kc, g.vc, torch.empty(0, dtype=torch.int64, device="cuda"))
+    pa().copy_blocks(g.kc, g.vc, torch.empty(0, 2, dtype=torch.int64, device="cuda"))
+    out0 = torch.empty(0, 2, 64, dtype=torch.float16, device="cuda")
+    pa().decode(out0, out0, g.kc, g.vc, g.bt[:0], g.ctx[:0], 0.1, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(before_k.view(torch.int16), g.kc.view(torch.int16))
+
+
+def test_block_relabelling_is_bitwise_invariant():
+    case = wl.random_case(303, 6, 4, 128, 16, "bf16", ctx_range=(1, 1500), spare_blocks=11)
+    g = GpuCase(case)
+    base = g.decode().clone()
+    pi = torch.from_numpy(np.random.default_rng(5).permutation(case.num_blocks)).cuda()
+    kc = torch.empty_like(g.kc)
+    vc = torch.empty_like(g.vc)
+    kc[pi] = g.kc
+    vc[pi] = g.vc
+    bt = torch.where(g.bt >= 0, pi[g.bt.clamp(min=0).long()].int(), g.bt)
+    out = g.decode(out=torch.empty_like(base), bt=bt, kc=kc, vc=vc)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), base.view(torch.int16))
+
+
+def test_split_partitions_agree():
+    """Any KV partition size gives the same result up to fp32 summation order:
+    outputs are O(1) (convex combinations of N(0,1) rows), so the bound is
+    absolute, 1e-6, and every split also matches the oracle to 1e-5."""
+    case = wl.random_case(304, 5, 4, 128, 16, "f32", ctx=[2048, 1999, 1024, 513, 64])
+    g = GpuCase(case)
+    outs = {p: g.decode(partition=p, out=torch.empty_like(g.q)) for p in (16, 64, 100, 512, 2048)}
+    torch.cuda.synchronize()
+    ref = outs[2048].double()
+    oref = oracle_decode(case, case.k_cache, case.v_cache)
+    for p, o in outs.items():
+        d = (o.double() - ref).abs().max().item()
+        log(f"split {p} vs unsplit: max abs diff {d:.2e}")
+        assert d <= 1e-6, p
+        assert_close(o, oref, "f32", f"split {p}")
+
+
+def test_fork_reads_through_copy_bitwise():
+    case = wl.config4(block_size=16, num_prompts=4, num_heads=8, head_dim=128, pool_tokens=16384)
+    g = GpuCase(case)
+    g.run_step(0)
+    g.run_step(1)
+    pre_ctx = torch.full_like(g.ctx, 500)
+    forked = g.decode(ctx=pre_ctx, max_context_len=500, out=torch.empty_like(g.q)).clone()
+    bt = g.bt.clone()
+    for p in range(4):
+        bt[4 * p : 4 * p + 4] = g.bt[4 * p + 3]  # every sample reads the original blocks
+    shared = g.decode(ctx=pre_ctx, bt=bt, max_context_len=500, out=torch.empty_like(g.q))
+    torch.cuda.synchronize()
+    assert torch.equal(forked.view(torch.int16), shared.view(torch.int16))
+
+
+def test_out_of_pool_block_id_gives_nan():
+    case = wl.random_case(305, 3, 2, 64, 8, "f16", ctx=[20, 20, 5])
+    g = GpuCase(case)
+    bt = g.bt.clone()
+    bt[0, 1] = case.num_blocks + 100  # outside the pool: the kernel must not read it
+    bt[2, 0] = -3
+    out = g.decode(bt=bt)
+    torch.cuda.synchronize()
+    got = out.float().cpu()
+    assert torch.isnan(got[0]).all() and torch.isnan(got[2]).all()
+    assert torch.isfinite(got[1]).all()
+
+
+def test_runs_on_a_side_stream():
+    case = wl.random_case(306, 4, 4, 128, 16, "f16", ctx_range=(100, 900))
+    g = GpuCase(case)
+    ref = g.decode(out=torch.empty_like(g.q)).clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        out = g.decode(out=torch.empty_like(g.q), partition=128)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    assert (out.float() - ref.float()).abs().max().item() <= 2e-3

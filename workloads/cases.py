@@ -177,12 +177,15 @@ def config1() -> Case:
     return _paged_case("config1", "f32", 1, 8, 4, 16, [5, 16, 37], seed, perm, 0, scale=1.0 / math.sqrt(8.0))
 
 
-def config2(num_seqs: int = 64) -> Case:
+def config2(num_seqs: int = 64, n_append: int = 0) -> Case:
+    """LLaMA-7B-shaped decode layer.  With ``n_append`` = 1 the last context
+    token of every sequence is written by an append step (a serving decode
+    step: store the current token's K/V, then attend)."""
     seed = BASE_SEED + 2
     rng = np.random.default_rng(seed)
     ctx = rng.integers(128, 2049, 64)[:num_seqs]
     perm = rng.permutation(8192)
-    return _paged_case("config2", "f16", 32, 128, 16, 8192, ctx, seed, perm, 0)
+    return _paged_case("config2", "f16", 32, 128, 16, 8192, ctx, seed, perm, n_append)
 
 
 def config3_lengths() -> np.ndarray:
@@ -198,12 +201,12 @@ def config3() -> Case:
     return _paged_case("config3", "f16", 40, 128, 16, 16384, ctx, seed, perm, 1)
 
 
-def config5(num_heads: int = 96) -> Case:
+def config5(num_heads: int = 96, n_append: int = 0) -> Case:
     seed = BASE_SEED + 5
     rng = np.random.default_rng(seed)
     ctx = rng.integers(1024, 2049, 128)
     perm = rng.permutation(16384)
-    return _paged_case("config5", "bf16", num_heads, 128, 16, 16384, ctx, seed, perm, 0)
+    return _paged_case("config5", "bf16", num_heads, 128, 16, 16384, ctx, seed, perm, n_append)
 
 
 def config4(
