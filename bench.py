@@ -261,7 +261,7 @@ def main():
             "num_blocks": case.num_blocks,
             "sum_context_len": int(case.context_lens.sum()),
             "max_context_len": max_ctx,
-            "partition_tokens": args.partition or pa.DEFAULT_PARTITION_TOKENS,
+            "partition_tokens": pa.partition_tokens(S, H, max_ctx, args.partition),
             "pool_copies_rotated": len(pools),
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),

@@ -60,13 +60,27 @@ typedef enum {
  * of two in [1, 256]; num_seqs and num_heads at most 65535. */
 
 /*
+ * pa_decode_partition_tokens - KV partition length pa_decode will use.
+ *
+ * Each (sequence, head) context is split into partitions of this many tokens,
+ * one workgroup each.  A positive `partition_size` is returned unchanged.  0
+ * selects the default: the largest power of two in [256, 4096], and not above
+ * the next power of two of max_context_len, for which
+ * num_seqs * num_heads * ceil(max_context_len / P) is at least 8192, so the
+ * grid keeps all compute units busy until its end.  Returns 0 for invalid
+ * sizes.
+ */
+int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_heads, int32_t max_context_len,
+                                   int32_t partition_size);
+
+/*
  * pa_decode_workspace_size - bytes of device scratch pa_decode needs.
  *
- * Long contexts are split into KV partitions of `partition_size` tokens (0
- * selects the library default); each partition's unnormalised partial result
- * goes to the workspace and a second kernel merges them.  Returns 0 when no
- * sequence can span two partitions (then pa_decode accepts a NULL workspace),
- * and 0 for invalid sizes.
+ * When a context spans several partitions, each partition's unnormalised
+ * partial result (fp32 accumulator, maximum, sum) goes to the workspace and a
+ * second kernel merges them.  Returns 0 when no sequence can span two
+ * partitions (then pa_decode accepts a NULL workspace), and 0 for invalid
+ * sizes.  `partition_size` as for pa_decode_partition_tokens.
  */
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                 int32_t max_context_len, int32_t partition_size);
@@ -96,11 +110,14 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t hea
  *                  a device-to-host copy); must be <= max_blocks_per_seq * B
  *   num_blocks     N, the number of physical blocks in each cache
  *   scale          finite softmax scale (1/sqrt(D) for standard attention)
- *   partition_size tokens per KV partition, 0 = default (512)
+ *   partition_size tokens per KV partition, 0 = default (see
+ *                  pa_decode_partition_tokens); ceil(P / B) + 1 <= 8192
  *   workspace      device scratch of at least pa_decode_workspace_size(...)
  *                  bytes, 4-byte aligned; contents need no initialisation
  *
- * query, out and both caches must be 16-byte aligned.  Device-side guards:
+ * query, out and both caches must be 16-byte aligned, and one block of one
+ * cache (num_heads * block_size * head_dim elements) below 2^31 elements.
+ * Device-side guards:
  * a context length of 0 yields zeros; a context length below 0 or above
  * max_context_len, or a needed block id outside [0, N), yields NaN for that
  * (sequence, head) without reading outside the caches.

@@ -26,15 +26,14 @@ __all__ = [
     "reshape_and_cache",
     "copy_blocks",
     "status_string",
-    "DEFAULT_PARTITION_TOKENS",
+    "partition_tokens",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
-DEFAULT_PARTITION_TOKENS = 512
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is not built; run `python -m paged_kv_cache_322_amd.build` "
+        f"{LIB_PATH} is not built; run `python paged_kv_cache_322_amd/build.py` "
         "(or __graft_entry__.build()) first"
     )
 
@@ -46,6 +45,8 @@ _i64 = ctypes.c_int64
 
 lib.pa_status_string.restype = ctypes.c_char_p
 lib.pa_status_string.argtypes = [ctypes.c_int]
+lib.pa_decode_partition_tokens.restype = _i32
+lib.pa_decode_partition_tokens.argtypes = [_i32, _i32, _i32, _i32]
 lib.pa_decode_workspace_size.restype = ctypes.c_size_t
 lib.pa_decode_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32]
 lib.pa_decode.restype = ctypes.c_int
@@ -98,6 +99,11 @@ def _code(dtype: torch.dtype) -> int:
         return _DTYPE_CODE[dtype]
     except KeyError:
         raise TypeError(f"unsupported element type {dtype}; use float32, float16 or bfloat16") from None
+
+
+def partition_tokens(num_seqs: int, num_heads: int, max_context_len: int, partition_size: int = 0) -> int:
+    """KV partition length ``decode`` uses (``partition_size`` 0 = library default)."""
+    return int(lib.pa_decode_partition_tokens(num_seqs, num_heads, max_context_len, partition_size))
 
 
 def decode_workspace_size(num_seqs: int, num_heads: int, head_dim: int, max_context_len: int,

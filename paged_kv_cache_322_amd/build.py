@@ -1,6 +1,8 @@
 """Build libpa.so (the gfx950 HIP kernels and their C ABI) in place.
 
-    python -m paged_kv_cache_322_amd.build
+    python paged_kv_cache_322_amd/build.py
+
+(Run it as a script: importing the package loads the existing libpa.so.)
 
 Compiles every source under ``csrc/`` with hipcc for gfx950 and links them
 into ``libpa.so`` next to this file.  Always rebuilds.

@@ -20,8 +20,9 @@ bool supported_block_size(int32_t b) { return b >= 1 && b <= 256 && (b & (b - 1)
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int resolve_partition(int32_t partition_size) {
-    return partition_size == 0 ? pa::kDefaultPartitionTokens : partition_size;
+int resolve_partition(int32_t partition_size, int32_t num_seqs, int32_t num_heads, int32_t max_context_len) {
+    return partition_size != 0 ? partition_size
+                               : pa::default_partition_tokens(num_seqs, num_heads, max_context_len);
 }
 
 int64_t parts_for(int32_t max_context_len, int part) {
@@ -51,11 +52,17 @@ const char* pa_status_string(int status) {
     }
 }
 
+int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_heads, int32_t max_context_len,
+                                   int32_t partition_size) {
+    if (num_seqs < 0 || num_heads <= 0 || max_context_len < 0 || partition_size < 0) return 0;
+    return resolve_partition(partition_size, num_seqs, num_heads, max_context_len);
+}
+
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                 int32_t max_context_len, int32_t partition_size) {
     if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || max_context_len < 0 || partition_size < 0)
         return 0;
-    const int part = resolve_partition(partition_size);
+    const int part = resolve_partition(partition_size, num_seqs, num_heads, max_context_len);
     return workspace_bytes_for(num_seqs, num_heads, head_dim, parts_for(max_context_len, part));
 }
 
@@ -74,14 +81,16 @@ int pa_decode(void* out, const void* query, const void* k_cache, const void* v_c
     if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
         return PA_ERR_INVALID;
     if (!isfinite(scale)) return PA_ERR_INVALID;
+    // One block of one cache must be addressable with 32-bit element offsets.
+    if (static_cast<int64_t>(num_heads) * block_size * head_dim > 0x7FFFFFFF) return PA_ERR_INVALID;
     if (!aligned16(out) || !aligned16(query) || !aligned16(k_cache) || !aligned16(v_cache))
         return PA_ERR_INVALID;
-    const int part = resolve_partition(partition_size);
+    const int part = resolve_partition(partition_size, num_seqs, num_heads, max_context_len);
     // A partition may start mid-block, so it touches at most ceil(P/B) + 1 blocks.
-    if ((static_cast<int64_t>(part) + block_size - 1) / block_size + 1 > pa::kMaxPartitionBlocks)
-        return PA_ERR_INVALID;
+    const int64_t staged = pa::partition_blocks(part, block_size);
+    if (staged > pa::kMaxPartitionBlocks) return PA_ERR_INVALID;
     const int64_t parts = parts_for(max_context_len, part);
-    if (parts > 0x7FFFFFFF) return PA_ERR_INVALID;
+    if (parts > 65535) return PA_ERR_INVALID;  // grid dimension limit
     const size_t need = workspace_bytes_for(num_seqs, num_heads, head_dim, parts);
     if (need) {
         if (!workspace) return PA_ERR_NULL;
@@ -106,6 +115,7 @@ int pa_decode(void* out, const void* query, const void* k_cache, const void* v_c
     a.dtype = dtype;
     a.part_tokens = part;
     a.max_parts = static_cast<int>(parts);
+    a.staged_blocks = static_cast<int>(staged);
     a.workspace = need ? workspace : nullptr;
     a.stream = static_cast<hipStream_t>(stream);
     return hip_status(pa::launch_decode(a));

@@ -6,7 +6,7 @@
 // physical blocks found through the sequence's block table.
 //
 // Work decomposition.  The context of every (sequence, head) is cut into KV
-// partitions of P tokens; one workgroup of four wavefronts handles one
+// partitions of P tokens; one workgroup of kWgWaves wavefronts handles one
 // (partition, head, sequence).  Decode attention is a matrix-vector product:
 // each K and V byte is used once, so the kernel is bound by HBM bandwidth and
 // uses no matrix cores.  Inside a workgroup:
@@ -15,12 +15,15 @@
 //   * a wavefront processes U tokens per step.  A token's row of D elements
 //     is spread over LPR = D / (16 / elem) lanes, each lane loading 16 bytes,
 //     so one wave-wide load instruction covers 64 / LPR whole token rows and
-//     every lane issues NL loads of K and NL loads of V per step, all before
-//     using any of them;
-//   * q.k partial dots are summed across a row's lanes with DPP permutes, the
-//     running maximum is shared across rows, and each lane keeps its own
-//     running sum and fp32 accumulators for its slice of D (online softmax,
-//     exponentials taken base 2 with log2(e) folded into the query);
+//     every lane issues NL loads of K and NL loads of V per step.  The loads
+//     of a wavefront's next step are issued before the current step is
+//     computed (software pipelining), so every wavefront keeps K and V bytes
+//     in flight while it computes;
+//   * q.k partial dots are summed across a row's lanes with DPP permutes.
+//     Each row of lanes keeps its own running maximum, running sum and fp32
+//     accumulators for its slice of D (online softmax, exponentials taken
+//     base 2 with log2(e) folded into the query), so the loop needs no
+//     exchange between rows; rows are merged once at the end;
 //   * wavefronts interleave steps, then merge their (max, sum, accumulators)
 //     through LDS.
 //
@@ -32,18 +35,37 @@
 #include "pa_device.h"
 #include "pa_internal.h"
 
+// Tuning switches (compile-time).  Defaults are the measured best on MI355X.
+#ifndef PA_PREFETCH
+#define PA_PREFETCH 1  // issue the next step's loads before computing the current one
+#endif
+#ifndef PA_NT_LOADS
+#define PA_NT_LOADS 1  // non-temporal K/V loads
+#endif
+#ifndef PA_STEP_TOKENS
+#define PA_STEP_TOKENS 16  // target tokens per wavefront step
+#endif
+#ifndef PA_WG_WAVES
+#define PA_WG_WAVES 8  // wavefronts per workgroup
+#endif
+#ifndef PA_PART_MAJOR
+#define PA_PART_MAJOR 1  // 1: partition index is the slowest grid dimension
+#endif
+
 namespace pa {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
+constexpr int kWgWaves = PA_WG_WAVES;
+constexpr int kThreads = kWgWaves * kWave;
+constexpr int kMergeMaxParts = 256;  // partition weights cached in LDS by the merge kernel
 
 template <class T, int D>
 struct DecodeShape {
     static constexpr int VEC = kVec<T>;
-    static constexpr int LPR = D / VEC;         // lanes per token row
-    static constexpr int TPL = kWave / LPR;     // token rows per wave-wide load
-    static constexpr int NL = (16 / TPL) < 1 ? 1 : ((16 / TPL) > 8 ? 8 : (16 / TPL));
-    static constexpr int U = NL * TPL;          // tokens per wavefront step
+    static constexpr int LPR = D / VEC;      // lanes per token row
+    static constexpr int TPL = kWave / LPR;  // token rows per wave-wide load
+    static constexpr int NL0 = PA_STEP_TOKENS / TPL;
+    static constexpr int NL = NL0 < 1 ? 1 : (NL0 > 8 ? 8 : NL0);  // loads of K (and of V) per lane per step
+    static constexpr int U = NL * TPL;       // tokens per wavefront step
     static_assert(LPR >= 1 && LPR <= kWave && (kWave % LPR) == 0, "unsupported head_dim");
 };
 
@@ -58,12 +80,17 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(
     using Sh = DecodeShape<T, D>;
     constexpr int VEC = Sh::VEC, LPR = Sh::LPR, TPL = Sh::TPL, NL = Sh::NL, U = Sh::U;
 
-    __shared__ int s_blk[kMaxPartitionBlocks];
-    __shared__ float s_m[kWaves], s_l[kWaves];
-    __shared__ float s_o[kWaves][D];
+    extern __shared__ int s_blk[];  // this partition's block ids (dynamic size)
+    __shared__ float s_m[kWgWaves], s_l[kWgWaves];
+    __shared__ float s_o[kWgWaves][D];
 
+#if PA_PART_MAJOR
+    const int h = blockIdx.x, s = blockIdx.y, part = blockIdx.z;
+#else
     const int part = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+#endif
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int row = lane / LPR, col = lane % LPR;
     const int64_t sh = static_cast<int64_t>(s) * num_heads + h;
     const int ctx = context_lens[s];
@@ -81,7 +108,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(
     const int t_end = min(ctx, t_begin + part_tokens);
     const int bmask = (1 << log2_bs) - 1;
     const int j0 = t_begin >> log2_bs;
-    const int nblk = ((t_end - 1) >> log2_bs) - j0 + 1;  // <= kMaxPartitionBlocks (host check)
+    const int nblk = ((t_end - 1) >> log2_bs) - j0 + 1;  // <= staged_blocks (host sizes the LDS)
 
     // Stage this partition's physical block ids; flag ids outside the pool.
     const int32_t* bt = block_tables + static_cast<int64_t>(s) * max_blocks_per_seq;
@@ -97,32 +124,37 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(
     for (int v = 0; v < VEC; ++v) qf[v] *= qscale;
     __syncthreads();
 
-    const int64_t blk_stride = (static_cast<int64_t>(num_heads) << log2_bs) * D;
-    const int64_t head_off = (static_cast<int64_t>(h) << log2_bs) * D + col * VEC;
+    // Element offsets: block b starts at b * blk_stride (host guarantees
+    // H * B * D < 2^31); this lane's channels of head h at lane_off in it.
+    const uint32_t blk_stride = static_cast<uint32_t>(num_heads << log2_bs) * D;
+    const uint32_t lane_off = (static_cast<uint32_t>(h) << log2_bs) * D + col * VEC;
 
-    float m = -INFINITY;  // running max of base-2 scores (wave-uniform)
-    float l = 0.0f;       // running sum of exp2(score - m) over this lane's row
-    float acc[VEC];
+    float m = -INFINITY;  // running max of this row's base-2 scores
+    float l = 0.0f;       // running sum of exp2(score - m) over this row's tokens
+    float acc[VEC];       // running sum of exp2(score - m) * v over this row's tokens
 #pragma unroll
     for (int v = 0; v < VEC; ++v) acc[v] = 0.0f;
     int bad = 0;
 
-    const int niter = (t_end - t_begin + U - 1) / U;
-    for (int it = wave; it < niter; it += kWaves) {
+    auto load_step = [&](int it, uint4 (&kr)[NL], uint4 (&vr)[NL]) {
         const int tb = t_begin + it * U;
-        uint4 kr[NL], vr[NL];
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
             // Tokens past the partition re-read the last valid token (always
-            // in bounds) and are masked out of the softmax below.
+            // in bounds) and are masked out of the softmax.
             const int t = min(tb + i * TPL + row, t_end - 1);
             int b = s_blk[(t >> log2_bs) - j0];
             bad |= (b < 0);
             b = max(b, 0);
-            const int64_t e = b * blk_stride + head_off + static_cast<int64_t>(t & bmask) * D;
-            kr[i] = load16(kc + e);
-            vr[i] = load16(vc + e);
+            const uint64_t e = static_cast<uint64_t>(static_cast<uint32_t>(b)) * blk_stride + lane_off +
+                               static_cast<uint32_t>(t & bmask) * D;
+            kr[i] = load16<PA_NT_LOADS>(kc + e);
+            vr[i] = load16<PA_NT_LOADS>(vc + e);
         }
+    };
+
+    auto compute_step = [&](int it, const uint4 (&kr)[NL], const uint4 (&vr)[NL]) {
+        const int tb = t_begin + it * U;
         float sc[NL];
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
@@ -137,15 +169,17 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(
         float mx = sc[0];
 #pragma unroll
         for (int i = 1; i < NL; ++i) mx = fmaxf(mx, sc[i]);
-        mx = group_reduce<LPR, kWave>(mx, OpMax{});
-        const float m_new = fmaxf(m, mx);  // finite: token tb is always valid
-        const float alpha = exp2f(m - m_new);
+        const float m_new = fmaxf(m, mx);
+        // A row whose tokens so far are all masked keeps m = -inf; use 0 as
+        // its reference so no inf - inf appears (its weights stay 0).
+        const float m_ref = (m_new == -INFINITY) ? 0.0f : m_new;
+        const float alpha = fast_exp2(m - m_ref);
         l *= alpha;
 #pragma unroll
         for (int v = 0; v < VEC; ++v) acc[v] *= alpha;
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
-            const float p = exp2f(sc[i] - m_new);
+            const float p = fast_exp2(sc[i] - m_ref);
             l += p;
             float vf[VEC];
             widen16<T>(vr[i], vf);
@@ -153,38 +187,68 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(
             for (int v = 0; v < VEC; ++v) acc[v] = fmaf(p, vf[v], acc[v]);
         }
         m = m_new;
-    }
+    };
 
-    // Combine the rows of each wavefront: rows hold disjoint tokens.
-    l = group_reduce<LPR, kWave>(l, OpAdd{});
+    const int niter = (t_end - t_begin + U - 1) / U;
+    int it = wave;
+#if PA_PREFETCH
+    if (it < niter) {
+        uint4 ka[NL], va[NL], kb[NL], vb[NL];
+        load_step(it, ka, va);
+        while (true) {
+            int nx = it + kWgWaves;
+            if (nx < niter) load_step(nx, kb, vb);
+            compute_step(it, ka, va);
+            if (nx >= niter) break;
+            it = nx;
+            nx = it + kWgWaves;
+            if (nx < niter) load_step(nx, ka, va);
+            compute_step(it, kb, vb);
+            if (nx >= niter) break;
+            it = nx;
+        }
+    }
+#else
+    for (; it < niter; it += kWgWaves) {
+        uint4 ka[NL], va[NL];
+        load_step(it, ka, va);
+        compute_step(it, ka, va);
+    }
+#endif
+
+    // Merge the rows of each wavefront (rows hold disjoint tokens): rescale
+    // every row to the wave maximum, then sum.
+    const float mw = group_reduce<LPR, kWave>(m, OpMax{});
+    const float fr = (m == -INFINITY) ? 0.0f : fast_exp2(m - mw);
+    l = group_reduce<LPR, kWave>(l * fr, OpAdd{});
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) acc[v] = xor_sum_from<LPR>(acc[v]);
+    for (int v = 0; v < VEC; ++v) acc[v] = xor_sum_from<LPR>(acc[v] * fr);
     if (row == 0) {
 #pragma unroll
         for (int v = 0; v < VEC; ++v) s_o[wave][col * VEC + v] = acc[v];
     }
     if (lane == 0) {
-        s_m[wave] = m;
+        s_m[wave] = mw;
         s_l[wave] = l;
     }
     bad = __syncthreads_or(bad);
 
-    // Combine the wavefronts.  Wave 0 always processed token t_begin.
+    // Merge the wavefronts.  Wave 0 always processed token t_begin.
     float M = s_m[0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w]);
-    float f[kWaves];
+    for (int w = 1; w < kWgWaves; ++w) M = fmaxf(M, s_m[w]);
+    float f[kWgWaves];
     float L = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-        f[w] = (s_m[w] == -INFINITY) ? 0.0f : exp2f(s_m[w] - M);
+    for (int w = 0; w < kWgWaves; ++w) {
+        f[w] = (s_m[w] == -INFINITY) ? 0.0f : fast_exp2(s_m[w] - M);
         L = fmaf(f[w], s_l[w], L);
     }
     const bool single = ctx <= part_tokens;
     for (int d = tid; d < D; d += kThreads) {
         float O = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) O = fmaf(f[w], s_o[w][d], O);
+        for (int w = 0; w < kWgWaves; ++w) O = fmaf(f[w], s_o[w][d], O);
         if (bad) O = __builtin_nanf("");
         if (single) {
             out[sh * D + d] = narrow<T>(O / L);
@@ -200,13 +264,15 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(
 
 // Merge the partitions of every (sequence, head) whose context spans more
 // than one partition: with M the largest partition maximum, each partition's
-// sum and accumulator are rescaled by exp2(m_p - M) and added.
+// sum and accumulator are rescaled by exp2(m_p - M) and added.  Lane p reads
+// partition p's statistics, so they arrive in one round trip.
 template <class T, int D>
 __global__ __launch_bounds__(kWave) void decode_merge_kernel(
     typename T::bits* __restrict__ out, const float* __restrict__ ws_o,
     const float* __restrict__ ws_m, const float* __restrict__ ws_l,
     const int32_t* __restrict__ context_lens, int num_heads, int max_context_len, int part_tokens,
     int max_parts) {
+    __shared__ float s_w[kMergeMaxParts];
     const int h = blockIdx.x, s = blockIdx.y;
     const int ctx = context_lens[s];
     if (ctx <= part_tokens || ctx > max_context_len) return;  // written by the partition kernel
@@ -214,14 +280,25 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(
     const int64_t sh = static_cast<int64_t>(s) * num_heads + h;
     const float* wm = ws_m + sh * max_parts;
     const float* wl = ws_l + sh * max_parts;
+    const int lane = threadIdx.x;
     float M = -INFINITY;
-    for (int p = 0; p < np; ++p) M = fmaxf(M, wm[p]);
+    for (int p = lane; p < np; p += kWave) M = fmaxf(M, wm[p]);
+    M = group_reduce<1, kWave>(M, OpMax{});
     float L = 0.0f;
-    for (int p = 0; p < np; ++p) L = fmaf(exp2f(wm[p] - M), wl[p], L);
+    for (int p = lane; p < np; p += kWave) {
+        const float w = fast_exp2(wm[p] - M);
+        if (p < kMergeMaxParts) s_w[p] = w;
+        L = fmaf(w, wl[p], L);
+    }
+    L = group_reduce<1, kWave>(L, OpAdd{});
+    __syncthreads();
     const float* wo = ws_o + sh * max_parts * D;
-    for (int d = threadIdx.x; d < D; d += kWave) {
+    for (int d = lane; d < D; d += kWave) {
         float O = 0.0f;
-        for (int p = 0; p < np; ++p) O = fmaf(exp2f(wm[p] - M), wo[p * D + d], O);
+        for (int p = 0; p < np; ++p) {
+            const float w = p < kMergeMaxParts ? s_w[p] : fast_exp2(wm[p] - M);
+            O = fmaf(w, wo[p * D + d], O);
+        }
         out[sh * D + d] = narrow<T>(O / L);
     }
 }
@@ -236,8 +313,13 @@ static hipError_t launch_decode_t(const DecodeArgs& a) {
     const size_t n_sh = static_cast<size_t>(a.num_seqs) * a.num_heads * a.max_parts;
     float* ws_m = ws_o ? ws_o + n_sh * D : nullptr;
     float* ws_l = ws_o ? ws_m + n_sh : nullptr;
+#if PA_PART_MAJOR
+    dim3 grid(a.num_heads, a.num_seqs, a.max_parts);
+#else
     dim3 grid(a.max_parts, a.num_heads, a.num_seqs);
-    hipLaunchKernelGGL((decode_partition_kernel<T, D>), grid, dim3(kThreads), 0, a.stream, out, ws_o,
+#endif
+    const size_t lds = static_cast<size_t>(a.staged_blocks) * sizeof(int);
+    hipLaunchKernelGGL((decode_partition_kernel<T, D>), grid, dim3(kThreads), lds, a.stream, out, ws_o,
                        ws_m, ws_l, static_cast<const bits*>(a.query),
                        static_cast<const bits*>(a.k_cache), static_cast<const bits*>(a.v_cache),
                        a.block_tables, a.context_lens, a.num_heads, log2_bs, a.max_blocks_per_seq,

@@ -80,7 +80,23 @@ __device__ __forceinline__ uint16_t narrow<BF16>(float x) {
     return static_cast<uint16_t>(u >> 16);
 }
 
-__device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte global load.  NT = 1 marks it non-temporal (streamed data that is
+// read once), which lets the memory system skip keeping it in the caches.
+template <int NT = 0>
+__device__ __forceinline__ uint4 load16(const void* p) {
+    u32x4 v;
+    if constexpr (NT)
+        v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    else
+        v = *reinterpret_cast<const u32x4*>(p);
+    return uint4{v.x, v.y, v.z, v.w};
+}
+
+// 2^x with the hardware v_exp_f32 (no denormal-range fix-up: callers only
+// take it of non-positive arguments whose tiny results may flush to zero).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------------------
 // Wavefront reductions.

@@ -7,10 +7,31 @@
 
 namespace pa {
 
-// Largest number of physical blocks one KV partition may touch; bounds the
-// LDS array that stages a partition's block ids.
-constexpr int kMaxPartitionBlocks = 512;
-constexpr int kDefaultPartitionTokens = 512;
+// Largest number of physical blocks one KV partition may touch (its block
+// ids are staged in LDS: at most 32 KB).
+constexpr int kMaxPartitionBlocks = 8192;
+
+// Default KV partition: the largest power of two in [256, 4096] tokens (and
+// not above the next power of two of the longest context) that still yields
+// at least kTargetWorkItems (sequence, head, partition) work items, so that
+// the 256 compute units stay busy to the end of the grid.
+constexpr int kMinDefaultPartition = 256;
+constexpr int kMaxDefaultPartition = 4096;
+constexpr int64_t kTargetWorkItems = 8192;
+
+inline int default_partition_tokens(int64_t num_seqs, int64_t num_heads, int64_t max_context_len) {
+    int part = kMinDefaultPartition;
+    while (part < kMaxDefaultPartition && part < max_context_len) part *= 2;
+    const int64_t pairs = num_seqs * num_heads;
+    while (part > kMinDefaultPartition && pairs * ((max_context_len + part - 1) / part) < kTargetWorkItems)
+        part /= 2;
+    return part;
+}
+
+// Blocks a partition of `part` tokens can touch when it starts mid-block.
+inline int64_t partition_blocks(int64_t part, int64_t block_size) {
+    return (part + block_size - 1) / block_size + 1;
+}
 
 struct DecodeArgs {
     void* out;
@@ -25,6 +46,7 @@ struct DecodeArgs {
     float scale;
     int dtype;
     int part_tokens, max_parts;
+    int staged_blocks;  // LDS entries for a partition's block ids
     void* workspace;  // float [S*H*max_parts*D] then [S*H*max_parts] x 2; NULL when max_parts == 1
     hipStream_t stream;
 };

@@ -26,7 +26,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert {"pa_decode", "pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_workspace_size",
-            "pa_status_string"} <= set(names)
+            "pa_decode_partition_tokens", "pa_status_string"} <= set(names)
     lib = ctypes.CDLL(pa.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -38,9 +38,25 @@ def test_status_strings():
     assert pa.status_string(99) == "PA_ERR_UNKNOWN"
 
 
+def test_default_partition_heuristic():
+    # Largest power of two in [256, 4096] (<= next pow2 of the longest context)
+    # giving >= 8192 (sequence, head, partition) items.
+    assert pa.partition_tokens(64, 32, 2013) == 512  # LLaMA-7B-shaped batch
+    assert pa.partition_tokens(256, 40, 2048) == 2048  # OPT-13B-shaped batch
+    assert pa.partition_tokens(128, 96, 2048) == 2048  # OPT-175B-shaped batch
+    assert pa.partition_tokens(256, 40, 756) == 1024
+    assert pa.partition_tokens(3, 1, 37) == 256
+    assert pa.partition_tokens(1, 8, 100000) == 256  # few pairs: as many partitions as possible
+    assert pa.partition_tokens(4096, 64, 100000) == 4096
+    assert pa.partition_tokens(64, 32, 2013, 100) == 100  # explicit sizes pass through
+    assert pa.partition_tokens(-1, 32, 10) == 0
+
+
 def test_workspace_size():
-    assert pa.decode_workspace_size(64, 32, 128, 512) == 0  # one partition suffices
-    assert pa.decode_workspace_size(64, 32, 128, 513) == 64 * 32 * 2 * 130 * 4
+    assert pa.decode_workspace_size(64, 32, 128, 256) == 0  # one default partition suffices
+    assert pa.decode_workspace_size(64, 32, 128, 513) == 64 * 32 * 3 * 130 * 4  # default 256
+    assert pa.decode_workspace_size(64, 32, 128, 513, 512) == 64 * 32 * 2 * 130 * 4
+    assert pa.decode_workspace_size(128, 96, 128, 2048) == 0  # default 2048
     assert pa.decode_workspace_size(128, 96, 128, 2048, 256) == 128 * 96 * 8 * 130 * 4
     assert pa.decode_workspace_size(3, 1, 8, 37, 16) == 3 * 1 * 3 * 10 * 4
     assert pa.decode_workspace_size(-1, 1, 8, 37, 16) == 0
@@ -70,8 +86,10 @@ def test_decode_host_checks():
     assert dec(scale=math.inf) == INVALID
     assert dec(query=P + 8) == INVALID  # misaligned
     assert dec(part=-1) == INVALID
-    assert dec(B=1, part=600, maxc=8) == INVALID  # partition spans too many blocks for LDS staging
+    assert dec(B=1, part=9000, maxc=8) == INVALID  # partition spans too many blocks for LDS staging
+    assert dec(H=65535, B=256, D=256) == INVALID  # one block above 2^31 elements
     assert dec(maxc=100, part=16) == NULL  # split needs a workspace
+    assert dec(maxc=2000000, W=200000, part=16) == INVALID  # more partitions than grid rows
     need = pa.decode_workspace_size(2, 4, 128, 100, 16)
     assert dec(maxc=100, part=16, ws=P, wsb=need - 1) == INVALID
     assert dec(maxc=100, part=16, ws=P + 2, wsb=need) == INVALID

@@ -14,8 +14,17 @@ import pytest
 
 import workloads as wl
 
-MAX_PART_BLOCKS = 512
-DEFAULT_PART = 512
+MAX_PART_BLOCKS = 8192
+
+
+def default_partition(S, H, max_ctx):
+    """Mirror of the library's default partition rule."""
+    part = 256
+    while part < 4096 and part < max_ctx:
+        part *= 2
+    while part > 256 and S * H * (-(-max_ctx // part)) < 8192:
+        part //= 2
+    return part
 
 
 def shape(elem, D):
@@ -28,7 +37,8 @@ def shape(elem, D):
 
 def check_decode_bounds(S, H, D, B, N, W, elem, ctx, bt, max_ctx, part):
     vec, lpr, tpl, nl, U = shape(elem, D)
-    assert (part + B - 1) // B + 1 <= MAX_PART_BLOCKS  # host check in pa_decode
+    staged = (part + B - 1) // B + 1
+    assert staged <= MAX_PART_BLOCKS  # host check in pa_decode; LDS holds `staged` ids
     assert max_ctx <= W * B  # host check in pa_decode
     log2b = B.bit_length() - 1
     assert 1 << log2b == B
@@ -48,7 +58,7 @@ def check_decode_bounds(S, H, D, B, N, W, elem, ctx, bt, max_ctx, part):
             t_end = min(c, t_begin + part)
             j0 = t_begin >> log2b
             nblk = ((t_end - 1) >> log2b) - j0 + 1
-            assert 1 <= nblk <= MAX_PART_BLOCKS
+            assert 1 <= nblk <= staged
             assert 0 <= j0 and j0 + nblk - 1 < W  # block-table row reads
             niter = (t_end - t_begin + U - 1) // U
             ts = np.arange(niter)[:, None, None] * U + np.arange(nl)[None, :, None] * tpl + np.arange(tpl)[None, None, :]
@@ -81,7 +91,7 @@ def test_decode_index_bounds(name, make, part):
     case = make()
     B = case.block_size
     max_ctx = case.max_context_len
-    p = DEFAULT_PART if part == 0 else part
+    p = default_partition(case.num_seqs, case.num_heads, max_ctx) if part == 0 else part
     if p == 1 << 30:
         p = max(1, max_ctx)  # a single partition covers every context
     if (p + B - 1) // B + 1 > MAX_PART_BLOCKS:
