@@ -40,6 +40,7 @@ METRIC = "paged decode attention: KV-read GB/s and % of HBM peak; decode tokens/
 WORKLOADS = {
     2: "llama7b-decode-layer: 64 seqs, ctx U[128,2048], H=32, D=128, f16, B=16, 8192-block pool",
     3: "opt13b-decode-layer: 256 seqs, ctx lognormal(median 300, sigma 0.9) in [16,2048], H=40, D=128, f16, B=16",
+    4: "parallel-sampling-cow: 64 prompts x 4 samples, prompt 500, suffix U[0,256], H=40, D=128, f16",
     5: "opt175b-decode-layer: 128 seqs, ctx U[1024,2048], H=96, D=128, bf16, B=16, 16384-block pool",
 }
 
@@ -51,6 +52,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2, choices=sorted(WORKLOADS))
     ap.add_argument("--partition", type=int, default=0, help="KV partition tokens (0 = library default)")
+    ap.add_argument("--block-size", type=int, default=16, help="block size for config 4 (8, 16 or 32)")
     ap.add_argument("--rotate", type=int, default=2, help="independent pool copies cycled across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle baseline")
@@ -61,24 +63,39 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def make_case(cfg):
+def make_case(cfg, block_size=16):
     import workloads as wl
 
     if cfg == 2:
         return wl.config2(n_append=1)
     if cfg == 3:
         return wl.config3()
+    if cfg == 4:
+        return wl.config4(block_size=block_size)
     return wl.config5(n_append=1)
 
 
-def algorithmic_bytes(case):
+def algorithmic_bytes(case, timed_steps):
     e = case.elem_bytes
     S, H, D, B = case.num_seqs, case.num_heads, case.head_dim, case.block_size
     ctx = case.context_lens.astype(np.int64)
     decode = 2 * e * H * D * int(ctx.sum()) + 2 * S * H * D * e + 4 * int(np.ceil(ctx / B).sum()) + 4 * S
-    T = sum(st.slot_mapping.size for st in case.steps)
+    T = sum(st.slot_mapping.size for st in timed_steps)
     append = 4 * T * H * D * e + 8 * T
     return decode, append
+
+
+def unique_kv_bytes(case):
+    """K+V bytes of the distinct (block, slot) positions the decode reads:
+    blocks shared by several sequences count once."""
+    B = case.block_size
+    seen = {}
+    for s in range(case.num_seqs):
+        n = int(case.context_lens[s])
+        for j in range(-(-n // B)):
+            b = int(case.block_tables[s, j])
+            seen[b] = max(seen.get(b, 0), min(B, n - j * B))
+    return 2 * case.elem_bytes * case.num_heads * case.head_dim * sum(seen.values())
 
 
 def traffic_from_profiles(kernel_src_sha):
@@ -110,7 +127,16 @@ def kernel_source_sha():
     return h.hexdigest()
 
 
-def cpu_baseline(case, target_s, step_bytes):
+def cpu_baseline(case, target_s, timed_steps, setup_pools=None):
+    """The float64 oracle on the same kind of step, on a bounded sample.
+
+    Times oracle.reshape_and_cache (the sample's new rows; the oracle copies
+    the whole pool each call, as it stands) followed by oracle.paged_decode,
+    for the first k sequences of the batch, with k the whole batch when that
+    fits about a third of ``target_s`` and fewer otherwise.  Repeats until
+    ``target_s`` of CPU time or 10 runs and reports the best run, as GB/s over
+    the same algorithmic bytes the GPU figure uses (restricted to the sample).
+    """
     import oracle
 
     try:
@@ -119,23 +145,50 @@ def cpu_baseline(case, target_s, step_bytes):
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         blas_threads = 1
-    st = case.steps[0]
-    best, total, reps = math.inf, 0.0, 0
-    while reps < 3 and (reps == 0 or total < target_s):
+    k0, v0 = setup_pools if setup_pools is not None else (case.k_cache, case.v_cache)
+    for st in timed_steps:
+        assert st.slot_mapping.size == case.num_seqs  # one new row per sequence, in sequence order
+
+    def run(k):
         t0 = time.perf_counter()
-        kc, vc = oracle.reshape_and_cache(st.key, st.value, case.k_cache, case.v_cache, st.slot_mapping)
-        oracle.paged_decode(case.q, kc, vc, case.block_tables, case.context_lens, case.scale, case.dtype)
-        dt = time.perf_counter() - t0
+        kc, vc = k0, v0
+        for st in timed_steps:
+            kc, vc = oracle.reshape_and_cache(st.key[:k], st.value[:k], kc, vc, st.slot_mapping[:k])
+        oracle.paged_decode(case.q[:k], kc, vc, case.block_tables[:k], case.context_lens[:k], case.scale,
+                            case.dtype)
+        return time.perf_counter() - t0
+
+    S = case.num_seqs
+    # The oracle's append copies the whole pool (a fixed cost); the decode
+    # cost grows with the sequences sampled.  Size k from both.
+    t0 = time.perf_counter()
+    for st in timed_steps:
+        oracle.reshape_and_cache(st.key[:1], st.value[:1], k0, v0, st.slot_mapping[:1])
+    t_fixed = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.paged_decode(case.q[:1], k0, v0, case.block_tables[:1], case.context_lens[:1], case.scale, case.dtype)
+    t_seq = max(time.perf_counter() - t0, 1e-4) * float(case.context_lens.mean()) / max(1, int(case.context_lens[0]))
+    budget = target_s / 3 - t_fixed
+    k = S if t_fixed + t_seq * S <= target_s / 3 else max(1, min(S, int(budget / t_seq)))
+    best, total, reps = math.inf, 0.0, 0
+    while reps < 10 and (reps < 2 or total < target_s):
+        dt = run(k)
         best, total, reps = min(best, dt), total + dt, reps + 1
-        del kc, vc
+    e = case.elem_bytes
+    H, D, B = case.num_heads, case.head_dim, case.block_size
+    ctx = case.context_lens[:k].astype(np.int64)
+    nbytes = 2 * e * H * D * int(ctx.sum()) + 2 * k * H * D * e + 4 * int(np.ceil(ctx / B).sum()) + 4 * k
+    nbytes += sum(4 * k * H * D * e + 8 * k for _ in timed_steps)
     return {
-        "value": round(step_bytes / best / 1e9, 4),
+        "value": round(nbytes / best / 1e9, 4),
         "unit": "GB/s",
         "cores": int(blas_threads),
         "kind": "oracle",
-        "sample": f"whole batch (all {case.num_seqs} sequences, append + decode), best of {reps} "
-                  f"({best:.2f} s each, float64 numpy; host has {len(os.sched_getaffinity(0))} cpus)",
-        "seconds_per_step": round(best, 4),
+        "sample": f"first {k} of {S} sequences ({'append + ' if timed_steps else ''}decode), best of {reps} runs "
+                  f"({best:.2f} s each; float64 numpy, BLAS threads {blas_threads}; host has "
+                  f"{len(os.sched_getaffinity(0))} cpus)",
+        "seconds_per_run": round(best, 4),
+        "sample_bytes": int(nbytes),
     }
 
 
@@ -153,11 +206,18 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     import paged_kv_cache_322_amd as pa
-    from workloads import to_storage  # noqa: F401  (imported for side-effect-free check)
 
     dev = torch.device("cuda:0")
     log(f"building workload config {args.config}")
-    case = make_case(args.config)
+    case = make_case(args.config, args.block_size)
+    import workloads as wl
+
+    # Config 4's prompt write, fork copies and suffix writes are set-up; the
+    # other configs time their one-token-per-sequence append with the decode.
+    if args.config == 4:
+        setup_steps, timed_steps = list(case.steps), []
+    else:
+        setup_steps, timed_steps = [], list(case.steps)
     dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[case.dtype]
 
     def up(a):
@@ -167,10 +227,17 @@ def main():
         return torch.from_numpy(a).to(dev)
 
     S, H, D, B = case.num_seqs, case.num_heads, case.head_dim, case.block_size
-    st = case.steps[0]
     q, bt, ctx = up(case.q), up(case.block_tables), up(case.context_lens)
-    k_new, v_new, slots = up(st.key), up(st.value), up(st.slot_mapping)
-    pools = [(up(case.k_cache), up(case.v_cache)) for _ in range(max(1, args.rotate))]
+    appends = [(up(st.key), up(st.value), up(st.slot_mapping)) for st in timed_steps]
+    pools = []
+    for _ in range(max(1, args.rotate)):
+        kc, vc = up(case.k_cache), up(case.v_cache)
+        for st in setup_steps:
+            if isinstance(st, wl.AppendStep):
+                pa.reshape_and_cache(up(st.key), up(st.value), kc, vc, up(st.slot_mapping))
+            else:
+                pa.copy_blocks(kc, vc, up(st.pairs))
+        pools.append((kc, vc))
     out = torch.empty_like(q)
     max_ctx = case.max_context_len
     ws_bytes = pa.decode_workspace_size(S, H, D, max_ctx, args.partition)
@@ -181,7 +248,8 @@ def main():
         kc, vc = pools[i % len(pools)]
         if ev is not None:
             ev[0].record()
-        pa.reshape_and_cache(k_new, v_new, kc, vc, slots)
+        for k_new, v_new, slots in appends:
+            pa.reshape_and_cache(k_new, v_new, kc, vc, slots)
         if ev is not None:
             ev[1].record()
         pa.decode(out, q, kc, vc, bt, ctx, case.scale, max_ctx, partition_size=args.partition, workspace=ws)
@@ -232,11 +300,13 @@ def main():
     probe = time_copies(4096)
     log(f"copy_blocks: {cow}; copy probe: {probe}")
 
-    decode_bytes, append_bytes = algorithmic_bytes(case)
+    decode_bytes, append_bytes = algorithmic_bytes(case, timed_steps)
     step_bytes = decode_bytes + append_bytes
     value = step_bytes / (ms_step * 1e-3) / 1e9
     achieved = decode_bytes / (decode_ms * 1e-3) / 1e9
-    traffic = traffic_from_profiles(kernel_source_sha())
+    # The committed counters cover the default workload at the default partition.
+    traffic = (traffic_from_profiles(kernel_source_sha())
+               if args.config == 2 and args.partition in (0, pa.partition_tokens(S, H, max_ctx)) else None)
 
     result = {
         "metric": METRIC,
@@ -253,7 +323,8 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": WORKLOADS[args.config],
-            "step": "reshape_and_cache (1 new token per sequence) + pa_decode",
+            "step": ("reshape_and_cache (1 new token per sequence) + pa_decode" if timed_steps else
+                     "pa_decode (prompt write, copy-on-write fork and suffix writes done before timing)"),
             "num_seqs": S,
             "num_heads": H,
             "head_dim": D,
@@ -278,13 +349,29 @@ def main():
             "algorithmic_bytes_per_launch": int(decode_bytes),
             "avg_launch_us": round(decode_ms * 1e3, 2),
         },
-        "append_us": round(append_ms * 1e3, 2),
+        "append_us": round(append_ms * 1e3, 2) if timed_steps else None,
         "copy_blocks": cow,
         "hbm_copy_probe": probe,
     }
+    if args.config == 4:
+        ub = unique_kv_bytes(case)
+        result["unique_kv_bytes"] = int(ub)
+        result["unique_kv_GBps"] = round(ub / (decode_ms * 1e-3) / 1e9, 1)
+        result["kv_memory_saved_by_sharing"] = round(case.meta["kv_memory_saved"], 4)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on the same batch")
-        result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds, step_bytes)
+        setup_pools = None
+        if setup_steps:
+            import oracle
+
+            kc, vc = case.k_cache, case.v_cache
+            for st in setup_steps:
+                if isinstance(st, wl.AppendStep):
+                    kc, vc = oracle.reshape_and_cache(st.key, st.value, kc, vc, st.slot_mapping)
+                else:
+                    kc, vc = oracle.copy_blocks(kc, vc, st.pairs)
+            setup_pools = (kc, vc)
+        result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds, timed_steps, setup_pools)
     print(json.dumps(result), flush=True)
 
 
