@@ -339,7 +339,8 @@ def main():
         "decode_tokens_per_s": round(S / (ms_step * 1e-3), 1),
         "step_bytes": int(step_bytes),
         "roofline": {
-            "kernel": "pa_decode (partition kernel + merge kernel), event-timed",
+            "kernel": "pa_decode (decode_partition_kernel, plus decode_merge_kernel when a context is split), "
+                      "event-timed",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,

@@ -63,12 +63,19 @@ typedef enum {
  * pa_decode_partition_tokens - KV partition length pa_decode will use.
  *
  * Each (sequence, head) context is split into partitions of this many tokens,
- * one workgroup each.  A positive `partition_size` is returned unchanged.  0
- * selects the default: the largest power of two in [256, 4096], and not above
- * the next power of two of max_context_len, for which
- * num_seqs * num_heads * ceil(max_context_len / P) is at least 8192, so the
- * grid keeps all compute units busy until its end.  Returns 0 for invalid
- * sizes.
+ * one workgroup each; workgroups are dispatched in grid order.  A positive
+ * `partition_size` is returned unchanged.  0 selects the default, from the
+ * number of (sequence, head) pairs S*H:
+ *   S*H >= 8192:  the whole context (next power of two of max_context_len,
+ *                 clamped to [256, 4096]) per workgroup, in batch order;
+ *   1024 <= S*H < 8192 and S <= 512:  whole contexts as above, dispatched
+ *                 longest context first (no split, no merge launch);
+ *   otherwise:    the largest power of two in [256, 4096] (not above the
+ *                 next power of two of max_context_len) that still gives
+ *                 S*H*ceil(max_context_len / P) >= 8192 work items, in
+ *                 batch order.
+ * Longest-first order applies only when no context is split.
+ * Returns 0 for invalid sizes.
  */
 int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_heads, int32_t max_context_len,
                                    int32_t partition_size);

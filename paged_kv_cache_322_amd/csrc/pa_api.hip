@@ -21,8 +21,7 @@ bool supported_block_size(int32_t b) { return b >= 1 && b <= 256 && (b & (b - 1)
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int resolve_partition(int32_t partition_size, int32_t num_seqs, int32_t num_heads, int32_t max_context_len) {
-    return partition_size != 0 ? partition_size
-                               : pa::default_partition_tokens(num_seqs, num_heads, max_context_len);
+    return pa::plan_decode(num_seqs, num_heads, max_context_len, partition_size).part_tokens;
 }
 
 int64_t parts_for(int32_t max_context_len, int part) {
@@ -85,7 +84,8 @@ int pa_decode(void* out, const void* query, const void* k_cache, const void* v_c
     if (static_cast<int64_t>(num_heads) * block_size * head_dim > 0x7FFFFFFF) return PA_ERR_INVALID;
     if (!aligned16(out) || !aligned16(query) || !aligned16(k_cache) || !aligned16(v_cache))
         return PA_ERR_INVALID;
-    const int part = resolve_partition(partition_size, num_seqs, num_heads, max_context_len);
+    const pa::DecodePlan plan = pa::plan_decode(num_seqs, num_heads, max_context_len, partition_size);
+    const int part = plan.part_tokens;
     // A partition may start mid-block, so it touches at most ceil(P/B) + 1 blocks.
     const int64_t staged = pa::partition_blocks(part, block_size);
     if (staged > pa::kMaxPartitionBlocks) return PA_ERR_INVALID;
@@ -116,6 +116,7 @@ int pa_decode(void* out, const void* query, const void* k_cache, const void* v_c
     a.part_tokens = part;
     a.max_parts = static_cast<int>(parts);
     a.staged_blocks = static_cast<int>(staged);
+    a.longest_first = plan.longest_first;
     a.workspace = need ? workspace : nullptr;
     a.stream = static_cast<hipStream_t>(stream);
     return hip_status(pa::launch_decode(a));

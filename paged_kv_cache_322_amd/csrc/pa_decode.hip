@@ -56,6 +56,7 @@ namespace pa {
 
 constexpr int kWgWaves = PA_WG_WAVES;
 constexpr int kThreads = kWgWaves * kWave;
+static_assert(kMaxLptSeqs <= kThreads, "one thread ranks one sequence");
 constexpr int kMergeMaxParts = 256;  // partition weights cached in LDS by the merge kernel
 
 template <class T, int D>
@@ -75,8 +76,8 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(
     float* __restrict__ ws_l, const typename T::bits* __restrict__ q,
     const typename T::bits* __restrict__ kc, const typename T::bits* __restrict__ vc,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
-    int num_heads, int log2_bs, int max_blocks_per_seq, int max_context_len, int64_t num_blocks,
-    int part_tokens, int max_parts, float qscale) {
+    int num_seqs, int num_heads, int log2_bs, int max_blocks_per_seq, int max_context_len,
+    int64_t num_blocks, int part_tokens, int max_parts, int longest_first, float qscale) {
     using Sh = DecodeShape<T, D>;
     constexpr int VEC = Sh::VEC, LPR = Sh::LPR, TPL = Sh::TPL, NL = Sh::NL, U = Sh::U;
 
@@ -85,11 +86,32 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(
     __shared__ float s_o[kWgWaves][D];
 
 #if PA_PART_MAJOR
-    const int h = blockIdx.x, s = blockIdx.y, part = blockIdx.z;
+    const int h = blockIdx.x, srow = blockIdx.y, part = blockIdx.z;
 #else
-    const int part = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+    const int part = blockIdx.x, h = blockIdx.y, srow = blockIdx.z;
 #endif
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    int s = srow;
+    if (longest_first) {
+        // Grid row r handles the sequence of rank r in decreasing context
+        // length (ties by index), so the longest contexts are dispatched
+        // first.  num_seqs <= kMaxLptSeqs <= kThreads (host check).
+        __shared__ int s_len[kMaxLptSeqs];
+        __shared__ int s_pick;
+        if (tid < num_seqs) s_len[tid] = context_lens[tid];
+        __syncthreads();
+        if (tid < num_seqs) {
+            const int c = s_len[tid];
+            int rank = 0;
+            for (int j = 0; j < num_seqs; ++j) {
+                const int cj = s_len[j];
+                rank += (cj > c) || (cj == c && j < tid);
+            }
+            if (rank == srow) s_pick = tid;
+        }
+        __syncthreads();
+        s = s_pick;
+    }
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int row = lane / LPR, col = lane % LPR;
     const int64_t sh = static_cast<int64_t>(s) * num_heads + h;
@@ -322,8 +344,9 @@ static hipError_t launch_decode_t(const DecodeArgs& a) {
     hipLaunchKernelGGL((decode_partition_kernel<T, D>), grid, dim3(kThreads), lds, a.stream, out, ws_o,
                        ws_m, ws_l, static_cast<const bits*>(a.query),
                        static_cast<const bits*>(a.k_cache), static_cast<const bits*>(a.v_cache),
-                       a.block_tables, a.context_lens, a.num_heads, log2_bs, a.max_blocks_per_seq,
-                       a.max_context_len, a.num_blocks, a.part_tokens, a.max_parts, qscale);
+                       a.block_tables, a.context_lens, a.num_seqs, a.num_heads, log2_bs,
+                       a.max_blocks_per_seq, a.max_context_len, a.num_blocks, a.part_tokens, a.max_parts,
+                       a.longest_first ? 1 : 0, qscale);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || a.max_parts <= 1) return err;
     hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(a.num_heads, a.num_seqs), dim3(kWave), 0,

@@ -11,21 +11,53 @@ namespace pa {
 // ids are staged in LDS: at most 32 KB).
 constexpr int kMaxPartitionBlocks = 8192;
 
-// Default KV partition: the largest power of two in [256, 4096] tokens (and
-// not above the next power of two of the longest context) that still yields
-// at least kTargetWorkItems (sequence, head, partition) work items, so that
-// the 256 compute units stay busy to the end of the grid.
+// Launch plan of pa_decode.
+//
+// Work items are (sequence, head, KV partition).  The hardware dispatches
+// workgroups in grid order, so the order of the items decides how evenly the
+// 256 compute units finish.
+//  * Many (sequence, head) pairs (>= kManyPairs): whole contexts up to 4096
+//    tokens per item, in batch order (the items are many and short enough).
+//  * Fewer pairs but at least kLptPairs, and at most kMaxLptSeqs sequences:
+//    whole contexts, dispatched longest first (each workgroup finds the
+//    sequence of its rank; longest-processing-time-first list scheduling).
+//    No split means no merge launch.
+//  * Otherwise: split contexts into the largest power-of-two partition in
+//    [256, 4096] that still gives >= kManyPairs items, in batch order.
+// A caller-given partition length overrides the length choice.  Longest-first
+// order is used only when no context is split: with splits, the empty
+// partitions of short sequences would pay for the ranking before exiting.
 constexpr int kMinDefaultPartition = 256;
 constexpr int kMaxDefaultPartition = 4096;
-constexpr int64_t kTargetWorkItems = 8192;
+constexpr int64_t kManyPairs = 8192;
+constexpr int64_t kLptPairs = 1024;
+constexpr int kMaxLptSeqs = 512;
 
-inline int default_partition_tokens(int64_t num_seqs, int64_t num_heads, int64_t max_context_len) {
-    int part = kMinDefaultPartition;
-    while (part < kMaxDefaultPartition && part < max_context_len) part *= 2;
+struct DecodePlan {
+    int part_tokens;
+    bool longest_first;
+};
+
+inline DecodePlan plan_decode(int64_t num_seqs, int64_t num_heads, int64_t max_context_len, int partition_size) {
     const int64_t pairs = num_seqs * num_heads;
-    while (part > kMinDefaultPartition && pairs * ((max_context_len + part - 1) / part) < kTargetWorkItems)
-        part /= 2;
-    return part;
+    int whole = kMinDefaultPartition;
+    while (whole < kMaxDefaultPartition && whole < max_context_len) whole *= 2;
+    DecodePlan p{whole, false};
+    const bool can_sort = num_seqs <= kMaxLptSeqs;
+    if (pairs >= kManyPairs) {
+        p.part_tokens = whole;
+    } else if (pairs >= kLptPairs && can_sort) {
+        p.part_tokens = whole;
+        p.longest_first = true;
+    } else {
+        int part = whole;
+        while (part > kMinDefaultPartition && pairs * ((max_context_len + part - 1) / part) < kManyPairs)
+            part /= 2;
+        p.part_tokens = part;
+    }
+    if (partition_size > 0) p.part_tokens = partition_size;
+    if (p.part_tokens < max_context_len) p.longest_first = false;
+    return p;
 }
 
 // Blocks a partition of `part` tokens can touch when it starts mid-block.
@@ -47,6 +79,7 @@ struct DecodeArgs {
     int dtype;
     int part_tokens, max_parts;
     int staged_blocks;  // LDS entries for a partition's block ids
+    bool longest_first; // map grid rows to sequences in decreasing context length
     void* workspace;  // float [S*H*max_parts*D] then [S*H*max_parts] x 2; NULL when max_parts == 1
     hipStream_t stream;
 };

@@ -39,9 +39,10 @@ def test_status_strings():
 
 
 def test_default_partition_heuristic():
-    # Largest power of two in [256, 4096] (<= next pow2 of the longest context)
-    # giving >= 8192 (sequence, head, partition) items.
-    assert pa.partition_tokens(64, 32, 2013) == 512  # LLaMA-7B-shaped batch
+    # Many pairs, or 1024..8191 pairs over <= 512 sequences: whole contexts.
+    # Otherwise the largest power of two in [256, 4096] giving >= 8192 items.
+    assert pa.partition_tokens(64, 32, 2013) == 2048  # LLaMA-7B-shaped batch: whole, longest first
+    assert pa.partition_tokens(600, 2, 2013) == 256  # too many sequences to rank: split
     assert pa.partition_tokens(256, 40, 2048) == 2048  # OPT-13B-shaped batch
     assert pa.partition_tokens(128, 96, 2048) == 2048  # OPT-175B-shaped batch
     assert pa.partition_tokens(256, 40, 756) == 1024
@@ -54,7 +55,8 @@ def test_default_partition_heuristic():
 
 def test_workspace_size():
     assert pa.decode_workspace_size(64, 32, 128, 256) == 0  # one default partition suffices
-    assert pa.decode_workspace_size(64, 32, 128, 513) == 64 * 32 * 3 * 130 * 4  # default 256
+    assert pa.decode_workspace_size(64, 32, 128, 513) == 0  # whole contexts (1024), longest first
+    assert pa.decode_workspace_size(8, 32, 128, 513) == 8 * 32 * 3 * 130 * 4  # few pairs: default 256
     assert pa.decode_workspace_size(64, 32, 128, 513, 512) == 64 * 32 * 2 * 130 * 4
     assert pa.decode_workspace_size(128, 96, 128, 2048) == 0  # default 2048
     assert pa.decode_workspace_size(128, 96, 128, 2048, 256) == 128 * 96 * 8 * 130 * 4

@@ -18,10 +18,13 @@ MAX_PART_BLOCKS = 8192
 
 
 def default_partition(S, H, max_ctx):
-    """Mirror of the library's default partition rule."""
-    part = 256
-    while part < 4096 and part < max_ctx:
-        part *= 2
+    """Mirror of the library's default partition rule (plan_decode)."""
+    whole = 256
+    while whole < 4096 and whole < max_ctx:
+        whole *= 2
+    if S * H >= 8192 or (S * H >= 1024 and S <= 512):
+        return whole
+    part = whole
     while part > 256 and S * H * (-(-max_ctx // part)) < 8192:
         part //= 2
     return part
