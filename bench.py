@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--config", type=int, default=2, choices=sorted(WORKLOADS))
     ap.add_argument("--partition", type=int, default=0, help="KV partition tokens (0 = library default)")
     ap.add_argument("--block-size", type=int, default=16, help="block size for config 4 (8, 16 or 32)")
+    ap.add_argument("--shared-blocks", choices=["auto", "on", "off"], default="auto",
+                    help="PA_DECODE_SHARED_BLOCKS (cached K/V loads); auto = on for config 4, whose samples share "
+                         "prompt blocks")
     ap.add_argument("--rotate", type=int, default=2, help="independent pool copies cycled across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle baseline")
@@ -76,13 +79,19 @@ def make_case(cfg, block_size=16):
 
 
 def algorithmic_bytes(case, timed_steps):
+    """(decode bytes, store bytes) of one step.
+
+    decode: K and V of every context token (the newest token's included,
+    wherever it is read from), q, out, block ids, context lengths.
+    store: writing the newest tokens' K and V rows into the caches.
+    """
     e = case.elem_bytes
     S, H, D, B = case.num_seqs, case.num_heads, case.head_dim, case.block_size
     ctx = case.context_lens.astype(np.int64)
     decode = 2 * e * H * D * int(ctx.sum()) + 2 * S * H * D * e + 4 * int(np.ceil(ctx / B).sum()) + 4 * S
     T = sum(st.slot_mapping.size for st in timed_steps)
-    append = 4 * T * H * D * e + 8 * T
-    return decode, append
+    store = 2 * T * H * D * e
+    return decode, store
 
 
 def unique_kv_bytes(case):
@@ -178,7 +187,7 @@ def cpu_baseline(case, target_s, timed_steps, setup_pools=None):
     H, D, B = case.num_heads, case.head_dim, case.block_size
     ctx = case.context_lens[:k].astype(np.int64)
     nbytes = 2 * e * H * D * int(ctx.sum()) + 2 * k * H * D * e + 4 * int(np.ceil(ctx / B).sum()) + 4 * k
-    nbytes += sum(4 * k * H * D * e + 8 * k for _ in timed_steps)
+    nbytes += sum(2 * k * H * D * e for _ in timed_steps)
     return {
         "value": round(nbytes / best / 1e9, 4),
         "unit": "GB/s",
@@ -244,35 +253,60 @@ def main():
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
-    def step(i, ev=None):
+    shared = args.shared_blocks == "on" or (args.shared_blocks == "auto" and args.config == 4)
+    fused = bool(timed_steps)
+    if fused:
+        assert len(timed_steps) == 1 and timed_steps[0].slot_mapping.size == S  # one newest row per sequence
+        k_new, v_new, slots = appends[0]
+
+    def step_fused(i, ev=None):
         kc, vc = pools[i % len(pools)]
         if ev is not None:
             ev[0].record()
-        for k_new, v_new, slots in appends:
-            pa.reshape_and_cache(k_new, v_new, kc, vc, slots)
+        pa.append_decode(out, q, k_new, v_new, kc, vc, bt, ctx, case.scale, max_ctx,
+                         partition_size=args.partition, workspace=ws, shared_blocks=shared)
         if ev is not None:
             ev[1].record()
-        pa.decode(out, q, kc, vc, bt, ctx, case.scale, max_ctx, partition_size=args.partition, workspace=ws)
+
+    def step_two(i, ev=None):
+        kc, vc = pools[i % len(pools)]
+        if ev is not None:
+            ev[0].record()
+        for kn, vn, sl in appends:
+            pa.reshape_and_cache(kn, vn, kc, vc, sl)
+        if ev is not None:
+            ev[1].record()
+        pa.decode(out, q, kc, vc, bt, ctx, case.scale, max_ctx, partition_size=args.partition, workspace=ws,
+                  shared_blocks=shared)
         if ev is not None:
             ev[2].record()
 
-    log(f"warmup {args.warmup} steps")
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    def run(step, nev):
+        """Step time from an uninstrumented pass; per-launch times from a
+        second pass with HIP events around each launch."""
+        for i in range(args.warmup):
+            step(i)
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        for i in range(args.steps):
+            step(i)
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / args.steps
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            step(i, evs[i])
+        torch.cuda.synchronize()
+        spans = [float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j in range(nev - 1)]
+        return ms, spans
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record()
-    for i in range(args.steps):
-        step(i, evs[i])
-    t_end.record()
-    torch.cuda.synchronize()
-    ms_step = t_start.elapsed_time(t_end) / args.steps
-    append_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    decode_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    log(f"timed {args.steps} steps: {ms_step*1e3:.1f} us/step (append {append_ms*1e3:.1f} us, decode {decode_ms*1e3:.1f} us)")
+    log(f"warmup {args.warmup} steps, then {args.steps} timed steps")
+    ms_step, (append_ms, launch_ms) = run(step_two, 3)
+    log(f"step {ms_step*1e3:.1f} us (append {append_ms*1e3:.1f} us, decode {launch_ms*1e3:.1f} us)")
+    if fused:
+        fused_ms, (fused_launch_ms,) = run(step_fused, 2)
+        log(f"fused step {fused_ms*1e3:.1f} us (launch {fused_launch_ms*1e3:.1f} us)")
 
     # Copy-on-write block copies, timed beside the step on the first pool:
     # a fork-sized batch (192 pairs) and a large batch used as the HBM copy probe.
@@ -300,10 +334,10 @@ def main():
     probe = time_copies(4096)
     log(f"copy_blocks: {cow}; copy probe: {probe}")
 
-    decode_bytes, append_bytes = algorithmic_bytes(case, timed_steps)
-    step_bytes = decode_bytes + append_bytes
+    decode_bytes, store_bytes = algorithmic_bytes(case, timed_steps)
+    step_bytes = decode_bytes + store_bytes
     value = step_bytes / (ms_step * 1e-3) / 1e9
-    achieved = decode_bytes / (decode_ms * 1e-3) / 1e9
+    achieved = decode_bytes / (launch_ms * 1e-3) / 1e9
     # The committed counters cover the default workload at the default partition.
     traffic = (traffic_from_profiles(kernel_source_sha())
                if args.config == 2 and args.partition in (0, pa.partition_tokens(S, H, max_ctx)) else None)
@@ -323,7 +357,7 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": WORKLOADS[args.config],
-            "step": ("reshape_and_cache (1 new token per sequence) + pa_decode" if timed_steps else
+            "step": ("pa_reshape_and_cache (1 new token per sequence) + pa_decode" if fused else
                      "pa_decode (prompt write, copy-on-write fork and suffix writes done before timing)"),
             "num_seqs": S,
             "num_heads": H,
@@ -334,6 +368,7 @@ def main():
             "max_context_len": max_ctx,
             "partition_tokens": pa.partition_tokens(S, H, max_ctx, args.partition),
             "pool_copies_rotated": len(pools),
+            "shared_blocks_flag": shared,
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "decode_tokens_per_s": round(S / (ms_step * 1e-3), 1),
@@ -348,16 +383,19 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
             "algorithmic_bytes_per_launch": int(decode_bytes),
-            "avg_launch_us": round(decode_ms * 1e3, 2),
+            "avg_launch_us": round(launch_ms * 1e3, 2),
         },
-        "append_us": round(append_ms * 1e3, 2) if timed_steps else None,
+        "append_us": round(append_ms * 1e3, 2) if fused else None,
+        "fused": ({"entry_point": "pa_append_decode", "ms_per_step": round(fused_ms, 5),
+                   "GB/s": round(step_bytes / (fused_ms * 1e-3) / 1e9, 1),
+                   "launch_us": round(fused_launch_ms * 1e3, 2)} if fused else None),
         "copy_blocks": cow,
         "hbm_copy_probe": probe,
     }
     if args.config == 4:
         ub = unique_kv_bytes(case)
         result["unique_kv_bytes"] = int(ub)
-        result["unique_kv_GBps"] = round(ub / (decode_ms * 1e-3) / 1e9, 1)
+        result["unique_kv_GBps"] = round(ub / (launch_ms * 1e-3) / 1e9, 1)
         result["kv_memory_saved_by_sharing"] = round(case.meta["kv_memory_saved"], 4)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on the same batch")

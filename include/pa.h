@@ -7,6 +7,8 @@
  *   pa_decode             single-query (decode) attention over the blocks
  *   pa_reshape_and_cache  write new tokens' K/V rows into slot-mapped blocks
  *   pa_copy_blocks        copy-on-write duplication of whole blocks
+ *   pa_append_decode      pa_reshape_and_cache of each sequence's newest
+ *                         token fused with pa_decode (one launch)
  *
  * Memory layout (every array dense, row-major, no padding):
  *   query, out          [num_seqs, num_heads, head_dim]              element type `dtype`
@@ -55,6 +57,13 @@ typedef enum {
     PA_ERR_INVALID = 3,     /* sizes, alignment, scale or workspace out of range */
     PA_ERR_HIP = 4          /* the HIP runtime rejected a launch */
 } pa_status;
+
+/* pa_decode / pa_append_decode flags. */
+#define PA_DECODE_SHARED_BLOCKS 1u /* some blocks are read by several sequences of the batch
+                                      (forked samples, shared prefixes): load K/V through the
+                                      caches so sibling sequences hit in L2.  Without it, K/V
+                                      are streamed with non-temporal loads, the faster choice
+                                      when every block is read once.  Results are identical. */
 
 /* Supported shapes: head_dim in {8, 16, 32, 64, 128, 256}; block_size a power
  * of two in [1, 256]; num_seqs and num_heads at most 65535. */
@@ -119,6 +128,7 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t hea
  *   scale          finite softmax scale (1/sqrt(D) for standard attention)
  *   partition_size tokens per KV partition, 0 = default (see
  *                  pa_decode_partition_tokens); ceil(P / B) + 1 <= 8192
+ *   flags          0 or PA_DECODE_SHARED_BLOCKS (other bits: PA_ERR_INVALID)
  *   workspace      device scratch of at least pa_decode_workspace_size(...)
  *                  bytes, 4-byte aligned; contents need no initialisation
  *
@@ -133,8 +143,33 @@ int pa_decode(void* out, const void* query, const void* k_cache, const void* v_c
               const int32_t* block_tables, const int32_t* context_lens,
               int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t block_size,
               int32_t max_blocks_per_seq, int32_t max_context_len, int64_t num_blocks,
-              float scale, int32_t dtype, int32_t partition_size,
+              float scale, int32_t dtype, int32_t partition_size, uint32_t flags,
               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_append_decode - one decode step: store every sequence's newest K/V row,
+ * then attend over the whole context, in a single launch.
+ *
+ * The same result as pa_reshape_and_cache with
+ *   slot_mapping[s] = block_tables[s][(ctx_s - 1) / B] * B + (ctx_s - 1) % B
+ * followed by pa_decode (the newest token of a sequence is its last context
+ * token; a new block is taken only when the current one is full, Velog "LLM
+ * Inference 8: PagedAttention", how PagedAttention works).  key and value
+ * are [S, H, D] in `dtype`, 16-byte aligned: row s is token ctx_s - 1 of
+ * sequence s.  The workgroup whose KV partition holds that token writes the
+ * rows into both caches and reads them from key/value directly.  A sequence
+ * with context length 0 (or an impossible one, see pa_decode) stores
+ * nothing.  Other arguments, errors and guards as for pa_decode; the block
+ * holding a newest token must not be shared with another sequence (copy it
+ * first with pa_copy_blocks).
+ */
+int pa_append_decode(void* out, const void* query, const void* key, const void* value,
+                     void* k_cache, void* v_cache, const int32_t* block_tables,
+                     const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                     int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                     int32_t max_context_len, int64_t num_blocks, float scale, int32_t dtype,
+                     int32_t partition_size, uint32_t flags, void* workspace, size_t workspace_bytes,
+                     void* stream);
 
 /*
  * pa_reshape_and_cache - store new tokens' keys and values in their slots.

@@ -9,11 +9,13 @@ to closed forms, invariants, a library routine, brute force on tiny inputs
 and the pages' own block-table layouts.
 """
 from .paged_attention import (
+    append_decode,
     attention,
     blocks_held,
     copy_blocks,
     logical_kv,
     merge_partials,
+    newest_token_slots,
     paged_decode,
     partial_attention,
     reshape_and_cache,
@@ -22,11 +24,13 @@ from .paged_attention import (
 )
 
 __all__ = [
+    "append_decode",
     "attention",
     "blocks_held",
     "copy_blocks",
     "logical_kv",
     "merge_partials",
+    "newest_token_slots",
     "paged_decode",
     "partial_attention",
     "reshape_and_cache",

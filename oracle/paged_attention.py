@@ -216,3 +216,28 @@ def copy_blocks(k_cache, v_cache, pairs):
         kc[dst] = k_cache[src]
         vc[dst] = v_cache[src]
     return kc, vc
+
+
+# ---------------------------------------------------------------------------
+# One decode step: store each sequence's newest token, then attend
+# ---------------------------------------------------------------------------
+
+
+def newest_token_slots(block_tables, context_lens, block_size):
+    """Slot of every sequence's newest token (position ctx - 1): block
+    (ctx - 1) // B of its table at offset (ctx - 1) % B; -1 when ctx <= 0."""
+    out = np.full(len(context_lens), -1, dtype=np.int64)
+    for s, ctx in enumerate(context_lens):
+        if ctx > 0:
+            b, off = token_location(block_tables[s], int(ctx) - 1, block_size)
+            out[s] = b * block_size + off
+    return out
+
+
+def append_decode(q, key, value, k_cache, v_cache, block_tables, context_lens, scale, dtype):
+    """The newest token's rows (key, value [S, H, D]) stored at their slots,
+    then paged decode over the updated pools.  Returns (out, k_cache', v_cache')."""
+    B = k_cache.shape[2]
+    slots = newest_token_slots(block_tables, context_lens, B)
+    kc, vc = reshape_and_cache(key, value, k_cache, v_cache, slots)
+    return paged_decode(q, kc, vc, block_tables, context_lens, scale, dtype), kc, vc

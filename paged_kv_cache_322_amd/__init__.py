@@ -22,6 +22,7 @@ __all__ = [
     "LIB_PATH",
     "lib",
     "decode",
+    "append_decode",
     "decode_workspace_size",
     "reshape_and_cache",
     "copy_blocks",
@@ -50,14 +51,19 @@ lib.pa_decode_partition_tokens.argtypes = [_i32, _i32, _i32, _i32]
 lib.pa_decode_workspace_size.restype = ctypes.c_size_t
 lib.pa_decode_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32]
 lib.pa_decode.restype = ctypes.c_int
+_u32 = ctypes.c_uint32
 lib.pa_decode.argtypes = [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i64,
-                          ctypes.c_float, _i32, _i32, _p, ctypes.c_size_t, _p]
+                          ctypes.c_float, _i32, _i32, _u32, _p, ctypes.c_size_t, _p]
+lib.pa_append_decode.restype = ctypes.c_int
+lib.pa_append_decode.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i64,
+                                 ctypes.c_float, _i32, _i32, _u32, _p, ctypes.c_size_t, _p]
 lib.pa_reshape_and_cache.restype = ctypes.c_int
 lib.pa_reshape_and_cache.argtypes = [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i64, _i32, _p]
 lib.pa_copy_blocks.restype = ctypes.c_int
 lib.pa_copy_blocks.argtypes = [_p, _p, _p, _i32, _i32, _i32, _i32, _i64, _i32, _p]
 
 _DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+SHARED_BLOCKS = 1  # PA_DECODE_SHARED_BLOCKS
 
 
 class PagedAttentionError(RuntimeError):
@@ -112,16 +118,8 @@ def decode_workspace_size(num_seqs: int, num_heads: int, head_dim: int, max_cont
     return int(lib.pa_decode_workspace_size(num_seqs, num_heads, head_dim, max_context_len, partition_size))
 
 
-def decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
-           block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float, max_context_len: int,
-           partition_size: int = 0, workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Paged single-query attention (``pa_decode``); writes and returns ``out``.
-
-    out, query [S, H, D]; key_cache, value_cache [N, H, B, D]; block_tables
-    int32 [S, W]; context_lens int32 [S]; ``max_context_len`` a host bound on
-    context_lens.  ``workspace`` (uint8, >= decode_workspace_size bytes) is
-    allocated from torch's caching allocator when not given.
-    """
+def _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, max_context_len,
+                 partition_size, workspace, stream):
     _dev(query, "query", ndim=3)
     dt = query.dtype
     _dev(out, "out", dt, 3)
@@ -144,13 +142,51 @@ def decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor, valu
     if workspace is not None:
         _dev(workspace, "workspace")
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    st = lib.pa_decode(
-        out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
-        block_tables.data_ptr(), context_lens.data_ptr(), S, H, D, B, block_tables.shape[1],
-        int(max_context_len), N, float(scale), _code(dt), int(partition_size), ws_ptr, ws_bytes,
-        _stream_handle(query.device, stream),
-    )
+    tail = (block_tables.data_ptr(), context_lens.data_ptr(), S, H, D, B, block_tables.shape[1],
+            int(max_context_len), N)
+    return dt, tail, ws_ptr, ws_bytes
+
+
+def decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+           block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float, max_context_len: int,
+           partition_size: int = 0, workspace: Optional[torch.Tensor] = None, stream=None,
+           shared_blocks: bool = False) -> torch.Tensor:
+    """Paged single-query attention (``pa_decode``); writes and returns ``out``.
+
+    out, query [S, H, D]; key_cache, value_cache [N, H, B, D]; block_tables
+    int32 [S, W]; context_lens int32 [S]; ``max_context_len`` a host bound on
+    context_lens.  ``workspace`` (uint8, >= decode_workspace_size bytes) is
+    allocated from torch's caching allocator when not given.
+    ``shared_blocks``: some blocks are read by several sequences (forked
+    samples, shared prefixes): load K/V through the caches.
+    """
+    dt, tail, ws_ptr, ws_bytes = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens,
+                                              max_context_len, partition_size, workspace, stream)
+    st = lib.pa_decode(out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(), *tail,
+                       float(scale), _code(dt), int(partition_size), SHARED_BLOCKS if shared_blocks else 0,
+                       ws_ptr, ws_bytes, _stream_handle(query.device, stream))
     _check(st, "pa_decode")
+    return out
+
+
+def append_decode(out: torch.Tensor, query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                  key_cache: torch.Tensor, value_cache: torch.Tensor, block_tables: torch.Tensor,
+                  context_lens: torch.Tensor, scale: float, max_context_len: int, partition_size: int = 0,
+                  workspace: Optional[torch.Tensor] = None, stream=None, shared_blocks: bool = False) -> torch.Tensor:
+    """One decode step (``pa_append_decode``): store key/value [S, H, D] as the
+    newest token (position context_lens[s] - 1) of every sequence, then
+    attend; writes the caches and ``out``, returns ``out``."""
+    dt, tail, ws_ptr, ws_bytes = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens,
+                                              max_context_len, partition_size, workspace, stream)
+    _dev(key, "key", dt, 3)
+    _dev(value, "value", dt, 3)
+    if tuple(key.shape) != tuple(query.shape) or tuple(value.shape) != tuple(query.shape):
+        raise ValueError("key/value must have the query's shape [S, H, D]")
+    st = lib.pa_append_decode(out.data_ptr(), query.data_ptr(), key.data_ptr(), value.data_ptr(),
+                              key_cache.data_ptr(), value_cache.data_ptr(), *tail, float(scale), _code(dt),
+                              int(partition_size), SHARED_BLOCKS if shared_blocks else 0, ws_ptr, ws_bytes,
+                              _stream_handle(query.device, stream))
+    _check(st, "pa_append_decode")
     return out
 
 

@@ -39,9 +39,6 @@
 #ifndef PA_PREFETCH
 #define PA_PREFETCH 1  // issue the next step's loads before computing the current one
 #endif
-#ifndef PA_NT_LOADS
-#define PA_NT_LOADS 1  // non-temporal K/V loads
-#endif
 #ifndef PA_STEP_TOKENS
 #define PA_STEP_TOKENS 16  // target tokens per wavefront step
 #endif
@@ -70,11 +67,19 @@ struct DecodeShape {
     static_assert(LPR >= 1 && LPR <= kWave && (kWave % LPR) == 0, "unsupported head_dim");
 };
 
-template <class T, int D>
+// APPEND: the newest token of every sequence (position ctx - 1) arrives in
+// knew/vnew [S, H, D]; the workgroup whose partition holds it stores that
+// head's rows into the caches and reads them from knew/vnew directly.
+// NT: K/V loads are non-temporal (streamed once; measured ~10% faster when no
+// block is shared).  Without NT they are ordinary cached loads, so sequences
+// that share blocks (forked samples, common prefixes) hit in L2 when their
+// workgroups run close together.
+template <class T, int D, bool APPEND, bool NT>
 __global__ __launch_bounds__(kThreads) void decode_partition_kernel(
     typename T::bits* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_m,
     float* __restrict__ ws_l, const typename T::bits* __restrict__ q,
-    const typename T::bits* __restrict__ kc, const typename T::bits* __restrict__ vc,
+    typename T::bits* __restrict__ kc, typename T::bits* __restrict__ vc,
+    const typename T::bits* __restrict__ knew, const typename T::bits* __restrict__ vnew,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
     int num_seqs, int num_heads, int log2_bs, int max_blocks_per_seq, int max_context_len,
     int64_t num_blocks, int part_tokens, int max_parts, int longest_first, float qscale) {
@@ -110,12 +115,12 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(
             if (rank == srow) s_pick = tid;
         }
         __syncthreads();
-        s = s_pick;
+        s = __builtin_amdgcn_readfirstlane(s_pick);  // uniform: keep s and all it decides in SGPRs
     }
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int row = lane / LPR, col = lane % LPR;
     const int64_t sh = static_cast<int64_t>(s) * num_heads + h;
-    const int ctx = context_lens[s];
+    const int ctx = __builtin_amdgcn_readfirstlane(context_lens[s]);
 
     if (ctx <= 0 || ctx > max_context_len) {
         // Empty context -> zeros; impossible length -> NaN.  Partition 0 writes.
@@ -144,7 +149,13 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(
     widen16<T>(load16(q + sh * D + col * VEC), qf);
 #pragma unroll
     for (int v = 0; v < VEC; ++v) qf[v] *= qscale;
-    __syncthreads();
+    __syncthreads();  // s_blk is staged
+
+    // APPEND: in the workgroup whose partition holds the newest token (ctx-1),
+    // the step that covers it (always the partition's last step) reads that
+    // token's rows from knew/vnew instead of the caches, and the lanes
+    // holding them store them into the caches.  All other steps are plain.
+    const bool newest_here = APPEND && t_end == ctx;
 
     // Element offsets: block b starts at b * blk_stride (host guarantees
     // H * B * D < 2^31); this lane's channels of head h at lane_off in it.
@@ -158,8 +169,11 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(
     for (int v = 0; v < VEC; ++v) acc[v] = 0.0f;
     int bad = 0;
 
+    const int niter = (t_end - t_begin + U - 1) / U;
+
     auto load_step = [&](int it, uint4 (&kr)[NL], uint4 (&vr)[NL]) {
         const int tb = t_begin + it * U;
+        const bool newest = APPEND && newest_here && it == niter - 1;  // wave-uniform
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
             // Tokens past the partition re-read the last valid token (always
@@ -170,13 +184,35 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(
             b = max(b, 0);
             const uint64_t e = static_cast<uint64_t>(static_cast<uint32_t>(b)) * blk_stride + lane_off +
                                static_cast<uint32_t>(t & bmask) * D;
-            kr[i] = load16<PA_NT_LOADS>(kc + e);
-            vr[i] = load16<PA_NT_LOADS>(vc + e);
+            const typename T::bits* kp = kc + e;
+            const typename T::bits* vp = vc + e;
+            if (newest && t == ctx - 1) {
+                kp = knew + sh * D + col * VEC;
+                vp = vnew + sh * D + col * VEC;
+            }
+            kr[i] = load16<NT>(kp);
+            vr[i] = load16<NT>(vp);
         }
     };
 
     auto compute_step = [&](int it, const uint4 (&kr)[NL], const uint4 (&vr)[NL]) {
         const int tb = t_begin + it * U;
+        if constexpr (APPEND) {
+            if (newest_here && it == niter - 1) {
+                // The one row of lanes whose (unclamped) token is ctx-1 stores it.
+                const int t = ctx - 1;
+                const int b = s_blk[(t >> log2_bs) - j0];
+                const uint64_t e = static_cast<uint64_t>(static_cast<uint32_t>(max(b, 0))) * blk_stride +
+                                   lane_off + static_cast<uint32_t>(t & bmask) * D;
+#pragma unroll
+                for (int i = 0; i < NL; ++i) {
+                    if (b >= 0 && tb + i * TPL + row == t) {
+                        *reinterpret_cast<uint4*>(kc + e) = kr[i];
+                        *reinterpret_cast<uint4*>(vc + e) = vr[i];
+                    }
+                }
+            }
+        }
         float sc[NL];
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
@@ -211,7 +247,6 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(
         m = m_new;
     };
 
-    const int niter = (t_end - t_begin + U - 1) / U;
     int it = wave;
 #if PA_PREFETCH
     if (it < niter) {
@@ -325,7 +360,7 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(
     }
 }
 
-template <class T, int D>
+template <class T, int D, bool APPEND, bool NT>
 static hipError_t launch_decode_t(const DecodeArgs& a) {
     const int log2_bs = __builtin_ctz(static_cast<unsigned>(a.block_size));
     const float qscale = a.scale * 1.4426950408889634f;  // log2(e)
@@ -341,9 +376,10 @@ static hipError_t launch_decode_t(const DecodeArgs& a) {
     dim3 grid(a.max_parts, a.num_heads, a.num_seqs);
 #endif
     const size_t lds = static_cast<size_t>(a.staged_blocks) * sizeof(int);
-    hipLaunchKernelGGL((decode_partition_kernel<T, D>), grid, dim3(kThreads), lds, a.stream, out, ws_o,
-                       ws_m, ws_l, static_cast<const bits*>(a.query),
-                       static_cast<const bits*>(a.k_cache), static_cast<const bits*>(a.v_cache),
+    hipLaunchKernelGGL((decode_partition_kernel<T, D, APPEND, NT>), grid, dim3(kThreads), lds, a.stream, out,
+                       ws_o, ws_m, ws_l, static_cast<const bits*>(a.query),
+                       static_cast<bits*>(a.k_cache), static_cast<bits*>(a.v_cache),
+                       static_cast<const bits*>(a.key_new), static_cast<const bits*>(a.value_new),
                        a.block_tables, a.context_lens, a.num_seqs, a.num_heads, log2_bs,
                        a.max_blocks_per_seq, a.max_context_len, a.num_blocks, a.part_tokens, a.max_parts,
                        a.longest_first ? 1 : 0, qscale);
@@ -355,26 +391,32 @@ static hipError_t launch_decode_t(const DecodeArgs& a) {
     return hipGetLastError();
 }
 
-template <class T>
+template <class T, bool APPEND, bool NT>
 static hipError_t launch_decode_dim(const DecodeArgs& a) {
     switch (a.head_dim) {
-        case 8: return launch_decode_t<T, 8>(a);
-        case 16: return launch_decode_t<T, 16>(a);
-        case 32: return launch_decode_t<T, 32>(a);
-        case 64: return launch_decode_t<T, 64>(a);
-        case 128: return launch_decode_t<T, 128>(a);
-        case 256: return launch_decode_t<T, 256>(a);
+        case 8: return launch_decode_t<T, 8, APPEND, NT>(a);
+        case 16: return launch_decode_t<T, 16, APPEND, NT>(a);
+        case 32: return launch_decode_t<T, 32, APPEND, NT>(a);
+        case 64: return launch_decode_t<T, 64, APPEND, NT>(a);
+        case 128: return launch_decode_t<T, 128, APPEND, NT>(a);
+        case 256: return launch_decode_t<T, 256, APPEND, NT>(a);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <bool APPEND, bool NT>
+static hipError_t launch_decode_type(const DecodeArgs& a) {
+    switch (a.dtype) {
+        case 0: return launch_decode_dim<F32, APPEND, NT>(a);
+        case 1: return launch_decode_dim<F16, APPEND, NT>(a);
+        case 2: return launch_decode_dim<BF16, APPEND, NT>(a);
         default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_decode(const DecodeArgs& a) {
-    switch (a.dtype) {
-        case 0: return launch_decode_dim<F32>(a);
-        case 1: return launch_decode_dim<F16>(a);
-        case 2: return launch_decode_dim<BF16>(a);
-        default: return hipErrorInvalidValue;
-    }
+    if (a.key_new) return a.cached_loads ? launch_decode_type<true, false>(a) : launch_decode_type<true, true>(a);
+    return a.cached_loads ? launch_decode_type<false, false>(a) : launch_decode_type<false, true>(a);
 }
 
 }  // namespace pa

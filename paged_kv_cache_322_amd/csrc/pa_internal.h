@@ -68,8 +68,10 @@ inline int64_t partition_blocks(int64_t part, int64_t block_size) {
 struct DecodeArgs {
     void* out;
     const void* query;
-    const void* k_cache;
-    const void* v_cache;
+    void* k_cache;  // written only when key_new is set
+    void* v_cache;
+    const void* key_new;    // [S, H, D] newest token's K (append mode) or NULL
+    const void* value_new;  // [S, H, D] newest token's V (append mode) or NULL
     const int32_t* block_tables;
     const int32_t* context_lens;
     int num_seqs, num_heads, head_dim, block_size;
@@ -80,6 +82,7 @@ struct DecodeArgs {
     int part_tokens, max_parts;
     int staged_blocks;  // LDS entries for a partition's block ids
     bool longest_first; // map grid rows to sequences in decreasing context length
+    bool cached_loads;  // ordinary (cached) K/V loads instead of non-temporal ones
     void* workspace;  // float [S*H*max_parts*D] then [S*H*max_parts] x 2; NULL when max_parts == 1
     hipStream_t stream;
 };

@@ -68,12 +68,13 @@ class GpuCase:
             self.run_step(i)
 
     def decode(self, partition: int = 0, out: torch.Tensor | None = None, bt=None, ctx=None, kc=None, vc=None,
-               max_context_len=None) -> torch.Tensor:
+               max_context_len=None, shared_blocks: bool = False) -> torch.Tensor:
         out = self.out if out is None else out
         c = self.case
         pa().decode(out, self.q, self.kc if kc is None else kc, self.vc if vc is None else vc,
                     self.bt if bt is None else bt, self.ctx if ctx is None else ctx, c.scale,
-                    c.max_context_len if max_context_len is None else max_context_len, partition_size=partition)
+                    c.max_context_len if max_context_len is None else max_context_len, partition_size=partition,
+                    shared_blocks=shared_blocks)
         return out
 
 

@@ -10,6 +10,7 @@ least one of them).
 """
 from __future__ import annotations
 
+import functools
 import json
 import math
 import os
@@ -20,6 +21,11 @@ import torch
 import workloads as wl
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+@functools.lru_cache(None)
+def _config3():
+    return wl.config3()
 
 
 def _golden(name):
@@ -396,6 +402,33 @@ def pin_split_merge(orc):
         assert np.abs(orc.merge_partials(parts) - ref).max() <= 1e-13
 
 
+def pin_newest_token_slots(orc):
+    """The newest token's slot agrees with the slots the host block pool
+    handed out when that token was appended (configs built independently of
+    the oracle), with the Digest flowchart's tables, and with ctx <= 0 -> -1;
+    append_decode equals append followed by decode."""
+    case = _config3()
+    st = case.steps[0]
+    assert np.array_equal(orc.newest_token_slots(case.block_tables, case.context_lens, 16), st.slot_mapping)
+    g = _golden("digest_flowchart_layout.json")
+    bt = np.full((2, 3), -1, dtype=np.int32)
+    bt[0, :3] = g["tables"]["seq1"]
+    bt[1, :2] = g["tables"]["seq2"]
+    # Seq1 with 33 tokens: token 32 is the first of block 2 (P1); Seq2 with 17: token 16 opens block 1 (P5).
+    assert orc.newest_token_slots(bt, np.array([33, 17]), 16).tolist() == [1 * 16 + 0, 5 * 16 + 0]
+    assert orc.newest_token_slots(bt, np.array([48, 0]), 16).tolist() == [1 * 16 + 15, -1]
+    small = wl.random_case(17, 4, 2, 8, 4, "bf16", ctx_range=(1, 30), n_append=1)
+    sa = small.steps[0]
+    out, kc, vc = orc.append_decode(small.q, sa.key, sa.value, small.k_cache, small.v_cache, small.block_tables,
+                                    small.context_lens, small.scale, small.dtype)
+    ref = brute_decode(small.q, *orc.reshape_and_cache(sa.key, sa.value, small.k_cache, small.v_cache,
+                                                       sa.slot_mapping), small.block_tables, small.context_lens,
+                       small.scale, small.dtype)
+    assert np.abs(out - ref).max() <= 1e-12
+    assert np.array_equal(wl.bits_view(kc), wl.bits_view(orc.reshape_and_cache(
+        sa.key, sa.value, small.k_cache, small.v_cache, sa.slot_mapping)[0]))
+
+
 ALL_PINS = [
     pin_widen,
     pin_bruteforce,
@@ -407,4 +440,5 @@ ALL_PINS = [
     pin_append,
     pin_cow,
     pin_split_merge,
+    pin_newest_token_slots,
 ]

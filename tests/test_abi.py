@@ -66,11 +66,11 @@ def test_workspace_size():
 
 def dec(**kw):
     a = dict(out=P, query=P, k=P, v=P, bt=P, ctx=P, S=2, H=4, D=128, B=16, W=8, maxc=100, N=64,
-             scale=0.1, dtype=1, part=0, ws=0, wsb=0)
+             scale=0.1, dtype=1, part=0, flags=0, ws=0, wsb=0)
     a.update(kw)
     return pa.lib.pa_decode(a["out"], a["query"], a["k"], a["v"], a["bt"], a["ctx"], a["S"], a["H"], a["D"],
-                            a["B"], a["W"], a["maxc"], a["N"], a["scale"], a["dtype"], a["part"], a["ws"],
-                            a["wsb"], None)
+                            a["B"], a["W"], a["maxc"], a["N"], a["scale"], a["dtype"], a["part"], a["flags"],
+                            a["ws"], a["wsb"], None)
 
 
 def test_decode_host_checks():
@@ -91,6 +91,7 @@ def test_decode_host_checks():
     assert dec(B=1, part=9000, maxc=8) == INVALID  # partition spans too many blocks for LDS staging
     assert dec(H=65535, B=256, D=256) == INVALID  # one block above 2^31 elements
     assert dec(maxc=100, part=16) == NULL  # split needs a workspace
+    assert dec(flags=2) == INVALID  # unknown flag bit
     assert dec(maxc=2000000, W=200000, part=16) == INVALID  # more partitions than grid rows
     need = pa.decode_workspace_size(2, 4, 128, 100, 16)
     assert dec(maxc=100, part=16, ws=P, wsb=need - 1) == INVALID
@@ -136,3 +137,20 @@ def test_binding_rejects_cpu_tensors():
     with pytest.raises(ValueError):
         pa.decode(t, t, t.view(2, 4, 1, 128), t.view(2, 4, 1, 128), torch.zeros(2, 1, dtype=torch.int32),
                   torch.ones(2, dtype=torch.int32), 0.1, 1)
+
+
+def test_append_decode_host_checks():
+    def ad(**kw):
+        a = dict(out=P, query=P, key=P, value=P, k=P, v=P, bt=P, ctx=P, S=2, H=4, D=128, B=16, W=8, maxc=100,
+                 N=64, scale=0.1, dtype=1, part=0, flags=0, ws=0, wsb=0)
+        a.update(kw)
+        return pa.lib.pa_append_decode(a["out"], a["query"], a["key"], a["value"], a["k"], a["v"], a["bt"],
+                                       a["ctx"], a["S"], a["H"], a["D"], a["B"], a["W"], a["maxc"], a["N"],
+                                       a["scale"], a["dtype"], a["part"], a["flags"], a["ws"], a["wsb"], None)
+
+    assert ad(S=0, key=0, value=0) == OK
+    assert ad(key=0) == NULL
+    assert ad(value=0) == NULL
+    assert ad(key=P + 2) == INVALID
+    assert ad(dtype=5) == UNSUP
+    assert ad(maxc=100, part=16) == NULL  # split needs a workspace

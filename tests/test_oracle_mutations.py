@@ -98,6 +98,10 @@ def _partial_no_max(q, K, V, scale):
     return s.max(), w.sum(), w @ V
 
 
+def _newest_off_by_one(block_tables, context_lens, block_size):
+    return _real["newest_token_slots"](block_tables, np.asarray(context_lens) + 1, block_size)
+
+
 MUTANTS = {
     "attention drops the scale": ("attention", _attention_no_scale),
     "softmax exponent sign flipped": ("attention", _attention_flipped),
@@ -113,6 +117,7 @@ MUTANTS = {
     "partials merged without rescaling": ("merge_partials", _merge_no_rescale),
     "heads transposed in the output": ("paged_decode", _decode_wrong_head),
     "partial stats use the wrong reference": ("partial_attention", _partial_no_max),
+    "newest token taken one position late": ("newest_token_slots", _newest_off_by_one),
 }
 
 
