@@ -71,10 +71,11 @@ typedef enum {
 /*
  * pa_decode_partition_tokens - KV partition length pa_decode will use.
  *
- * Each (sequence, head) context is split into partitions of this many tokens,
- * one workgroup each; workgroups are dispatched in grid order.  A positive
- * `partition_size` is returned unchanged.  0 selects the default, from the
- * number of (sequence, head) pairs S*H:
+ * Each (sequence, K/V head) context is split into partitions of this many
+ * tokens, one workgroup each (serving all query heads of that K/V head);
+ * workgroups are dispatched in grid order.  A positive `partition_size` is
+ * returned unchanged.  0 selects the default, from the number of
+ * (sequence, K/V head) pairs S*H (H = num_kv_heads here):
  *   S*H >= 8192:  the whole context (next power of two of max_context_len,
  *                 clamped to [256, 4096]) per workgroup, in batch order;
  *   1024 <= S*H < 8192 and S <= 512:  whole contexts as above, dispatched
@@ -86,7 +87,7 @@ typedef enum {
  * Longest-first order applies only when no context is split.
  * Returns 0 for invalid sizes.
  */
-int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_heads, int32_t max_context_len,
+int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
                                    int32_t partition_size);
 
 /*
@@ -98,8 +99,8 @@ int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_heads, int32_t 
  * partitions (then pa_decode accepts a NULL workspace), and 0 for invalid
  * sizes.  `partition_size` as for pa_decode_partition_tokens.
  */
-size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
-                                int32_t max_context_len, int32_t partition_size);
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t max_context_len, int32_t partition_size);
 
 /*
  * pa_decode - paged single-query attention.
@@ -113,13 +114,17 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t hea
  *   out[s,h,:] = sum_t softmax_t( scale * <query[s,h,:], K_s[t,h,:]> ) * V_s[t,h,:]
  *
  * over t = 0 .. context_lens[s]-1, where token t of sequence s is stored in
- * physical block block_tables[s][t / B] at offset t % B.  Arithmetic is fp32
+ * physical block block_tables[s][t / B] at offset t % B.  With
+ * num_kv_heads < num_heads (grouped-query attention, which the digest's
+ * related work names as an orthogonal way to shrink the cache) the caches
+ * hold num_kv_heads heads and query head h reads K/V head h / G,
+ * G = num_heads / num_kv_heads in {1, 2, 4, 8}.  Arithmetic is fp32
  * (fp32 accumulation of products of widened inputs); out is rounded to
  * `dtype` with round-to-nearest-even.
  *
  *   out            [S, H, D] written
  *   query          [S, H, D] read
- *   k_cache, v_cache  [N, H, B, D] read
+ *   k_cache, v_cache  [N, Hk, B, D] read, Hk = num_kv_heads
  *   block_tables   int32 [S, max_blocks_per_seq] read
  *   context_lens   int32 [S] read
  *   max_context_len  host upper bound of context_lens (sizes the grid without
@@ -133,7 +138,9 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t hea
  *                  bytes, 4-byte aligned; contents need no initialisation
  *
  * query, out and both caches must be 16-byte aligned, and one block of one
- * cache (num_heads * block_size * head_dim elements) below 2^31 elements.
+ * cache (num_kv_heads * block_size * head_dim elements) below 2^31 elements.
+ * num_heads must be a multiple of num_kv_heads (else PA_ERR_INVALID) with a
+ * built group size (else PA_ERR_UNSUPPORTED).
  * Device-side guards:
  * a context length of 0 yields zeros; a context length below 0 or above
  * max_context_len, or a needed block id outside [0, N), yields NaN for that
@@ -141,7 +148,7 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t hea
  */
 int pa_decode(void* out, const void* query, const void* k_cache, const void* v_cache,
               const int32_t* block_tables, const int32_t* context_lens,
-              int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t block_size,
+              int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
               int32_t max_blocks_per_seq, int32_t max_context_len, int64_t num_blocks,
               float scale, int32_t dtype, int32_t partition_size, uint32_t flags,
               void* workspace, size_t workspace_bytes, void* stream);
@@ -155,7 +162,7 @@ int pa_decode(void* out, const void* query, const void* k_cache, const void* v_c
  * followed by pa_decode (the newest token of a sequence is its last context
  * token; a new block is taken only when the current one is full, Velog "LLM
  * Inference 8: PagedAttention", how PagedAttention works).  key and value
- * are [S, H, D] in `dtype`, 16-byte aligned: row s is token ctx_s - 1 of
+ * are [S, Hk, D] in `dtype`, 16-byte aligned: row s is token ctx_s - 1 of
  * sequence s.  The workgroup whose KV partition holds that token writes the
  * rows into both caches and reads them from key/value directly.  A sequence
  * with context length 0 (or an impossible one, see pa_decode) stores
@@ -166,7 +173,7 @@ int pa_decode(void* out, const void* query, const void* k_cache, const void* v_c
 int pa_append_decode(void* out, const void* query, const void* key, const void* value,
                      void* k_cache, void* v_cache, const int32_t* block_tables,
                      const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
-                     int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                      int32_t max_context_len, int64_t num_blocks, float scale, int32_t dtype,
                      int32_t partition_size, uint32_t flags, void* workspace, size_t workspace_bytes,
                      void* stream);
@@ -183,7 +190,8 @@ int pa_append_decode(void* out, const void* query, const void* key, const void* 
  *   k_cache[slot / B, h, slot % B, :] = key[i, h, :]    for every head h
  *   v_cache[slot / B, h, slot % B, :] = value[i, h, :]
  *
- * A bit-exact copy (no arithmetic).  key, value [num_tokens, H, D] read;
+ * A bit-exact copy (no arithmetic).  key, value [num_tokens, H, D] read,
+ * H the caches' head count (num_kv_heads for grouped-query attention);
  * caches written in place.  key, value and the caches must be 16-byte
  * aligned.  Slots must be distinct (duplicates race); a slot at or beyond
  * num_blocks * B is skipped by the kernel.

@@ -113,10 +113,19 @@ def attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.n
 def paged_decode(q, k_cache, v_cache, block_tables, context_lens, scale, dtype) -> np.ndarray:
     """Single-query attention of every (sequence, head) over its paged context.
 
-    q [S, H, D]; k_cache, v_cache [N, H, B, D]; block_tables int [S, W];
+    q [S, H, D]; k_cache, v_cache [N, Hk, B, D]; block_tables int [S, W];
     context_lens int [S].  Returns float64 [S, H, D].
+
+    Hk may be smaller than H (grouped-query attention, named in the
+    PagedAttention digest's related work as a way to shrink the KV cache):
+    consecutive groups of G = H / Hk query heads share one K/V head, query
+    head h reading K/V head h // G.  Hk = H is ordinary multi-head attention.
     """
     S, H, D = q.shape
+    Hk = k_cache.shape[1]
+    if H % Hk:
+        raise ValueError(f"{H} query heads cannot be grouped over {Hk} K/V heads")
+    G = H // Hk
     out = np.zeros((S, H, D), dtype=np.float64)
     for s in range(S):
         ctx = int(context_lens[s])
@@ -126,7 +135,7 @@ def paged_decode(q, k_cache, v_cache, block_tables, context_lens, scale, dtype) 
         V = widen(logical_kv(v_cache, block_tables[s], ctx), dtype)
         qs = widen(q[s], dtype)
         for h in range(H):
-            out[s, h] = attention(qs[h], K[h], V[h], scale)
+            out[s, h] = attention(qs[h], K[h // G], V[h // G], scale)
     return out
 
 

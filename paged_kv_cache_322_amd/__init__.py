@@ -49,14 +49,14 @@ lib.pa_status_string.argtypes = [ctypes.c_int]
 lib.pa_decode_partition_tokens.restype = _i32
 lib.pa_decode_partition_tokens.argtypes = [_i32, _i32, _i32, _i32]
 lib.pa_decode_workspace_size.restype = ctypes.c_size_t
-lib.pa_decode_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32]
+lib.pa_decode_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32]
 lib.pa_decode.restype = ctypes.c_int
 _u32 = ctypes.c_uint32
-lib.pa_decode.argtypes = [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i64,
+lib.pa_decode.argtypes = [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i64,
                           ctypes.c_float, _i32, _i32, _u32, _p, ctypes.c_size_t, _p]
 lib.pa_append_decode.restype = ctypes.c_int
-lib.pa_append_decode.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i64,
-                                 ctypes.c_float, _i32, _i32, _u32, _p, ctypes.c_size_t, _p]
+lib.pa_append_decode.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                 _i64, ctypes.c_float, _i32, _i32, _u32, _p, ctypes.c_size_t, _p]
 lib.pa_reshape_and_cache.restype = ctypes.c_int
 lib.pa_reshape_and_cache.argtypes = [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i64, _i32, _p]
 lib.pa_copy_blocks.restype = ctypes.c_int
@@ -107,15 +107,16 @@ def _code(dtype: torch.dtype) -> int:
         raise TypeError(f"unsupported element type {dtype}; use float32, float16 or bfloat16") from None
 
 
-def partition_tokens(num_seqs: int, num_heads: int, max_context_len: int, partition_size: int = 0) -> int:
+def partition_tokens(num_seqs: int, num_kv_heads: int, max_context_len: int, partition_size: int = 0) -> int:
     """KV partition length ``decode`` uses (``partition_size`` 0 = library default)."""
-    return int(lib.pa_decode_partition_tokens(num_seqs, num_heads, max_context_len, partition_size))
+    return int(lib.pa_decode_partition_tokens(num_seqs, num_kv_heads, max_context_len, partition_size))
 
 
 def decode_workspace_size(num_seqs: int, num_heads: int, head_dim: int, max_context_len: int,
-                          partition_size: int = 0) -> int:
+                          partition_size: int = 0, num_kv_heads: Optional[int] = None) -> int:
     """Bytes of scratch ``decode`` needs (0 if no sequence spans two partitions)."""
-    return int(lib.pa_decode_workspace_size(num_seqs, num_heads, head_dim, max_context_len, partition_size))
+    hk = num_heads if num_kv_heads is None else num_kv_heads
+    return int(lib.pa_decode_workspace_size(num_seqs, num_heads, hk, head_dim, max_context_len, partition_size))
 
 
 def _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, max_context_len,
@@ -131,18 +132,19 @@ def _decode_args(out, query, key_cache, value_cache, block_tables, context_lens,
     N, Hk, B, Dk = key_cache.shape
     if tuple(out.shape) != (S, H, D) or tuple(value_cache.shape) != tuple(key_cache.shape):
         raise ValueError("out/value_cache shapes do not match query/key_cache")
-    if Hk != H or Dk != D:
-        raise ValueError(f"key_cache heads/head_dim {Hk}/{Dk} != query {H}/{D}")
+    if Dk != D or H % Hk:
+        raise ValueError(f"key_cache heads/head_dim {Hk}/{Dk} do not fit query {H}/{D} "
+                         "(query heads must be a multiple of K/V heads)")
     if block_tables.shape[0] != S or context_lens.shape[0] != S:
         raise ValueError("block_tables / context_lens must have one row per sequence")
-    need = decode_workspace_size(S, H, D, max_context_len, partition_size)
+    need = decode_workspace_size(S, H, D, max_context_len, partition_size, Hk)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
     ws_ptr, ws_bytes = 0, 0
     if workspace is not None:
         _dev(workspace, "workspace")
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    tail = (block_tables.data_ptr(), context_lens.data_ptr(), S, H, D, B, block_tables.shape[1],
+    tail = (block_tables.data_ptr(), context_lens.data_ptr(), S, H, Hk, D, B, block_tables.shape[1],
             int(max_context_len), N)
     return dt, tail, ws_ptr, ws_bytes
 
@@ -153,7 +155,8 @@ def decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor, valu
            shared_blocks: bool = False) -> torch.Tensor:
     """Paged single-query attention (``pa_decode``); writes and returns ``out``.
 
-    out, query [S, H, D]; key_cache, value_cache [N, H, B, D]; block_tables
+    out, query [S, H, D]; key_cache, value_cache [N, Hk, B, D] (Hk divides H:
+    grouped-query attention when Hk < H); block_tables
     int32 [S, W]; context_lens int32 [S]; ``max_context_len`` a host bound on
     context_lens.  ``workspace`` (uint8, >= decode_workspace_size bytes) is
     allocated from torch's caching allocator when not given.
@@ -173,15 +176,16 @@ def append_decode(out: torch.Tensor, query: torch.Tensor, key: torch.Tensor, val
                   key_cache: torch.Tensor, value_cache: torch.Tensor, block_tables: torch.Tensor,
                   context_lens: torch.Tensor, scale: float, max_context_len: int, partition_size: int = 0,
                   workspace: Optional[torch.Tensor] = None, stream=None, shared_blocks: bool = False) -> torch.Tensor:
-    """One decode step (``pa_append_decode``): store key/value [S, H, D] as the
+    """One decode step (``pa_append_decode``): store key/value [S, Hk, D] as the
     newest token (position context_lens[s] - 1) of every sequence, then
     attend; writes the caches and ``out``, returns ``out``."""
     dt, tail, ws_ptr, ws_bytes = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens,
                                               max_context_len, partition_size, workspace, stream)
     _dev(key, "key", dt, 3)
     _dev(value, "value", dt, 3)
-    if tuple(key.shape) != tuple(query.shape) or tuple(value.shape) != tuple(query.shape):
-        raise ValueError("key/value must have the query's shape [S, H, D]")
+    kv_shape = (query.shape[0], key_cache.shape[1], query.shape[2])
+    if tuple(key.shape) != kv_shape or tuple(value.shape) != kv_shape:
+        raise ValueError(f"key/value must have shape [S, Hk, D] = {kv_shape}")
     st = lib.pa_append_decode(out.data_ptr(), query.data_ptr(), key.data_ptr(), value.data_ptr(),
                               key_cache.data_ptr(), value_cache.data_ptr(), *tail, float(scale), _code(dt),
                               int(partition_size), SHARED_BLOCKS if shared_blocks else 0, ws_ptr, ws_bytes,

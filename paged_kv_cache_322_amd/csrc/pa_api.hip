@@ -51,17 +51,18 @@ const char* pa_status_string(int status) {
     }
 }
 
-int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_heads, int32_t max_context_len,
+int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
                                    int32_t partition_size) {
-    if (num_seqs < 0 || num_heads <= 0 || max_context_len < 0 || partition_size < 0) return 0;
-    return resolve_partition(partition_size, num_seqs, num_heads, max_context_len);
+    if (num_seqs < 0 || num_kv_heads <= 0 || max_context_len < 0 || partition_size < 0) return 0;
+    return resolve_partition(partition_size, num_seqs, num_kv_heads, max_context_len);
 }
 
-size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                                 int32_t max_context_len, int32_t partition_size) {
-    if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || max_context_len < 0 || partition_size < 0)
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_context_len < 0 ||
+        partition_size < 0)
         return 0;
-    const int part = resolve_partition(partition_size, num_seqs, num_heads, max_context_len);
+    const int part = resolve_partition(partition_size, num_seqs, num_kv_heads, max_context_len);
     return workspace_bytes_for(num_seqs, num_heads, head_dim, parts_for(max_context_len, part));
 }
 
@@ -73,7 +74,8 @@ namespace {
 // decode; the caches are written only in append mode.
 int decode_common(void* out, const void* query, const void* key, const void* value, void* k_cache,
                   void* v_cache, const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
-                  int32_t num_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                  int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                  int32_t max_blocks_per_seq,
                   int32_t max_context_len, int64_t num_blocks, float scale, int32_t dtype,
                   int32_t partition_size, uint32_t flags, void* workspace, size_t workspace_bytes, void* stream,
                   bool append) {
@@ -82,19 +84,21 @@ int decode_common(void* out, const void* query, const void* key, const void* val
     if (num_seqs == 0) return PA_OK;  // nothing to read or write
     if (!out || !query || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
     if (append && (!key || !value)) return PA_ERR_NULL;
-    if (num_seqs < 0 || num_seqs > 65535 || num_heads <= 0 || num_heads > 65535 ||
+    if (num_seqs < 0 || num_seqs > 65535 || num_heads <= 0 || num_heads > 65535 || num_kv_heads <= 0 ||
         max_blocks_per_seq <= 0 || max_context_len < 0 || num_blocks <= 0 || partition_size < 0)
         return PA_ERR_INVALID;
+    if (num_heads % num_kv_heads) return PA_ERR_INVALID;
+    if (!pa::supported_group(num_heads / num_kv_heads)) return PA_ERR_UNSUPPORTED;
     if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
         return PA_ERR_INVALID;
     if (!isfinite(scale)) return PA_ERR_INVALID;
     if (flags & ~static_cast<uint32_t>(PA_DECODE_SHARED_BLOCKS)) return PA_ERR_INVALID;
     // One block of one cache must be addressable with 32-bit element offsets.
-    if (static_cast<int64_t>(num_heads) * block_size * head_dim > 0x7FFFFFFF) return PA_ERR_INVALID;
+    if (static_cast<int64_t>(num_kv_heads) * block_size * head_dim > 0x7FFFFFFF) return PA_ERR_INVALID;
     if (!aligned16(out) || !aligned16(query) || !aligned16(k_cache) || !aligned16(v_cache))
         return PA_ERR_INVALID;
     if (append && (!aligned16(key) || !aligned16(value))) return PA_ERR_INVALID;
-    const pa::DecodePlan plan = pa::plan_decode(num_seqs, num_heads, max_context_len, partition_size);
+    const pa::DecodePlan plan = pa::plan_decode(num_seqs, num_kv_heads, max_context_len, partition_size);
     const int part = plan.part_tokens;
     // A partition may start mid-block, so it touches at most ceil(P/B) + 1 blocks.
     const int64_t staged = pa::partition_blocks(part, block_size);
@@ -118,6 +122,7 @@ int decode_common(void* out, const void* query, const void* key, const void* val
     a.context_lens = context_lens;
     a.num_seqs = num_seqs;
     a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
     a.head_dim = head_dim;
     a.block_size = block_size;
     a.max_blocks_per_seq = max_blocks_per_seq;
@@ -141,25 +146,27 @@ extern "C" {
 
 int pa_decode(void* out, const void* query, const void* k_cache, const void* v_cache,
               const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
-              int32_t num_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+              int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+              int32_t max_blocks_per_seq,
               int32_t max_context_len, int64_t num_blocks, float scale, int32_t dtype,
               int32_t partition_size, uint32_t flags, void* workspace, size_t workspace_bytes, void* stream) {
     // The caches are only read: the const_cast feeds a read-only path.
     return decode_common(out, query, nullptr, nullptr, const_cast<void*>(k_cache), const_cast<void*>(v_cache),
-                         block_tables, context_lens, num_seqs, num_heads, head_dim, block_size,
+                         block_tables, context_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                          max_blocks_per_seq, max_context_len, num_blocks, scale, dtype, partition_size, flags,
                          workspace, workspace_bytes, stream, false);
 }
 
 int pa_append_decode(void* out, const void* query, const void* key, const void* value, void* k_cache,
                      void* v_cache, const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
-                     int32_t num_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                     int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                     int32_t max_blocks_per_seq,
                      int32_t max_context_len, int64_t num_blocks, float scale, int32_t dtype,
                      int32_t partition_size, uint32_t flags, void* workspace, size_t workspace_bytes,
                      void* stream) {
     return decode_common(out, query, key, value, k_cache, v_cache, block_tables, context_lens, num_seqs,
-                         num_heads, head_dim, block_size, max_blocks_per_seq, max_context_len, num_blocks,
-                         scale, dtype, partition_size, flags, workspace, workspace_bytes, stream, true);
+                         num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, max_context_len,
+                         num_blocks, scale, dtype, partition_size, flags, workspace, workspace_bytes, stream, true);
 }
 
 int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,

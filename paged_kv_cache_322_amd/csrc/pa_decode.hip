@@ -1,422 +1,16 @@
-// Paged decode attention for gfx950.
-//
-// Operation (PagedAttention digest, irregular6612.github.io, section
-// "Method"): for each sequence s and head h, attention of the single query
-// q[s,h,:] over the sequence's context, whose K/V rows live in fixed-size
-// physical blocks found through the sequence's block table.
-//
-// Work decomposition.  The context of every (sequence, head) is cut into KV
-// partitions of P tokens; one workgroup of kWgWaves wavefronts handles one
-// (partition, head, sequence).  Decode attention is a matrix-vector product:
-// each K and V byte is used once, so the kernel is bound by HBM bandwidth and
-// uses no matrix cores.  Inside a workgroup:
-//
-//   * the partition's physical block ids are staged in LDS once;
-//   * a wavefront processes U tokens per step.  A token's row of D elements
-//     is spread over LPR = D / (16 / elem) lanes, each lane loading 16 bytes,
-//     so one wave-wide load instruction covers 64 / LPR whole token rows and
-//     every lane issues NL loads of K and NL loads of V per step.  The loads
-//     of a wavefront's next step are issued before the current step is
-//     computed (software pipelining), so every wavefront keeps K and V bytes
-//     in flight while it computes;
-//   * q.k partial dots are summed across a row's lanes with DPP permutes.
-//     Each row of lanes keeps its own running maximum, running sum and fp32
-//     accumulators for its slice of D (online softmax, exponentials taken
-//     base 2 with log2(e) folded into the query), so the loop needs no
-//     exchange between rows; rows are merged once at the end;
-//   * wavefronts interleave steps, then merge their (max, sum, accumulators)
-//     through LDS.
-//
-// A sequence that fits one partition has its output written directly.  For
-// longer ones each partition writes its unnormalised accumulator, its
-// maximum and its sum to the workspace and a second kernel merges them.
-#include <math.h>
-
-#include "pa_device.h"
+// Decode launch dispatch by element type.  The kernels live in
+// pa_decode_impl.h and are instantiated by pa_decode_{f32,f16,bf16}.hip.
 #include "pa_internal.h"
-
-// Tuning switches (compile-time).  Defaults are the measured best on MI355X.
-#ifndef PA_PREFETCH
-#define PA_PREFETCH 1  // issue the next step's loads before computing the current one
-#endif
-#ifndef PA_STEP_TOKENS
-#define PA_STEP_TOKENS 16  // target tokens per wavefront step
-#endif
-#ifndef PA_WG_WAVES
-#define PA_WG_WAVES 8  // wavefronts per workgroup
-#endif
-#ifndef PA_PART_MAJOR
-#define PA_PART_MAJOR 1  // 1: partition index is the slowest grid dimension
-#endif
 
 namespace pa {
 
-constexpr int kWgWaves = PA_WG_WAVES;
-constexpr int kThreads = kWgWaves * kWave;
-static_assert(kMaxLptSeqs <= kThreads, "one thread ranks one sequence");
-constexpr int kMergeMaxParts = 256;  // partition weights cached in LDS by the merge kernel
-
-template <class T, int D>
-struct DecodeShape {
-    static constexpr int VEC = kVec<T>;
-    static constexpr int LPR = D / VEC;      // lanes per token row
-    static constexpr int TPL = kWave / LPR;  // token rows per wave-wide load
-    static constexpr int NL0 = PA_STEP_TOKENS / TPL;
-    static constexpr int NL = NL0 < 1 ? 1 : (NL0 > 8 ? 8 : NL0);  // loads of K (and of V) per lane per step
-    static constexpr int U = NL * TPL;       // tokens per wavefront step
-    static_assert(LPR >= 1 && LPR <= kWave && (kWave % LPR) == 0, "unsupported head_dim");
-};
-
-// APPEND: the newest token of every sequence (position ctx - 1) arrives in
-// knew/vnew [S, H, D]; the workgroup whose partition holds it stores that
-// head's rows into the caches and reads them from knew/vnew directly.
-// NT: K/V loads are non-temporal (streamed once; measured ~10% faster when no
-// block is shared).  Without NT they are ordinary cached loads, so sequences
-// that share blocks (forked samples, common prefixes) hit in L2 when their
-// workgroups run close together.
-template <class T, int D, bool APPEND, bool NT>
-__global__ __launch_bounds__(kThreads) void decode_partition_kernel(
-    typename T::bits* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_m,
-    float* __restrict__ ws_l, const typename T::bits* __restrict__ q,
-    typename T::bits* __restrict__ kc, typename T::bits* __restrict__ vc,
-    const typename T::bits* __restrict__ knew, const typename T::bits* __restrict__ vnew,
-    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
-    int num_seqs, int num_heads, int log2_bs, int max_blocks_per_seq, int max_context_len,
-    int64_t num_blocks, int part_tokens, int max_parts, int longest_first, float qscale) {
-    using Sh = DecodeShape<T, D>;
-    constexpr int VEC = Sh::VEC, LPR = Sh::LPR, TPL = Sh::TPL, NL = Sh::NL, U = Sh::U;
-
-    extern __shared__ int s_blk[];  // this partition's block ids (dynamic size)
-    __shared__ float s_m[kWgWaves], s_l[kWgWaves];
-    __shared__ float s_o[kWgWaves][D];
-
-#if PA_PART_MAJOR
-    const int h = blockIdx.x, srow = blockIdx.y, part = blockIdx.z;
-#else
-    const int part = blockIdx.x, h = blockIdx.y, srow = blockIdx.z;
-#endif
-    const int tid = threadIdx.x, lane = tid & (kWave - 1);
-    int s = srow;
-    if (longest_first) {
-        // Grid row r handles the sequence of rank r in decreasing context
-        // length (ties by index), so the longest contexts are dispatched
-        // first.  num_seqs <= kMaxLptSeqs <= kThreads (host check).
-        __shared__ int s_len[kMaxLptSeqs];
-        __shared__ int s_pick;
-        if (tid < num_seqs) s_len[tid] = context_lens[tid];
-        __syncthreads();
-        if (tid < num_seqs) {
-            const int c = s_len[tid];
-            int rank = 0;
-            for (int j = 0; j < num_seqs; ++j) {
-                const int cj = s_len[j];
-                rank += (cj > c) || (cj == c && j < tid);
-            }
-            if (rank == srow) s_pick = tid;
-        }
-        __syncthreads();
-        s = __builtin_amdgcn_readfirstlane(s_pick);  // uniform: keep s and all it decides in SGPRs
-    }
-    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int row = lane / LPR, col = lane % LPR;
-    const int64_t sh = static_cast<int64_t>(s) * num_heads + h;
-    const int ctx = __builtin_amdgcn_readfirstlane(context_lens[s]);
-
-    if (ctx <= 0 || ctx > max_context_len) {
-        // Empty context -> zeros; impossible length -> NaN.  Partition 0 writes.
-        if (part == 0) {
-            const float v = (ctx == 0) ? 0.0f : __builtin_nanf("");
-            for (int d = tid; d < D; d += kThreads) out[sh * D + d] = narrow<T>(v);
-        }
-        return;
-    }
-    const int t_begin = part * part_tokens;
-    if (t_begin >= ctx) return;
-    const int t_end = min(ctx, t_begin + part_tokens);
-    const int bmask = (1 << log2_bs) - 1;
-    const int j0 = t_begin >> log2_bs;
-    const int nblk = ((t_end - 1) >> log2_bs) - j0 + 1;  // <= staged_blocks (host sizes the LDS)
-
-    // Stage this partition's physical block ids; flag ids outside the pool.
-    const int32_t* bt = block_tables + static_cast<int64_t>(s) * max_blocks_per_seq;
-    for (int i = tid; i < nblk; i += kThreads) {
-        const int b = bt[j0 + i];
-        s_blk[i] = (b >= 0 && b < num_blocks) ? b : -1;
-    }
-
-    // This lane's slice of the query, scaled by scale * log2(e).
-    float qf[VEC];
-    widen16<T>(load16(q + sh * D + col * VEC), qf);
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) qf[v] *= qscale;
-    __syncthreads();  // s_blk is staged
-
-    // APPEND: in the workgroup whose partition holds the newest token (ctx-1),
-    // the step that covers it (always the partition's last step) reads that
-    // token's rows from knew/vnew instead of the caches, and the lanes
-    // holding them store them into the caches.  All other steps are plain.
-    const bool newest_here = APPEND && t_end == ctx;
-
-    // Element offsets: block b starts at b * blk_stride (host guarantees
-    // H * B * D < 2^31); this lane's channels of head h at lane_off in it.
-    const uint32_t blk_stride = static_cast<uint32_t>(num_heads << log2_bs) * D;
-    const uint32_t lane_off = (static_cast<uint32_t>(h) << log2_bs) * D + col * VEC;
-
-    float m = -INFINITY;  // running max of this row's base-2 scores
-    float l = 0.0f;       // running sum of exp2(score - m) over this row's tokens
-    float acc[VEC];       // running sum of exp2(score - m) * v over this row's tokens
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) acc[v] = 0.0f;
-    int bad = 0;
-
-    const int niter = (t_end - t_begin + U - 1) / U;
-
-    auto load_step = [&](int it, uint4 (&kr)[NL], uint4 (&vr)[NL]) {
-        const int tb = t_begin + it * U;
-        const bool newest = APPEND && newest_here && it == niter - 1;  // wave-uniform
-#pragma unroll
-        for (int i = 0; i < NL; ++i) {
-            // Tokens past the partition re-read the last valid token (always
-            // in bounds) and are masked out of the softmax.
-            const int t = min(tb + i * TPL + row, t_end - 1);
-            int b = s_blk[(t >> log2_bs) - j0];
-            bad |= (b < 0);
-            b = max(b, 0);
-            const uint64_t e = static_cast<uint64_t>(static_cast<uint32_t>(b)) * blk_stride + lane_off +
-                               static_cast<uint32_t>(t & bmask) * D;
-            const typename T::bits* kp = kc + e;
-            const typename T::bits* vp = vc + e;
-            if (newest && t == ctx - 1) {
-                kp = knew + sh * D + col * VEC;
-                vp = vnew + sh * D + col * VEC;
-            }
-            kr[i] = load16<NT>(kp);
-            vr[i] = load16<NT>(vp);
-        }
-    };
-
-    auto compute_step = [&](int it, const uint4 (&kr)[NL], const uint4 (&vr)[NL]) {
-        const int tb = t_begin + it * U;
-        if constexpr (APPEND) {
-            if (newest_here && it == niter - 1) {
-                // The one row of lanes whose (unclamped) token is ctx-1 stores it.
-                const int t = ctx - 1;
-                const int b = s_blk[(t >> log2_bs) - j0];
-                const uint64_t e = static_cast<uint64_t>(static_cast<uint32_t>(max(b, 0))) * blk_stride +
-                                   lane_off + static_cast<uint32_t>(t & bmask) * D;
-#pragma unroll
-                for (int i = 0; i < NL; ++i) {
-                    if (b >= 0 && tb + i * TPL + row == t) {
-                        *reinterpret_cast<uint4*>(kc + e) = kr[i];
-                        *reinterpret_cast<uint4*>(vc + e) = vr[i];
-                    }
-                }
-            }
-        }
-        float sc[NL];
-#pragma unroll
-        for (int i = 0; i < NL; ++i) {
-            float kf[VEC];
-            widen16<T>(kr[i], kf);
-            float d = 0.0f;
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) d = fmaf(qf[v], kf[v], d);
-            d = group_reduce<1, LPR>(d, OpAdd{});
-            sc[i] = (tb + i * TPL + row < t_end) ? d : -INFINITY;
-        }
-        float mx = sc[0];
-#pragma unroll
-        for (int i = 1; i < NL; ++i) mx = fmaxf(mx, sc[i]);
-        const float m_new = fmaxf(m, mx);
-        // A row whose tokens so far are all masked keeps m = -inf; use 0 as
-        // its reference so no inf - inf appears (its weights stay 0).
-        const float m_ref = (m_new == -INFINITY) ? 0.0f : m_new;
-        const float alpha = fast_exp2(m - m_ref);
-        l *= alpha;
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) acc[v] *= alpha;
-#pragma unroll
-        for (int i = 0; i < NL; ++i) {
-            const float p = fast_exp2(sc[i] - m_ref);
-            l += p;
-            float vf[VEC];
-            widen16<T>(vr[i], vf);
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) acc[v] = fmaf(p, vf[v], acc[v]);
-        }
-        m = m_new;
-    };
-
-    int it = wave;
-#if PA_PREFETCH
-    if (it < niter) {
-        uint4 ka[NL], va[NL], kb[NL], vb[NL];
-        load_step(it, ka, va);
-        while (true) {
-            int nx = it + kWgWaves;
-            if (nx < niter) load_step(nx, kb, vb);
-            compute_step(it, ka, va);
-            if (nx >= niter) break;
-            it = nx;
-            nx = it + kWgWaves;
-            if (nx < niter) load_step(nx, ka, va);
-            compute_step(it, kb, vb);
-            if (nx >= niter) break;
-            it = nx;
-        }
-    }
-#else
-    for (; it < niter; it += kWgWaves) {
-        uint4 ka[NL], va[NL];
-        load_step(it, ka, va);
-        compute_step(it, ka, va);
-    }
-#endif
-
-    // Merge the rows of each wavefront (rows hold disjoint tokens): rescale
-    // every row to the wave maximum, then sum.
-    const float mw = group_reduce<LPR, kWave>(m, OpMax{});
-    const float fr = (m == -INFINITY) ? 0.0f : fast_exp2(m - mw);
-    l = group_reduce<LPR, kWave>(l * fr, OpAdd{});
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) acc[v] = xor_sum_from<LPR>(acc[v] * fr);
-    if (row == 0) {
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) s_o[wave][col * VEC + v] = acc[v];
-    }
-    if (lane == 0) {
-        s_m[wave] = mw;
-        s_l[wave] = l;
-    }
-    bad = __syncthreads_or(bad);
-
-    // Merge the wavefronts.  Wave 0 always processed token t_begin.
-    float M = s_m[0];
-#pragma unroll
-    for (int w = 1; w < kWgWaves; ++w) M = fmaxf(M, s_m[w]);
-    float f[kWgWaves];
-    float L = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWgWaves; ++w) {
-        f[w] = (s_m[w] == -INFINITY) ? 0.0f : fast_exp2(s_m[w] - M);
-        L = fmaf(f[w], s_l[w], L);
-    }
-    const bool single = ctx <= part_tokens;
-    for (int d = tid; d < D; d += kThreads) {
-        float O = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kWgWaves; ++w) O = fmaf(f[w], s_o[w][d], O);
-        if (bad) O = __builtin_nanf("");
-        if (single) {
-            out[sh * D + d] = narrow<T>(O / L);
-        } else {
-            ws_o[(sh * max_parts + part) * D + d] = O;
-        }
-    }
-    if (!single && tid == 0) {
-        ws_m[sh * max_parts + part] = M;
-        ws_l[sh * max_parts + part] = L;
-    }
-}
-
-// Merge the partitions of every (sequence, head) whose context spans more
-// than one partition: with M the largest partition maximum, each partition's
-// sum and accumulator are rescaled by exp2(m_p - M) and added.  Lane p reads
-// partition p's statistics, so they arrive in one round trip.
-template <class T, int D>
-__global__ __launch_bounds__(kWave) void decode_merge_kernel(
-    typename T::bits* __restrict__ out, const float* __restrict__ ws_o,
-    const float* __restrict__ ws_m, const float* __restrict__ ws_l,
-    const int32_t* __restrict__ context_lens, int num_heads, int max_context_len, int part_tokens,
-    int max_parts) {
-    __shared__ float s_w[kMergeMaxParts];
-    const int h = blockIdx.x, s = blockIdx.y;
-    const int ctx = context_lens[s];
-    if (ctx <= part_tokens || ctx > max_context_len) return;  // written by the partition kernel
-    const int np = (ctx + part_tokens - 1) / part_tokens;
-    const int64_t sh = static_cast<int64_t>(s) * num_heads + h;
-    const float* wm = ws_m + sh * max_parts;
-    const float* wl = ws_l + sh * max_parts;
-    const int lane = threadIdx.x;
-    float M = -INFINITY;
-    for (int p = lane; p < np; p += kWave) M = fmaxf(M, wm[p]);
-    M = group_reduce<1, kWave>(M, OpMax{});
-    float L = 0.0f;
-    for (int p = lane; p < np; p += kWave) {
-        const float w = fast_exp2(wm[p] - M);
-        if (p < kMergeMaxParts) s_w[p] = w;
-        L = fmaf(w, wl[p], L);
-    }
-    L = group_reduce<1, kWave>(L, OpAdd{});
-    __syncthreads();
-    const float* wo = ws_o + sh * max_parts * D;
-    for (int d = lane; d < D; d += kWave) {
-        float O = 0.0f;
-        for (int p = 0; p < np; ++p) {
-            const float w = p < kMergeMaxParts ? s_w[p] : fast_exp2(wm[p] - M);
-            O = fmaf(w, wo[p * D + d], O);
-        }
-        out[sh * D + d] = narrow<T>(O / L);
-    }
-}
-
-template <class T, int D, bool APPEND, bool NT>
-static hipError_t launch_decode_t(const DecodeArgs& a) {
-    const int log2_bs = __builtin_ctz(static_cast<unsigned>(a.block_size));
-    const float qscale = a.scale * 1.4426950408889634f;  // log2(e)
-    using bits = typename T::bits;
-    auto* out = static_cast<bits*>(a.out);
-    float* ws_o = static_cast<float*>(a.workspace);
-    const size_t n_sh = static_cast<size_t>(a.num_seqs) * a.num_heads * a.max_parts;
-    float* ws_m = ws_o ? ws_o + n_sh * D : nullptr;
-    float* ws_l = ws_o ? ws_m + n_sh : nullptr;
-#if PA_PART_MAJOR
-    dim3 grid(a.num_heads, a.num_seqs, a.max_parts);
-#else
-    dim3 grid(a.max_parts, a.num_heads, a.num_seqs);
-#endif
-    const size_t lds = static_cast<size_t>(a.staged_blocks) * sizeof(int);
-    hipLaunchKernelGGL((decode_partition_kernel<T, D, APPEND, NT>), grid, dim3(kThreads), lds, a.stream, out,
-                       ws_o, ws_m, ws_l, static_cast<const bits*>(a.query),
-                       static_cast<bits*>(a.k_cache), static_cast<bits*>(a.v_cache),
-                       static_cast<const bits*>(a.key_new), static_cast<const bits*>(a.value_new),
-                       a.block_tables, a.context_lens, a.num_seqs, a.num_heads, log2_bs,
-                       a.max_blocks_per_seq, a.max_context_len, a.num_blocks, a.part_tokens, a.max_parts,
-                       a.longest_first ? 1 : 0, qscale);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess || a.max_parts <= 1) return err;
-    hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(a.num_heads, a.num_seqs), dim3(kWave), 0,
-                       a.stream, out, ws_o, ws_m, ws_l, a.context_lens, a.num_heads,
-                       a.max_context_len, a.part_tokens, a.max_parts);
-    return hipGetLastError();
-}
-
-template <class T, bool APPEND, bool NT>
-static hipError_t launch_decode_dim(const DecodeArgs& a) {
-    switch (a.head_dim) {
-        case 8: return launch_decode_t<T, 8, APPEND, NT>(a);
-        case 16: return launch_decode_t<T, 16, APPEND, NT>(a);
-        case 32: return launch_decode_t<T, 32, APPEND, NT>(a);
-        case 64: return launch_decode_t<T, 64, APPEND, NT>(a);
-        case 128: return launch_decode_t<T, 128, APPEND, NT>(a);
-        case 256: return launch_decode_t<T, 256, APPEND, NT>(a);
-        default: return hipErrorInvalidValue;
-    }
-}
-
-template <bool APPEND, bool NT>
-static hipError_t launch_decode_type(const DecodeArgs& a) {
-    switch (a.dtype) {
-        case 0: return launch_decode_dim<F32, APPEND, NT>(a);
-        case 1: return launch_decode_dim<F16, APPEND, NT>(a);
-        case 2: return launch_decode_dim<BF16, APPEND, NT>(a);
-        default: return hipErrorInvalidValue;
-    }
-}
-
 hipError_t launch_decode(const DecodeArgs& a) {
-    if (a.key_new) return a.cached_loads ? launch_decode_type<true, false>(a) : launch_decode_type<true, true>(a);
-    return a.cached_loads ? launch_decode_type<false, false>(a) : launch_decode_type<false, true>(a);
+    switch (a.dtype) {
+        case 0: return launch_decode_f32(a);
+        case 1: return launch_decode_f16(a);
+        case 2: return launch_decode_bf16(a);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace pa

@@ -1,0 +1,9 @@
+// Decode kernels for f16 caches (one translation unit per element type so
+// the instances compile in parallel).
+#include "pa_decode_impl.h"
+
+namespace pa {
+
+hipError_t launch_decode_f16(const DecodeArgs& a) { return launch_decode_type<F16>(a); }
+
+}  // namespace pa

@@ -74,7 +74,7 @@ struct DecodeArgs {
     const void* value_new;  // [S, H, D] newest token's V (append mode) or NULL
     const int32_t* block_tables;
     const int32_t* context_lens;
-    int num_seqs, num_heads, head_dim, block_size;
+    int num_seqs, num_heads, num_kv_heads, head_dim, block_size;  // num_heads = G * num_kv_heads
     int max_blocks_per_seq, max_context_len;
     int64_t num_blocks;
     float scale;
@@ -88,6 +88,12 @@ struct DecodeArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs& a);
+hipError_t launch_decode_f32(const DecodeArgs& a);
+hipError_t launch_decode_f16(const DecodeArgs& a);
+hipError_t launch_decode_bf16(const DecodeArgs& a);
+
+// Query heads per K/V head with built kernels.
+inline bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
 
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
                                     const int64_t* slot_mapping, int num_tokens, int num_heads,

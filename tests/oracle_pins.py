@@ -56,6 +56,7 @@ def brute_decode(q, kc, vc, bt, ctx, scale, dtype) -> np.ndarray:
     qw, kw, vw = torch_widen(q, dtype), torch_widen(kc, dtype), torch_widen(vc, dtype)
     S, H, D = q.shape
     B = kc.shape[2]
+    G = H // kc.shape[1]  # query heads per K/V head
     out = np.zeros((S, H, D))
     for s in range(S):
         n = int(ctx[s])
@@ -63,12 +64,13 @@ def brute_decode(q, kc, vc, bt, ctx, scale, dtype) -> np.ndarray:
             continue
         loc = [(int(bt[s][t // B]), t % B) for t in range(n)]
         for h in range(H):
-            sc = [scale * math.fsum(float(qw[s, h, d]) * float(kw[b, h, o, d]) for d in range(D)) for b, o in loc]
+            hk = h // G
+            sc = [scale * math.fsum(float(qw[s, h, d]) * float(kw[b, hk, o, d]) for d in range(D)) for b, o in loc]
             mx = max(sc)
             e = [math.exp(x - mx) for x in sc]
             z = math.fsum(e)
             for d in range(D):
-                out[s, h, d] = math.fsum(e[t] * float(vw[b, h, o, d]) for t, (b, o) in enumerate(loc)) / z
+                out[s, h, d] = math.fsum(e[t] * float(vw[b, hk, o, d]) for t, (b, o) in enumerate(loc)) / z
     return out
 
 
@@ -104,6 +106,8 @@ def _small_cases():
     yield wl.random_case(3, 3, 1, 8, 3, "bf16", ctx_range=(1, 17))
     yield wl.random_case(4, 2, 2, 8, 1, "f32", ctx=[1, 9])
     yield wl.random_case(5, 3, 2, 8, 4, "bf16", ctx=[0, 4, 11])
+    yield wl.random_case(18, 3, 4, 8, 4, "f16", ctx=[3, 9, 14], num_kv_heads=2)
+    yield wl.random_case(19, 2, 4, 4, 2, "f32", ctx=[5, 1], num_kv_heads=1)
 
 
 # ---------------------------------------------------------------------------
@@ -429,6 +433,28 @@ def pin_newest_token_slots(orc):
         sa.key, sa.value, small.k_cache, small.v_cache, sa.slot_mapping)[0]))
 
 
+def pin_grouped_query(orc):
+    """Grouped-query attention: the same as multi-head attention over a cache
+    whose K/V heads are each repeated G times, and the same as torch's
+    scaled_dot_product_attention with enable_gqa on the contiguous tensors."""
+    for dtype, H, Hk in (("f32", 8, 2), ("bf16", 6, 3), ("f16", 4, 1), ("f32", 4, 4)):
+        case = wl.random_case(20 + H + Hk, 3, H, 16, 4, dtype, ctx_range=(1, 30), num_kv_heads=Hk)
+        G = H // Hk
+        got = _decode(orc, case)
+        kc = np.repeat(case.k_cache, G, axis=1)  # head h of the copy = K/V head h // G
+        vc = np.repeat(case.v_cache, G, axis=1)
+        assert np.array_equal(got, _decode(orc, case, kc=kc, vc=vc)), (dtype, H, Hk)
+        for s in range(case.num_seqs):
+            n = int(case.context_lens[s])
+            rows_k = np.stack([case.k_cache[case.block_tables[s][t // 4], :, t % 4, :] for t in range(n)], axis=1)
+            rows_v = np.stack([case.v_cache[case.block_tables[s][t // 4], :, t % 4, :] for t in range(n)], axis=1)
+            tq = torch.from_numpy(torch_widen(case.q[s], dtype)).reshape(1, H, 1, 16)
+            tk = torch.from_numpy(torch_widen(rows_k, dtype)).unsqueeze(0)
+            tv = torch.from_numpy(torch_widen(rows_v, dtype)).unsqueeze(0)
+            ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=case.scale, enable_gqa=True)
+            assert np.abs(got[s] - ref.reshape(H, 16).numpy()).max() <= 1e-12
+
+
 ALL_PINS = [
     pin_widen,
     pin_bruteforce,
@@ -441,4 +467,5 @@ ALL_PINS = [
     pin_cow,
     pin_split_merge,
     pin_newest_token_slots,
+    pin_grouped_query,
 ]

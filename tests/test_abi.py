@@ -65,10 +65,11 @@ def test_workspace_size():
 
 
 def dec(**kw):
-    a = dict(out=P, query=P, k=P, v=P, bt=P, ctx=P, S=2, H=4, D=128, B=16, W=8, maxc=100, N=64,
+    a = dict(out=P, query=P, k=P, v=P, bt=P, ctx=P, S=2, H=4, Hk=None, D=128, B=16, W=8, maxc=100, N=64,
              scale=0.1, dtype=1, part=0, flags=0, ws=0, wsb=0)
     a.update(kw)
-    return pa.lib.pa_decode(a["out"], a["query"], a["k"], a["v"], a["bt"], a["ctx"], a["S"], a["H"], a["D"],
+    hk = a["H"] if a["Hk"] is None else a["Hk"]
+    return pa.lib.pa_decode(a["out"], a["query"], a["k"], a["v"], a["bt"], a["ctx"], a["S"], a["H"], hk, a["D"],
                             a["B"], a["W"], a["maxc"], a["N"], a["scale"], a["dtype"], a["part"], a["flags"],
                             a["ws"], a["wsb"], None)
 
@@ -92,8 +93,12 @@ def test_decode_host_checks():
     assert dec(H=65535, B=256, D=256) == INVALID  # one block above 2^31 elements
     assert dec(maxc=100, part=16) == NULL  # split needs a workspace
     assert dec(flags=2) == INVALID  # unknown flag bit
+    assert dec(H=8, Hk=3) == INVALID  # query heads not a multiple of K/V heads
+    assert dec(H=48, Hk=3) == UNSUP  # group of 16 query heads per K/V head not built
+    assert dec(H=4, Hk=0) == INVALID
     assert dec(maxc=2000000, W=200000, part=16) == INVALID  # more partitions than grid rows
     need = pa.decode_workspace_size(2, 4, 128, 100, 16)
+    assert pa.decode_workspace_size(2, 8, 128, 100, 16, num_kv_heads=2) == 2 * 8 * 7 * 130 * 4
     assert dec(maxc=100, part=16, ws=P, wsb=need - 1) == INVALID
     assert dec(maxc=100, part=16, ws=P + 2, wsb=need) == INVALID
 
@@ -145,8 +150,9 @@ def test_append_decode_host_checks():
                  N=64, scale=0.1, dtype=1, part=0, flags=0, ws=0, wsb=0)
         a.update(kw)
         return pa.lib.pa_append_decode(a["out"], a["query"], a["key"], a["value"], a["k"], a["v"], a["bt"],
-                                       a["ctx"], a["S"], a["H"], a["D"], a["B"], a["W"], a["maxc"], a["N"],
-                                       a["scale"], a["dtype"], a["part"], a["flags"], a["ws"], a["wsb"], None)
+                                       a["ctx"], a["S"], a["H"], a["H"], a["D"], a["B"], a["W"], a["maxc"],
+                                       a["N"], a["scale"], a["dtype"], a["part"], a["flags"], a["ws"], a["wsb"],
+                                       None)
 
     assert ad(S=0, key=0, value=0) == OK
     assert ad(key=0) == NULL

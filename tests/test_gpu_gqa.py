@@ -1,0 +1,78 @@
+"""Grouped-query attention (num_kv_heads < num_heads) through the C ABI,
+against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from gpu_helpers import GpuCase, assert_close, assert_pool_equal, log, oracle_decode, pa, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def test_gqa_llama3_8b_shape():
+    case = wl.gqa_config("llama3-8b")
+    g = GpuCase(case)
+    ref = oracle_decode(case, case.k_cache, case.v_cache)
+    for part in (0, 256):
+        out = g.decode(partition=part, out=torch.empty_like(g.q))
+        torch.cuda.synchronize()
+        assert_close(out, ref, case.dtype, f"{case.name} partition={part}")
+
+
+def test_gqa_llama2_70b_tp8_share_sampled():
+    case = wl.gqa_config("llama2-70b-tp8")
+    g = GpuCase(case)
+    order = np.argsort(case.context_lens)
+    seqs = sorted(set(order[::16].tolist() + [int(order[-1]), int(order[0])]))
+    ref = oracle_decode(case, case.k_cache, case.v_cache, seqs)
+    out = g.decode()
+    torch.cuda.synchronize()
+    assert_close(out, ref, case.dtype, case.name, seqs=seqs)
+
+
+SWEEP = [
+    # dtype, H, Hk, D, B, ctx, partition
+    ("f16", 8, 4, 128, 16, [1, 17, 300, 1299], 0),
+    ("bf16", 16, 4, 128, 16, [2, 16, 513, 1025], 64),
+    ("f32", 8, 1, 64, 8, [5, 100, 901], 100),
+    ("f16", 16, 2, 256, 32, [3, 64, 511, 777], 0),
+    ("bf16", 8, 1, 128, 16, [1, 4000], 0),
+    ("f32", 4, 2, 8, 4, [5, 16, 37], 4),
+    ("f16", 32, 4, 64, 1, [1, 2, 129], 16),
+]
+
+
+@pytest.mark.parametrize("dtype,H,Hk,D,B,ctx,part", SWEEP,
+                         ids=[f"{c[0]}-H{c[1]}-Hk{c[2]}-D{c[3]}-B{c[4]}-P{c[6]}" for c in SWEEP])
+def test_gqa_sweep(dtype, H, Hk, D, B, ctx, part):
+    case = wl.random_case(500 + H + Hk + D + B, len(ctx), H, D, B, dtype, ctx=ctx, num_kv_heads=Hk, spare_blocks=3)
+    g = GpuCase(case)
+    ref = oracle_decode(case, case.k_cache, case.v_cache)
+    out = g.decode(partition=part, out=torch.empty_like(g.q))
+    torch.cuda.synchronize()
+    assert_close(out, ref, dtype, f"{case.name} H={H} Hk={Hk}", strict=False)
+    # Cached loads: identical bits.
+    out2 = g.decode(partition=part, out=torch.empty_like(g.q), shared_blocks=True)
+    torch.cuda.synchronize()
+    iv = torch.int32 if dtype == "f32" else torch.int16
+    assert torch.equal(out.view(iv), out2.view(iv))
+
+
+@pytest.mark.parametrize("Hk", [1, 2, 8])
+def test_gqa_append_decode(Hk):
+    case = wl.random_case(520 + Hk, 5, 8, 128, 16, "f16", ctx=[1, 16, 17, 700, 1500], n_append=1,
+                          num_kv_heads=Hk, spare_blocks=3)
+    st = case.steps[0]
+    assert st.key.shape == (5, Hk, 128)
+    g = GpuCase(case)
+    out = torch.empty_like(g.q)
+    pa().append_decode(out, g.q, to_gpu(st.key, "f16"), to_gpu(st.value, "f16"), g.kc, g.vc, g.bt, g.ctx,
+                       case.scale, case.max_context_len)
+    torch.cuda.synchronize()
+    ref, kc, vc = oracle.append_decode(case.q, st.key, st.value, case.k_cache, case.v_cache, case.block_tables,
+                                       case.context_lens, case.scale, "f16")
+    assert_pool_equal(g.kc, kc, "f16", f"K Hk={Hk}")
+    assert_pool_equal(g.vc, vc, "f16", f"V Hk={Hk}")
+    assert_close(out, ref, "f16", f"gqa append_decode Hk={Hk}", strict=False)

@@ -30,16 +30,17 @@ def default_partition(S, H, max_ctx):
     return part
 
 
-def shape(elem, D):
+def shape(elem, D, G=1):
     vec = 16 // elem
     lpr = D // vec
     tpl = 64 // lpr
-    nl = max(1, min(8, 16 // tpl))
+    nl = max(1, min(8, (16 if G <= 2 else 8) // tpl))
     return vec, lpr, tpl, nl, nl * tpl
 
 
-def check_decode_bounds(S, H, D, B, N, W, elem, ctx, bt, max_ctx, part):
-    vec, lpr, tpl, nl, U = shape(elem, D)
+def check_decode_bounds(S, H, D, B, N, W, elem, ctx, bt, max_ctx, part, G=1):
+    """H is the caches' head count (K/V heads); G query heads share each."""
+    vec, lpr, tpl, nl, U = shape(elem, D, G)
     staged = (part + B - 1) // B + 1
     assert staged <= MAX_PART_BLOCKS  # host check in pa_decode; LDS holds `staged` ids
     assert max_ctx <= W * B  # host check in pa_decode
@@ -73,8 +74,8 @@ def check_decode_bounds(S, H, D, B, N, W, elem, ctx, bt, max_ctx, part):
             b = np.where((b >= 0) & (b < N), b, 0)  # invalid ids are flagged and replaced by 0
             e = b.astype(np.int64) * blk_stride + (t & (B - 1)).astype(np.int64) * D
             assert e.min() >= 0 and e.max() + head_off_max + vec <= cache_elems
-            if c > part:
-                assert ((s * H + H - 1) * max_parts + p) * D + D <= ws_o_elems
+            if c > part:  # workspace rows are per query head: S * H * G of them
+                assert ((s * H * G + H * G - 1) * max_parts + p) * D + D <= ws_o_elems * G
 
 
 CASES = [
@@ -85,6 +86,7 @@ CASES = [
     ("config4-B32", functools.lru_cache(None)(lambda: wl.config4(block_size=32, num_heads=1, head_dim=128))),
     ("config5", functools.lru_cache(None)(lambda: wl.config5(num_heads=2))),
     ("edge", functools.lru_cache(None)(lambda: wl.random_case(21, 5, 2, 64, 1, "bf16", ctx=[0, 1, 2, 513, 700]))),
+    ("gqa-llama3-8b", functools.lru_cache(None)(lambda: wl.gqa_config("llama3-8b"))),
 ]
 
 
@@ -94,14 +96,14 @@ def test_decode_index_bounds(name, make, part):
     case = make()
     B = case.block_size
     max_ctx = case.max_context_len
-    p = default_partition(case.num_seqs, case.num_heads, max_ctx) if part == 0 else part
+    p = default_partition(case.num_seqs, case.num_kv_heads, max_ctx) if part == 0 else part
     if p == 1 << 30:
         p = max(1, max_ctx)  # a single partition covers every context
     if (p + B - 1) // B + 1 > MAX_PART_BLOCKS:
         pytest.skip("partition rejected by the host check")
-    check_decode_bounds(case.num_seqs, case.num_heads, case.head_dim, B, case.num_blocks,
+    check_decode_bounds(case.num_seqs, case.num_kv_heads, case.head_dim, B, case.num_blocks,
                         case.block_tables.shape[1], case.elem_bytes, case.context_lens,
-                        case.block_tables, max_ctx, p)
+                        case.block_tables, max_ctx, p, G=case.num_heads // case.num_kv_heads)
 
 
 def test_invalid_ids_are_clamped_in_the_model():

@@ -102,6 +102,15 @@ def _newest_off_by_one(block_tables, context_lens, block_size):
     return _real["newest_token_slots"](block_tables, np.asarray(context_lens) + 1, block_size)
 
 
+def _decode_gqa_modulo(q, k_cache, v_cache, block_tables, context_lens, scale, dtype):
+    """Query head h reads K/V head h % Hk instead of h // G."""
+    H, Hk = q.shape[1], k_cache.shape[1]
+    perm = np.array([(h % Hk) * (H // Hk) + h // Hk for h in range(H)]) if H != Hk else np.arange(H)
+    out = _real["paged_decode"](q[:, perm], k_cache, v_cache, block_tables, context_lens, scale, dtype)
+    inv = np.argsort(perm)
+    return out[:, inv]
+
+
 MUTANTS = {
     "attention drops the scale": ("attention", _attention_no_scale),
     "softmax exponent sign flipped": ("attention", _attention_flipped),
@@ -118,6 +127,7 @@ MUTANTS = {
     "heads transposed in the output": ("paged_decode", _decode_wrong_head),
     "partial stats use the wrong reference": ("partial_attention", _partial_no_max),
     "newest token taken one position late": ("newest_token_slots", _newest_off_by_one),
+    "query heads grouped round-robin over K/V heads": ("paged_decode", _decode_gqa_modulo),
 }
 
 

@@ -7,6 +7,7 @@ attention, cache-write or block-copy computation lives here.
 from .blockpool import BlockPool, PoolExhausted, SeqBlocks, append_tokens, cow_last_block, fork, tables_array
 from .cases import (
     CONFIG_NAMES,
+    GQA_NAMES,
     AppendStep,
     Case,
     CopyStep,
@@ -17,6 +18,7 @@ from .cases import (
     config3_lengths,
     config4,
     config5,
+    gqa_config,
     normal_storage,
     random_case,
 )

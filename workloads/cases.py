@@ -51,7 +51,7 @@ Step = Union[AppendStep, CopyStep]
 class Case:
     name: str
     dtype: str
-    num_heads: int
+    num_heads: int  # query heads
     head_dim: int
     block_size: int
     num_blocks: int
@@ -63,6 +63,10 @@ class Case:
     scale: float
     steps: List[Step] = field(default_factory=list)
     meta: dict = field(default_factory=dict)
+
+    @property
+    def num_kv_heads(self) -> int:
+        return int(self.k_cache.shape[1])
 
     @property
     def num_seqs(self) -> int:
@@ -110,17 +114,19 @@ def _fill_history(cache: np.ndarray, seqs: Sequence[SeqBlocks], hist: Sequence[i
             o += r
 
 
-def _paged_case(name, dtype, H, D, B, N, ctx, seed, perm, n_append: int, scale=None) -> Case:
+def _paged_case(name, dtype, H, D, B, N, ctx, seed, perm, n_append: int, scale=None, Hk=None) -> Case:
     """Sequences with ``ctx[i] - n_append`` history tokens in a permuted pool and
-    ``n_append`` new tokens per sequence written by an append step."""
+    ``n_append`` new tokens per sequence written by an append step.  The
+    caches hold ``Hk`` K/V heads (default: one per query head)."""
+    Hk = H if Hk is None else Hk
     pool = BlockPool(N, B, perm)
     seqs = [SeqBlocks() for _ in ctx]
     hist = [int(c) - n_append for c in ctx]
     assert min(hist) >= 0
     for s, h in zip(seqs, hist):
         append_tokens(pool, s, h)
-    k_cache = canary_fill((N, H, B, D), dtype)
-    v_cache = canary_fill((N, H, B, D), dtype)
+    k_cache = canary_fill((N, Hk, B, D), dtype)
+    v_cache = canary_fill((N, Hk, B, D), dtype)
     _fill_history(k_cache, seqs, hist, seed, "k", dtype)
     _fill_history(v_cache, seqs, hist, seed, "v", dtype)
     steps: List[Step] = []
@@ -133,8 +139,8 @@ def _paged_case(name, dtype, H, D, B, N, ctx, seed, perm, n_append: int, scale=N
         T = len(slots)
         steps.append(
             AppendStep(
-                normal_storage(seed, "k_new", (T, H, D), dtype),
-                normal_storage(seed, "v_new", (T, H, D), dtype),
+                normal_storage(seed, "k_new", (T, Hk, D), dtype),
+                normal_storage(seed, "v_new", (T, Hk, D), dtype),
                 np.asarray(slots, dtype=np.int64),
             )
         )
@@ -293,6 +299,35 @@ def config4(
     )
 
 
+GQA_NAMES = {
+    "llama3-8b": "llama3-8b-gqa-decode: 64 seqs ctx U[128,2048], H=32 query / 8 K/V heads, D=128, f16, B=16",
+    "llama2-70b-tp8": "llama2-70b-gqa-tp8-share: 128 seqs ctx U[512,4096], H=8 query / 1 K/V head, D=128, bf16, B=16",
+}
+
+
+def gqa_config(kind: str = "llama3-8b", n_append: int = 0) -> Case:
+    """Grouped-query decode layers (query heads share K/V heads).
+
+    llama3-8b: the LLaMA-7B-shaped batch of config 2 with 32 query heads over
+    8 K/V heads (groups of 4).  llama2-70b-tp8: one tensor-parallel rank's
+    share of a 64-query / 8-K/V-head layer (8 query heads over 1 K/V head,
+    groups of 8), 128 sequences of 512..4096 tokens.
+    """
+    if kind == "llama3-8b":
+        seed = BASE_SEED + 6
+        rng = np.random.default_rng(seed)
+        ctx = rng.integers(128, 2049, 64)
+        perm = rng.permutation(8192)
+        return _paged_case("gqa-llama3-8b", "f16", 32, 128, 16, 8192, ctx, seed, perm, n_append, Hk=8)
+    if kind == "llama2-70b-tp8":
+        seed = BASE_SEED + 7
+        rng = np.random.default_rng(seed)
+        ctx = rng.integers(512, 4097, 128)
+        perm = rng.permutation(32768)
+        return _paged_case("gqa-llama2-70b-tp8", "bf16", 8, 128, 16, 32768, ctx, seed, perm, n_append, Hk=1)
+    raise ValueError(kind)
+
+
 def config(n: int, **kw) -> Case:
     return {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}[n](**kw)
 
@@ -314,6 +349,7 @@ def random_case(
     spare_blocks: int = 3,
     n_append: int = 0,
     scale: Optional[float] = None,
+    num_kv_heads: Optional[int] = None,
 ) -> Case:
     """A small paged case with a seeded random physical placement."""
     rng = np.random.default_rng([BASE_SEED, seed])
@@ -324,5 +360,6 @@ def random_case(
     N = need + spare_blocks
     perm = rng.permutation(N)
     return _paged_case(
-        f"random-{seed}", dtype, num_heads, head_dim, block_size, N, ctx, seed * 7919 + 17, perm, n_append, scale=scale
+        f"random-{seed}", dtype, num_heads, head_dim, block_size, N, ctx, seed * 7919 + 17, perm, n_append,
+        scale=scale, Hk=num_kv_heads,
     )
