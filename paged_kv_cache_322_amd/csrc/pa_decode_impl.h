@@ -12,8 +12,14 @@
 // KV partitions of P tokens; one workgroup of kWgWaves wavefronts handles one
 // (K/V head, sequence, partition) for all G query heads of that K/V head, so
 // every K/V byte is loaded once.  Decode attention is a matrix-vector product
-// per query head: about G flops per byte, so the kernel is bound by HBM
-// bandwidth and uses no matrix cores.  Inside a workgroup:
+// per query head: about G flops per byte.  This vector-ALU kernel serves
+// multi-head attention (G = 1), fp32 caches and head sizes below 64; with
+// 16-bit caches and G >= 2 the per-token ALU work (which grows with G) no
+// longer hides under the HBM time and decode_mfma_kernel (pa_decode_mfma.h)
+// runs instead.  Measured with 16-bit multi-head attention, the two kernels
+// tie on long contexts and this one is ~15% faster on short ones (a tile
+// pipeline of two steps per wavefront, which the matrix-core kernel cannot
+// afford in registers).  Inside a workgroup:
 //
 //   * the partition's physical block ids are staged in LDS once;
 //   * a wavefront processes U tokens per step.  A token's row of D elements
@@ -41,6 +47,7 @@
 
 #include <math.h>
 
+#include "pa_decode_mfma.h"
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -395,6 +402,21 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(
     }
 }
 
+#ifndef PA_MFMA_MIN_G
+#define PA_MFMA_MIN_G 2  // smallest group size served by the matrix-core kernel
+#endif
+
+// The matrix-core kernel serves 16-bit caches with D in {64, 128, 256} when
+// a K/V head has at least PA_MFMA_MIN_G query heads (measured 2-3x faster
+// than the vector kernel at G = 4 and 8).
+template <class T, int D, int G>
+constexpr bool kUseMfma = sizeof(typename T::bits) == 2 && (D == 64 || D == 128 || D == 256) && G >= PA_MFMA_MIN_G;
+
+// Its static LDS is at most ~36 KB; partitions staging more block ids than
+// this (tiny blocks with very long forced partitions) keep the total within
+// 64 KB by taking the vector kernel.
+constexpr int kMfmaMaxStaged = 6144;
+
 template <class T, int D, int G, bool APPEND, bool NT>
 hipError_t launch_decode_t(const DecodeArgs& a) {
     const int log2_bs = __builtin_ctz(static_cast<unsigned>(a.block_size));
@@ -407,12 +429,32 @@ hipError_t launch_decode_t(const DecodeArgs& a) {
     float* ws_l = ws_o ? ws_m + n_sh : nullptr;
     dim3 grid(a.num_kv_heads, a.num_seqs, a.max_parts);
     const size_t lds = static_cast<size_t>(a.staged_blocks) * sizeof(int);
-    hipLaunchKernelGGL((decode_partition_kernel<T, D, G, APPEND, NT>), grid, dim3(kThreads), lds, a.stream, out,
-                       ws_o, ws_m, ws_l, static_cast<const bits*>(a.query), static_cast<bits*>(a.k_cache),
-                       static_cast<bits*>(a.v_cache), static_cast<const bits*>(a.key_new),
-                       static_cast<const bits*>(a.value_new), a.block_tables, a.context_lens, a.num_seqs,
-                       a.num_kv_heads, log2_bs, a.max_blocks_per_seq, a.max_context_len, a.num_blocks,
-                       a.part_tokens, a.max_parts, a.longest_first ? 1 : 0, qscale);
+    if constexpr (kUseMfma<T, D, G>) {
+        if (a.staged_blocks <= kMfmaMaxStaged) {
+            hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, APPEND, NT>), grid, dim3(kMfmaThreads), lds, a.stream,
+                               out, ws_o, ws_m, ws_l, static_cast<const bits*>(a.query),
+                               static_cast<bits*>(a.k_cache), static_cast<bits*>(a.v_cache),
+                               static_cast<const bits*>(a.key_new), static_cast<const bits*>(a.value_new),
+                               a.block_tables, a.context_lens, a.num_seqs, a.num_kv_heads, log2_bs,
+                               a.max_blocks_per_seq, a.max_context_len, a.num_blocks, a.part_tokens, a.max_parts,
+                               a.longest_first ? 1 : 0, qscale);
+        } else {
+            hipLaunchKernelGGL((decode_partition_kernel<T, D, G, APPEND, NT>), grid, dim3(kThreads), lds, a.stream,
+                               out, ws_o, ws_m, ws_l, static_cast<const bits*>(a.query),
+                               static_cast<bits*>(a.k_cache), static_cast<bits*>(a.v_cache),
+                               static_cast<const bits*>(a.key_new), static_cast<const bits*>(a.value_new),
+                               a.block_tables, a.context_lens, a.num_seqs, a.num_kv_heads, log2_bs,
+                               a.max_blocks_per_seq, a.max_context_len, a.num_blocks, a.part_tokens, a.max_parts,
+                               a.longest_first ? 1 : 0, qscale);
+        }
+    } else {
+        hipLaunchKernelGGL((decode_partition_kernel<T, D, G, APPEND, NT>), grid, dim3(kThreads), lds, a.stream, out,
+                           ws_o, ws_m, ws_l, static_cast<const bits*>(a.query), static_cast<bits*>(a.k_cache),
+                           static_cast<bits*>(a.v_cache), static_cast<const bits*>(a.key_new),
+                           static_cast<const bits*>(a.value_new), a.block_tables, a.context_lens, a.num_seqs,
+                           a.num_kv_heads, log2_bs, a.max_blocks_per_seq, a.max_context_len, a.num_blocks,
+                           a.part_tokens, a.max_parts, a.longest_first ? 1 : 0, qscale);
+    }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || a.max_parts <= 1) return err;
     hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(a.num_heads, a.num_seqs), dim3(kWave), 0, a.stream, out,

@@ -1,0 +1,422 @@
+// Paged decode attention on the gfx950 matrix cores, for 16-bit caches and
+// grouped-query attention.
+//
+// Operation: as decode_partition_kernel (PagedAttention digest,
+// irregular6612.github.io, section "Method"): for each sequence and query
+// head, softmax(scale * q K^T) V over the sequence's paged context, the G
+// query heads of a K/V head sharing its K/V rows.
+//
+// Why matrix cores.  Per byte of K/V the G heads of a group need about G
+// flops.  On the vector ALUs (one lane row per token row, DPP reductions)
+// that costs ~31 G instructions per token and lane, which at G >= 4 no
+// longer fits under the HBM time.  Here a wavefront takes 16 tokens per
+// step and the group's heads, zero-padded to 16, form the other side of two
+// 16x16 matrix products:
+//
+//   S^T[token][head] = K[token][:] . Q[head][:]     v_mfma_f32_16x16x32_{f16,bf16}
+//   O^T[d][head]    += V^T[d][token] . P^T[token][head]   v_mfma_f32_16x16x16_{f16,bf16}
+//
+// Operand layouts (16x16xK products, lane L = 16 * g + c, c = L % 16):
+//   A (M x K): lane L holds row c, the K-slice of group g;
+//   B (K x N): lane L holds column c, the K-slice of group g;
+//   C (M x N): lane L holds rows 4g..4g+3 of column c.
+// Which channel goes to which K position is free as long as A and B agree,
+// so:
+//   * q.k: lane L loads 16 bytes of token c's key row (channels
+//     32 ks + 8 g .. +7 for k-step ks) and the same channels of query head c;
+//     the result gives lane L the scores of tokens 4g..4g+3 for head c;
+//   * p.v: the contraction index is the token.  Lane L loads 16 bytes of
+//     each of the rows of tokens 4g..4g+3 (channels E c .. E c + E - 1,
+//     E = D / 16); output tile t (of E) takes channel E m + t for its row m.
+//     One v_perm per register gathers element t of the four rows into the A
+//     operand.  The B operand is this lane's own four probabilities: the
+//     score layout above is exactly the P^T layout, so no data moves between
+//     lanes.  Lane L ends holding, for head c, channels D/4 g .. D/4 g + D/4-1.
+//   * Probabilities enter the product as 16-bit values.  To keep fp32
+//     accuracy each p is split into hi = p truncated to 16 bits and
+//     lo = (p - hi) truncated, and both products are accumulated (relative
+//     weight error below 2^-16; the product of a 16-bit p and a 16-bit v is
+//     exact in the fp32 accumulator).
+// Softmax runs online per 16-token tile: the tile's maximum per head is
+// shared across the four lane groups (two cross-row exchanges), the
+// accumulators are rescaled only when some head's maximum grows, and the
+// running sums are kept per lane and added at the end.
+//
+// Work decomposition, grid, LDS staging of block ids, longest-first mapping,
+// workspace layout and device-side guards are those of
+// decode_partition_kernel: one workgroup per (K/V head, sequence, partition).
+#pragma once
+
+#include <math.h>
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+#ifndef PA_MFMA_WAVES
+#define PA_MFMA_WAVES 8  // wavefronts per workgroup of the matrix-core kernel
+#endif
+
+#ifndef PA_MFMA_PREFETCH
+#define PA_MFMA_PREFETCH 0  // keep the next tile's loads in flight while computing (measured slower: +36 VGPRs cost a wave of occupancy)
+#endif
+
+constexpr int kMfmaWaves = PA_MFMA_WAVES;
+constexpr bool kMfmaPrefetch = PA_MFMA_PREFETCH;
+constexpr int kMfmaThreads = kMfmaWaves * kWave;
+constexpr int kMfmaTile = 16;            // tokens per wavefront step
+constexpr int kMfmaMergeFloats = 8192;   // LDS floats for the cross-wave merge (32 KB)
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Matrix-core operations per 16-bit element type.
+template <class T>
+struct MfmaOps;
+
+template <>
+struct MfmaOps<F16> {
+    __device__ static __forceinline__ f32x4 qk(u32x4 a, u32x4 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b),
+                                                      c, 0, 0, 0);
+    }
+    __device__ static __forceinline__ f32x4 pv(u32x2 a, u32x2 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), c,
+                                                     0, 0, 0);
+    }
+    // Two probabilities -> packed hi words and packed lo words (round toward zero).
+    __device__ static __forceinline__ void split(float p0, float p1, uint32_t& hi, uint32_t& lo) {
+        const auto h = __builtin_amdgcn_cvt_pkrtz(p0, p1);
+        const float r0 = p0 - static_cast<float>(h[0]);
+        const float r1 = p1 - static_cast<float>(h[1]);
+        hi = __builtin_bit_cast(uint32_t, h);
+        lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
+    }
+};
+
+template <>
+struct MfmaOps<BF16> {
+    __device__ static __forceinline__ f32x4 qk(u32x4 a, u32x4 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                       c, 0, 0, 0);
+    }
+    __device__ static __forceinline__ f32x4 pv(u32x2 a, u32x2 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a), __builtin_bit_cast(i16x4, b),
+                                                         c, 0, 0, 0);
+    }
+    __device__ static __forceinline__ void split(float p0, float p1, uint32_t& hi, uint32_t& lo) {
+        const uint32_t u0 = f32_as_u32(p0), u1 = f32_as_u32(p1);
+        const float r0 = p0 - u32_as_f32(u0 & 0xFFFF0000u);
+        const float r1 = p1 - u32_as_f32(u1 & 0xFFFF0000u);
+        hi = __builtin_amdgcn_perm(u1, u0, 0x07060302u);  // upper halves: p0 low, p1 high
+        lo = __builtin_amdgcn_perm(f32_as_u32(r1), f32_as_u32(r0), 0x07060302u);
+    }
+};
+
+// NW consecutive 32-bit words (NW in {2, 4, 8}) from global memory.
+template <int NW, int NT>
+__device__ __forceinline__ void load_words(const void* p, uint32_t (&w)[NW]) {
+    if constexpr (NW == 2) {
+        u32x2 v;
+        if constexpr (NT)
+            v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+        else
+            v = *reinterpret_cast<const u32x2*>(p);
+        w[0] = v.x;
+        w[1] = v.y;
+    } else {
+#pragma unroll
+        for (int i = 0; i < NW / 4; ++i) {
+            const uint4 v = load16<NT>(static_cast<const uint32_t*>(p) + 4 * i);
+            w[4 * i + 0] = v.x;
+            w[4 * i + 1] = v.y;
+            w[4 * i + 2] = v.z;
+            w[4 * i + 3] = v.w;
+        }
+    }
+}
+
+template <int NW>
+__device__ __forceinline__ void store_words(void* p, const uint32_t (&w)[NW]) {
+#pragma unroll
+    for (int i = 0; i < NW; ++i) static_cast<uint32_t*>(p)[i] = w[i];
+}
+
+__device__ __forceinline__ u32x4 as_u32x4(const uint4& v) { return u32x4{v.x, v.y, v.z, v.w}; }
+
+// Sequence handled by grid row `row` under longest-first order: the one of
+// rank `row` in decreasing context length, ties by index.  Needs
+// num_seqs <= kMaxLptSeqs (host check); every thread returns the same value.
+template <int THREADS>
+__device__ __forceinline__ int longest_first_seq(const int32_t* __restrict__ context_lens, int num_seqs, int row,
+                                                 int tid) {
+    __shared__ int s_len[kMaxLptSeqs];
+    __shared__ int s_pick;
+    for (int i = tid; i < num_seqs; i += THREADS) s_len[i] = context_lens[i];
+    __syncthreads();
+    for (int i = tid; i < num_seqs; i += THREADS) {
+        const int c = s_len[i];
+        int rank = 0;
+        for (int j = 0; j < num_seqs; ++j) {
+            const int cj = s_len[j];
+            rank += (cj > c) || (cj == c && j < i);
+        }
+        if (rank == row) s_pick = i;
+    }
+    __syncthreads();
+    return __builtin_amdgcn_readfirstlane(s_pick);
+}
+
+template <class T, int D, int G, bool APPEND, bool NT>
+__global__ __launch_bounds__(kMfmaThreads) void decode_mfma_kernel(
+    typename T::bits* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_m,
+    float* __restrict__ ws_l, const typename T::bits* __restrict__ q, typename T::bits* __restrict__ kc,
+    typename T::bits* __restrict__ vc, const typename T::bits* __restrict__ knew,
+    const typename T::bits* __restrict__ vnew, const int32_t* __restrict__ block_tables,
+    const int32_t* __restrict__ context_lens, int num_seqs, int num_kv_heads, int log2_bs,
+    int max_blocks_per_seq, int max_context_len, int64_t num_blocks, int part_tokens, int max_parts,
+    int longest_first, float qscale) {
+    static_assert(sizeof(typename T::bits) == 2, "16-bit caches only");
+    static_assert(D == 64 || D == 128 || D == 256, "head_dim");
+    static_assert(G >= 1 && G <= 16, "group size");
+    constexpr int KS = D / 32;  // q.k k-steps (8 channels per lane each)
+    constexpr int E = D / 16;   // channels per lane of a V row = output tiles
+    constexpr int NW = E / 2;   // 32-bit words per lane of a V row
+    constexpr int DP = D + 4;   // padded LDS row
+    constexpr int HC0 = kMfmaMergeFloats / (kMfmaWaves * DP);
+    constexpr int HC = HC0 >= G ? G : (HC0 >= 8 ? 8 : (HC0 >= 4 ? 4 : (HC0 >= 2 ? 2 : 1)));  // heads per merge pass
+    static_assert(HC >= 1 && G % HC == 0, "merge chunk");
+    using bits = typename T::bits;
+    using Ops = MfmaOps<T>;
+
+    extern __shared__ int s_blk[];  // this partition's block ids (dynamic size)
+    __shared__ float s_m[kMfmaWaves][16], s_l[kMfmaWaves][16];
+    __shared__ float s_o[kMfmaWaves][HC][DP];
+
+    const int hk = blockIdx.x, srow = blockIdx.y, part = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int c = lane & 15, g = lane >> 4;
+    const int s = longest_first ? longest_first_seq<kMfmaThreads>(context_lens, num_seqs, srow, tid) : srow;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int num_heads = num_kv_heads * G;
+    const int64_t sh0 = static_cast<int64_t>(s) * num_heads + static_cast<int64_t>(hk) * G;
+    const int ctx = __builtin_amdgcn_readfirstlane(context_lens[s]);
+
+    if (ctx <= 0 || ctx > max_context_len) {
+        if (part == 0) {
+            const float v = (ctx == 0) ? 0.0f : __builtin_nanf("");
+            for (int d = tid; d < G * D; d += kMfmaThreads) out[sh0 * D + d] = narrow<T>(v);
+        }
+        return;
+    }
+    const int t_begin = part * part_tokens;
+    if (t_begin >= ctx) return;
+    const int t_end = min(ctx, t_begin + part_tokens);
+    const int bmask = (1 << log2_bs) - 1;
+    const int j0 = t_begin >> log2_bs;
+    const int nblk = ((t_end - 1) >> log2_bs) - j0 + 1;
+
+    const int32_t* bt = block_tables + static_cast<int64_t>(s) * max_blocks_per_seq;
+    for (int i = tid; i < nblk; i += kMfmaThreads) {
+        const int b = bt[j0 + i];
+        s_blk[i] = (b >= 0 && b < num_blocks) ? b : -1;
+    }
+
+    // B operand of q.k: query head c (zero for the padding heads c >= G).
+    u32x4 qv[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+        qv[ks] = (c < G) ? as_u32x4(load16(q + (sh0 + c) * D + 32 * ks + 8 * g)) : u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();  // s_blk is staged
+
+    const uint32_t blk_stride = static_cast<uint32_t>(num_kv_heads << log2_bs) * D;
+    const uint32_t head_off = (static_cast<uint32_t>(hk) << log2_bs) * D;
+    const bool newest_here = APPEND && t_end == ctx;
+    const int64_t kv_row = (static_cast<int64_t>(s) * num_kv_heads + hk) * D;  // row of knew/vnew
+
+    f32x4 acc[E];
+#pragma unroll
+    for (int t = 0; t < E; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    float m = -INFINITY;  // running maximum of head c's base-2 scores (same in the 4 lane groups)
+    float l = 0.0f;       // running sum of exp2(score - m) over this lane's tokens
+    int bad = 0;
+
+    const int ntile = (t_end - t_begin + kMfmaTile - 1) / kMfmaTile;
+
+    struct Tile {
+        uint4 k[KS];         // key row of token tb + c, channels 32 ks + 8 g .. +7
+        uint32_t v[4][NW];   // value rows of tokens tb + 4 g + i, channels E c .. E c + E - 1
+    };
+
+    // Issue the loads of tile `it`.  Tokens past the partition re-read its
+    // last token (always in bounds; masked out of the softmax).  In the
+    // newest tile t_end == ctx, and every lane whose clamped token is ctx - 1
+    // (the newest token and the masked lanes past it) reads the newest rows
+    // from knew/vnew, never the not-yet-written cache slot, whose contents
+    // may be anything (a masked token still multiplies its V row by p = 0,
+    // and 0 * NaN is NaN).
+    auto load_tile = [&](int it, Tile& tl) {
+        const int tb = t_begin + it * kMfmaTile;
+        const bool newest = APPEND && newest_here && it == ntile - 1;  // wave-uniform
+        const int tk = min(tb + c, t_end - 1);
+        const int bk = s_blk[(tk >> log2_bs) - j0];
+        bad |= (bk < 0);
+        const uint64_t ek = static_cast<uint64_t>(static_cast<uint32_t>(max(bk, 0))) * blk_stride + head_off +
+                            static_cast<uint32_t>(tk & bmask) * D + 8 * g;
+        const bits* kp = (newest && tk == ctx - 1) ? knew + kv_row + 8 * g : kc + ek;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) tl.k[ks] = load16<NT>(kp + 32 * ks);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int tv = min(tb + 4 * g + i, t_end - 1);
+            const int bv = s_blk[(tv >> log2_bs) - j0];
+            bad |= (bv < 0);
+            const uint64_t ev = static_cast<uint64_t>(static_cast<uint32_t>(max(bv, 0))) * blk_stride + head_off +
+                                static_cast<uint32_t>(tv & bmask) * D + E * c;
+            load_words<NW, NT>((newest && tv == ctx - 1) ? vnew + kv_row + E * c : vc + ev, tl.v[i]);
+        }
+    };
+
+    auto compute_tile = [&](int it, const Tile& tl) {
+        const int tb = t_begin + it * kMfmaTile;
+        if constexpr (APPEND) {
+            if (newest_here && it == ntile - 1) {
+                // The lanes whose own (unclamped) token is ctx - 1 store the
+                // newest rows they read from knew/vnew.
+                const int t = ctx - 1;
+                const int b = s_blk[(t >> log2_bs) - j0];
+                const uint64_t e = static_cast<uint64_t>(static_cast<uint32_t>(max(b, 0))) * blk_stride + head_off +
+                                   static_cast<uint32_t>(t & bmask) * D;
+                if (b >= 0 && tb + c == t) {
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks)
+                        *reinterpret_cast<uint4*>(kc + e + 8 * g + 32 * ks) = tl.k[ks];
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (b >= 0 && tb + 4 * g + i == t) store_words<NW>(vc + e + E * c, tl.v[i]);
+            }
+        }
+
+        // Scores S^T: lane (c, g) gets tokens tb + 4 g + j of head c.
+        f32x4 sc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) sc = Ops::qk(as_u32x4(tl.k[ks]), qv[ks], sc);
+
+        float x[4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            x[j] = (tb + 4 * g + j < t_end) ? sc[j] * qscale : -INFINITY;
+            mx = fmaxf(mx, x[j]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m, mx);  // finite: every tile holds a valid token
+        if (__builtin_amdgcn_ballot_w64(m_new > m)) {
+            const float alpha = fast_exp2(m - m_new);  // 0 on the first tile (m = -inf)
+            l *= alpha;
+#pragma unroll
+            for (int t = 0; t < E; ++t) acc[t] *= alpha;
+        }
+        m = m_new;
+        float p[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            p[j] = fast_exp2(x[j] - m);
+            l += p[j];
+        }
+        uint32_t ph0, pl0, ph1, pl1;
+        Ops::split(p[0], p[1], ph0, pl0);
+        Ops::split(p[2], p[3], ph1, pl1);
+        const u32x2 bh = u32x2{ph0, ph1}, bl = u32x2{pl0, pl1};
+
+        // O^T += V^T P^T, one output tile per channel offset t.
+#pragma unroll
+        for (int t = 0; t < E; ++t) {
+            const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+            const u32x2 a = u32x2{__builtin_amdgcn_perm(tl.v[1][t / 2], tl.v[0][t / 2], sel),
+                                  __builtin_amdgcn_perm(tl.v[3][t / 2], tl.v[2][t / 2], sel)};
+            acc[t] = Ops::pv(a, bh, acc[t]);
+            acc[t] = Ops::pv(a, bl, acc[t]);
+        }
+    };
+
+    int it = wave;
+    if constexpr (!kMfmaPrefetch) {
+        for (; it < ntile; it += kMfmaWaves) {
+            Tile ta;
+            load_tile(it, ta);
+            compute_tile(it, ta);
+        }
+    } else if (it < ntile) {
+        // Software pipeline: the next tile's loads are in flight while the
+        // current one is computed.
+        Tile ta, tb2;
+        load_tile(it, ta);
+        while (true) {
+            int nx = it + kMfmaWaves;
+            if (nx < ntile) load_tile(nx, tb2);
+            compute_tile(it, ta);
+            if (nx >= ntile) break;
+            it = nx;
+            nx = it + kMfmaWaves;
+            if (nx < ntile) load_tile(nx, ta);
+            compute_tile(it, tb2);
+            if (nx >= ntile) break;
+            it = nx;
+        }
+    }
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    bad = __syncthreads_or(bad);
+
+    // Merge the wavefronts through LDS, HC heads per pass.
+    const bool single = ctx <= part_tokens;
+    if (g == 0) {
+        s_m[wave][c] = m;
+        s_l[wave][c] = l;
+    }
+#pragma unroll
+    for (int c0 = 0; c0 < G; c0 += HC) {
+        if (c >= c0 && c < c0 + HC) {
+#pragma unroll
+            for (int t = 0; t < E; ++t)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) s_o[wave][c - c0][E * (4 * g + j) + t] = acc[t][j];
+        }
+        __syncthreads();
+        for (int idx = tid; idx < HC * D; idx += kMfmaThreads) {
+            const int hl = idx / D, d = idx % D, h = c0 + hl;
+            float M = s_m[0][h];
+#pragma unroll
+            for (int w = 1; w < kMfmaWaves; ++w) M = fmaxf(M, s_m[w][h]);
+            float L = 0.0f, O = 0.0f;
+#pragma unroll
+            for (int w = 0; w < kMfmaWaves; ++w) {
+                const float f = (s_m[w][h] == -INFINITY) ? 0.0f : fast_exp2(s_m[w][h] - M);
+                L = fmaf(f, s_l[w][h], L);
+                O = fmaf(f, s_o[w][hl][d], O);
+            }
+            if (bad) O = __builtin_nanf("");
+            const int64_t sh = sh0 + h;
+            if (single) {
+                out[sh * D + d] = narrow<T>(O / L);
+            } else {
+                ws_o[(sh * max_parts + part) * D + d] = O;
+                if (d == 0) {
+                    ws_m[sh * max_parts + part] = M;
+                    ws_l[sh * max_parts + part] = L;
+                }
+            }
+        }
+        if (c0 + HC < G) __syncthreads();  // s_o is reused by the next pass
+    }
+}
+
+}  // namespace pa

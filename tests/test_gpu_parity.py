@@ -121,6 +121,14 @@ def test_longest_context_and_full_table():
     full_parity(case, partitions=(0, 2048))
 
 
+def test_16bit_partition_beyond_matrix_core_staging():
+    # 16-bit caches normally take the matrix-core kernel; a partition that
+    # stages more than 6144 block ids (block size 1, 6300-token partition)
+    # takes the vector kernel instead.  Both must agree with the oracle.
+    case = wl.random_case(303, 2, 4, 128, 1, "bf16", ctx=[6400, 700], spare_blocks=3, num_kv_heads=1)
+    full_parity(case, partitions=(6300, 0), strict=False)
+
+
 def test_empty_calls_are_no_ops():
     case = wl.random_case(302, 2, 2, 64, 8, "f16", ctx=[3, 9])
     g = GpuCase(case)

@@ -1,10 +1,11 @@
-"""Host-side check of the decode kernel's address arithmetic.
+"""Host-side check of the decode kernels' address arithmetic.
 
-Mirrors the index formulas of the partition kernel in
-``paged_kv_cache_322_amd/csrc/pa_decode.hip`` (launch geometry, partition
-bounds, LDS staging of block ids, clamped token addresses, workspace slots)
-and asserts that, for every workload the GPU tests and the benchmark launch,
-every read and write stays inside its buffer.  Runs on the CPU only.
+Mirrors the index formulas of the vector partition kernel
+(``csrc/pa_decode_impl.h``) and of the matrix-core kernel
+(``csrc/pa_decode_mfma.h``): launch geometry, partition bounds, LDS staging
+of block ids and merge buffers, clamped token addresses, query and workspace
+slots, and asserts that, for every workload the GPU tests and the benchmark
+launch, every read and write stays inside its buffer.  Runs on the CPU only.
 """
 import functools
 import math
@@ -78,6 +79,78 @@ def check_decode_bounds(S, H, D, B, N, W, elem, ctx, bt, max_ctx, part, G=1):
                 assert ((s * H * G + H * G - 1) * max_parts + p) * D + D <= ws_o_elems * G
 
 
+MFMA_TILE = 16
+MFMA_WAVES = 8
+MFMA_MERGE_FLOATS = 8192
+
+
+def mfma_merge_heads(D, G):
+    hc0 = MFMA_MERGE_FLOATS // (MFMA_WAVES * (D + 4))
+    for hc in (G, 8, 4, 2, 1):
+        if hc <= hc0 or hc == 1:
+            return hc
+
+
+def check_mfma_bounds(S, Hk, G, D, B, N, W, ctx, bt, max_ctx, part):
+    """The matrix-core kernel: 16-token tiles; lane (c, g) = (lane % 16, lane // 16)
+    reads key channels 32 ks + 8 g .. +7 of token tb + c and value channels
+    E c .. E c + E - 1 (E = D / 16) of tokens tb + 4 g + i; the query operand
+    is head c < G; merge rows s_o[wave][c - c0][E (4 g + j) + t]."""
+    assert D in (64, 128, 256)
+    E = D // 16
+    KS = D // 32
+    c = np.arange(16)
+    g = np.arange(4)
+    # Per-lane channel extents inside one row of D elements.
+    k_lo = (32 * np.arange(KS)[:, None] + 8 * g[None, :]).ravel()
+    assert k_lo.min() >= 0 and k_lo.max() + 8 <= D
+    v_lo = E * c
+    assert v_lo.max() + E <= D
+    # Query rows: head sh0 + c for c < G only (the rest are zero operands).
+    H = Hk * G
+    q_rows = (np.arange(S)[:, None] * H + np.arange(Hk)[None, :] * G)[..., None] + np.arange(G)
+    assert q_rows.max() * D + D <= S * H * D
+    # Merge buffer indices.
+    hc = mfma_merge_heads(D, G)
+    assert G % hc == 0
+    col = E * (4 * g[:, None, None] + np.arange(4)[None, :, None]) + np.arange(E)[None, None, :]
+    assert col.min() >= 0 and col.max() < D
+    assert MFMA_WAVES * hc * (D + 4) <= MFMA_MERGE_FLOATS or hc == 1
+    log2b = B.bit_length() - 1
+    staged = (part + B - 1) // B + 1
+    blk_stride = Hk * B * D
+    cache_elems = N * Hk * B * D
+    max_parts = max(1, math.ceil(max_ctx / part))
+    for s in range(S):
+        cl = int(ctx[s])
+        if cl <= 0 or cl > max_ctx:
+            continue
+        for p in range(max_parts):
+            t_begin = p * part
+            if t_begin >= cl:
+                continue
+            t_end = min(cl, t_begin + part)
+            j0 = t_begin >> log2b
+            nblk = ((t_end - 1) >> log2b) - j0 + 1
+            assert 1 <= nblk <= staged and j0 + nblk - 1 < W
+            ntile = (t_end - t_begin + MFMA_TILE - 1) // MFMA_TILE
+            tb = t_begin + np.arange(ntile)[:, None] * MFMA_TILE
+            tk = np.minimum(tb + c[None, :], t_end - 1).ravel()
+            tv = np.minimum(tb + (4 * g[:, None] + np.arange(4)[None, :]).ravel()[None, :], t_end - 1).ravel()
+            for t, lo, width in ((tk, k_lo, 8), (tv, v_lo, E)):
+                assert t.min() >= t_begin
+                lds = (t >> log2b) - j0
+                assert lds.min() >= 0 and lds.max() < nblk
+                b = bt[s, j0 + lds]
+                b = np.where((b >= 0) & (b < N), b, 0)
+                e = b.astype(np.int64) * blk_stride + (Hk - 1) * B * D + (t & (B - 1)).astype(np.int64) * D
+                assert e.min() >= 0 and e.max() + lo.max() + width <= cache_elems
+            # The newest token (append) is token cl - 1, covered by the last tile.
+            if t_end == cl:
+                last = tb[-1, 0]
+                assert last <= cl - 1 < last + MFMA_TILE
+
+
 CASES = [
     ("config1", functools.lru_cache(None)(lambda: wl.config1())),
     ("config2", functools.lru_cache(None)(lambda: wl.config2())),
@@ -115,3 +188,38 @@ def test_invalid_ids_are_clamped_in_the_model():
     bt[0, 1] = 10**6
     bt[1, 0] = -7
     check_decode_bounds(2, 1, 8, 4, case.num_blocks, bt.shape[1], 4, case.context_lens, bt, 9, 4)
+
+
+MFMA_CASES = [c for c in CASES if c[0] in ("config2", "config3", "config5", "edge", "gqa-llama3-8b",
+                                            "config4-B8", "config4-B32")]
+
+
+@pytest.mark.parametrize("name,make", MFMA_CASES, ids=[c[0] for c in MFMA_CASES])
+@pytest.mark.parametrize("part", [0, 16, 64, 512, 1 << 30])
+def test_mfma_index_bounds(name, make, part):
+    case = make()
+    if case.head_dim not in (64, 128, 256) or case.elem_bytes != 2:
+        pytest.skip("matrix-core kernel serves 16-bit caches with D in {64, 128, 256}")
+    B = case.block_size
+    max_ctx = case.max_context_len
+    p = default_partition(case.num_seqs, case.num_kv_heads, max_ctx) if part == 0 else part
+    if p == 1 << 30:
+        p = max(1, max_ctx)
+    if (p + B - 1) // B + 1 > 6144:
+        pytest.skip("such partitions take the vector kernel")
+    check_mfma_bounds(case.num_seqs, case.num_kv_heads, case.num_heads // case.num_kv_heads, case.head_dim, B,
+                      case.num_blocks, case.block_tables.shape[1], case.context_lens, case.block_tables, max_ctx, p)
+
+
+def test_mfma_gqa70b_bounds():
+    case = wl.gqa_config("llama2-70b-tp8")
+    check_mfma_bounds(case.num_seqs, case.num_kv_heads, 8, case.head_dim, case.block_size, case.num_blocks,
+                      case.block_tables.shape[1], case.context_lens, case.block_tables, case.max_context_len, 256)
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_mfma_bounds_all_shapes(D, G):
+    case = wl.random_case(23, 3, 2 * G, D, 8, "f16", ctx=[1, 37, 300], num_kv_heads=2)
+    check_mfma_bounds(3, 2, G, D, 8, case.num_blocks, case.block_tables.shape[1], case.context_lens,
+                      case.block_tables, case.max_context_len, 64)
