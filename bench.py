@@ -114,10 +114,17 @@ def unique_kv_bytes(case):
     return 2 * case.elem_bytes * case.num_kv_heads * case.head_dim * sum(seen.values())
 
 
-def traffic_from_profiles(kernel_src_sha):
-    """HBM bytes per decode launch from the committed counter summary, if it
-    was taken on the current kernel source; else None."""
-    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "decode_llama7b_counters.txt")
+# Committed HBM counter summaries (rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled
+# by a copy kernel of known size), per workload at its default plan.
+COUNTER_FILES = {"2": "decode_llama7b_counters.txt", "gqa8b": "decode_gqa_llama3_8b_counters.txt"}
+
+
+def traffic_from_profiles(config, kernel_src_sha):
+    """HBM bytes per decode launch from the committed counter summary of this
+    workload, if it was taken on the current kernel source; else None."""
+    if config not in COUNTER_FILES:
+        return None
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", COUNTER_FILES[config])
     if not os.path.exists(path):
         return None
     vals = {}
@@ -133,12 +140,22 @@ def traffic_from_profiles(kernel_src_sha):
         return None
 
 
+def decode_kernel_name(case):
+    """The decode kernel the library runs for this shape: the matrix-core
+    kernel for 16-bit caches with D in {64, 128, 256} and grouped heads, else
+    the vector-ALU kernel."""
+    G = case.num_heads // case.num_kv_heads
+    if case.elem_bytes == 2 and case.head_dim in (64, 128, 256) and G >= 2:
+        return "decode_mfma_kernel"
+    return "decode_partition_kernel"
+
+
 def kernel_source_sha():
     import hashlib
 
     root = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_cache_322_amd", "csrc")
     h = hashlib.sha256()
-    for name in ("pa_decode_impl.h", "pa_device.h", "pa_internal.h"):
+    for name in ("pa_decode_impl.h", "pa_decode_mfma.h", "pa_device.h", "pa_internal.h"):
         h.update(open(os.path.join(root, name), "rb").read())
     return h.hexdigest()
 
@@ -345,9 +362,10 @@ def main():
     step_bytes = decode_bytes + store_bytes
     value = step_bytes / (ms_step * 1e-3) / 1e9
     achieved = decode_bytes / (launch_ms * 1e-3) / 1e9
-    # The committed counters cover the default workload at the default partition.
-    traffic = (traffic_from_profiles(kernel_source_sha())
-               if args.config == "2" and args.partition in (0, pa.partition_tokens(S, H, max_ctx)) else None)
+    # The committed counters cover each profiled workload at its default partition.
+    default_part = pa.partition_tokens(S, H, max_ctx, num_kv_heads=case.num_kv_heads)
+    traffic = (traffic_from_profiles(args.config, kernel_source_sha())
+               if args.partition in (0, default_part) else None)
 
     result = {
         "metric": METRIC,
@@ -374,7 +392,7 @@ def main():
             "num_blocks": case.num_blocks,
             "sum_context_len": int(case.context_lens.sum()),
             "max_context_len": max_ctx,
-            "partition_tokens": pa.partition_tokens(S, case.num_kv_heads, max_ctx, args.partition),
+            "partition_tokens": pa.partition_tokens(S, H, max_ctx, args.partition, num_kv_heads=case.num_kv_heads),
             "pool_copies_rotated": len(pools),
             "shared_blocks_flag": shared,
         },
@@ -382,8 +400,8 @@ def main():
         "decode_tokens_per_s": round(S / (ms_step * 1e-3), 1),
         "step_bytes": int(step_bytes),
         "roofline": {
-            "kernel": "pa_decode (decode_partition_kernel, plus decode_merge_kernel when a context is split), "
-                      "event-timed",
+            "kernel": f"pa_decode ({decode_kernel_name(case)}, plus decode_merge_kernel when a context is "
+                      "split), event-timed",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,

@@ -75,20 +75,23 @@ typedef enum {
  * tokens, one workgroup each (serving all query heads of that K/V head);
  * workgroups are dispatched in grid order.  A positive `partition_size` is
  * returned unchanged.  0 selects the default, from the number of
- * (sequence, K/V head) pairs S*H (H = num_kv_heads here):
- *   S*H >= 8192:  the whole context (next power of two of max_context_len,
- *                 clamped to [256, 4096]) per workgroup, in batch order;
- *   1024 <= S*H < 8192 and S <= 512:  whole contexts as above, dispatched
- *                 longest context first (no split, no merge launch);
- *   otherwise:    the largest power of two in [256, 4096] (not above the
- *                 next power of two of max_context_len) that still gives
- *                 S*H*ceil(max_context_len / P) >= 8192 work items, in
- *                 batch order.
+ * (sequence, K/V head) pairs R = num_seqs * num_kv_heads and the group size
+ * G = num_heads / num_kv_heads, with Pmin = 256 and Rlpt = 1024 for G = 1,
+ * Pmin = 512 and Rlpt = 512 for G >= 2:
+ *   R >= 8192:  the whole context (next power of two of max_context_len,
+ *               clamped to [Pmin, 4096]) per workgroup, in batch order;
+ *   Rlpt <= R < 8192 and num_seqs <= 512:  whole contexts as above,
+ *               dispatched longest context first (no split, no merge launch);
+ *   otherwise:  the largest power of two in [Pmin, 4096] (not above the
+ *               next power of two of max_context_len) that still gives
+ *               R * ceil(max_context_len / P) >= 8192 work items, in batch
+ *               order.
  * Longest-first order applies only when no context is split.
- * Returns 0 for invalid sizes.
+ * Returns 0 for invalid sizes (num_heads not a multiple of num_kv_heads
+ * included).
  */
-int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
-                                   int32_t partition_size);
+int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                   int32_t max_context_len, int32_t partition_size);
 
 /*
  * pa_decode_workspace_size - bytes of device scratch pa_decode needs.

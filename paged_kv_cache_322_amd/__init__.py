@@ -47,7 +47,7 @@ _i64 = ctypes.c_int64
 lib.pa_status_string.restype = ctypes.c_char_p
 lib.pa_status_string.argtypes = [ctypes.c_int]
 lib.pa_decode_partition_tokens.restype = _i32
-lib.pa_decode_partition_tokens.argtypes = [_i32, _i32, _i32, _i32]
+lib.pa_decode_partition_tokens.argtypes = [_i32, _i32, _i32, _i32, _i32]
 lib.pa_decode_workspace_size.restype = ctypes.c_size_t
 lib.pa_decode_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32]
 lib.pa_decode.restype = ctypes.c_int
@@ -107,9 +107,12 @@ def _code(dtype: torch.dtype) -> int:
         raise TypeError(f"unsupported element type {dtype}; use float32, float16 or bfloat16") from None
 
 
-def partition_tokens(num_seqs: int, num_kv_heads: int, max_context_len: int, partition_size: int = 0) -> int:
-    """KV partition length ``decode`` uses (``partition_size`` 0 = library default)."""
-    return int(lib.pa_decode_partition_tokens(num_seqs, num_kv_heads, max_context_len, partition_size))
+def partition_tokens(num_seqs: int, num_heads: int, max_context_len: int, partition_size: int = 0,
+                     num_kv_heads: Optional[int] = None) -> int:
+    """KV partition length ``decode`` uses (``partition_size`` 0 = library default;
+    ``num_kv_heads`` defaults to ``num_heads``, multi-head attention)."""
+    hk = num_heads if num_kv_heads is None else num_kv_heads
+    return int(lib.pa_decode_partition_tokens(num_seqs, num_heads, hk, max_context_len, partition_size))
 
 
 def decode_workspace_size(num_seqs: int, num_heads: int, head_dim: int, max_context_len: int,

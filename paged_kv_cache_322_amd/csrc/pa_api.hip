@@ -20,8 +20,10 @@ bool supported_block_size(int32_t b) { return b >= 1 && b <= 256 && (b & (b - 1)
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int resolve_partition(int32_t partition_size, int32_t num_seqs, int32_t num_heads, int32_t max_context_len) {
-    return pa::plan_decode(num_seqs, num_heads, max_context_len, partition_size).part_tokens;
+int resolve_partition(int32_t partition_size, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                      int32_t max_context_len) {
+    return pa::plan_decode(num_seqs, num_kv_heads, num_heads / num_kv_heads, max_context_len, partition_size)
+        .part_tokens;
 }
 
 int64_t parts_for(int32_t max_context_len, int part) {
@@ -51,18 +53,20 @@ const char* pa_status_string(int status) {
     }
 }
 
-int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
-                                   int32_t partition_size) {
-    if (num_seqs < 0 || num_kv_heads <= 0 || max_context_len < 0 || partition_size < 0) return 0;
-    return resolve_partition(partition_size, num_seqs, num_kv_heads, max_context_len);
+int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                   int32_t max_context_len, int32_t partition_size) {
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads || max_context_len < 0 ||
+        partition_size < 0)
+        return 0;
+    return resolve_partition(partition_size, num_seqs, num_heads, num_kv_heads, max_context_len);
 }
 
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                                 int32_t max_context_len, int32_t partition_size) {
-    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_context_len < 0 ||
-        partition_size < 0)
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads || head_dim <= 0 ||
+        max_context_len < 0 || partition_size < 0)
         return 0;
-    const int part = resolve_partition(partition_size, num_seqs, num_kv_heads, max_context_len);
+    const int part = resolve_partition(partition_size, num_seqs, num_heads, num_kv_heads, max_context_len);
     return workspace_bytes_for(num_seqs, num_heads, head_dim, parts_for(max_context_len, part));
 }
 
@@ -98,7 +102,8 @@ int decode_common(void* out, const void* query, const void* key, const void* val
     if (!aligned16(out) || !aligned16(query) || !aligned16(k_cache) || !aligned16(v_cache))
         return PA_ERR_INVALID;
     if (append && (!aligned16(key) || !aligned16(value))) return PA_ERR_INVALID;
-    const pa::DecodePlan plan = pa::plan_decode(num_seqs, num_kv_heads, max_context_len, partition_size);
+    const pa::DecodePlan plan =
+        pa::plan_decode(num_seqs, num_kv_heads, num_heads / num_kv_heads, max_context_len, partition_size);
     const int part = plan.part_tokens;
     // A partition may start mid-block, so it touches at most ceil(P/B) + 1 blocks.
     const int64_t staged = pa::partition_blocks(part, block_size);

@@ -13,24 +13,41 @@ constexpr int kMaxPartitionBlocks = 8192;
 
 // Launch plan of pa_decode.
 //
-// Work items are (sequence, head, KV partition).  The hardware dispatches
-// workgroups in grid order, so the order of the items decides how evenly the
-// 256 compute units finish.
-//  * Many (sequence, head) pairs (>= kManyPairs): whole contexts up to 4096
-//    tokens per item, in batch order (the items are many and short enough).
-//  * Fewer pairs but at least kLptPairs, and at most kMaxLptSeqs sequences:
-//    whole contexts, dispatched longest first (each workgroup finds the
-//    sequence of its rank; longest-processing-time-first list scheduling).
-//    No split means no merge launch.
+// Work items are (sequence, K/V head, KV partition).  The hardware
+// dispatches workgroups in grid order, so the order of the items decides how
+// evenly the 256 compute units finish.
+//  * Many (sequence, K/V head) pairs (>= kManyPairs): whole contexts up to
+//    4096 tokens per item, in batch order (the items are many and short
+//    enough).
+//  * Fewer pairs but at least the longest-first threshold, and at most
+//    kMaxLptSeqs sequences: whole contexts, dispatched longest first (each
+//    workgroup finds the sequence of its rank; longest-processing-time-first
+//    list scheduling).  No split means no merge launch.
 //  * Otherwise: split contexts into the largest power-of-two partition in
-//    [256, 4096] that still gives >= kManyPairs items, in batch order.
-// A caller-given partition length overrides the length choice.  Longest-first
-// order is used only when no context is split: with splits, the empty
-// partitions of short sequences would pay for the ranking before exiting.
-constexpr int kMinDefaultPartition = 256;
+//    [minimum, 4096] that still gives >= kManyPairs items, in batch order.
+// The longest-first threshold and the minimum partition depend on the group
+// size G (query heads per K/V head), because G >= 2 runs the matrix-core
+// kernel, whose workgroups carry less per-token work and more fixed cost:
+//   G = 1:  longest first from 1024 pairs, partitions of at least 256 tokens;
+//   G >= 2: longest first from 512 pairs, partitions of at least 512 tokens
+// (measured on MI355X: LLaMA-3-8B-shaped GQA batch 72 -> 64 us, a one-K/V-head
+// 128-sequence batch 49 -> 46 us; for multi-head batches the G = 1 values
+// measured best).  A caller-given partition length overrides the length
+// choice.  Longest-first order is used only when no context is split: with
+// splits, the empty partitions of short sequences would pay for the ranking
+// before exiting.
+#ifndef PA_LPT_PAIRS
+#define PA_LPT_PAIRS 1024
+#endif
+#ifndef PA_MIN_PART
+#define PA_MIN_PART 256
+#endif
+constexpr int kMinDefaultPartition = PA_MIN_PART;
+constexpr int kMinGroupedPartition = 512;
 constexpr int kMaxDefaultPartition = 4096;
 constexpr int64_t kManyPairs = 8192;
-constexpr int64_t kLptPairs = 1024;
+constexpr int64_t kLptPairs = PA_LPT_PAIRS;
+constexpr int64_t kLptGroupedPairs = 512;
 constexpr int kMaxLptSeqs = 512;
 
 struct DecodePlan {
@@ -38,21 +55,23 @@ struct DecodePlan {
     bool longest_first;
 };
 
-inline DecodePlan plan_decode(int64_t num_seqs, int64_t num_heads, int64_t max_context_len, int partition_size) {
-    const int64_t pairs = num_seqs * num_heads;
-    int whole = kMinDefaultPartition;
+inline DecodePlan plan_decode(int64_t num_seqs, int64_t num_kv_heads, int64_t group, int64_t max_context_len,
+                              int partition_size) {
+    const int64_t pairs = num_seqs * num_kv_heads;
+    const int min_part = group >= 2 ? kMinGroupedPartition : kMinDefaultPartition;
+    const int64_t lpt_pairs = group >= 2 ? kLptGroupedPairs : kLptPairs;
+    int whole = min_part;
     while (whole < kMaxDefaultPartition && whole < max_context_len) whole *= 2;
     DecodePlan p{whole, false};
     const bool can_sort = num_seqs <= kMaxLptSeqs;
     if (pairs >= kManyPairs) {
         p.part_tokens = whole;
-    } else if (pairs >= kLptPairs && can_sort) {
+    } else if (pairs >= lpt_pairs && can_sort) {
         p.part_tokens = whole;
         p.longest_first = true;
     } else {
         int part = whole;
-        while (part > kMinDefaultPartition && pairs * ((max_context_len + part - 1) / part) < kManyPairs)
-            part /= 2;
+        while (part > min_part && pairs * ((max_context_len + part - 1) / part) < kManyPairs) part /= 2;
         p.part_tokens = part;
     }
     if (partition_size > 0) p.part_tokens = partition_size;

@@ -53,6 +53,30 @@ def test_default_partition_heuristic():
     assert pa.partition_tokens(-1, 32, 10) == 0
 
 
+def test_default_partition_heuristic_grouped():
+    # G >= 2 (matrix-core kernel): longest first from 512 pairs, partitions of
+    # at least 512 tokens.
+    assert pa.partition_tokens(64, 32, 2048, num_kv_heads=8) == 2048  # LLaMA-3-8B shape: 512 pairs, whole
+    assert pa.partition_tokens(64, 32, 2048, num_kv_heads=32) == 2048  # 2048 multi-head pairs: whole too
+    assert pa.partition_tokens(16, 32, 2048) == 256  # 512 multi-head pairs: split to 256 tokens
+    assert pa.partition_tokens(128, 8, 4096, num_kv_heads=1) == 512  # 128 pairs, minimum 512
+    assert pa.partition_tokens(128, 8, 300, num_kv_heads=1) == 512  # whole context rounds up to 512
+    assert pa.partition_tokens(2, 30, 100, num_kv_heads=8) == 0  # 30 heads over 8 K/V heads: invalid
+    assert pa.partition_tokens(2, 8, 100, 64, num_kv_heads=1) == 64  # explicit sizes pass through
+
+
+def test_plan_mirror_matches_library():
+    """The host-side bounds model mirrors the library's plan; check the mirror
+    against the library over a grid of shapes."""
+    import test_kernel_index_bounds as tb
+
+    for S in (1, 3, 16, 64, 200, 513, 4096):
+        for H, Hk in ((1, 1), (8, 1), (32, 8), (32, 32), (40, 40), (96, 96), (64, 8)):
+            for maxc in (1, 37, 256, 300, 513, 2048, 4096, 100000):
+                assert pa.partition_tokens(S, H, maxc, num_kv_heads=Hk) == tb.default_partition(S, Hk, maxc, H // Hk), \
+                    (S, H, Hk, maxc)
+
+
 def test_workspace_size():
     assert pa.decode_workspace_size(64, 32, 128, 256) == 0  # one default partition suffices
     assert pa.decode_workspace_size(64, 32, 128, 513) == 0  # whole contexts (1024), longest first
@@ -62,6 +86,11 @@ def test_workspace_size():
     assert pa.decode_workspace_size(128, 96, 128, 2048, 256) == 128 * 96 * 8 * 130 * 4
     assert pa.decode_workspace_size(3, 1, 8, 37, 16) == 3 * 1 * 3 * 10 * 4
     assert pa.decode_workspace_size(-1, 1, 8, 37, 16) == 0
+    # One K/V head serving 8 query heads, 128 sequences up to 4096 tokens:
+    # partitions of 512 tokens, 8 of them.
+    assert pa.decode_workspace_size(128, 8, 128, 4096, num_kv_heads=1) == 128 * 8 * 8 * 130 * 4
+    assert pa.decode_workspace_size(64, 32, 128, 2048, num_kv_heads=8) == 0  # whole contexts, longest first
+    assert pa.decode_workspace_size(2, 30, 128, 100, num_kv_heads=8) == 0  # invalid grouping
 
 
 def dec(**kw):

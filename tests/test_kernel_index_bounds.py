@@ -18,15 +18,16 @@ import workloads as wl
 MAX_PART_BLOCKS = 8192
 
 
-def default_partition(S, H, max_ctx):
+def default_partition(S, Hk, max_ctx, G=1):
     """Mirror of the library's default partition rule (plan_decode)."""
-    whole = 256
+    pmin, lpt = (512, 512) if G >= 2 else (256, 1024)
+    whole = pmin
     while whole < 4096 and whole < max_ctx:
         whole *= 2
-    if S * H >= 8192 or (S * H >= 1024 and S <= 512):
+    if S * Hk >= 8192 or (S * Hk >= lpt and S <= 512):
         return whole
     part = whole
-    while part > 256 and S * H * (-(-max_ctx // part)) < 8192:
+    while part > pmin and S * Hk * (-(-max_ctx // part)) < 8192:
         part //= 2
     return part
 
@@ -169,7 +170,8 @@ def test_decode_index_bounds(name, make, part):
     case = make()
     B = case.block_size
     max_ctx = case.max_context_len
-    p = default_partition(case.num_seqs, case.num_kv_heads, max_ctx) if part == 0 else part
+    G = case.num_heads // case.num_kv_heads
+    p = default_partition(case.num_seqs, case.num_kv_heads, max_ctx, G) if part == 0 else part
     if p == 1 << 30:
         p = max(1, max_ctx)  # a single partition covers every context
     if (p + B - 1) // B + 1 > MAX_PART_BLOCKS:
@@ -202,7 +204,8 @@ def test_mfma_index_bounds(name, make, part):
         pytest.skip("matrix-core kernel serves 16-bit caches with D in {64, 128, 256}")
     B = case.block_size
     max_ctx = case.max_context_len
-    p = default_partition(case.num_seqs, case.num_kv_heads, max_ctx) if part == 0 else part
+    G = case.num_heads // case.num_kv_heads
+    p = default_partition(case.num_seqs, case.num_kv_heads, max_ctx, G) if part == 0 else part
     if p == 1 << 30:
         p = max(1, max_ctx)
     if (p + B - 1) // B + 1 > 6144:
