@@ -22,16 +22,19 @@ from .paged_attention import (
     token_location,
     widen,
 )
+from .prefill import causal_rows, paged_prefill
 
 __all__ = [
     "append_decode",
     "attention",
+    "causal_rows",
     "blocks_held",
     "copy_blocks",
     "logical_kv",
     "merge_partials",
     "newest_token_slots",
     "paged_decode",
+    "paged_prefill",
     "partial_attention",
     "reshape_and_cache",
     "token_location",

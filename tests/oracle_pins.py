@@ -469,3 +469,159 @@ ALL_PINS = [
     pin_newest_token_slots,
     pin_grouped_query,
 ]
+
+
+# ---------------------------------------------------------------------------
+# Prefill pins (take the oracle.prefill module)
+# ---------------------------------------------------------------------------
+
+
+def brute_prefill(q, kc, vc, bt, ctx, query_start, scale, dtype) -> np.ndarray:
+    """Per-token loops over the prefill definition: row i of sequence s sits
+    at position ctx_s - n_s + i and attends to positions 0 .. that position;
+    token t is found at block bt[s][t // B], slot t % B.  math.fsum sums,
+    math.exp weights.  Tiny inputs only."""
+    qw, kw, vw = torch_widen(q, dtype), torch_widen(kc, dtype), torch_widen(vc, dtype)
+    T, H, D = q.shape
+    B = kc.shape[2]
+    G = H // kc.shape[1]
+    out = np.zeros((T, H, D))
+    for s in range(len(ctx)):
+        r0, r1 = int(query_start[s]), int(query_start[s + 1])
+        n, c = r1 - r0, int(ctx[s])
+        for i in range(n):
+            pos = c - n + i
+            loc = [(int(bt[s][t // B]), t % B) for t in range(pos + 1)]
+            for h in range(H):
+                hk = h // G
+                sc = [scale * math.fsum(float(qw[r0 + i, h, d]) * float(kw[b, hk, o, d]) for d in range(D))
+                      for b, o in loc]
+                mx = max(sc)
+                e = [math.exp(x - mx) for x in sc]
+                z = math.fsum(e)
+                for d in range(D):
+                    out[r0 + i, h, d] = math.fsum(e[t] * float(vw[b, hk, o, d]) for t, (b, o) in enumerate(loc)) / z
+    return out
+
+
+def _prefill_small_cases():
+    yield wl.random_prefill_case(1, [0, 5, 17], [3, 1, 20], 2, 8, 4, "f32")
+    yield wl.random_prefill_case(2, [0, 0], [7, 1], 2, 4, 2, "f16")
+    yield wl.random_prefill_case(3, [9, 2, 0, 4], [2, 6, 5, 1], 4, 8, 3, "bf16", num_kv_heads=2)
+    yield wl.random_prefill_case(4, [1], [12], 4, 4, 1, "f32", num_kv_heads=1)
+
+
+def _prefill_pools(case):
+    """Pools after the case's chunk is written, by explicit loops (no oracle)."""
+    kc, vc = case.k_cache.copy(), case.v_cache.copy()
+    B = kc.shape[2]
+    for st in case.steps:
+        for i, slot in enumerate(st.slot_mapping):
+            b, o = int(slot) // B, int(slot) % B
+            kc[b, :, o, :] = st.key[i]
+            vc[b, :, o, :] = st.value[i]
+    return kc, vc
+
+
+def _prefill(orc, case, kc, vc, q=None, ctx=None, qs=None, scale=None):
+    return orc.paged_prefill(case.q if q is None else q, kc, vc, case.block_tables,
+                             case.context_lens if ctx is None else ctx,
+                             case.query_start if qs is None else qs,
+                             case.scale if scale is None else scale, case.dtype)
+
+
+def pin_prefill_bruteforce(orp):
+    """Prefill oracle == per-token brute force on tiny ragged paged cases,
+    incl. whole prompts (no prefix), single-row chunks, B = 1 and groups."""
+    for case in _prefill_small_cases():
+        kc, vc = _prefill_pools(case)
+        got = _prefill(orp, case, kc, vc)
+        ref = brute_prefill(case.q, kc, vc, case.block_tables, case.context_lens, case.query_start, case.scale,
+                            case.dtype)
+        err = np.abs(got - ref).max()
+        assert err <= 1e-12, (case.name, err)
+
+
+def pin_prefill_library(orp):
+    """Contiguous K/V scattered into a pool by loops: a whole-prompt prefill
+    equals torch's causal scaled_dot_product_attention, and a chunk after a
+    prefix equals the last rows of that causal attention over the whole
+    sequence (torch aligns its causal mask to the first query, so the chunk's
+    offset is checked against an independent placement)."""
+    rng = np.random.default_rng(21)
+    for dtype, H, Hk, D, B, ctx, n in (("f32", 2, 2, 16, 4, 23, 23), ("f16", 4, 2, 32, 8, 40, 13),
+                                       ("bf16", 2, 1, 8, 16, 17, 1), ("f32", 3, 3, 8, 2, 9, 5)):
+        nb = -(-ctx // B)
+        N = nb + 3
+        table = rng.permutation(N)[:nb]
+        K = wl.to_storage(rng.standard_normal((Hk, ctx, D), dtype=np.float32), dtype)
+        V = wl.to_storage(rng.standard_normal((Hk, ctx, D), dtype=np.float32), dtype)
+        Qall = wl.to_storage(rng.standard_normal((ctx, H, D), dtype=np.float32), dtype)
+        kc = scatter_contiguous(K, table, B, N, dtype)
+        vc = scatter_contiguous(V, table, B, N, dtype)
+        bt = np.full((1, nb + 1), -1, dtype=np.int32)
+        bt[0, :nb] = table
+        scale = 1.0 / math.sqrt(D)
+        q = np.ascontiguousarray(Qall[ctx - n:])
+        got = orp.paged_prefill(q, kc, vc, bt, np.array([ctx], np.int32), np.array([0, n], np.int32), scale, dtype)
+        G = H // Hk
+        tq = torch.from_numpy(torch_widen(Qall, dtype)).permute(1, 0, 2).unsqueeze(0)  # [1, H, ctx, D]
+        tk = torch.from_numpy(torch_widen(K, dtype)).repeat_interleave(G, dim=0).unsqueeze(0)
+        tv = torch.from_numpy(torch_widen(V, dtype)).repeat_interleave(G, dim=0).unsqueeze(0)
+        full = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True, scale=scale)
+        ref = full[0].permute(1, 0, 2).numpy()[ctx - n:]
+        err = np.abs(got - ref).max()
+        assert err <= 1e-12, (dtype, H, Hk, ctx, n, err)
+
+
+def pin_prefill_single_query(orp):
+    """Chunks of one row are decode queries: the result equals the
+    brute-force decode of the same queries over the same contexts."""
+    case = wl.random_prefill_case(5, [4, 0, 11], [1, 1, 1], 4, 8, 4, "f16", num_kv_heads=2)
+    kc, vc = _prefill_pools(case)
+    got = _prefill(orp, case, kc, vc)
+    ref = brute_decode(case.q, kc, vc, case.block_tables, case.context_lens, case.scale, case.dtype)
+    assert np.abs(got - ref).max() <= 1e-12
+
+
+def pin_prefill_chunking(orp):
+    """Prefilling a prompt in chunks gives each row exactly the value the
+    whole-prompt prefill gives it (a row depends only on its position)."""
+    case = wl.random_prefill_case(6, [0], [21], 2, 8, 4, "bf16")
+    kc, vc = _prefill_pools(case)
+    whole = _prefill(orp, case, kc, vc)
+    for cuts in ((5, 21), (1, 2, 21), (20, 21)):
+        r0 = 0
+        for r1 in cuts:
+            part = orp.paged_prefill(case.q[r0:r1], kc, vc, case.block_tables, np.array([r1], np.int32),
+                                     np.array([0, r1 - r0], np.int32), case.scale, case.dtype)
+            assert np.array_equal(part, whole[r0:r1]), cuts
+            r0 = r1
+
+
+def pin_prefill_closed_forms(orp):
+    """scale = 0: the row at position p is the mean of V rows 0 .. p (a
+    running mean); the first row of a whole prompt is V row 0 exactly."""
+    case = wl.random_prefill_case(7, [3, 0], [6, 5], 2, 8, 4, "f32")
+    kc, vc = _prefill_pools(case)
+    got = _prefill(orp, case, kc, vc, scale=0.0)
+    B = kc.shape[2]
+    vw = torch_widen(vc, "f32")
+    for s in range(case.num_seqs):
+        r0, r1 = int(case.query_start[s]), int(case.query_start[s + 1])
+        n, c = r1 - r0, int(case.context_lens[s])
+        rows = np.stack([vw[int(case.block_tables[s][t // B]), :, t % B, :] for t in range(c)])  # [c, H, D]
+        run_mean = np.cumsum(rows, axis=0) / np.arange(1, c + 1)[:, None, None]
+        assert np.abs(got[r0:r1] - run_mean[c - n:]).max() <= 1e-12
+    exact = _prefill(orp, case, kc, vc)
+    b0 = int(case.block_tables[1][0])
+    assert np.array_equal(exact[int(case.query_start[1])], vw[b0, :, 0, :])
+
+
+PREFILL_PINS = [
+    pin_prefill_bruteforce,
+    pin_prefill_library,
+    pin_prefill_single_query,
+    pin_prefill_chunking,
+    pin_prefill_closed_forms,
+]

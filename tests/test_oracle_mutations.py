@@ -142,3 +142,81 @@ def test_mutant_is_caught(name, monkeypatch):
         except Exception as e:  # a pin rejecting the mutant, by assertion or otherwise
             failures.append((pin.__name__, type(e).__name__))
     assert failures, f"no pin caught the planted mistake: {name}"
+
+
+# ---------------------------------------------------------------------------
+# Prefill oracle mutants (checked against oracle_pins.PREFILL_PINS)
+# ---------------------------------------------------------------------------
+
+import oracle.prefill as opr  # noqa: E402
+from oracle_pins import PREFILL_PINS  # noqa: E402
+
+_real_pf = {name: getattr(opr, name) for name in ("causal_rows", "paged_prefill")}
+
+
+def _rows_no_diagonal(Q, K, V, scale, first_pos):
+    """Each query attends to the keys strictly before it (its own key missing)."""
+    out = np.empty((Q.shape[0], Q.shape[1]))
+    for i in range(Q.shape[0]):
+        p = first_pos + i
+        m = max(p, 1)
+        out[i] = opa.attention(Q[i], K[:m], V[:m], scale)
+    return out
+
+
+def _rows_unmasked(Q, K, V, scale, first_pos):
+    """Every query attends to the whole context (no causal mask)."""
+    return np.stack([opa.attention(Q[i], K, V, scale) for i in range(Q.shape[0])])
+
+
+def _rows_top_left(Q, K, V, scale, first_pos):
+    """The chunk placed at the start of the context instead of its end."""
+    return _real_pf["causal_rows"](Q, K, V, scale, 0)
+
+
+def _rows_one_early(Q, K, V, scale, first_pos):
+    """The chunk placed one position early (each query misses its own key
+    once a prefix exists)."""
+    return _real_pf["causal_rows"](Q, K, V, scale, max(first_pos - 1, 0))
+
+
+def _prefill_fixed_stride(q, k_cache, v_cache, block_tables, context_lens, query_start, scale, dtype):
+    """Packed rows read as if every sequence's chunk had the longest length."""
+    qs = np.asarray(query_start)
+    n_max = int(np.diff(qs).max())
+    fake = np.minimum(np.arange(len(qs)) * n_max, qs[-1])
+    fake = np.maximum.accumulate(np.minimum(fake, qs[-1]))
+    fake[-1] = qs[-1]
+    return _real_pf["paged_prefill"](q, k_cache, v_cache, block_tables, context_lens, fake, scale, dtype)
+
+
+def _prefill_gqa_modulo(q, k_cache, v_cache, block_tables, context_lens, query_start, scale, dtype):
+    """Query head h reads K/V head h % Hk instead of h // G."""
+    H, Hk = q.shape[1], k_cache.shape[1]
+    perm = np.array([(h % Hk) * (H // Hk) + h // Hk for h in range(H)]) if H != Hk else np.arange(H)
+    out = _real_pf["paged_prefill"](q[:, perm], k_cache, v_cache, block_tables, context_lens, query_start, scale,
+                                    dtype)
+    return out[:, np.argsort(perm)]
+
+
+PREFILL_MUTANTS = {
+    "causal mask drops the diagonal": ("causal_rows", _rows_no_diagonal),
+    "no causal mask": ("causal_rows", _rows_unmasked),
+    "chunk aligned to the start of the context": ("causal_rows", _rows_top_left),
+    "chunk placed one position early": ("causal_rows", _rows_one_early),
+    "packed rows read with a fixed stride": ("paged_prefill", _prefill_fixed_stride),
+    "prefill heads grouped round-robin over K/V heads": ("paged_prefill", _prefill_gqa_modulo),
+}
+
+
+@pytest.mark.parametrize("name", list(PREFILL_MUTANTS))
+def test_prefill_mutant_is_caught(name, monkeypatch):
+    attr, fn = PREFILL_MUTANTS[name]
+    monkeypatch.setattr(opr, attr, fn)
+    failures = []
+    for pin in PREFILL_PINS:
+        try:
+            pin(opr)
+        except Exception as e:
+            failures.append((pin.__name__, type(e).__name__))
+    assert failures, f"no pin caught the planted mistake: {name}"

@@ -3,7 +3,8 @@ import pytest
 
 import oracle
 import oracle.paged_attention as opa
-from oracle_pins import ALL_PINS
+import oracle.prefill as opr
+from oracle_pins import ALL_PINS, PREFILL_PINS
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=[p.__name__ for p in ALL_PINS])
@@ -11,12 +12,17 @@ def test_oracle_pin(pin):
     pin(opa)
 
 
+@pytest.mark.parametrize("pin", PREFILL_PINS, ids=[p.__name__ for p in PREFILL_PINS])
+def test_prefill_oracle_pin(pin):
+    pin(opr)
+
+
 def test_oracle_imports_only_numpy():
     """The oracle shares no code with the GPU path: it imports numpy only."""
     import ast
     import inspect
 
-    for mod in (oracle, opa):
+    for mod in (oracle, opa, opr):
         tree = ast.parse(inspect.getsource(mod))
         names = set()
         for node in ast.walk(tree):

@@ -111,3 +111,34 @@ def test_random_case_ctx_zero_and_padding():
     c = wl.random_case(3, 3, 2, 8, 4, "f16", ctx=[0, 1, 9])
     assert (c.block_tables[0] == -1).all()
     _check_case(c)
+
+
+@pytest.mark.parametrize("kind", ["llama7b", "llama3-8b", "prompts"])
+def test_prefill_config_structure(kind):
+    case = wl.prefill_config(kind)
+    qs = case.query_start
+    n = np.diff(qs)
+    assert qs[0] == 0 and qs[-1] == case.num_tokens == case.q.shape[0]
+    assert (n >= 1).all() and (n <= case.context_lens).all()
+    st = case.steps[0]
+    assert st.slot_mapping.size == case.num_tokens
+    # The chunk's slots are the positions ctx - n .. ctx - 1 of each sequence, in order.
+    B = case.block_size
+    r = 0
+    for s in range(case.num_seqs):
+        c = int(case.context_lens[s])
+        for pos in range(c - int(n[s]), c):
+            slot = int(st.slot_mapping[r])
+            assert slot == int(case.block_tables[s, pos // B]) * B + pos % B
+            r += 1
+    if kind == "prompts":
+        assert (n == case.context_lens).all()  # whole prompts, nothing cached before
+    else:
+        assert (n == 512).all() and case.num_seqs == 16
+
+
+def test_random_prefill_case_is_seeded():
+    a = wl.random_prefill_case(9, [2, 0], [3, 4], 2, 8, 4, "bf16")
+    b = wl.random_prefill_case(9, [2, 0], [3, 4], 2, 8, 4, "bf16")
+    assert np.array_equal(a.q, b.q) and np.array_equal(a.block_tables, b.block_tables)
+    assert np.array_equal(a.k_cache.view(np.uint16), b.k_cache.view(np.uint16))

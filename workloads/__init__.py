@@ -8,6 +8,7 @@ from .blockpool import BlockPool, PoolExhausted, SeqBlocks, append_tokens, cow_l
 from .cases import (
     CONFIG_NAMES,
     GQA_NAMES,
+    PREFILL_NAMES,
     AppendStep,
     Case,
     CopyStep,
@@ -20,7 +21,9 @@ from .cases import (
     config5,
     gqa_config,
     normal_storage,
+    prefill_config,
     random_case,
+    random_prefill_case,
 )
 from .rng import normal_f32
 from .storage import CANARY_BITS, DTYPES, ELEM_BYTES, NP_BITS, NP_STORAGE, bits_view, canary_fill, f32_to_bf16_bits, to_storage

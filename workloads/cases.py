@@ -63,6 +63,10 @@ class Case:
     scale: float
     steps: List[Step] = field(default_factory=list)
     meta: dict = field(default_factory=dict)
+    # Prefill cases: int32 [S + 1]; sequence s owns query rows
+    # query_start[s] .. query_start[s + 1] - 1 of q (packed [T, H, D]).
+    # None for decode cases (one query row per sequence).
+    query_start: Optional[np.ndarray] = None
 
     @property
     def num_kv_heads(self) -> int:
@@ -70,7 +74,18 @@ class Case:
 
     @property
     def num_seqs(self) -> int:
+        return int(self.context_lens.shape[0])
+
+    @property
+    def num_tokens(self) -> int:
+        """Query rows: one per sequence for decode, the packed chunks for prefill."""
         return int(self.q.shape[0])
+
+    @property
+    def query_lens(self) -> np.ndarray:
+        if self.query_start is None:
+            return np.ones(self.num_seqs, dtype=np.int64)
+        return np.diff(self.query_start).astype(np.int64)
 
     @property
     def max_context_len(self) -> int:
@@ -160,6 +175,58 @@ def _paged_case(name, dtype, H, D, B, N, ctx, seed, perm, n_append: int, scale=N
         scale=(1.0 / math.sqrt(D)) if scale is None else scale,
         steps=steps,
         meta={"blocks_used": pool.used},
+    )
+
+
+def _prefill_case(name, dtype, H, D, B, N, prefix, chunk, seed, perm, Hk=None, scale=None) -> Case:
+    """Chunked prefill.  Sequence i already holds ``prefix[i]`` tokens in the
+    cache (earlier chunks of its prompt, or a cached shared prefix) and brings
+    ``chunk[i]`` new prompt tokens.  An append step writes the chunk's K/V
+    rows into the sequence's blocks (new blocks only when the current one is
+    full); the chunk's queries are packed into q [T, H, D], T = sum(chunk),
+    with ``query_start`` [S + 1] marking each sequence's rows.  After the
+    step the context length is prefix + chunk."""
+    Hk = H if Hk is None else Hk
+    prefix = [int(p) for p in prefix]
+    chunk = [int(c) for c in chunk]
+    assert len(prefix) == len(chunk) and min(chunk) >= 1 and min(prefix) >= 0
+    pool = BlockPool(N, B, perm)
+    seqs = [SeqBlocks() for _ in prefix]
+    for s, p in zip(seqs, prefix):
+        append_tokens(pool, s, p)
+    k_cache = canary_fill((N, Hk, B, D), dtype)
+    v_cache = canary_fill((N, Hk, B, D), dtype)
+    _fill_history(k_cache, seqs, prefix, seed, "k", dtype)
+    _fill_history(v_cache, seqs, prefix, seed, "v", dtype)
+    slots: List[int] = []
+    for s, n in zip(seqs, chunk):
+        sl, pairs = append_tokens(pool, s, n)
+        assert not pairs
+        slots.extend(sl)
+    T = len(slots)
+    step = AppendStep(
+        normal_storage(seed, "k_chunk", (T, Hk, D), dtype),
+        normal_storage(seed, "v_chunk", (T, Hk, D), dtype),
+        np.asarray(slots, dtype=np.int64),
+    )
+    qs = np.zeros(len(chunk) + 1, dtype=np.int32)
+    qs[1:] = np.cumsum(chunk)
+    return Case(
+        name=name,
+        dtype=dtype,
+        num_heads=H,
+        head_dim=D,
+        block_size=B,
+        num_blocks=N,
+        q=normal_storage(seed, "q_chunk", (T, H, D), dtype),
+        k_cache=k_cache,
+        v_cache=v_cache,
+        block_tables=tables_array(seqs),
+        context_lens=np.asarray([p + c for p, c in zip(prefix, chunk)], dtype=np.int32),
+        scale=(1.0 / math.sqrt(D)) if scale is None else scale,
+        steps=[step],
+        meta={"blocks_used": pool.used, "prefix": np.asarray(prefix), "chunk": np.asarray(chunk)},
+        query_start=qs,
     )
 
 
@@ -326,6 +393,59 @@ def gqa_config(kind: str = "llama3-8b", n_append: int = 0) -> Case:
         perm = rng.permutation(32768)
         return _paged_case("gqa-llama2-70b-tp8", "bf16", 8, 128, 16, 32768, ctx, seed, perm, n_append, Hk=1)
     raise ValueError(kind)
+
+
+PREFILL_NAMES = {
+    "llama7b": "llama7b-chunked-prefill: 16 seqs, 512-token chunks over cached prefixes U[0,1536], H=32, D=128, f16, B=16",
+    "llama3-8b": "llama3-8b-chunked-prefill: 16 seqs, 512-token chunks over cached prefixes U[0,1536], 32 query / 8 K/V heads, D=128, f16, B=16",
+    "prompts": "llama7b-prompt-prefill: 32 whole prompts, lognormal(300, 0.9) lengths clipped [16, 2048], H=32, D=128, bf16, B=16",
+}
+
+
+def prefill_config(kind: str = "llama7b") -> Case:
+    """Prefill workloads (the step before decode).
+
+    llama7b / llama3-8b: one chunked-prefill step.  Each of 16 sequences has
+    a cached prefix of U[0, 1536] tokens (earlier chunks) and brings a
+    512-token chunk; the LLaMA-7B-shaped layer (32 heads) and the
+    LLaMA-3-8B-shaped one (32 query over 8 K/V heads).
+    prompts: whole-prompt prefill of 32 prompts with the chat-like lognormal
+    length mix of config 3 (no cached prefix), bf16.
+    """
+    if kind in ("llama7b", "llama3-8b"):
+        seed = BASE_SEED + 8
+        rng = np.random.default_rng(seed)
+        prefix = rng.integers(0, 1537, 16)
+        perm = rng.permutation(4096)
+        Hk = 32 if kind == "llama7b" else 8
+        return _prefill_case(f"prefill-{kind}", "f16", 32, 128, 16, 4096, prefix, [512] * 16, seed, perm, Hk=Hk)
+    if kind == "prompts":
+        seed = BASE_SEED + 9
+        rng = np.random.default_rng(seed)
+        lens = np.clip(np.round(rng.lognormal(math.log(300.0), 0.9, 32)), 16, 2048).astype(np.int64)
+        perm = rng.permutation(4096)
+        return _prefill_case("prefill-prompts", "bf16", 32, 128, 16, 4096, [0] * 32, lens, seed, perm)
+    raise ValueError(kind)
+
+
+def random_prefill_case(
+    seed: int,
+    prefix: Sequence[int],
+    chunk: Sequence[int],
+    num_heads: int,
+    head_dim: int,
+    block_size: int,
+    dtype: str,
+    num_kv_heads: Optional[int] = None,
+    spare_blocks: int = 3,
+) -> Case:
+    """Small chunked-prefill case for parity tests (seeded, permuted pool)."""
+    rng = np.random.default_rng([BASE_SEED, 77, seed])
+    need = sum(-(-(int(p) + int(c)) // block_size) for p, c in zip(prefix, chunk))
+    N = need + spare_blocks
+    perm = rng.permutation(N)
+    return _prefill_case(f"prefill-random-{seed}", dtype, num_heads, head_dim, block_size, N, prefix, chunk,
+                         BASE_SEED * 1000 + seed, perm, Hk=num_kv_heads)
 
 
 def config(n: int, **kw) -> Case:
