@@ -9,6 +9,8 @@
  *   pa_copy_blocks        copy-on-write duplication of whole blocks
  *   pa_append_decode      pa_reshape_and_cache of each sequence's newest
  *                         token fused with pa_decode (one launch)
+ *   pa_prefill            causal attention of new prompt tokens (chunks)
+ *                         over the paged context
  *
  * Memory layout (every array dense, row-major, no padding):
  *   query, out          [num_seqs, num_heads, head_dim]              element type `dtype`
@@ -222,6 +224,52 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
 int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pairs, int32_t num_pairs,
                    int32_t num_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
                    int32_t dtype, void* stream);
+
+/*
+ * pa_prefill - causal attention of new prompt tokens over the paged context
+ * (whole-prompt and chunked prefill).
+ *
+ * Page "vLLM PagedAttention and continuous batching architecture"
+ * (tech.blogsailing.com), sections 3 and 5, and page "KV cache and
+ * PagedAttention: LLM inference speed and GPU throughput" (allinfo.ai.kr),
+ * key insights: newly arrived prompts are prefilled against the paged KV
+ * cache, with chunked prefill in fixed-size chunks after the prompt's
+ * earlier chunks (or a cached shared prefix).  Each sequence s brings a
+ * chunk of n_s query rows whose K/V rows are already stored (e.g. by
+ * pa_reshape_and_cache) at positions ctx_s - n_s .. ctx_s - 1 of its
+ * context.  Row i of the chunk attends causally to positions
+ * 0 .. ctx_s - n_s + i:
+ *
+ *   out[r, h, :] = sum_t softmax_t( scale * <query[r,h,:], K_s[t, h/G, :]> ) * V_s[t, h/G, :]
+ *
+ * with r = query_start[s] + i, t over 0 .. ctx_s - n_s + i, and token t at
+ * block block_tables[s][t / B], offset t % B.  G = num_heads / num_kv_heads
+ * (any divisor).  Arithmetic as pa_decode: q.k products and p.v products of
+ * the stored 16-bit values accumulated in fp32, out rounded to `dtype`
+ * (nearest-even).
+ *
+ *   out, query     [num_tokens, num_heads, head_dim], packed by sequence
+ *   query_start    int32 [num_seqs + 1], device: rising from 0 to num_tokens;
+ *                  sequence s owns rows query_start[s] .. query_start[s+1]-1
+ *   context_lens   int32 [num_seqs], device: ctx_s, the chunk included
+ *   k_cache, v_cache  [num_blocks, num_kv_heads, block_size, head_dim] read
+ *   block_tables   int32 [num_seqs, max_blocks_per_seq]
+ *   max_query_len  host upper bound of every n_s (sizes the grid)
+ *   max_context_len  host upper bound of every ctx_s; <= max_blocks_per_seq *
+ *                  block_size and ceil(max_context_len / block_size) <= 4096
+ *
+ * Built for dtype PA_F16 and PA_BF16 with head_dim 64 or 128 (others:
+ * PA_ERR_UNSUPPORTED).  query, out and the caches 16-byte aligned.  Ownership,
+ * streams and host-side errors as for pa_decode.  Device-side guards: a
+ * sequence with n_s <= 0 is skipped; n_s > ctx_s or ctx_s > max_context_len
+ * gives NaN rows; a needed block id outside [0, num_blocks) gives NaN for
+ * the rows of that (64-row tile, head) without reading outside the caches.
+ */
+int pa_prefill(void* out, const void* query, const void* k_cache, const void* v_cache,
+               const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start,
+               int32_t num_seqs, int32_t num_tokens, int32_t num_heads, int32_t num_kv_heads,
+               int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int32_t max_query_len,
+               int32_t max_context_len, int64_t num_blocks, float scale, int32_t dtype, void* stream);
 
 /* Human-readable name of a pa_status value (static storage; never NULL). */
 const char* pa_status_string(int status);

@@ -1,4 +1,4 @@
-"""Paged decode attention for AMD Instinct MI355X (gfx950).
+"""Paged decode and prefill attention for AMD Instinct MI355X (gfx950).
 
 Thin ctypes binding over ``libpa.so`` (C ABI declared in ``include/pa.h``).
 The functions here only check tensor shapes and types, turn torch tensors
@@ -28,6 +28,7 @@ __all__ = [
     "copy_blocks",
     "status_string",
     "partition_tokens",
+    "prefill",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
@@ -61,6 +62,9 @@ lib.pa_reshape_and_cache.restype = ctypes.c_int
 lib.pa_reshape_and_cache.argtypes = [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i64, _i32, _p]
 lib.pa_copy_blocks.restype = ctypes.c_int
 lib.pa_copy_blocks.argtypes = [_p, _p, _p, _i32, _i32, _i32, _i32, _i64, _i32, _p]
+lib.pa_prefill.restype = ctypes.c_int
+lib.pa_prefill.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                           _i64, ctypes.c_float, _i32, _p]
 
 _DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 SHARED_BLOCKS = 1  # PA_DECODE_SHARED_BLOCKS
@@ -236,3 +240,40 @@ def copy_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor, block_pairs:
         H, D, B, N, _code(dt), _stream_handle(key_cache.device, stream),
     )
     _check(st, "pa_copy_blocks")
+
+
+def prefill(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+            block_tables: torch.Tensor, context_lens: torch.Tensor, query_start: torch.Tensor, scale: float,
+            max_query_len: int, max_context_len: int, stream=None) -> torch.Tensor:
+    """Causal attention of packed query chunks over the paged context (``pa_prefill``).
+
+    out, query [T, H, D] (f16/bf16, D in {64, 128}); key_cache, value_cache
+    [N, Hk, B, D] with the chunks' K/V already written; block_tables int32
+    [S, W]; context_lens int32 [S] (chunks included); query_start int32
+    [S + 1] (sequence s owns query rows query_start[s] .. query_start[s+1]-1,
+    at positions ctx - n .. ctx - 1); host bounds ``max_query_len`` and
+    ``max_context_len``.  Writes and returns ``out``.
+    """
+    _dev(query, "query", ndim=3)
+    dt = query.dtype
+    _dev(out, "out", dt, 3)
+    _dev(key_cache, "key_cache", dt, 4)
+    _dev(value_cache, "value_cache", dt, 4)
+    _dev(block_tables, "block_tables", torch.int32, 2)
+    _dev(context_lens, "context_lens", torch.int32, 1)
+    _dev(query_start, "query_start", torch.int32, 1)
+    T, H, D = query.shape
+    N, Hk, B, Dk = key_cache.shape
+    S = context_lens.shape[0]
+    if tuple(out.shape) != (T, H, D) or tuple(value_cache.shape) != tuple(key_cache.shape):
+        raise ValueError("out/value_cache shapes do not match query/key_cache")
+    if Dk != D or H % Hk:
+        raise ValueError(f"key_cache heads/head_dim {Hk}/{Dk} do not fit query {H}/{D}")
+    if block_tables.shape[0] != S or query_start.shape[0] != S + 1:
+        raise ValueError("block_tables needs one row and query_start S + 1 entries for S sequences")
+    st = lib.pa_prefill(out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+                        block_tables.data_ptr(), context_lens.data_ptr(), query_start.data_ptr(), S, T, H, Hk, D,
+                        B, block_tables.shape[1], int(max_query_len), int(max_context_len), N, float(scale),
+                        _code(dt), _stream_handle(query.device, stream))
+    _check(st, "pa_prefill")
+    return out

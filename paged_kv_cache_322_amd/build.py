@@ -22,8 +22,8 @@ LIB = os.path.join(HERE, "libpa.so")
 OBJDIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["pa_decode.hip", "pa_decode_f32.hip", "pa_decode_f16.hip", "pa_decode_bf16.hip", "pa_cache.hip",
-           "pa_api.hip"]
+SOURCES = ["pa_decode.hip", "pa_decode_f32.hip", "pa_decode_f16.hip", "pa_decode_bf16.hip", "pa_prefill.hip",
+           "pa_cache.hip", "pa_api.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",

@@ -206,3 +206,54 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pairs, int
 }
 
 }  // extern "C"
+
+extern "C" int pa_prefill(void* out, const void* query, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start,
+                          int32_t num_seqs, int32_t num_tokens, int32_t num_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int32_t max_query_len,
+                          int32_t max_context_len, int64_t num_blocks, float scale, int32_t dtype, void* stream) {
+    if ((dtype != PA_F16 && dtype != PA_BF16) || (head_dim != 64 && head_dim != 128) ||
+        !supported_block_size(block_size))
+        return PA_ERR_UNSUPPORTED;
+    if (num_seqs == 0 || num_tokens == 0) return PA_OK;  // nothing to compute
+    if (!out || !query || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
+        return PA_ERR_NULL;
+    if (num_seqs < 0 || num_seqs > 65535 || num_tokens < 0 || num_heads <= 0 || num_heads > 65535 ||
+        num_kv_heads <= 0 || max_blocks_per_seq <= 0 || max_query_len < 0 || max_context_len < 0 ||
+        num_blocks <= 0)
+        return PA_ERR_INVALID;
+    if (num_heads % num_kv_heads) return PA_ERR_INVALID;
+    if (max_query_len > max_context_len) return PA_ERR_INVALID;
+    if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
+        return PA_ERR_INVALID;
+    if (!isfinite(scale)) return PA_ERR_INVALID;
+    if (static_cast<int64_t>(num_kv_heads) * block_size * head_dim > 0x7FFFFFFF) return PA_ERR_INVALID;
+    if (!aligned16(out) || !aligned16(query) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_INVALID;
+    const int64_t ids = (static_cast<int64_t>(max_context_len) + block_size - 1) / block_size;
+    if (ids > pa::kMaxPrefillIds) return PA_ERR_INVALID;
+    if (max_query_len == 0) return PA_OK;
+    if ((static_cast<int64_t>(max_query_len) + 63) / 64 > 65535) return PA_ERR_INVALID;
+
+    pa::PrefillArgs a;
+    a.out = out;
+    a.query = query;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.query_start = query_start;
+    a.num_seqs = num_seqs;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.head_dim = head_dim;
+    a.block_size = block_size;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.max_query_len = max_query_len;
+    a.max_context_len = max_context_len;
+    a.num_blocks = num_blocks;
+    a.scale = scale;
+    a.dtype = dtype;
+    a.staged_ids = static_cast<int>(ids < 1 ? 1 : ids);
+    a.stream = static_cast<hipStream_t>(stream);
+    return hip_status(pa::launch_prefill(a));
+}

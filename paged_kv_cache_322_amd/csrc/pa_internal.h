@@ -114,6 +114,29 @@ hipError_t launch_decode_bf16(const DecodeArgs& a);
 // Query heads per K/V head with built kernels.
 inline bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
 
+// Prefill (pa_prefill): causal attention of packed query chunks over the
+// paged context.  16-bit caches, head_dim 64 or 128.
+constexpr int kMaxPrefillIds = 4096;  // block ids of one context staged in LDS (16 KB)
+
+struct PrefillArgs {
+    void* out;
+    const void* query;
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* block_tables;
+    const int32_t* context_lens;
+    const int32_t* query_start;
+    int num_seqs, num_heads, num_kv_heads, head_dim, block_size;
+    int max_blocks_per_seq, max_query_len, max_context_len;
+    int64_t num_blocks;
+    float scale;
+    int dtype;
+    int staged_ids;  // LDS entries for a context's block ids
+    hipStream_t stream;
+};
+
+hipError_t launch_prefill(const PrefillArgs& a);
+
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
                                     const int64_t* slot_mapping, int num_tokens, int num_heads,
                                     int row_bytes, int block_size, int64_t num_blocks,

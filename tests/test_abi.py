@@ -189,3 +189,38 @@ def test_append_decode_host_checks():
     assert ad(key=P + 2) == INVALID
     assert ad(dtype=5) == UNSUP
     assert ad(maxc=100, part=16) == NULL  # split needs a workspace
+
+
+def pf(**kw):
+    a = dict(out=P, query=P, k=P, v=P, bt=P, ctx=P, qs=P, S=2, T=10, H=4, Hk=None, D=128, B=16, W=8, mq=8,
+             maxc=100, N=64, scale=0.1, dtype=1)
+    a.update(kw)
+    hk = a["H"] if a["Hk"] is None else a["Hk"]
+    return pa.lib.pa_prefill(a["out"], a["query"], a["k"], a["v"], a["bt"], a["ctx"], a["qs"], a["S"], a["T"],
+                             a["H"], hk, a["D"], a["B"], a["W"], a["mq"], a["maxc"], a["N"], a["scale"],
+                             a["dtype"], None)
+
+
+def test_prefill_host_checks():
+    # Every call here fails validation or is an empty no-op: none launches.
+    assert pf(S=0, out=0) == OK
+    assert pf(T=0, out=0) == OK
+    assert pf(mq=0) == OK  # no query rows anywhere
+    assert pf(dtype=0) == UNSUP  # fp32 prefill not built
+    assert pf(dtype=3) == UNSUP
+    assert pf(D=256) == UNSUP
+    assert pf(D=32) == UNSUP
+    assert pf(B=12) == UNSUP
+    assert pf(out=0) == NULL
+    assert pf(qs=0) == NULL
+    assert pf(ctx=0) == NULL
+    assert pf(H=0) == INVALID
+    assert pf(H=8, Hk=3) == INVALID
+    assert pf(H=4, Hk=0) == INVALID
+    assert pf(mq=101) == INVALID  # a chunk longer than any context
+    assert pf(maxc=8 * 16 + 1) == INVALID
+    assert pf(B=1, W=5000, maxc=4097, mq=8) == INVALID  # more block ids than LDS staging holds
+    assert pf(scale=math.nan) == INVALID
+    assert pf(query=P + 8) == INVALID
+    assert pf(S=70000) == INVALID
+    assert pf(T=-1) == INVALID

@@ -1,0 +1,193 @@
+"""Paged prefill (pa_prefill) on the GPU against the float64 oracle.
+
+Chunked-prefill batches shaped like a LLaMA-7B layer and a LLaMA-3-8B
+(grouped-query) layer, a whole-prompt bf16 batch with the chat-like length
+mix, a sweep of ragged shapes (chunks of 1 row, chunks crossing 64-row tiles,
+whole prompts, block sizes 1..256, groups 1..8), and the invariants:
+chunked == whole-prompt rows, single-row chunks == pa_decode, guards.
+The oracle runs on sampled sequences for the large batches.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from gpu_helpers import assert_close, log, pa, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+class PrefillRun:
+    """A prefill case resident on the GPU, its chunk written by reshape_and_cache."""
+
+    def __init__(self, case: wl.Case):
+        self.case = case
+        d = case.dtype
+        self.q = to_gpu(case.q, d)
+        self.kc = to_gpu(case.k_cache, d)
+        self.vc = to_gpu(case.v_cache, d)
+        self.bt = to_gpu(case.block_tables)
+        self.ctx = to_gpu(case.context_lens)
+        self.qs = to_gpu(case.query_start)
+        st = case.steps[0]
+        pa().reshape_and_cache(to_gpu(st.key, d), to_gpu(st.value, d), self.kc, self.vc, to_gpu(st.slot_mapping))
+        self.out = torch.full_like(self.q, float("nan"))
+
+    def run(self, max_query_len=None):
+        c = self.case
+        mq = int(np.diff(c.query_start).max()) if max_query_len is None else max_query_len
+        pa().prefill(self.out, self.q, self.kc, self.vc, self.bt, self.ctx, self.qs, c.scale, mq, c.max_context_len)
+        torch.cuda.synchronize()
+        return self.out
+
+
+def oracle_pools(case):
+    st = case.steps[0]
+    return oracle.reshape_and_cache(st.key, st.value, case.k_cache, case.v_cache, st.slot_mapping)
+
+
+def oracle_rows(case, kc, vc, seqs):
+    """Oracle output for the given sequences only, and their packed row indices."""
+    seqs = list(seqs)
+    qs = case.query_start
+    rows = np.concatenate([np.arange(qs[s], qs[s + 1]) for s in seqs])
+    sub_qs = np.zeros(len(seqs) + 1, dtype=np.int64)
+    sub_qs[1:] = np.cumsum([qs[s + 1] - qs[s] for s in seqs])
+    ref = oracle.paged_prefill(case.q[rows], kc, vc, case.block_tables[seqs], case.context_lens[seqs], sub_qs,
+                               case.scale, case.dtype)
+    return ref, rows
+
+
+def check(case, seqs=None, strict=True, max_query_len=None):
+    run = PrefillRun(case)
+    log(f"{case.name}: prefill over {case.num_tokens} rows")
+    out = run.run(max_query_len)
+    kc, vc = oracle_pools(case)
+    seqs = range(case.num_seqs) if seqs is None else seqs
+    ref, rows = oracle_rows(case, kc, vc, seqs)
+    got = out[torch.from_numpy(rows).cuda()]
+    assert_close(got, ref, case.dtype, f"{case.name} prefill", strict=strict)
+    return run
+
+
+def _sample(case, k=3):
+    lens = case.context_lens
+    order = np.argsort(lens, kind="stable")
+    return sorted({int(order[0]), int(order[len(order) // 2]), int(order[-1])})
+
+
+def test_prefill_llama7b_chunked():
+    case = wl.prefill_config("llama7b")
+    check(case, seqs=_sample(case))
+
+
+def test_prefill_llama3_8b_gqa_chunked():
+    case = wl.prefill_config("llama3-8b")
+    check(case, seqs=_sample(case))
+
+
+def test_prefill_whole_prompts_bf16():
+    # A whole prompt's first rows attend to a handful of tokens, so |out|
+    # reaches ~3 there, where bf16's half-ulp (2^-7 on [2, 4)) exceeds 2e-3:
+    # the bound is 2e-3 or one output ulp, as for the short decode contexts.
+    case = wl.prefill_config("prompts")
+    check(case, seqs=_sample(case), strict=False)
+
+
+SWEEP = [
+    # dtype, H, Hk, D, B, prefix, chunk
+    ("f16", 4, 4, 128, 16, [0, 17, 100], [64, 1, 33]),
+    ("bf16", 8, 2, 64, 8, [0, 5], [130, 70]),
+    ("f16", 4, 1, 64, 1, [3, 0, 40], [1, 200, 9]),
+    ("bf16", 2, 2, 128, 32, [31, 32, 33], [1, 32, 65]),
+    ("f16", 6, 3, 128, 4, [0], [257]),
+    ("bf16", 8, 8, 64, 256, [300, 0], [20, 300]),
+    ("f16", 16, 2, 128, 16, [1000, 0, 7], [63, 129, 1]),
+]
+
+
+@pytest.mark.parametrize("dtype,H,Hk,D,B,prefix,chunk", SWEEP,
+                         ids=[f"{s[0]}-H{s[1]}-Hk{s[2]}-D{s[3]}-B{s[4]}" for s in SWEEP])
+def test_prefill_sweep(dtype, H, Hk, D, B, prefix, chunk):
+    case = wl.random_prefill_case(len(prefix) * 7 + D + B, prefix, chunk, H, D, B, dtype, num_kv_heads=Hk)
+    # Short contexts give |out| near 1-3: 2e-3 or one output ulp, as for decode.
+    check(case, strict=False)
+    # A generous max_query_len (up to the context bound the ABI allows) only
+    # adds workgroups that exit.
+    mq = min(int(max(chunk)) + 130, case.max_context_len)
+    if mq > max(chunk):
+        check(case, strict=False, max_query_len=mq)
+
+
+def test_prefill_chunks_match_whole_prompt():
+    """Prefilling a prompt in three chunks gives the rows the whole-prompt
+    prefill gives (within one output ulp)."""
+    whole = wl.random_prefill_case(41, [0], [300], 8, 128, 16, "f16", num_kv_heads=2)
+    run = PrefillRun(whole)
+    ref = run.run().clone()
+    q = run.q
+    for r0, r1 in ((0, 100), (100, 101), (101, 300)):
+        ctx = torch.tensor([r1], dtype=torch.int32, device="cuda")
+        qs = torch.tensor([0, r1 - r0], dtype=torch.int32, device="cuda")
+        out = torch.empty_like(q[r0:r1])
+        pa().prefill(out, q[r0:r1].contiguous(), run.kc, run.vc, run.bt, ctx, qs, whole.scale, r1 - r0, 300)
+        torch.cuda.synchronize()
+        diff = (out.float() - ref[r0:r1].float()).abs().max().item()
+        log(f"chunk rows {r0}..{r1 - 1}: max |chunk - whole| = {diff:.3e}")
+        assert diff <= 2e-3, diff
+
+
+def test_prefill_single_rows_match_decode():
+    """Chunks of one row are decode queries: pa_prefill and pa_decode agree."""
+    case = wl.random_prefill_case(42, [5, 200, 0, 1023], [1, 1, 1, 1], 8, 128, 16, "bf16", num_kv_heads=4)
+    run = PrefillRun(case)
+    out = run.run()
+    dec = torch.empty_like(out)
+    pa().decode(dec, run.q, run.kc, run.vc, run.bt, run.ctx, case.scale, case.max_context_len)
+    torch.cuda.synchronize()
+    diff = (out.float() - dec.float()).abs().max().item()
+    log(f"single-row prefill vs decode: max diff {diff:.3e}")
+    kc, vc = oracle_pools(case)
+    ref, _ = oracle_rows(case, kc, vc, range(case.num_seqs))
+    assert_close(out, ref, case.dtype, "single-row prefill", strict=False)
+    assert diff <= 2e-3 * 2
+
+
+def test_prefill_guards():
+    """ctx < n gives NaN rows for that sequence only; an out-of-pool block id
+    gives NaN for the rows of the tile that needs it; an empty chunk writes
+    nothing.  Nothing faults."""
+    case = wl.random_prefill_case(43, [10, 0, 4], [5, 70, 3], 4, 64, 8, "f16")
+    run = PrefillRun(case)
+    kc, vc = oracle_pools(case)
+    # Sequence 0: claim ctx 4 < n 5.
+    ctx = case.context_lens.copy()
+    ctx[0] = 4
+    run.ctx = to_gpu(ctx)
+    out = run.run()
+    qs = case.query_start
+    assert torch.isnan(out[qs[0]:qs[1]].float()).all()
+    ref, rows = oracle_rows(case, kc, vc, [1, 2])
+    assert_close(out[torch.from_numpy(rows).cuda()], ref, case.dtype, "guard: other sequences", strict=False)
+    # Sequence 1: an out-of-pool id in its last block.
+    run.ctx = to_gpu(case.context_lens)
+    bt = case.block_tables.copy()
+    nb = -(-int(case.context_lens[1]) // case.block_size)
+    bt[1, nb - 1] = case.num_blocks + 5
+    run.bt = to_gpu(bt)
+    run.out.fill_(0)
+    out = run.run()
+    rows1 = out[qs[1]:qs[2]].float()
+    assert torch.isnan(rows1[-1]).all()  # the last row needs the last block
+    ref, rows = oracle_rows(case, kc, vc, [0, 2])
+    assert_close(out[torch.from_numpy(rows).cuda()], ref, case.dtype, "guard: bad id elsewhere", strict=False)
+    # An empty chunk: sequence 2 with no rows leaves the output untouched.
+    qs2 = case.query_start.copy()
+    qs2[3] = qs2[2]
+    run.bt = to_gpu(case.block_tables)
+    run.qs = to_gpu(qs2)
+    run.out.fill_(7.0)
+    pa().prefill(run.out, run.q, run.kc, run.vc, run.bt, run.ctx, run.qs, case.scale, 70, case.max_context_len)
+    torch.cuda.synchronize()
+    assert (run.out[qs[2]:qs[3]].float() == 7.0).all()

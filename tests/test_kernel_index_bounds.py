@@ -226,3 +226,92 @@ def test_mfma_bounds_all_shapes(D, G):
     case = wl.random_case(23, 3, 2 * G, D, 8, "f16", ctx=[1, 37, 300], num_kv_heads=2)
     check_mfma_bounds(3, 2, G, D, 8, case.num_blocks, case.block_tables.shape[1], case.context_lens,
                       case.block_tables, case.max_context_len, 64)
+
+
+# ---------------------------------------------------------------------------
+# Prefill kernel (csrc/pa_prefill.hip)
+# ---------------------------------------------------------------------------
+
+PF_ROWS, PF_KEYS, PF_THREADS, PF_MAX_IDS = 64, 32, 256, 4096
+
+
+def check_prefill_bounds(case, max_query_len=None):
+    """Grid (H, S, ceil(max_query_len / 64)); wavefront w of a workgroup owns
+    chunk rows r0 + 16 w + c; query loads read row min(row, n - 1), channels
+    32 ks + 8 g .. +7; block ids of keys 0 .. kv_end - 1 are staged; tile
+    loads read key kp < kv_end at chunk 8 cc of its row; LDS reads stay in
+    the [2][32][D + 8] tiles; output rows < n, channels D/4 g .. +D/4."""
+    T, H, D = case.q.shape
+    N, Hk, B, _ = case.k_cache.shape
+    S = case.num_seqs
+    W = case.block_tables.shape[1]
+    qs = case.query_start
+    n_all = np.diff(qs)
+    mq = int(n_all.max()) if max_query_len is None else max_query_len
+    assert mq >= n_all.max()
+    maxc = case.max_context_len
+    ids_cap = -(-maxc // B)
+    assert ids_cap <= PF_MAX_IDS and maxc <= W * B
+    n_qt = -(-mq // PF_ROWS)
+    KS, E, CPR = D // 32, D // 16, D // 8
+    assert (PF_KEYS * CPR) % PF_THREADS == 0
+    cpt = PF_KEYS * CPR // PF_THREADS
+    G = H // Hk
+    c = np.arange(16)
+    g = np.arange(4)
+    # Channel extents inside a row.
+    assert (32 * (KS - 1) + 8 * g.max() + 8) <= D and E * c.max() + E <= D
+    cache_elems = N * Hk * B * D
+    for s in range(S):
+        n, ctx = int(n_all[s]), int(case.context_lens[s])
+        assert 1 <= n <= ctx <= maxc
+        for qt in range(n_qt):
+            r0 = qt * PF_ROWS
+            if r0 >= n:
+                continue
+            first = ctx - n
+            last_row = min(r0 + PF_ROWS, n) - 1
+            kv_end = first + last_row + 1
+            assert kv_end <= ctx
+            nids = ((kv_end - 1) // B) + 1
+            assert nids <= ids_cap and nids <= W
+            ntiles = -(-kv_end // PF_KEYS)
+            # query rows read
+            rows = np.minimum(r0 + np.arange(PF_ROWS), n - 1)
+            assert int(qs[s]) + rows.max() < T
+            # tile loads
+            tid = np.arange(PF_THREADS)
+            for kt in range(ntiles):
+                for u in range(cpt):
+                    ci = tid + u * PF_THREADS
+                    kk, cc = ci // CPR, ci % CPR
+                    assert kk.max() < PF_KEYS
+                    kp = kt * PF_KEYS + kk
+                    live = kp < kv_end
+                    idx = kp[live] // B
+                    assert idx.size == 0 or idx.max() < nids
+                    b = case.block_tables[s, idx]
+                    b = np.where((b >= 0) & (b < N), b, 0).astype(np.int64)
+                    e = b * Hk * B * D + (Hk - 1) * B * D + (kp[live] % B) * D + 8 * cc[live]
+                    assert e.size == 0 or (e.min() >= 0 and e.max() + 8 <= cache_elems)
+            # LDS rows read by the compute: keys 16 sub + c and 16 sub + 4 g + j < 32
+            assert 16 + 15 < PF_KEYS and 16 + 4 * 3 + 3 < PF_KEYS
+        # output rows
+        assert int(qs[s]) + n - 1 < T
+    assert (H - 1) // G < Hk
+
+
+PF_CASES = [
+    ("prefill-llama7b", functools.lru_cache(None)(lambda: wl.prefill_config("llama7b"))),
+    ("prefill-llama3-8b", functools.lru_cache(None)(lambda: wl.prefill_config("llama3-8b"))),
+    ("prefill-prompts", functools.lru_cache(None)(lambda: wl.prefill_config("prompts"))),
+    ("prefill-ragged", functools.lru_cache(None)(
+        lambda: wl.random_prefill_case(31, [0, 1, 63, 200, 5], [1, 64, 65, 130, 3], 4, 64, 1, "bf16", num_kv_heads=2))),
+]
+
+
+@pytest.mark.parametrize("name,make", PF_CASES, ids=[c[0] for c in PF_CASES])
+def test_prefill_index_bounds(name, make):
+    case = make()
+    check_prefill_bounds(case)
+    check_prefill_bounds(case, max_query_len=int(np.diff(case.query_start).max()) + 100)
