@@ -44,7 +44,16 @@ WORKLOADS = {
     "5": "opt175b-decode-layer: 128 seqs, ctx U[1024,2048], H=96, D=128, bf16, B=16, 16384-block pool",
     "gqa8b": "llama3-8b-gqa-decode-layer: 64 seqs, ctx U[128,2048], 32 query / 8 K/V heads, D=128, f16, B=16",
     "gqa70b": "llama2-70b-gqa-tp8-share: 128 seqs, ctx U[512,4096], 8 query / 1 K/V head, D=128, bf16, B=16",
+    "prefill-llama7b": "llama7b-chunked-prefill: 16 seqs x 512-token chunks over cached prefixes U[0,1536], H=32, "
+                       "D=128, f16, B=16",
+    "prefill-gqa8b": "llama3-8b-chunked-prefill: 16 seqs x 512-token chunks over cached prefixes U[0,1536], "
+                     "32 query / 8 K/V heads, D=128, f16, B=16",
+    "prefill-prompts": "llama7b-prompt-prefill: 32 whole prompts, lognormal(median 300, sigma 0.9) lengths in "
+                       "[16,2048], H=32, D=128, bf16, B=16",
 }
+PREFILL_KINDS = {"prefill-llama7b": "llama7b", "prefill-gqa8b": "llama3-8b", "prefill-prompts": "prompts"}
+MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak, vendor figure
+PREFILL_METRIC = "paged prefill attention: TFLOP/s and % of MFMA peak"
 
 
 def parse():
@@ -81,6 +90,8 @@ def make_case(cfg, block_size=16):
         return wl.gqa_config("llama3-8b", n_append=1)
     if cfg == "gqa70b":
         return wl.gqa_config("llama2-70b-tp8", n_append=1)
+    if cfg in PREFILL_KINDS:
+        return wl.prefill_config(PREFILL_KINDS[cfg])
     return wl.config5(n_append=1)
 
 
@@ -116,7 +127,10 @@ def unique_kv_bytes(case):
 
 # Committed HBM counter summaries (rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled
 # by a copy kernel of known size), per workload at its default plan.
-COUNTER_FILES = {"2": "decode_llama7b_counters.txt", "gqa8b": "decode_gqa_llama3_8b_counters.txt"}
+COUNTER_FILES = {"2": "decode_llama7b_counters.txt", "gqa8b": "decode_gqa_llama3_8b_counters.txt",
+                 "prefill-llama7b": "prefill_llama7b_counters.txt"}
+DECODE_SOURCES = ("pa_decode_impl.h", "pa_decode_mfma.h", "pa_device.h", "pa_internal.h")
+PREFILL_SOURCES = ("pa_prefill.hip", "pa_decode_mfma.h", "pa_device.h", "pa_internal.h")
 
 
 def traffic_from_profiles(config, kernel_src_sha):
@@ -150,12 +164,12 @@ def decode_kernel_name(case):
     return "decode_partition_kernel"
 
 
-def kernel_source_sha():
+def kernel_source_sha(sources=DECODE_SOURCES):
     import hashlib
 
     root = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_cache_322_amd", "csrc")
     h = hashlib.sha256()
-    for name in ("pa_decode_impl.h", "pa_decode_mfma.h", "pa_device.h", "pa_internal.h"):
+    for name in sources:
         h.update(open(os.path.join(root, name), "rb").read())
     return h.hexdigest()
 
@@ -243,6 +257,8 @@ def main():
     dev = torch.device("cuda:0")
     log(f"building workload config {args.config}")
     case = make_case(args.config, args.block_size)
+    if args.config in PREFILL_KINDS:
+        return bench_prefill(args, case, pa, torch, dev)
     import workloads as wl
 
     # Config 4's prompt write, fork copies and suffix writes are set-up; the
@@ -437,6 +453,174 @@ def main():
                     kc, vc = oracle.copy_blocks(kc, vc, st.pairs)
             setup_pools = (kc, vc)
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds, timed_steps, setup_pools)
+    print(json.dumps(result), flush=True)
+
+
+def prefill_flops(case, seqs=None):
+    """Algorithmic flops of one prefill call: for every query row at position
+    p and every head, 2*D for q.k and 2*D for p.v over the p + 1 keys it
+    attends to."""
+    n = case.query_lens
+    ctx = case.context_lens.astype(np.int64)
+    idx = range(case.num_seqs) if seqs is None else seqs
+    pairs = 0
+    for s in idx:
+        first = int(ctx[s] - n[s])
+        pairs += int(n[s]) * (first + 1) + int(n[s]) * (int(n[s]) - 1) // 2
+    return 4 * case.head_dim * case.num_heads * pairs
+
+
+def cpu_baseline_prefill(case, target_s):
+    """The float64 oracle on the host for the first k sequences of the batch:
+    oracle.reshape_and_cache of their chunk rows, then oracle.paged_prefill,
+    with k sized so one run takes about a third of ``target_s``.  Reported as
+    TFLOP/s over the same algorithmic flops the GPU figure uses."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    st = case.steps[0]
+    qs = case.query_start
+
+    def run(k):
+        t0 = time.perf_counter()
+        r1 = int(qs[k])
+        kc, vc = oracle.reshape_and_cache(st.key[:r1], st.value[:r1], case.k_cache, case.v_cache,
+                                          st.slot_mapping[:r1])
+        oracle.paged_prefill(case.q[:r1], kc, vc, case.block_tables[:k], case.context_lens[:k], qs[: k + 1],
+                             case.scale, case.dtype)
+        return time.perf_counter() - t0
+
+    t1 = run(1)
+    per_flop = t1 / max(1, prefill_flops(case, [0]))
+    k = 1
+    while k < case.num_seqs and per_flop * prefill_flops(case, range(k + 1)) <= target_s / 3:
+        k += 1
+    best, total, reps = math.inf, 0.0, 0
+    while reps < 5 and (reps < 2 or total < target_s):
+        dt = run(k)
+        best, total, reps = min(best, dt), total + dt, reps + 1
+    flops = prefill_flops(case, range(k))
+    return {
+        "value": round(flops / best / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": f"first {k} of {case.num_seqs} sequences (chunk append + prefill), best of {reps} runs "
+                  f"({best:.2f} s each; float64 numpy, BLAS threads {blas_threads}; host has "
+                  f"{len(os.sched_getaffinity(0))} cpus)",
+        "seconds_per_run": round(best, 4),
+        "sample_flops": int(flops),
+    }
+
+
+def bench_prefill(args, case, pa, torch, dev):
+    """One step = pa_reshape_and_cache of every sequence's chunk K/V, then
+    pa_prefill of the chunk queries over the paged context."""
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if case.dtype == "bf16" and a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    S, H, D, B = case.num_seqs, case.num_heads, case.head_dim, case.block_size
+    st = case.steps[0]
+    q, bt, ctx, qs = up(case.q), up(case.block_tables), up(case.context_lens), up(case.query_start)
+    kn, vn, slots = up(st.key), up(st.value), up(st.slot_mapping)
+    pools = [(up(case.k_cache), up(case.v_cache)) for _ in range(max(1, args.rotate))]
+    out = torch.empty_like(q)
+    mq, mc = int(case.query_lens.max()), case.max_context_len
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        kc, vc = pools[i % len(pools)]
+        if ev is not None:
+            ev[0].record()
+        pa.reshape_and_cache(kn, vn, kc, vc, slots)
+        if ev is not None:
+            ev[1].record()
+        pa.prefill(out, q, kc, vc, bt, ctx, qs, case.scale, mq, mc)
+        if ev is not None:
+            ev[2].record()
+
+    log(f"warmup {args.warmup} steps, then {args.steps} timed steps")
+    for i in range(args.warmup):
+        step(i)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(args.steps):
+        step(i)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    append_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    launch_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    log(f"step {ms_step*1e3:.1f} us (append {append_ms*1e3:.1f} us, prefill {launch_ms*1e3:.1f} us)")
+
+    flops = prefill_flops(case)
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (launch_ms * 1e-3) / 1e12
+    traffic = traffic_from_profiles(args.config, kernel_source_sha(PREFILL_SOURCES))
+    e = case.elem_bytes
+    Hk = case.num_kv_heads
+    kv_bytes = 2 * e * Hk * D * int(case.context_lens.astype(np.int64).sum())
+    result = {
+        "metric": PREFILL_METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": case.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": WORKLOADS[args.config],
+            "step": "pa_reshape_and_cache (the chunks' K/V rows) + pa_prefill",
+            "num_seqs": S,
+            "num_heads": H,
+            "num_kv_heads": Hk,
+            "head_dim": D,
+            "block_size": B,
+            "num_blocks": case.num_blocks,
+            "query_rows": case.num_tokens,
+            "sum_context_len": int(case.context_lens.sum()),
+            "max_query_len": mq,
+            "max_context_len": mc,
+        },
+        "pct_of_mfma_peak": round(100 * value / MFMA_PEAK_TFLOPS, 2),
+        "prefill_tokens_per_s": round(case.num_tokens / (ms_step * 1e-3), 1),
+        "step_flops": int(flops),
+        "roofline": {
+            "kernel": "pa_prefill (prefill_kernel), event-timed",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_PEAK_TFLOPS, 4),
+            "traffic": traffic,
+            "algorithmic_flops_per_launch": int(flops),
+            "avg_launch_us": round(launch_ms * 1e3, 2),
+            "kv_bytes_read_once": int(kv_bytes),
+        },
+        "append_us": round(append_ms * 1e3, 2),
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample of the batch")
+        result["cpu_baseline"] = cpu_baseline_prefill(case, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 

@@ -263,7 +263,7 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pairs, int
  * streams and host-side errors as for pa_decode.  Device-side guards: a
  * sequence with n_s <= 0 is skipped; n_s > ctx_s or ctx_s > max_context_len
  * gives NaN rows; a needed block id outside [0, num_blocks) gives NaN for
- * the rows of that (64-row tile, head) without reading outside the caches.
+ * the rows of that (128-row tile, head) without reading outside the caches.
  */
 int pa_prefill(void* out, const void* query, const void* k_cache, const void* v_cache,
                const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start,

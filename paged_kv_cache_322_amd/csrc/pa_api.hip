@@ -232,7 +232,7 @@ extern "C" int pa_prefill(void* out, const void* query, const void* k_cache, con
     const int64_t ids = (static_cast<int64_t>(max_context_len) + block_size - 1) / block_size;
     if (ids > pa::kMaxPrefillIds) return PA_ERR_INVALID;
     if (max_query_len == 0) return PA_OK;
-    if ((static_cast<int64_t>(max_query_len) + 63) / 64 > 65535) return PA_ERR_INVALID;
+    if ((static_cast<int64_t>(max_query_len) + 127) / 128 > 65535) return PA_ERR_INVALID;
 
     pa::PrefillArgs a;
     a.out = out;

@@ -1,5 +1,5 @@
 // Paged prefill attention on the gfx950 matrix cores (prompt and chunked
-// prefill).
+// prefill).  Host side: pa_prefill in pa_api.hip.
 //
 // Operation: page "vLLM PagedAttention and continuous batching architecture"
 // (tech.blogsailing.com), sections 3 and 5, and page "KV cache and
@@ -13,8 +13,9 @@
 //
 // Unlike decode, this is a real matrix product: a tile of M query rows
 // against N keys is M*N*D multiply-adds for (M + N)*D loaded elements, so the
-// kernel is matrix-core bound.  Design (one workgroup = 4 wavefronts = 64
-// query rows of one sequence and one query head, 16 rows per wavefront):
+// kernel is matrix-core bound.  Design (one workgroup = 4 wavefronts = 128
+// query rows of one sequence and one query head; a wavefront owns two blocks
+// of 16 rows, so every K and V operand it reads from LDS feeds two products):
 //
 //   * the K and V rows of a 32-key tile are gathered through the block table
 //     (ids staged in LDS once) into double-buffered LDS, the next tile's
@@ -33,8 +34,13 @@
 //     accumulated, so the weights keep ~16 bits (the product of two 16-bit
 //     values is exact in the fp32 accumulator);
 //   * online softmax per row in base 2, tile maximum shared across the four
-//     lane groups of a row with two cross-row exchanges, accumulators
-//     rescaled only when a row maximum grows;
+//     lane groups of a row with two cross-row exchanges; the reference
+//     maximum moves (and the accumulators are rescaled) only when a tile
+//     exceeds it by more than 2^8, so the rescale is rare; the score scale is
+//     one fused multiply-add;
+//   * at most 2 wavefronts per SIMD (launch bound): the compiler then keeps
+//     the accumulators in VGPRs (MFMA with VGPR C/D) instead of shuttling
+//     them through AGPRs;
 //   * causal masking per element; a wavefront skips tiles entirely past its
 //     rows; workgroups are dispatched last query tile first (they have the
 //     most keys).
@@ -49,8 +55,14 @@ namespace {
 
 constexpr int kPfWaves = 4;
 constexpr int kPfThreads = kPfWaves * kWave;
-constexpr int kPfRows = 16 * kPfWaves;  // query rows per workgroup
-constexpr int kPfKeys = 32;             // keys per tile
+constexpr int kPfBlocks = 2;                        // 16-row blocks per wavefront
+constexpr int kPfRows = 16 * kPfBlocks * kPfWaves;  // query rows per workgroup
+constexpr int kPfKeys = 32;                         // keys per tile
+// The running maximum used as the softmax reference moves only when a tile's
+// maximum exceeds it by more than this (log2 units), so the accumulators are
+// rescaled rarely; probabilities stay below 2^8 (no overflow in f16/bf16 or
+// fp32; the hi + lo split keeps their relative precision).
+constexpr float kPfRescaleSlack = 8.0f;
 
 template <int D>
 struct PfShape {
@@ -83,7 +95,7 @@ __device__ __forceinline__ void lds_read_words(const uint16_t* p, uint32_t (&w)[
 }
 
 template <class T, int D>
-__global__ __launch_bounds__(kPfThreads) void prefill_kernel(
+__global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ query_start, int num_heads,
@@ -91,6 +103,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(
     float qscale) {
     using Sh = PfShape<D>;
     constexpr int KS = Sh::KS, E = Sh::E, NW = Sh::NW, LD = Sh::LD, CPR = Sh::CPR, CPT = Sh::CPT;
+    constexpr int RB = kPfBlocks;
     using Ops = MfmaOps<T>;
 
     extern __shared__ int s_ids[];  // block ids of keys 0 .. kv_end - 1 (dynamic size)
@@ -107,13 +120,16 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(
     const int r0 = qt * kPfRows;  // first row of this workgroup within the chunk
     if (n <= 0 || r0 >= n) return;
     const int ctx = __builtin_amdgcn_readfirstlane(context_lens[s]);
-    const int wr0 = r0 + 16 * wave;  // first row of this wavefront
+    const int wr0 = r0 + 16 * RB * wave;  // first row of this wavefront
     if (ctx < n || ctx > max_context_len) {
         // Impossible lengths: NaN rows, nothing read.
-        const int row = wr0 + c;
-        if (row < n) {
-            for (int d = g; d < D; d += 4)
-                out[(static_cast<int64_t>(q0 + row) * num_heads + h) * D + d] = narrow<T>(__builtin_nanf(""));
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            const int row = wr0 + 16 * rb + c;
+            if (row < n) {
+                for (int d = g; d < D; d += 4)
+                    out[(static_cast<int64_t>(q0 + row) * num_heads + h) * D + d] = narrow<T>(__builtin_nanf(""));
+            }
         }
         return;
     }
@@ -132,13 +148,20 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(
         s_ids[i] = (b >= 0 && b < num_blocks) ? b : -1;
     }
 
-    // B operand of q.k: this wavefront's query row c (rows past the chunk
-    // re-read its last row; they are never written).
-    const int qrow = min(wr0 + c, n - 1);
-    const uint16_t* qp = q + (static_cast<int64_t>(q0 + qrow) * num_heads + h) * D + 8 * g;
-    u32x4 qv[KS];
+    // B operands of q.k: query rows wr0 + 16 rb + c (rows past the chunk
+    // re-read its last row; they are never written).  A negative scale is
+    // folded into the query by flipping its sign bits (exact), so the scale
+    // applied to the scores is >= 0 and the maximum commutes with it.
+    const uint32_t sign = qscale < 0.0f ? 0x80008000u : 0u;
+    const float sc_mul = fabsf(qscale);
+    u32x4 qv[RB][KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qv[ks] = as_u32x4(load16(qp + 32 * ks));
+    for (int rb = 0; rb < RB; ++rb) {
+        const int qrow = min(wr0 + 16 * rb + c, n - 1);
+        const uint16_t* qp = q + (static_cast<int64_t>(q0 + qrow) * num_heads + h) * D + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qv[rb][ks] = as_u32x4(load16(qp + 32 * ks)) ^ sign;
+    }
     __syncthreads();  // s_ids staged
 
     const uint32_t blk_stride = static_cast<uint32_t>(num_kv_heads << log2_bs) * D;
@@ -176,14 +199,19 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(
         }
     };
 
-    f32x4 acc[E];
+    f32x4 acc[RB][E];
+    float m[RB], l[RB];  // per row c: softmax reference (same in the 4 lane groups), this lane's sum
+    int pos[RB];         // position of this lane's row in each block (padding rows clamped)
 #pragma unroll
-    for (int t = 0; t < E; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    float m = -INFINITY;  // running maximum of row c (same in the 4 lane groups)
-    float l = 0.0f;       // running sum over this lane's keys
-    const int wpos0 = first_pos + wr0;                    // position of this wavefront's row 0
-    const int pos_c = min(wpos0 + c, ctx - 1);            // this lane's row position (padding rows clamped)
-    const int wave_last_key = min(wpos0 + 15, ctx - 1);   // wave-uniform
+    for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+        for (int t = 0; t < E; ++t) acc[rb][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        m[rb] = -INFINITY;
+        l[rb] = 0.0f;
+        pos[rb] = min(first_pos + wr0 + 16 * rb + c, ctx - 1);
+    }
+    const int wpos0 = first_pos + wr0;                        // position of the wavefront's first row
+    const int wave_last_key = min(wpos0 + 16 * RB - 1, ctx - 1);  // wave-uniform
 
     load_tile(0);
     store_tile(0);
@@ -193,47 +221,62 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(
         if (kt + 1 < ntiles) load_tile(kt + 1);
         const int k0 = kt * kPfKeys;
         if (wr0 < n && k0 <= wave_last_key) {
-            // Scores S^T: lane (c, g) gets keys k0 + 16 sub + 4 g + j of row c.
-            f32x4 sc[2];
+            // Scores S^T: lane (c, g) gets keys k0 + 16 sub + 4 g + j of row
+            // wr0 + 16 rb + c.  Each key operand serves both row blocks.
+            f32x4 sc[RB][2];
 #pragma unroll
-            for (int sub = 0; sub < 2; ++sub) {
-                sc[sub] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-                const uint16_t* kr = &sK[buf][16 * sub + c][8 * g];
+            for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    sc[sub] = Ops::qk(as_u32x4(*reinterpret_cast<const uint4*>(kr + 32 * ks)), qv[ks], sc[sub]);
-            }
-            float x[8];
-            float mx = -INFINITY;
+                for (int sub = 0; sub < 2; ++sub) sc[rb][sub] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int sub = 0; sub < 2; ++sub)
+            for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int kp = k0 + 16 * sub + 4 * g + j;
-                    const float v = (kp <= pos_c) ? sc[sub][j] * qscale : -INFINITY;
-                    x[4 * sub + j] = v;
-                    mx = fmaxf(mx, v);
+                for (int sub = 0; sub < 2; ++sub) {
+                    const u32x4 kop = as_u32x4(*reinterpret_cast<const uint4*>(&sK[buf][16 * sub + c][8 * g + 32 * ks]));
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb) sc[rb][sub] = Ops::qk(kop, qv[rb][ks], sc[rb][sub]);
                 }
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m, mx);  // finite: tile 0 holds key 0, valid for every row
-            if (__builtin_amdgcn_ballot_w64(m_new > m)) {
-                const float alpha = fast_exp2(m - m_new);
-                l *= alpha;
-#pragma unroll
-                for (int t = 0; t < E; ++t) acc[t] *= alpha;
             }
-            m = m_new;
-            float p[8];
+            u32x4 bh[RB], bl[RB];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                p[i] = fast_exp2(x[i] - m);
-                l += p[i];
+            for (int rb = 0; rb < RB; ++rb) {
+                // Keys above the diagonal exist only in tiles reaching past
+                // the block's first row (wave-uniform test).
+                const bool full = k0 + kPfKeys - 1 <= wpos0 + 16 * rb;
+                float raw[8];
+                float mx = -INFINITY;
+#pragma unroll
+                for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        float v = sc[rb][sub][j];
+                        if (!full) v = (k0 + 16 * sub + 4 * g + j <= pos[rb]) ? v : -INFINITY;
+                        raw[4 * sub + j] = v;
+                        mx = fmaxf(mx, v);
+                    }
+                mx = fmaxf(mx, __shfl_xor(mx, 16));
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                mx *= sc_mul;  // every row has a valid key here: finite (tile 0 holds key 0)
+                if (__builtin_amdgcn_ballot_w64(mx > m[rb] + kPfRescaleSlack)) {
+                    const float m_new = fmaxf(m[rb], mx);
+                    const float alpha = fast_exp2(m[rb] - m_new);  // 0 on the first tile (m = -inf)
+                    l[rb] *= alpha;
+#pragma unroll
+                    for (int t = 0; t < E; ++t) acc[rb][t] *= alpha;
+                    m[rb] = m_new;
+                }
+                float p[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    p[i] = fast_exp2(fmaf(raw[i], sc_mul, -m[rb]));  // masked: exp2(-inf) = 0
+                    l[rb] += p[i];
+                }
+                uint32_t ph[4], pl[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Ops::split(p[2 * i], p[2 * i + 1], ph[i], pl[i]);
+                bh[rb] = u32x4{ph[0], ph[1], ph[2], ph[3]};
+                bl[rb] = u32x4{pl[0], pl[1], pl[2], pl[3]};
             }
-            uint32_t ph[4], pl[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Ops::split(p[2 * i], p[2 * i + 1], ph[i], pl[i]);
-            const u32x4 bh = u32x4{ph[0], ph[1], ph[2], ph[3]}, bl = u32x4{pl[0], pl[1], pl[2], pl[3]};
 
             // Value rows of keys 16 sub + 4 g + j, channels E c .. E c + E - 1.
             uint32_t vr[8][NW];
@@ -249,34 +292,41 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(
                                       __builtin_amdgcn_perm(vr[3][w], vr[2][w], sel),
                                       __builtin_amdgcn_perm(vr[5][w], vr[4][w], sel),
                                       __builtin_amdgcn_perm(vr[7][w], vr[6][w], sel)};
-                acc[t] = Ops::qk(a, bh, acc[t]);
-                acc[t] = Ops::qk(a, bl, acc[t]);
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    acc[rb][t] = Ops::qk(a, bh[rb], acc[rb][t]);
+                    acc[rb][t] = Ops::qk(a, bl[rb], acc[rb][t]);
+                }
             }
         }
         if (kt + 1 < ntiles) store_tile(buf ^ 1);
         __syncthreads();
     }
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
     bad = __syncthreads_or(bad);
 
-    // Lane (c, g) holds row c, channels D/4 g .. D/4 g + D/4 - 1.
-    const int row = wr0 + c;
-    if (row < n) {
-        const float inv = bad ? __builtin_nanf("") : 1.0f / l;
-        uint16_t* op = out + (static_cast<int64_t>(q0 + row) * num_heads + h) * D + (D / 4) * g;
-        uint32_t packed[D / 8];
+    // Lane (c, g) holds row wr0 + 16 rb + c, channels D/4 g .. D/4 g + D/4 - 1.
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+    for (int rb = 0; rb < RB; ++rb) {
+        float lt = l[rb];
+        lt += __shfl_xor(lt, 16);
+        lt += __shfl_xor(lt, 32);
+        const int row = wr0 + 16 * rb + c;
+        if (row < n) {
+            const float inv = bad ? __builtin_nanf("") : 1.0f / lt;
+            uint16_t* op = out + (static_cast<int64_t>(q0 + row) * num_heads + h) * D + (D / 4) * g;
+            uint32_t packed[D / 8];
 #pragma unroll
-            for (int t = 0; t < E; t += 2) {
-                const uint32_t lo = narrow<T>(acc[t][j] * inv), hi = narrow<T>(acc[t + 1][j] * inv);
-                packed[(E * j + t) / 2] = lo | (hi << 16);
-            }
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int i = 0; i < D / 32; ++i)
-            reinterpret_cast<uint4*>(op)[i] =
-                uint4{packed[4 * i + 0], packed[4 * i + 1], packed[4 * i + 2], packed[4 * i + 3]};
+                for (int t = 0; t < E; t += 2) {
+                    const uint32_t lo = narrow<T>(acc[rb][t][j] * inv), hi = narrow<T>(acc[rb][t + 1][j] * inv);
+                    packed[(E * j + t) / 2] = lo | (hi << 16);
+                }
+#pragma unroll
+            for (int i = 0; i < D / 32; ++i)
+                reinterpret_cast<uint4*>(op)[i] =
+                    uint4{packed[4 * i + 0], packed[4 * i + 1], packed[4 * i + 2], packed[4 * i + 3]};
+        }
     }
 }
 

@@ -232,12 +232,12 @@ def test_mfma_bounds_all_shapes(D, G):
 # Prefill kernel (csrc/pa_prefill.hip)
 # ---------------------------------------------------------------------------
 
-PF_ROWS, PF_KEYS, PF_THREADS, PF_MAX_IDS = 64, 32, 256, 4096
+PF_ROWS, PF_KEYS, PF_THREADS, PF_MAX_IDS = 128, 32, 256, 4096
 
 
 def check_prefill_bounds(case, max_query_len=None):
-    """Grid (H, S, ceil(max_query_len / 64)); wavefront w of a workgroup owns
-    chunk rows r0 + 16 w + c; query loads read row min(row, n - 1), channels
+    """Grid (H, S, ceil(max_query_len / 128)); wavefront w of a workgroup owns
+    chunk rows r0 + 32 w + 16 rb + c (rb = 0, 1); query loads read row min(row, n - 1), channels
     32 ks + 8 g .. +7; block ids of keys 0 .. kv_end - 1 are staged; tile
     loads read key kp < kv_end at chunk 8 cc of its row; LDS reads stay in
     the [2][32][D + 8] tiles; output rows < n, channels D/4 g .. +D/4."""
