@@ -19,6 +19,7 @@ from .paged_attention import (
     paged_decode,
     partial_attention,
     reshape_and_cache,
+    swap_blocks,
     token_location,
     widen,
 )
@@ -37,6 +38,7 @@ __all__ = [
     "paged_prefill",
     "partial_attention",
     "reshape_and_cache",
+    "swap_blocks",
     "token_location",
     "widen",
 ]

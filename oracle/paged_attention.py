@@ -227,6 +227,33 @@ def copy_blocks(k_cache, v_cache, pairs):
     return kc, vc
 
 
+def swap_blocks(src_k, src_v, dst_k, dst_v, pairs):
+    """Move whole blocks between two pools (swapping).
+
+    PagedAttention digest, Method (scheduling) and glossary: under memory
+    pressure a preempted request's KV blocks are moved to CPU RAM and moved
+    back when it resumes (the page on vLLM PagedAttention and continuous
+    batching, section 3, names the same swap space).  For every (src, dst)
+    pair, block dst of the destination pools becomes block src of the source
+    pools: all heads, slots and channels of K and of V, bit for bit.  The
+    pools may differ in their number of blocks (a host swap space is sized on
+    its own); destinations must be distinct.  Returns new destination pools.
+    """
+    kd, vd = dst_k.copy(), dst_v.copy()
+    pr = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
+    if pr.size:
+        src, dst = pr[:, 0], pr[:, 1]
+        if np.unique(dst).size != dst.size:
+            raise ValueError("duplicate destination blocks")
+        if src.min() < 0 or src.max() >= src_k.shape[0] or dst.min() < 0 or dst.max() >= kd.shape[0]:
+            raise IndexError("block id outside its pool")
+        if src_k.shape[1:] != kd.shape[1:]:
+            raise ValueError("pools disagree on heads, block size or head_dim")
+        kd[dst] = src_k[src]
+        vd[dst] = src_v[src]
+    return kd, vd
+
+
 # ---------------------------------------------------------------------------
 # One decode step: store each sequence's newest token, then attend
 # ---------------------------------------------------------------------------

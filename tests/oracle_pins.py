@@ -625,3 +625,42 @@ PREFILL_PINS = [
     pin_prefill_chunking,
     pin_prefill_closed_forms,
 ]
+
+
+def pin_swap(orc):
+    """Swapping out to a smaller host pool and back in under new block ids
+    restores every block bit for bit; blocks not named keep their bits; and
+    decode through the relabelled table equals decode before the swap."""
+    case = wl.random_case(24, 3, 2, 8, 4, "bf16", ctx=[7, 13, 4], spare_blocks=9)
+    N = case.num_blocks
+    held = [sorted(int(b) for b in case.block_tables[s] if b >= 0) for s in range(case.num_seqs)]
+    # Preempt sequence 1: its blocks go to host slots 0.. in table order.
+    nb1 = -(-int(case.context_lens[1]) // case.block_size)
+    out_ids = [int(case.block_tables[1, j]) for j in range(nb1)]
+    host_k = wl.canary_fill((nb1 + 2,) + case.k_cache.shape[1:], "bf16")
+    host_v = wl.canary_fill((nb1 + 2,) + case.v_cache.shape[1:], "bf16")
+    out_pairs = np.array([[b, i + 1] for i, b in enumerate(out_ids)], dtype=np.int64)
+    hk, hv = orc.swap_blocks(case.k_cache, case.v_cache, host_k, host_v, out_pairs)
+    for i, b in enumerate(out_ids):
+        assert np.array_equal(hk[i + 1].view(np.uint16), case.k_cache[b].view(np.uint16))
+        assert np.array_equal(hv[i + 1].view(np.uint16), case.v_cache[b].view(np.uint16))
+    for i in (0, nb1 + 1):  # host slots not named keep their canaries
+        assert np.array_equal(hk[i].view(np.uint16), host_k[i].view(np.uint16))
+    # Resume: swap back into free device blocks (ids not used by any sequence).
+    used = {b for h in held for b in h}
+    free = [b for b in range(N) if b not in used][:nb1]
+    in_pairs = np.array([[i + 1, f] for i, f in enumerate(free)], dtype=np.int64)
+    kc2, vc2 = orc.swap_blocks(hk, hv, case.k_cache, case.v_cache, in_pairs)
+    for i, f in enumerate(free):
+        assert np.array_equal(kc2[f].view(np.uint16), case.k_cache[out_ids[i]].view(np.uint16))
+    keep = [b for b in range(N) if b not in free]
+    assert np.array_equal(kc2[keep].view(np.uint16), case.k_cache[keep].view(np.uint16))
+    bt = case.block_tables.copy()
+    bt[1, :nb1] = free
+    got = orc.paged_decode(case.q, kc2, vc2, bt, case.context_lens, case.scale, case.dtype)
+    ref = brute_decode(case.q, case.k_cache, case.v_cache, case.block_tables, case.context_lens, case.scale,
+                       case.dtype)
+    assert np.abs(got - ref).max() <= 1e-12
+
+
+ALL_PINS.append(pin_swap)

@@ -111,6 +111,17 @@ def _decode_gqa_modulo(q, k_cache, v_cache, block_tables, context_lens, scale, d
     return out[:, inv]
 
 
+def _swap_k_only(src_k, src_v, dst_k, dst_v, pairs):
+    kd, _ = _real["swap_blocks"](src_k, src_v, dst_k, dst_v, pairs)
+    return kd, dst_v.copy()
+
+
+def _swap_reversed_pairs(src_k, src_v, dst_k, dst_v, pairs):
+    """(dst, src) read as (src, dst)."""
+    pr = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)[:, ::-1]
+    return _real["swap_blocks"](src_k, src_v, dst_k, dst_v, np.ascontiguousarray(pr))
+
+
 MUTANTS = {
     "attention drops the scale": ("attention", _attention_no_scale),
     "softmax exponent sign flipped": ("attention", _attention_flipped),
@@ -128,6 +139,8 @@ MUTANTS = {
     "partial stats use the wrong reference": ("partial_attention", _partial_no_max),
     "newest token taken one position late": ("newest_token_slots", _newest_off_by_one),
     "query heads grouped round-robin over K/V heads": ("paged_decode", _decode_gqa_modulo),
+    "swap moves K only": ("swap_blocks", _swap_k_only),
+    "swap pairs read backwards": ("swap_blocks", _swap_reversed_pairs),
 }
 
 
