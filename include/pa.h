@@ -11,6 +11,8 @@
  *                         token fused with pa_decode (one launch)
  *   pa_prefill            causal attention of new prompt tokens (chunks)
  *                         over the paged context
+ *   pa_swap_blocks        whole blocks between the device caches and a
+ *                         pinned host pool (preemption by swapping)
  *
  * Memory layout (every array dense, row-major, no padding):
  *   query, out          [num_seqs, num_heads, head_dim]              element type `dtype`
@@ -25,7 +27,8 @@
  *
  * Ownership and execution: every pointer argument other than the scalars is
  * device memory owned by the caller (query, caches, tables, lengths, slot
- * mapping, pairs, out, workspace).  The library allocates nothing, frees
+ * mapping, pairs, out, workspace); pa_swap_blocks also takes pinned host
+ * memory.  The library allocates nothing, frees
  * nothing and never synchronises: each call validates its arguments on the
  * host, enqueues its kernels on `stream` (a hipStream_t; NULL is the null
  * stream) and returns.  The library keeps no global state, so calls are
@@ -270,6 +273,36 @@ int pa_prefill(void* out, const void* query, const void* k_cache, const void* v_
                int32_t num_seqs, int32_t num_tokens, int32_t num_heads, int32_t num_kv_heads,
                int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int32_t max_query_len,
                int32_t max_context_len, int64_t num_blocks, float scale, int32_t dtype, void* stream);
+
+/*
+ * pa_swap_blocks - move whole blocks between two pools (swapping).
+ *
+ * PagedAttention digest (irregular6612.github.io), section "Method"
+ * (scheduling) and its glossary: when memory runs short a preempted
+ * request's KV blocks are moved to CPU RAM, and moved back when it resumes;
+ * the page "vLLM PagedAttention and continuous batching architecture"
+ * (tech.blogsailing.com), section 3, names the same swap space.  For every
+ * pair (src, dst) in block_pairs:
+ *
+ *   dst_k[dst] = src_k[src];  dst_v[dst] = src_v[src]
+ *
+ * whole blocks (all heads, slots and channels), bit-exact.  Swap-out passes
+ * the device caches as src and a host pool as dst; swap-in the reverse.
+ * The two pools have the same [*, num_heads, block_size, head_dim] block
+ * shape and their own block counts.  Every pool, and block_pairs (int64
+ * [num_pairs, 2]), must be device memory or pinned, mapped host memory
+ * (hipHostMalloc; torch's pin_memory=True): pageable host memory is
+ * rejected with PA_ERR_INVALID before anything is enqueued, as are
+ * pointers the HIP runtime does not know.  The pools must be 16-byte
+ * aligned.  Destinations must be distinct (and, within one pool, disjoint
+ * from the sources); a pair with an id outside its pool is skipped by the
+ * kernel.  One kernel launch on `stream` moves every pair (the host-side
+ * loads or stores cross the host link); ownership and errors otherwise as
+ * for pa_copy_blocks.
+ */
+int pa_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v, const int64_t* block_pairs,
+                   int32_t num_pairs, int32_t num_heads, int32_t head_dim, int32_t block_size,
+                   int64_t src_num_blocks, int64_t dst_num_blocks, int32_t dtype, void* stream);
 
 /* Human-readable name of a pa_status value (static storage; never NULL). */
 const char* pa_status_string(int status);

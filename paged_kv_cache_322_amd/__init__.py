@@ -29,6 +29,7 @@ __all__ = [
     "status_string",
     "partition_tokens",
     "prefill",
+    "swap_blocks",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
@@ -62,6 +63,8 @@ lib.pa_reshape_and_cache.restype = ctypes.c_int
 lib.pa_reshape_and_cache.argtypes = [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i64, _i32, _p]
 lib.pa_copy_blocks.restype = ctypes.c_int
 lib.pa_copy_blocks.argtypes = [_p, _p, _p, _i32, _i32, _i32, _i32, _i64, _i32, _p]
+lib.pa_swap_blocks.restype = ctypes.c_int
+lib.pa_swap_blocks.argtypes = [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i64, _i64, _i32, _p]
 lib.pa_prefill.restype = ctypes.c_int
 lib.pa_prefill.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                            _i64, ctypes.c_float, _i32, _p]
@@ -277,3 +280,47 @@ def prefill(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor, val
                         _code(dt), _stream_handle(query.device, stream))
     _check(st, "pa_prefill")
     return out
+
+
+def _pool(t: torch.Tensor, name: str, dtype=None, ndim=None) -> None:
+    """A tensor the library may dereference on the device: on the GPU, or in
+    pinned (page-locked, mapped) host memory."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type == "cpu" and not t.is_pinned():
+        raise ValueError(f"{name} is pageable host memory; allocate it with pin_memory=True")
+    if t.device.type not in ("cpu", "cuda"):
+        raise ValueError(f"{name} must be on a GPU or in pinned host memory, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+
+
+def swap_blocks(dst_k: torch.Tensor, dst_v: torch.Tensor, src_k: torch.Tensor, src_v: torch.Tensor,
+                block_pairs: torch.Tensor, stream=None) -> None:
+    """Move whole blocks between two pools (``pa_swap_blocks``): dst[d] = src[s]
+    for each (s, d) row of int64 ``block_pairs``.  Pools are [N, H, B, D] on the
+    GPU or in pinned host memory (swap-out: GPU -> host; swap-in: host -> GPU);
+    the launch goes on ``stream`` (default: the current stream of the GPU)."""
+    _pool(src_k, "src_k", ndim=4)
+    dt = src_k.dtype
+    _pool(src_v, "src_v", dt, 4)
+    _pool(dst_k, "dst_k", dt, 4)
+    _pool(dst_v, "dst_v", dt, 4)
+    _pool(block_pairs, "block_pairs", torch.int64)
+    if block_pairs.numel() % 2:
+        raise ValueError("block_pairs must have shape [n, 2]")
+    Ns, H, B, D = src_k.shape
+    Nd = dst_k.shape[0]
+    if tuple(src_v.shape) != tuple(src_k.shape) or tuple(dst_v.shape) != tuple(dst_k.shape):
+        raise ValueError("K and V pools of one side differ in shape")
+    if tuple(dst_k.shape[1:]) != (H, B, D):
+        raise ValueError("the pools disagree on heads, block size or head_dim")
+    dev = next((t.device for t in (dst_k, src_k) if t.device.type == "cuda"), torch.device("cuda"))
+    st = lib.pa_swap_blocks(dst_k.data_ptr(), dst_v.data_ptr(), src_k.data_ptr(), src_v.data_ptr(),
+                            block_pairs.data_ptr(), block_pairs.numel() // 2, H, D, B, Ns, Nd, _code(dt),
+                            _stream_handle(dev, stream))
+    _check(st, "pa_swap_blocks")

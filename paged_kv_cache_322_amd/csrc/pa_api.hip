@@ -38,6 +38,19 @@ size_t workspace_bytes_for(int64_t num_seqs, int64_t num_heads, int64_t head_dim
 
 int hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
 
+// True when a kernel may dereference p: device memory, or host memory
+// allocated pinned and mapped (hipHostMalloc, torch's pin_memory).  Pageable
+// host memory (or an unknown pointer) would fault on the device.
+bool device_accessible(const void* p) {
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+        (void)hipGetLastError();  // clear the sticky error the failed query leaves
+        return false;
+    }
+    if (attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged) return true;
+    return attr.type == hipMemoryTypeHost && attr.devicePointer == p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -203,6 +216,26 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pairs, int
         static_cast<int64_t>(num_heads) * block_size * head_dim * elem_bytes(dtype);
     return hip_status(pa::launch_copy_blocks(k_cache, v_cache, block_pairs, num_pairs, block_bytes,
                                              num_blocks, static_cast<hipStream_t>(stream)));
+}
+
+int pa_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v, const int64_t* block_pairs,
+                   int32_t num_pairs, int32_t num_heads, int32_t head_dim, int32_t block_size,
+                   int64_t src_num_blocks, int64_t dst_num_blocks, int32_t dtype, void* stream) {
+    if (!supported_dtype(dtype) || !supported_head_dim(head_dim) || !supported_block_size(block_size))
+        return PA_ERR_UNSUPPORTED;
+    if (num_pairs < 0 || num_pairs > 65535 || num_heads <= 0 || src_num_blocks <= 0 || dst_num_blocks <= 0)
+        return PA_ERR_INVALID;
+    if (num_pairs == 0) return PA_OK;  // nothing to move
+    if (!dst_k || !dst_v || !src_k || !src_v || !block_pairs) return PA_ERR_NULL;
+    if (!aligned16(dst_k) || !aligned16(dst_v) || !aligned16(src_k) || !aligned16(src_v)) return PA_ERR_INVALID;
+    if (!device_accessible(dst_k) || !device_accessible(dst_v) || !device_accessible(src_k) ||
+        !device_accessible(src_v) || !device_accessible(block_pairs))
+        return PA_ERR_INVALID;
+    const int64_t block_bytes =
+        static_cast<int64_t>(num_heads) * block_size * head_dim * elem_bytes(dtype);
+    return hip_status(pa::launch_copy_pool_blocks(dst_k, dst_v, src_k, src_v, block_pairs, num_pairs, block_bytes,
+                                                  src_num_blocks, dst_num_blocks,
+                                                  static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

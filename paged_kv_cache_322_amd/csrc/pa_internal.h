@@ -145,4 +145,8 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pairs, int num_pairs,
                               int64_t block_bytes, int64_t num_blocks, hipStream_t stream);
 
+hipError_t launch_copy_pool_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                                   const int64_t* block_pairs, int num_pairs, int64_t block_bytes,
+                                   int64_t src_num_blocks, int64_t dst_num_blocks, hipStream_t stream);
+
 }  // namespace pa

@@ -224,3 +224,38 @@ def test_prefill_host_checks():
     assert pf(query=P + 8) == INVALID
     assert pf(S=70000) == INVALID
     assert pf(T=-1) == INVALID
+
+
+def swap(**kw):
+    a = dict(dk=P, dv=P, sk=P, sv=P, pairs=P, n=4, H=4, D=128, B=16, Ns=64, Nd=8, dtype=1)
+    a.update(kw)
+    return pa.lib.pa_swap_blocks(a["dk"], a["dv"], a["sk"], a["sv"], a["pairs"], a["n"], a["H"], a["D"], a["B"],
+                                 a["Ns"], a["Nd"], a["dtype"], None)
+
+
+def test_swap_host_checks():
+    # No call here reaches a launch: each fails a check, or has nothing to move.
+    assert swap(n=0, dk=0) == OK
+    assert swap(dtype=3) == UNSUP
+    assert swap(D=96) == UNSUP
+    assert swap(B=3) == UNSUP
+    assert swap(n=-1) == INVALID
+    assert swap(n=70000) == INVALID
+    assert swap(Ns=0) == INVALID
+    assert swap(Nd=0) == INVALID
+    assert swap(H=0) == INVALID
+    assert swap(dk=0) == NULL
+    assert swap(pairs=0) == NULL
+    assert swap(sk=P + 8) == INVALID  # misaligned
+    # A pointer the HIP runtime does not know (pageable memory, garbage) is
+    # rejected on the host, never handed to a kernel.
+    assert swap() == INVALID
+
+
+def test_swap_binding_rejects_pageable_host_tensors():
+    import torch
+
+    t = torch.zeros((2, 1, 4, 8), dtype=torch.float16)  # pageable host memory
+    pairs = torch.zeros((1, 2), dtype=torch.int64)
+    with pytest.raises(ValueError):
+        pa.swap_blocks(t, t.clone(), t.clone(), t.clone(), pairs)
