@@ -37,6 +37,9 @@ import numpy as np
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, vendor figure
 METRIC = "paged decode attention: KV-read GB/s and % of HBM peak; decode tokens/s"
+SWAP_WORKLOAD = ("swap-llama7b: preempt 16 of the 64 LLaMA-7B-shaped decode sequences (config 2): swap their "
+                 "K/V blocks out to a pinned host pool and back in under new ids; H=32, D=128, f16, B=16")
+LINK_PEAK_GBPS = 64.0  # PCIe 5.0 x16, one direction, nominal
 WORKLOADS = {
     "2": "llama7b-decode-layer: 64 seqs, ctx U[128,2048], H=32, D=128, f16, B=16, 8192-block pool",
     "3": "opt13b-decode-layer: 256 seqs, ctx lognormal(median 300, sigma 0.9) in [16,2048], H=40, D=128, f16, B=16",
@@ -50,6 +53,7 @@ WORKLOADS = {
                      "32 query / 8 K/V heads, D=128, f16, B=16",
     "prefill-prompts": "llama7b-prompt-prefill: 32 whole prompts, lognormal(median 300, sigma 0.9) lengths in "
                        "[16,2048], H=32, D=128, bf16, B=16",
+    "swap": SWAP_WORKLOAD,
 }
 PREFILL_KINDS = {"prefill-llama7b": "llama7b", "prefill-gqa8b": "llama3-8b", "prefill-prompts": "prompts"}
 MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak, vendor figure
@@ -92,6 +96,8 @@ def make_case(cfg, block_size=16):
         return wl.gqa_config("llama2-70b-tp8", n_append=1)
     if cfg in PREFILL_KINDS:
         return wl.prefill_config(PREFILL_KINDS[cfg])
+    if cfg == "swap":
+        return wl.config2()
     return wl.config5(n_append=1)
 
 
@@ -259,6 +265,8 @@ def main():
     case = make_case(args.config, args.block_size)
     if args.config in PREFILL_KINDS:
         return bench_prefill(args, case, pa, torch, dev)
+    if args.config == "swap":
+        return bench_swap(args, case, pa, torch, dev)
     import workloads as wl
 
     # Config 4's prompt write, fork copies and suffix writes are set-up; the
@@ -621,6 +629,99 @@ def bench_prefill(args, case, pa, torch, dev):
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample of the batch")
         result["cpu_baseline"] = cpu_baseline_prefill(case, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def bench_swap(args, case, pa, torch, dev):
+    """Preemption by swapping: the blocks of 16 of config 2's 64 sequences
+    move to a pinned host pool (swap-out) and back under new device ids
+    (swap-in), one pa_swap_blocks launch each.  Reference: one DMA copy of
+    the same number of bytes between a contiguous device buffer and pinned
+    host memory (torch's copy_, the runtime's copy engine)."""
+    S, H, D, B = case.num_seqs, case.num_heads, case.head_dim, case.block_size
+    preempt = list(range(0, S, 4))  # every fourth sequence: 16 of 64
+    ids = []
+    for s in preempt:
+        nb = -(-int(case.context_lens[s]) // B)
+        ids.extend(int(b) for b in case.block_tables[s, :nb])
+    n = len(ids)
+    used = set(int(b) for b in case.block_tables.ravel() if b >= 0)
+    free = [b for b in range(case.num_blocks) if b not in used]
+    assert len(free) >= n
+    kc = torch.from_numpy(case.k_cache).to(dev)
+    vc = torch.from_numpy(case.v_cache).to(dev)
+    hk = torch.empty((n,) + tuple(kc.shape[1:]), dtype=kc.dtype, pin_memory=True)
+    hv = torch.empty_like(hk, pin_memory=True)
+    out_pairs = torch.from_numpy(np.array([[b, i] for i, b in enumerate(ids)], dtype=np.int64)).to(dev)
+    in_pairs = torch.from_numpy(np.array([[i, f] for i, f in enumerate(free[:n])], dtype=np.int64)).to(dev)
+    block_bytes = H * B * D * case.elem_bytes
+    moved = 2 * n * block_bytes  # K and V, each direction
+    torch.cuda.synchronize()
+
+    def timed(fn, reps):
+        for _ in range(max(1, args.warmup // 5)):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    reps = max(3, args.steps // 5)
+    log(f"swap {n} blocks ({moved / 1e6:.1f} MB) out and in, {reps} repetitions each")
+    out_ms = timed(lambda: pa.swap_blocks(hk, hv, kc, vc, out_pairs), reps)
+    in_ms = timed(lambda: pa.swap_blocks(kc, vc, hk, hv, in_pairs), reps)
+    # Copy-engine reference: contiguous buffers of the same size.
+    dbuf = torch.empty(moved // 2, dtype=torch.uint8, device=dev)
+    hbuf = torch.empty(moved // 2, dtype=torch.uint8, pin_memory=True)
+    d2h_ms = timed(lambda: (hbuf.copy_(dbuf, non_blocking=True), hbuf.copy_(dbuf, non_blocking=True)), reps)
+    h2d_ms = timed(lambda: (dbuf.copy_(hbuf, non_blocking=True), dbuf.copy_(hbuf, non_blocking=True)), reps)
+    # Check the round trip once (bitwise) outside the timed region.
+    pa.swap_blocks(hk, hv, kc, vc, out_pairs)
+    pa.swap_blocks(kc, vc, hk, hv, in_pairs)
+    torch.cuda.synchronize()
+    src = torch.tensor(ids, device=dev)
+    dst = torch.tensor(free[:n], device=dev)
+    ok = bool(torch.equal(kc[dst].view(torch.int16), kc[src].view(torch.int16))
+              and torch.equal(vc[dst].view(torch.int16), vc[src].view(torch.int16)))
+    gbs = lambda ms: round(moved / (ms * 1e-3) / 1e9, 2)
+    step_ms = out_ms + in_ms
+    log(f"swap-out {out_ms*1e3:.1f} us ({gbs(out_ms)} GB/s), swap-in {in_ms*1e3:.1f} us ({gbs(in_ms)} GB/s); "
+        f"DMA reference D2H {gbs(d2h_ms)} GB/s, H2D {gbs(h2d_ms)} GB/s; round trip {'ok' if ok else 'MISMATCH'}")
+    result = {
+        "metric": "KV block swapping: host-link GB/s per direction",
+        "value": round(2 * moved / (step_ms * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": reps,
+        "warmup": max(1, args.warmup // 5),
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": case.dtype,
+        "data": "synthetic",
+        "config": {"workload": SWAP_WORKLOAD, "step": "pa_swap_blocks out (device -> pinned host) + in (host -> "
+                   "device)", "blocks": n, "block_bytes": block_bytes, "bytes_each_way": moved},
+        "swap_out_GBps": gbs(out_ms),
+        "swap_in_GBps": gbs(in_ms),
+        "dma_reference": {"d2h_GBps": gbs(d2h_ms), "h2d_GBps": gbs(h2d_ms),
+                          "what": "torch copy_ of one contiguous buffer of the same size (copy engine)"},
+        "round_trip_bitwise_ok": ok,
+        "roofline": {
+            "kernel": "pa_swap_blocks (copy_pool_blocks_kernel), event-timed, out and in",
+            "bound": "link",
+            "achieved": round(2 * moved / (step_ms * 1e-3) / 1e9, 2),
+            "peak": LINK_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(2 * moved / (step_ms * 1e-3) / 1e9 / LINK_PEAK_GBPS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": int(moved),
+        },
+    }
     print(json.dumps(result), flush=True)
 
 
