@@ -664,3 +664,220 @@ def pin_swap(orc):
 
 
 ALL_PINS.append(pin_swap)
+
+
+# ---------------------------------------------------------------------------
+# Block manager model pins (take the oracle.block_manager module)
+# ---------------------------------------------------------------------------
+
+
+def _bm_check_invariants(bm, B):
+    """Reference counts equal table references; free, evictable and held
+    blocks partition the pool; every table holds ceil(len / B) blocks; every
+    cached block is full and holds the tokens its key names."""
+    refs = [0] * bm.num_blocks
+    for s, t in bm.tables.items():
+        assert len(t) == -(-bm.lens[s] // B), (s, len(t), bm.lens[s])
+        for b in t:
+            refs[b] += 1
+    assert refs == bm.ref
+    free, ev = set(bm.free), set(bm.evictable)
+    held = {b for b in range(bm.num_blocks) if bm.ref[b] > 0}
+    assert len(free) == len(bm.free) and not (free & ev) and not (free & held) and not (ev & held)
+    assert free | ev | held == set(range(bm.num_blocks))
+    for key, b in bm.cache.items():
+        assert bm.key_of[b] == key and len(key[1]) == B
+
+
+def pin_bm_digest_flowchart(obm):
+    """The digest's flowchart: with B = 16 and blocks handed out as P3, P7,
+    P1, P5, P9, sequence 1 (33 tokens) gets P3, P7, P1; sequence 2, whose
+    prompt shares sequence 1's first 16 tokens, reuses the shared P3 and gets
+    P5 for its 17th token.  A write into a shared, partly filled block copies
+    it first (writer takes the copy): P3 -> P9 in a pool where P9 is next."""
+    g = _golden("digest_flowchart_layout.json")
+    B, N = g["block_size"], g["pool_blocks"]
+    order = [3, 7, 1, 5, 9] + [b for b in range(N) if b not in (3, 7, 1, 5, 9)]
+    bm = obm.BlockManagerModel(N, B, order, prefix_cache=True)
+    p1 = list(range(100, 133))
+    assert bm.add_seq(1, p1) == 0
+    bm.append(1, 33, p1)
+    p2 = p1[:16] + [999]
+    assert bm.add_seq(2, p2) == 16
+    bm.append(2, 1, p2[16:])
+    assert bm.table(1) == g["tables"]["seq1"] and bm.table(2) == g["tables"]["seq2"]
+    assert bm.ref[g["shared_block"]] == 2
+    _bm_check_invariants(bm, B)
+    cow = obm.BlockManagerModel(N, B, [g["cow"]["src"], g["cow"]["dst"]] +
+                                [b for b in range(N) if b not in (g["cow"]["src"], g["cow"]["dst"])])
+    cow.add_seq(1)
+    cow.append(1, 10)
+    cow.fork(1, 2)
+    slots, pairs = cow.append(2, 1)
+    assert pairs == [(g["cow"]["src"], g["cow"]["dst"])]
+    assert cow.table(2) == [g["cow"]["dst"]] and cow.table(1) == [g["cow"]["src"]]
+    assert slots == [g["cow"]["dst"] * B + 10] and cow.ref[g["cow"]["src"]] == 1
+    _bm_check_invariants(cow, B)
+
+
+def pin_bm_matches_harness(obm):
+    """Random append / fork / free traces give the same tables, slots and
+    copy pairs as the input generators' own allocator (written separately)."""
+    from workloads.blockpool import BlockPool, SeqBlocks, append_tokens, fork
+
+    for seed in range(6):
+        rng = np.random.default_rng(300 + seed)
+        N, B = 96, int(rng.choice([1, 2, 4, 8]))
+        order = rng.permutation(N)
+        bm = obm.BlockManagerModel(N, B, order)
+        pool = BlockPool(N, B, order)
+        live = {}  # seq id -> harness SeqBlocks
+        nxt = 0
+        for _ in range(60):
+            op = rng.integers(0, 4)
+            if op == 0 or not live:
+                n = int(rng.integers(0, 3 * B + 2))
+                if pool.used * 1.0 + n / B + 2 > N * 0.6:
+                    continue
+                live[nxt] = SeqBlocks()
+                bm.add_seq(nxt)
+                sl_h, pr_h = append_tokens(pool, live[nxt], n)
+                sl_m, pr_m = bm.append(nxt, n)
+                assert (sl_h, pr_h) == (sl_m, pr_m)
+                nxt += 1
+            elif op == 1:
+                s = int(rng.choice(list(live)))
+                n = int(rng.integers(1, B + 2))
+                if pool.used + n // B + 2 > N * 0.8:
+                    continue
+                sl_h, pr_h = append_tokens(pool, live[s], n)
+                sl_m, pr_m = bm.append(s, n)
+                assert (sl_h, [tuple(p) for p in pr_h]) == (sl_m, pr_m)
+            elif op == 2:
+                s = int(rng.choice(list(live)))
+                k = int(rng.integers(1, 4))
+                kids = fork(pool, live.pop(s), k)
+                for kid in kids:
+                    bm.fork(s, nxt)
+                    live[nxt] = kid
+                    nxt += 1
+                bm.free_seq(s)
+            else:
+                s = int(rng.choice(list(live)))
+                for b in live.pop(s).table:
+                    pool.release(b)
+                bm.free_seq(s)
+            for s, sb in live.items():
+                assert bm.table(s) == sb.table and bm.length(s) == sb.length
+            assert list(bm.free) == list(pool.free)
+            _bm_check_invariants(bm, B)
+
+
+def pin_bm_prefix_cache(obm):
+    """Hand-derived prefix-cache scenario (B = 4, blocks handed out 0, 1, 2, ...)."""
+    bm = obm.BlockManagerModel(12, 4, prefix_cache=True)
+    A = list(range(1, 11))                       # 10 tokens: blocks 0, 1 full, 2 partial
+    assert bm.add_seq(0, A) == 0
+    bm.append(0, 10, A)
+    assert bm.table(0) == [0, 1, 2]
+    Bp = list(range(1, 9)) + [50, 51]            # shares A's first two blocks
+    assert bm.add_seq(1, Bp) == 8
+    bm.append(1, 2, Bp[8:])
+    assert bm.table(1) == [0, 1, 3] and bm.ref[0] == 2 and bm.ref[1] == 2
+    C = [1, 2, 3, 4, 99, 98, 97, 96, 95]         # shares one block only
+    assert bm.add_seq(2, C) == 4
+    bm.append(2, 5, C[4:])
+    assert bm.table(2) == [0, 4, 5]
+    D = list(range(1, 9))                        # exactly two cached blocks: reuse one, compute the rest
+    assert bm.add_seq(3, D) == 4
+    bm.append(3, 4, D[4:])
+    assert bm.table(3) == [0, 6]                 # block 6 now duplicates block 1's content, uncached
+    Wrong = [9, 9, 9, 9, 5, 6, 7, 8, 1]          # second block matches A's tokens but the prefix differs
+    assert bm.add_seq(4, Wrong) == 0
+    for s in (0, 1, 2, 3, 4):
+        bm.free_seq(s)
+    _bm_check_invariants(bm, 4)
+    # Cached blocks survive their sequences and are reused from the evictable set.
+    E = list(range(1, 9)) + [7]
+    assert bm.add_seq(5, E) == 8
+    assert bm.table(5) == [0, 1] and bm.ref[0] == 1 and 0 not in bm.evictable
+    # Pool pressure: plain free blocks first, then the least recently released cached block.
+    plain = len(bm.free)
+    bm.add_seq(6)
+    bm.append(6, 4 * plain, list(range(1000, 1000 + 4 * plain)))  # uses every plain free block
+    assert not bm.free
+    lru = next(iter(bm.evictable))
+    key = bm.key_of[lru]
+    bm.append(6, 1, [2000])
+    assert bm.table(6)[-1] == lru and key not in bm.cache and lru not in bm.key_of
+    _bm_check_invariants(bm, 4)
+
+
+def pin_bm_out_of_blocks(obm):
+    """An append needing more blocks than are free changes nothing; one
+    needing exactly the free blocks succeeds."""
+    bm = obm.BlockManagerModel(5, 4)
+    bm.add_seq(0)
+    bm.append(0, 6)                              # 2 blocks, last partly filled
+    bm.fork(0, 1)
+    need = bm.blocks_needed(1, 1 + 4 * 3)        # copy of the shared last block + 3 new
+    assert need == 4 and bm.num_free() == 3
+    snap = (list(bm.free), list(bm.ref), bm.table(0), bm.table(1), bm.length(1))
+    try:
+        bm.append(1, 1 + 4 * 3)
+        raise AssertionError("append beyond the pool succeeded")
+    except obm.OutOfBlocks:
+        pass
+    assert snap == (list(bm.free), list(bm.ref), bm.table(0), bm.table(1), bm.length(1))
+    slots, pairs = bm.append(1, 1 + 4 * 2)       # exactly 3 blocks
+    assert len(pairs) == 1 and bm.num_free() == 0
+    _bm_check_invariants(bm, 4)
+
+
+def pin_bm_swap(obm):
+    """Swapping a sequence out and back in, with the data moved by the
+    oracle's swap_blocks along the returned pairs, leaves its decode
+    unchanged; the host pool is empty again afterwards."""
+    import oracle
+
+    rng = np.random.default_rng(33)
+    N, B, H, D = 12, 4, 2, 8
+    gpu = obm.BlockManagerModel(N, B, rng.permutation(N))
+    host = obm.BlockManagerModel(6, B)
+    for s, n in ((0, 7), (1, 9)):
+        gpu.add_seq(s)
+        gpu.append(s, n)
+    kc = wl.canary_fill((N, H, B, D), "f32")
+    vc = wl.canary_fill((N, H, B, D), "f32")
+    for s in (0, 1):
+        for t in range(gpu.length(s)):
+            b = gpu.table(s)[t // B]
+            kc[b, :, t % B, :] = rng.standard_normal((H, D))
+            vc[b, :, t % B, :] = rng.standard_normal((H, D))
+    q = rng.standard_normal((2, H, D)).astype(np.float32)
+    rows, lens = gpu.block_tables([0, 1], 4)
+    before = oracle.paged_decode(q, kc, vc, np.array(rows, np.int32), np.array(lens, np.int32), 0.3, "f32")
+    hk = wl.canary_fill((6, H, B, D), "f32")
+    hv = wl.canary_fill((6, H, B, D), "f32")
+    out_pairs = gpu.swap_out(1, host)
+    assert [p[0] for p in out_pairs] == rows[1][:3] and 1 not in gpu.tables and host.length(1) == 9
+    hk, hv = oracle.swap_blocks(kc, vc, hk, hv, out_pairs)
+    gpu.add_seq(2)
+    gpu.append(2, 9)                             # reuses the freed device blocks
+    in_pairs = gpu.swap_in(1, host)
+    assert host.num_free() == 6 and gpu.length(1) == 9
+    kc, vc = oracle.swap_blocks(hk, hv, kc, vc, in_pairs)
+    rows2, lens2 = gpu.block_tables([0, 1], 4)
+    after = oracle.paged_decode(q, kc, vc, np.array(rows2, np.int32), np.array(lens2, np.int32), 0.3, "f32")
+    assert np.array_equal(before, after)
+    _bm_check_invariants(gpu, B)
+    _bm_check_invariants(host, B)
+
+
+BM_PINS = [
+    pin_bm_digest_flowchart,
+    pin_bm_matches_harness,
+    pin_bm_prefix_cache,
+    pin_bm_out_of_blocks,
+    pin_bm_swap,
+]

@@ -233,3 +233,104 @@ def test_prefill_mutant_is_caught(name, monkeypatch):
         except Exception as e:
             failures.append((pin.__name__, type(e).__name__))
     assert failures, f"no pin caught the planted mistake: {name}"
+
+
+# ---------------------------------------------------------------------------
+# Block manager model mutants (checked against oracle_pins.BM_PINS)
+# ---------------------------------------------------------------------------
+
+import oracle.block_manager as obm  # noqa: E402
+from oracle_pins import BM_PINS  # noqa: E402
+
+_BMM = obm.BlockManagerModel
+_real_bm = {n: getattr(_BMM, n) for n in ("_allocate", "_release", "append", "add_seq", "_block_key", "swap_out")}
+
+
+def _bm_alloc_lifo(self):
+    if self.free:
+        self.free.rotate(1)  # take the most recently freed block instead of the oldest
+    return _real_bm["_allocate"](self)
+
+
+def _bm_release_leaks(self, b):
+    self.ref[b] -= 1  # never returns to the free list
+
+
+def _bm_append_no_cow(self, seq, n, tokens=None):
+    saved = self.ref
+    self.ref = _NoShare(saved)
+    try:
+        return _real_bm["append"](self, seq, n, tokens)
+    finally:
+        self.ref = saved
+
+
+class _NoShare(list):
+    """Reference counts that read as 1 for the write path (no copy-on-write)."""
+
+    def __init__(self, base):
+        super().__init__(base)
+        self.base = base
+
+    def __getitem__(self, i):
+        v = self.base[i]
+        return min(v, 1) if isinstance(i, int) else v
+
+    def __setitem__(self, i, v):
+        self.base[i] = v
+        super().__setitem__(i, v)
+
+
+def _bm_add_whole_prompt(self, seq, prompt=None):
+    """Prefix reuse may cover the entire prompt (nothing left to compute)."""
+    if prompt:
+        prompt = list(prompt) + [object()]  # one phantom token: the last real block becomes reusable
+    n = _real_bm["add_seq"](self, seq, prompt)
+    self.tokens[seq] = [t for t in self.tokens[seq] if not isinstance(t, object) or isinstance(t, int)]
+    return n
+
+
+def _bm_key_no_prefix(self, seq, j):
+    return ((), tuple(self.tokens[seq][j * self.B:(j + 1) * self.B]))
+
+
+def _bm_swap_reversed(self, seq, host):
+    """Pairs send the device blocks to the host blocks in reverse order while
+    the host table keeps the allocation order (data and table disagree)."""
+    pairs = _real_bm["swap_out"](self, seq, host)
+    hosts = [h for _, h in pairs][::-1]
+    return [(d, h) for (d, _), h in zip(pairs, hosts)]
+
+
+def _bm_append_unchecked(self, seq, n, tokens=None):
+    self.num_free = lambda: 1 << 30  # skips the up-front capacity check
+    try:
+        return _real_bm["append"](self, seq, n, tokens)
+    except obm.OutOfBlocks:
+        raise
+    finally:
+        del self.num_free
+
+
+BM_MUTANTS = {
+    "free list taken last-in first-out": ("_allocate", _bm_alloc_lifo),
+    "released blocks never freed": ("_release", _bm_release_leaks),
+    "no copy-on-write of a shared block": ("append", _bm_append_no_cow),
+    "prefix reuse covers the whole prompt": ("add_seq", _bm_add_whole_prompt),
+    "prefix identity ignores the blocks before": ("_block_key", _bm_key_no_prefix),
+    "swap-out pairs disagree with the host table": ("swap_out", _bm_swap_reversed),
+    "append without the capacity check": ("append", _bm_append_unchecked),
+}
+
+
+@pytest.mark.parametrize("name", list(BM_MUTANTS))
+def test_block_manager_mutant_is_caught(name, monkeypatch):
+    attr, fn = BM_MUTANTS[name]
+    monkeypatch.setattr(_BMM, attr, fn)
+    failures = []
+    for pin in BM_PINS:
+        try:
+            pin(obm)
+        except Exception as e:
+            failures.append((pin.__name__, type(e).__name__))
+    assert failures, f"no pin caught the planted mistake: {name}"

@@ -3,8 +3,9 @@ import pytest
 
 import oracle
 import oracle.paged_attention as opa
+import oracle.block_manager as obm
 import oracle.prefill as opr
-from oracle_pins import ALL_PINS, PREFILL_PINS
+from oracle_pins import ALL_PINS, BM_PINS, PREFILL_PINS
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=[p.__name__ for p in ALL_PINS])
@@ -15,6 +16,11 @@ def test_oracle_pin(pin):
 @pytest.mark.parametrize("pin", PREFILL_PINS, ids=[p.__name__ for p in PREFILL_PINS])
 def test_prefill_oracle_pin(pin):
     pin(opr)
+
+
+@pytest.mark.parametrize("pin", BM_PINS, ids=[p.__name__ for p in BM_PINS])
+def test_block_manager_model_pin(pin):
+    pin(obm)
 
 
 def test_oracle_imports_only_numpy():
