@@ -60,7 +60,8 @@ typedef enum {
     PA_ERR_NULL = 1,        /* a required pointer is NULL */
     PA_ERR_UNSUPPORTED = 2, /* dtype, head_dim or block_size outside the built kernels */
     PA_ERR_INVALID = 3,     /* sizes, alignment, scale or workspace out of range */
-    PA_ERR_HIP = 4          /* the HIP runtime rejected a launch */
+    PA_ERR_HIP = 4,         /* the HIP runtime rejected a launch */
+    PA_ERR_OUT_OF_BLOCKS = 5 /* block manager: not enough free blocks (nothing changed) */
 } pa_status;
 
 /* pa_decode / pa_append_decode flags. */

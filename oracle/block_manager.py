@@ -28,8 +28,10 @@ implements the same ones, so the two agree block id for block id):
   one copy when the partly filled last block is shared) are available, and
   changes nothing when they are not;
 * a block is identified for prefix caching once it is full, by its tokens
-  and the identity of the block before it (the whole prefix up to it);
-  the first full block with a given identity is the cached one;
+  and the identity of the sequence's block before it, i.e. by the whole
+  token prefix up to its end (whether or not that earlier block is the
+  cached one); the first full block with a given identity is the cached
+  one;
 * a new sequence reuses the cached blocks of its prompt's longest cached
   prefix of whole blocks, but always leaves at least one prompt token to be
   computed;
@@ -64,6 +66,7 @@ class BlockManagerModel:
         self.tables: Dict[int, List[int]] = {}
         self.lens: Dict[int, int] = {}
         self.tokens: Dict[int, List[int]] = {}
+        self.keys: Dict[int, List[tuple]] = {}  # per sequence: identity of each full block
         self.prefix_cache = prefix_cache
         self.cache: Dict[tuple, int] = {}      # prefix identity -> cached block
         self.key_of: Dict[int, tuple] = {}     # cached block -> its prefix identity
@@ -95,7 +98,7 @@ class BlockManagerModel:
                 self.free.append(b)
 
     def _block_key(self, seq: int, j: int) -> tuple:
-        prev = self.key_of.get(self.tables[seq][j - 1]) if j else ()
+        prev = self.keys[seq][j - 1] if j else ()
         toks = tuple(self.tokens[seq][j * self.B:(j + 1) * self.B])
         return (prev, toks)
 
@@ -106,18 +109,20 @@ class BlockManagerModel:
         least one token).  Returns the number of prompt tokens covered."""
         if seq in self.tables:
             raise KeyError(f"sequence {seq} exists")
-        self.tables[seq], self.lens[seq], self.tokens[seq] = [], 0, []
+        self.tables[seq], self.lens[seq], self.tokens[seq], self.keys[seq] = [], 0, [], []
         if not (self.prefix_cache and prompt):
             return 0
         prompt = [int(t) for t in prompt]
         prev: tuple = ()
         hit: List[int] = []
+        keys: List[tuple] = []
         for j in range((len(prompt) - 1) // self.B):  # leave >= 1 token to compute
             key = (prev, tuple(prompt[j * self.B:(j + 1) * self.B]))
             b = self.cache.get(key)
             if b is None:
                 break
             hit.append(b)
+            keys.append(key)
             prev = key
         for b in hit:
             if self.ref[b] == 0:
@@ -127,6 +132,7 @@ class BlockManagerModel:
         self.tables[seq] = hit
         self.lens[seq] = n
         self.tokens[seq] = prompt[:n]
+        self.keys[seq] = keys
         return n
 
     def blocks_needed(self, seq: int, n: int) -> int:
@@ -161,6 +167,7 @@ class BlockManagerModel:
                 self.tokens[seq].append(int(tokens[i]))
                 if off == B - 1:
                     key = self._block_key(seq, j)
+                    self.keys[seq].append(key)
                     if key not in self.cache:
                         self.cache[key] = table[j]
                         self.key_of[table[j]] = key
@@ -175,12 +182,14 @@ class BlockManagerModel:
         self.tables[child] = list(self.tables[parent])
         self.lens[child] = self.lens[parent]
         self.tokens[child] = list(self.tokens[parent])
+        self.keys[child] = list(self.keys[parent])
 
     def free_seq(self, seq: int) -> None:
         for b in self.tables.pop(seq):
             self._release(b)
         del self.lens[seq]
         del self.tokens[seq]
+        del self.keys[seq]
 
     # ----------------------------------------------------------- swapping
     def swap_out(self, seq: int, host: "BlockManagerModel") -> List[Tuple[int, int]]:
@@ -189,6 +198,7 @@ class BlockManagerModel:
         if host.num_free() < len(table):
             raise OutOfBlocks("host swap space full")
         host.tables[seq], host.lens[seq], host.tokens[seq] = [], self.lens[seq], list(self.tokens[seq])
+        host.keys[seq] = list(self.keys[seq])
         pairs = []
         for b in table:
             hb = host._allocate()
@@ -203,6 +213,7 @@ class BlockManagerModel:
         if self.num_free() < len(htable):
             raise OutOfBlocks("not enough device blocks to swap in")
         self.tables[seq], self.lens[seq], self.tokens[seq] = [], host.lens[seq], list(host.tokens[seq])
+        self.keys[seq] = list(host.keys[seq])
         pairs = []
         for hb in htable:
             b = self._allocate()

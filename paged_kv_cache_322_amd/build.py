@@ -23,7 +23,10 @@ OBJDIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
 SOURCES = ["pa_decode.hip", "pa_decode_f32.hip", "pa_decode_f16.hip", "pa_decode_bf16.hip", "pa_prefill.hip",
-           "pa_cache.hip", "pa_api.hip"]
+           "pa_cache.hip", "pa_api.hip", "pa_block_manager.cpp"]
+
+# Host-only C++ (the block manager): built by the host compiler.
+CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Werror", f"-I{os.path.join(ROOT, 'include')}"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",
@@ -54,7 +57,10 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(src: str) -> str:
         obj = os.path.join(OBJDIR, src + ".o")
-        cmd = [hipcc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        if src.endswith(".cpp"):
+            cmd = [shutil.which("g++") or "g++", *CXX_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        else:
+            cmd = [hipcc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)

@@ -62,6 +62,7 @@ const char* pa_status_string(int status) {
         case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: dtype, head_dim or block_size not built";
         case PA_ERR_INVALID: return "PA_ERR_INVALID: size, alignment, scale or workspace out of range";
         case PA_ERR_HIP: return "PA_ERR_HIP: the HIP runtime rejected a launch";
+        case PA_ERR_OUT_OF_BLOCKS: return "PA_ERR_OUT_OF_BLOCKS: not enough free KV blocks";
         default: return "PA_ERR_UNKNOWN";
     }
 }

@@ -794,6 +794,17 @@ def pin_bm_prefix_cache(obm):
     assert bm.table(3) == [0, 6]                 # block 6 now duplicates block 1's content, uncached
     Wrong = [9, 9, 9, 9, 5, 6, 7, 8, 1]          # second block matches A's tokens but the prefix differs
     assert bm.add_seq(4, Wrong) == 0
+    # Sequence 3's block 6 duplicates cached block 1, so it is not the cached
+    # one; a block filled after it is still identified by the whole prefix:
+    # extend sequence 3 by one block and look it up from a fresh prompt.
+    bm.append(3, 4, [20, 21, 22, 23])             # block 7 = prefix 1..8 + 20..23
+    assert bm.table(3) == [0, 6, 7]
+    F = list(range(1, 9)) + [20, 21, 22, 23, 0]
+    assert bm.add_seq(7, F) == 12 and bm.table(7) == [0, 1, 7]
+    bm.free_seq(7)
+    G = [5, 5, 5, 5, 5, 5, 5, 5, 20, 21, 22, 23, 0]  # same third block, different prefix: no hit past it
+    assert bm.add_seq(8, G) == 0
+    bm.free_seq(8)
     for s in (0, 1, 2, 3, 4):
         bm.free_seq(s)
     _bm_check_invariants(bm, 4)
