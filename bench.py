@@ -54,6 +54,9 @@ WORKLOADS = {
     "prefill-prompts": "llama7b-prompt-prefill: 32 whole prompts, lognormal(median 300, sigma 0.9) lengths in "
                        "[16,2048], H=32, D=128, bf16, B=16",
     "swap": SWAP_WORKLOAD,
+    "block-manager": "block-manager: host bookkeeping of a decode step for config 3's 256 sequences "
+                     "(lognormal(300, 0.9) contexts, B=16) and prefix-cached admission of 256 prompts sharing a "
+                     "512-token system prompt",
 }
 PREFILL_KINDS = {"prefill-llama7b": "llama7b", "prefill-gqa8b": "llama3-8b", "prefill-prompts": "prompts"}
 MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak, vendor figure
@@ -98,6 +101,8 @@ def make_case(cfg, block_size=16):
         return wl.prefill_config(PREFILL_KINDS[cfg])
     if cfg == "swap":
         return wl.config2()
+    if cfg == "block-manager":
+        return None
     return wl.config5(n_append=1)
 
 
@@ -261,6 +266,8 @@ def main():
     import paged_kv_cache_322_amd as pa
 
     dev = torch.device("cuda:0")
+    if args.config == "block-manager":
+        return bench_block_manager(args)
     log(f"building workload config {args.config}")
     case = make_case(args.config, args.block_size)
     if args.config in PREFILL_KINDS:
@@ -629,6 +636,95 @@ def bench_prefill(args, case, pa, torch, dev):
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample of the batch")
         result["cpu_baseline"] = cpu_baseline_prefill(case, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def bench_block_manager(args):
+    """Host-side cost of the library's C++ block manager, against the Python
+    reference model doing the same operations.
+
+    Decode step: config 3's 256 sequences (contexts lognormal(300, 0.9) in
+    [16, 2048], B = 16) each take one token (pa_bm_append_batch: slots and
+    copy pairs), then the step's block tables are exported
+    (pa_bm_block_tables).  Admission: 256 prompts of a 512-token shared system
+    prompt plus 64 own tokens enter with prefix caching (32 whole blocks
+    reused each) and reserve their own tokens."""
+    from paged_kv_cache_322_amd.block_manager import BlockManager
+    from oracle.block_manager import BlockManagerModel
+    import workloads as wl
+
+    lens = wl.config3_lengths()
+    S, B = len(lens), 16
+    steps = max(20, args.steps)
+    grow = -(-(steps + B) // B)  # blocks a sequence can gain over the timed steps
+    N = int(sum(-(-int(n) // B) for n in lens) + grow * S + 64)
+    order = np.random.default_rng(322).permutation(N)
+    width = int(max(-(-int(n) // B) for n in lens)) + grow
+
+    def setup(cls):
+        bm = cls(N, B, order)
+        for s, n in enumerate(lens):
+            bm.add_seq(s)
+            bm.append(s, int(n))
+        return bm
+
+    cpp, model = setup(BlockManager), setup(BlockManagerModel)
+    seqs = np.arange(S, dtype=np.int64)
+
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        cpp.append_batch(seqs)
+        cpp.block_tables_array(seqs, width)
+    cpp_step_us = (time.perf_counter() - t0) / steps * 1e6
+    msteps = max(3, steps // 10)
+    t0 = time.perf_counter()
+    for _ in range(msteps):
+        for s in range(S):
+            model.append(s, 1)
+        model.block_tables(list(range(S)), width)
+    model_step_us = (time.perf_counter() - t0) / msteps * 1e6
+
+    rng = np.random.default_rng(7)
+    system = rng.integers(0, 32000, 512).tolist()
+    prompts = [system + rng.integers(0, 32000, 64).tolist() for _ in range(256)]
+
+    def admit(cls):
+        bm = cls(256 * 40 + 64, B, prefix_cache=True)
+        t0 = time.perf_counter()
+        for i, p in enumerate(prompts):
+            c = bm.add_seq(i, p)
+            bm.append(i, len(p) - c, p[c:])
+        return (time.perf_counter() - t0) / len(prompts) * 1e6, bm
+
+    cpp_admit_us, cbm = admit(BlockManager)
+    model_admit_us, _ = admit(BlockManagerModel)
+    reused = sum(1 for b in range(cbm.num_blocks) if cbm.ref_count(b) == 256)
+    log(f"decode-step bookkeeping: C++ {cpp_step_us:.1f} us, Python model {model_step_us:.1f} us; "
+        f"admission: C++ {cpp_admit_us:.1f} us/prompt, model {model_admit_us:.1f} us/prompt; "
+        f"{reused} blocks shared by all 256 prompts")
+    result = {
+        "metric": "block manager: host microseconds of decode-step bookkeeping (256 sequences)",
+        "value": round(cpp_step_us, 2),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": 0,
+        "ms_per_step": round(cpp_step_us / 1e3, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int64",
+        "data": "synthetic",
+        "config": {"workload": WORKLOADS["block-manager"], "num_seqs": S, "block_size": B, "num_blocks": N,
+                   "table_width": width},
+        "admission_us_per_prompt": round(cpp_admit_us, 2),
+        "prefix_blocks_shared_by_all": reused,
+        "roofline": None,
+        "note": "host-side bookkeeping (no GPU kernel); for scale, config 3's decode kernel takes ~355 us per step",
+        "cpu_baseline": {"value": round(model_step_us, 2), "unit": "us/step", "cores": 1, "kind": "oracle",
+                         "sample": f"the Python reference model on the same decode step ({msteps} steps) and "
+                                   f"admissions ({model_admit_us:.1f} us/prompt)"},
+    }
     print(json.dumps(result), flush=True)
 
 
