@@ -67,7 +67,9 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warmup steps (default 10; 100 for the prefill workloads, about 30 ms: sustained "
+                         "matrix-core load slows the clocks for the first ~15 ms after an idle period)")
     ap.add_argument("--config", default="2", choices=sorted(WORKLOADS))
     ap.add_argument("--partition", type=int, default=0, help="KV partition tokens (0 = library default)")
     ap.add_argument("--block-size", type=int, default=16, help="block size for config 4 (8, 16 or 32)")
@@ -77,7 +79,10 @@ def parse():
     ap.add_argument("--rotate", type=int, default=2, help="independent pool copies cycled across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle baseline")
-    return ap.parse_args()
+    args = ap.parse_args()
+    if args.warmup is None:
+        args.warmup = 100 if args.config in PREFILL_KINDS else 10
+    return args
 
 
 def log(msg):

@@ -266,7 +266,10 @@ extern "C" int pa_prefill(void* out, const void* query, const void* k_cache, con
     const int64_t ids = (static_cast<int64_t>(max_context_len) + block_size - 1) / block_size;
     if (ids > pa::kMaxPrefillIds) return PA_ERR_INVALID;
     if (max_query_len == 0) return PA_OK;
-    if ((static_cast<int64_t>(max_query_len) + 127) / 128 > 65535) return PA_ERR_INVALID;
+    // One workgroup per (sequence, query head, 128-row tile), units padded to a multiple of 8.
+    const int64_t units = (static_cast<int64_t>(num_seqs) * num_kv_heads + 7) / 8 * 8;
+    if (units * (num_heads / num_kv_heads) * ((static_cast<int64_t>(max_query_len) + 127) / 128) > 0x7FFFFFFF)
+        return PA_ERR_INVALID;
 
     pa::PrefillArgs a;
     a.out = out;

@@ -27,23 +27,31 @@
 //     B-operand layout of the second product, so probabilities never move
 //     between lanes: O^T[d][row] += V^T[d][key] . P^T[key][row] on
 //     v_mfma_f32_16x16x32 with the tile's 32 keys as the contraction index.
-//     Lane (c, g) reads D/16 channels of each of its 8 value rows from LDS
-//     (16 lanes cover a row: conflict-free) and one v_perm per register
-//     builds the A operand of each output tile;
-//   * probabilities are split into hi + lo 16-bit parts (truncation), both
-//     accumulated, so the weights keep ~16 bits (the product of two 16-bit
-//     values is exact in the fp32 accumulator);
-//   * online softmax per row in base 2, tile maximum shared across the four
-//     lane groups of a row with two cross-row exchanges; the reference
-//     maximum moves (and the accumulators are rescaled) only when a tile
-//     exceeds it by more than 2^8, so the rescale is rare; the score scale is
-//     one fused multiply-add;
-//   * at most 2 wavefronts per SIMD (launch bound): the compiler then keeps
-//     the accumulators in VGPRs (MFMA with VGPR C/D) instead of shuttling
-//     them through AGPRs;
+//     The V^T operand comes straight out of the row-major V tile through
+//     gfx950's transposing LDS read (ds_read_b64_tr_b16): two per output
+//     tile, no register shuffles;
+//   * fp16 probabilities are one round-to-nearest fp16 operand (relative
+//     error <= 2^-11 each); bf16 ones are split into a truncated hi part and
+//     the remainder, both accumulated, so they keep ~16 bits (the product of
+//     two 16-bit values is exact in the fp32 accumulator);
+//   * online softmax per row in base 2; the tile maximum is shared across
+//     the four lane groups of a row with two gfx950 half-wave / row swaps
+//     (v_permlane32_swap, v_permlane16_swap); the reference maximum moves
+//     (and the accumulators are rescaled) only when a tile exceeds it by more
+//     than 2^8, so the rescale is rare; the score scale is one fused
+//     multiply-add;
+//   * register budget for 3 wavefronts per SIMD (<= 168 VGPRs, 3 workgroups
+//     per CU), accumulators in VGPRs (MFMA with VGPR C/D); LDS rows padded
+//     by 32 bytes;
 //   * causal masking per element; a wavefront skips tiles entirely past its
-//     rows; workgroups are dispatched last query tile first (they have the
-//     most keys).
+//     rows;
+//   * XCD-aware dispatch: the hardware hands workgroups to the 8 XCDs
+//     round-robin by linear id, each XCD with its own L2.  Every workgroup of
+//     one (sequence, K/V head) unit gets a linear id congruent to the unit
+//     mod 8, so the unit's G query heads and query tiles read its K/V through
+//     one L2; in dispatch order the last query tile (most keys) of every
+//     unit comes first, then the second last, and so on, and the G heads of
+//     a unit and tile are adjacent.
 #include <math.h>
 
 #include "pa_decode_mfma.h"  // MfmaOps, vector types
@@ -58,51 +66,84 @@ constexpr int kPfThreads = kPfWaves * kWave;
 constexpr int kPfBlocks = 2;                        // 16-row blocks per wavefront
 constexpr int kPfRows = 16 * kPfBlocks * kPfWaves;  // query rows per workgroup
 constexpr int kPfKeys = 32;                         // keys per tile
+constexpr int kXcds = 8;                            // MI355X: XCDs, each with its own L2
+constexpr int kPfPad = 16;                          // LDS row padding (elements): 32 bytes
 // The running maximum used as the softmax reference moves only when a tile's
 // maximum exceeds it by more than this (log2 units), so the accumulators are
 // rescaled rarely; probabilities stay below 2^8 (no overflow in f16/bf16 or
-// fp32; the hi + lo split keeps their relative precision).
+// fp32).
 constexpr float kPfRescaleSlack = 8.0f;
 
 template <int D>
 struct PfShape {
     static constexpr int KS = D / 32;                 // q.k k-steps
     static constexpr int E = D / 16;                  // channels per lane of a V row = output tiles
-    static constexpr int NW = E / 2;                  // 32-bit words per lane of a V row
-    static constexpr int LD = D + 8;                  // LDS row pitch (elements): 16-byte pad
+    static constexpr int LD = D + kPfPad;             // LDS row pitch (elements)
     static constexpr int CPR = D / 8;                 // 16-byte chunks per row
     static constexpr int CHUNKS = kPfKeys * CPR;      // 16-byte chunks per tile (each of K and V)
     static constexpr int CPT = CHUNKS / kPfThreads;   // chunks per thread per tile
-    static_assert(CHUNKS % kPfThreads == 0, "tile chunks must divide over the workgroup");
+    static_assert(CHUNKS % kPfThreads == 0 && CPR % CPT == 0, "tile chunks must divide over the workgroup");
 };
 
-template <int NW>
-__device__ __forceinline__ void lds_read_words(const uint16_t* p, uint32_t (&w)[NW]) {
-    if constexpr (NW == 2) {
-        const uint2 v = *reinterpret_cast<const uint2*>(p);
-        w[0] = v.x;
-        w[1] = v.y;
-    } else {
-#pragma unroll
-        for (int i = 0; i < NW / 4; ++i) {
-            const uint4 v = reinterpret_cast<const uint4*>(p)[i];
-            w[4 * i + 0] = v.x;
-            w[4 * i + 1] = v.y;
-            w[4 * i + 2] = v.z;
-            w[4 * i + 3] = v.w;
-        }
-    }
+// Maximum over the four lanes c, c + 16, c + 32, c + 48 (the lane groups g
+// holding one score row), with the gfx950 cross-row swaps instead of LDS
+// permutes.  v_permlane32_swap(a, b) exchanges the upper half-wave of a with
+// the lower half-wave of b; applied to two copies of x, the two results hold
+// x of the lower and of the upper half-wave in every lane, so their maximum
+// is the maximum over lanes i and i ^ 32.  v_permlane16_swap does the same
+// for rows of 16 lanes (i and i ^ 16).  (The results are copied to scalars
+// before the bit cast: a bit cast applied directly to an element of the
+// returned pair reads element 0 with this compiler.)
+__device__ __forceinline__ float swap_max(float x, bool rows32) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto r = rows32 ? __builtin_amdgcn_permlane32_swap(u, u, false, false)
+                          : __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const uint32_t r0 = r[0], r1 = r[1];
+    return fmaxf(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
+}
+
+__device__ __forceinline__ float max_over_groups(float x) {
+    return swap_max(swap_max(x, true), false);
+}
+
+// fp16 probabilities go to the matrix cores as one round-to-nearest fp16
+// operand (11 significant bits, relative error <= 2^-11 per probability);
+// bf16 ones as a truncated hi part plus the remainder (8 + 8 bits).
+template <class T>
+constexpr bool kPfSingleP = false;
+template <>
+constexpr bool kPfSingleP<F16> = true;
+
+__device__ __forceinline__ uint32_t pack_f16_rne(float p0, float p1) {
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{p0, p1}), f16x2_t));
+}
+
+constexpr int kPfWavesPerSimd = 3;  // register budget: <= 168 VGPRs, 3 workgroups per CU
+
+// gfx950 transposing LDS read (ds_read_b64_tr_b16).  In each group of 16
+// lanes, lanes 4r .. 4r + 3 each point at 4 consecutive 16-bit elements, the
+// four together a 16-element row segment r (r = 0..3); lane i of the group
+// receives column i of the 4 x 16 block, i.e. element i of segments 0..3.
+// p must be 8-byte aligned and point into LDS.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    typedef __attribute__((address_space(3))) uint16_t lds_u16;
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_u16*)p));
+    return __builtin_bit_cast(u32x2, v);
 }
 
 template <class T, int D>
-__global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(
+__global__ __launch_bounds__(kPfThreads, kPfWavesPerSimd) void prefill_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ query_start, int num_heads,
     int num_kv_heads, int log2_bs, int max_blocks_per_seq, int64_t num_blocks, int max_context_len, int n_qtiles,
-    float qscale) {
+    int num_units, float qscale) {
     using Sh = PfShape<D>;
-    constexpr int KS = Sh::KS, E = Sh::E, NW = Sh::NW, LD = Sh::LD, CPR = Sh::CPR, CPT = Sh::CPT;
+    constexpr int KS = Sh::KS, E = Sh::E, LD = Sh::LD, CPR = Sh::CPR, CPT = Sh::CPT;
     constexpr int RB = kPfBlocks;
     using Ops = MfmaOps<T>;
 
@@ -110,7 +151,20 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(
     __shared__ __align__(16) uint16_t sK[2][kPfKeys][LD];
     __shared__ __align__(16) uint16_t sV[2][kPfKeys][LD];
 
-    const int h = blockIdx.x, s = blockIdx.y, qt = n_qtiles - 1 - static_cast<int>(blockIdx.z);
+    // Linear id -> (query tile, unit, head): unit u = (sequence, K/V head)
+    // runs on XCD u % 8.  Per XCD, ids r8 = lin / 8 run through the query
+    // tiles last first; within a tile, through the XCD's units and, within a
+    // unit, its G query heads.  The grid holds ceil(units / 8) * 8 * G *
+    // n_qtiles workgroups; those of padding units return at once.
+    const int G = num_heads / num_kv_heads;
+    const int lin = static_cast<int>(blockIdx.x);
+    const int xcd = lin % kXcds, r8 = lin / kXcds;
+    const int per_tile = static_cast<int>(gridDim.x) / (kXcds * n_qtiles);  // units per XCD x G
+    const int qt = n_qtiles - 1 - r8 / per_tile;
+    const int unit = ((r8 % per_tile) / G) * kXcds + xcd;
+    if (unit >= num_units) return;
+    const int s = unit / num_kv_heads, hk = unit % num_kv_heads;
+    const int h = hk * G + r8 % G;
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int c = lane & 15, g = lane >> 4;
@@ -137,8 +191,6 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(
     const int last_row = min(r0 + kPfRows, n) - 1;      // last valid row of the workgroup
     const int kv_end = first_pos + last_row + 1;        // keys 0 .. kv_end - 1 are needed (<= ctx)
     const int ntiles = (kv_end + kPfKeys - 1) / kPfKeys;
-    const int G = num_heads / num_kv_heads;
-    const int hk = h / G;
     const int bmask = (1 << log2_bs) - 1;
     const int nids = ((kv_end - 1) >> log2_bs) + 1;
 
@@ -169,33 +221,29 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(
     int bad = 0;
 
     uint4 kreg[CPT], vreg[CPT];
+    // Thread tid moves CPT adjacent 16-byte chunks of one key row: row
+    // tid / (CPR / CPT), chunks CPT * (tid % (CPR / CPT)) + u.
+    const int ld_row = tid / (CPR / CPT), ld_chunk = CPT * (tid % (CPR / CPT));
     auto load_tile = [&](int kt) {
+        // Keys past kv_end (the last tile's tail) re-read key kv_end - 1:
+        // they are masked out of every row, and the value row read is a real
+        // one (finite, as 0 * V must be).
+        const int kp = min(kt * kPfKeys + ld_row, kv_end - 1);
+        const int b = s_ids[kp >> log2_bs];
+        bad |= (b < 0);
+        const uint64_t e = static_cast<uint64_t>(static_cast<uint32_t>(max(b, 0))) * blk_stride + head_off +
+                           static_cast<uint32_t>(kp & bmask) * D + 8 * ld_chunk;
 #pragma unroll
         for (int u = 0; u < CPT; ++u) {
-            const int ci = tid + u * kPfThreads;
-            const int kk = ci / CPR, cc = ci % CPR;
-            const int kp = kt * kPfKeys + kk;
-            if (kp < kv_end) {
-                const int b = s_ids[kp >> log2_bs];
-                bad |= (b < 0);
-                const uint64_t e = static_cast<uint64_t>(static_cast<uint32_t>(max(b, 0))) * blk_stride + head_off +
-                                   static_cast<uint32_t>(kp & bmask) * D + 8 * cc;
-                kreg[u] = load16(kc + e);
-                vreg[u] = load16(vc + e);
-            } else {
-                // Keys past the context: zeros (masked out; V must be finite).
-                kreg[u] = uint4{0u, 0u, 0u, 0u};
-                vreg[u] = uint4{0u, 0u, 0u, 0u};
-            }
+            kreg[u] = load16(kc + e + 8 * u);
+            vreg[u] = load16(vc + e + 8 * u);
         }
     };
     auto store_tile = [&](int buf) {
 #pragma unroll
         for (int u = 0; u < CPT; ++u) {
-            const int ci = tid + u * kPfThreads;
-            const int kk = ci / CPR, cc = ci % CPR;
-            *reinterpret_cast<uint4*>(&sK[buf][kk][8 * cc]) = kreg[u];
-            *reinterpret_cast<uint4*>(&sV[buf][kk][8 * cc]) = vreg[u];
+            *reinterpret_cast<uint4*>(&sK[buf][ld_row][8 * (ld_chunk + u)]) = kreg[u];
+            *reinterpret_cast<uint4*>(&sV[buf][ld_row][8 * (ld_chunk + u)]) = vreg[u];
         }
     };
 
@@ -244,19 +292,27 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(
                 // the block's first row (wave-uniform test).
                 const bool full = k0 + kPfKeys - 1 <= wpos0 + 16 * rb;
                 float raw[8];
-                float mx = -INFINITY;
 #pragma unroll
                 for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        float v = sc[rb][sub][j];
-                        if (!full) v = (k0 + 16 * sub + 4 * g + j <= pos[rb]) ? v : -INFINITY;
-                        raw[4 * sub + j] = v;
-                        mx = fmaxf(mx, v);
-                    }
-                mx = fmaxf(mx, __shfl_xor(mx, 16));
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
-                mx *= sc_mul;  // every row has a valid key here: finite (tile 0 holds key 0)
+                    for (int j = 0; j < 4; ++j) raw[4 * sub + j] = sc[rb][sub][j];
+                if (!full) {
+                    // Diagonal tile: key k0 + 16 sub + 4 g + j is visible to
+                    // this lane's row iff 16 sub + j <= pos - k0 - 4 g.  (The
+                    // empty asm keeps this a branch around the tile instead
+                    // of selects executed on every tile.)
+                    asm volatile("");
+                    const int lim = pos[rb] - k0 - 4 * g;
+#pragma unroll
+                    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            if (16 * sub + j > lim) raw[4 * sub + j] = -INFINITY;
+                }
+                float mx = -INFINITY;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) mx = fmaxf(mx, raw[i]);
+                mx = max_over_groups(mx) * sc_mul;  // every row has a valid key here: finite (tile 0 holds key 0)
                 if (__builtin_amdgcn_ballot_w64(mx > m[rb] + kPfRescaleSlack)) {
                     const float m_new = fmaxf(m[rb], mx);
                     const float alpha = fast_exp2(m[rb] - m_new);  // 0 on the first tile (m = -inf)
@@ -273,29 +329,31 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(
                 }
                 uint32_t ph[4], pl[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) Ops::split(p[2 * i], p[2 * i + 1], ph[i], pl[i]);
+                for (int i = 0; i < 4; ++i) {
+                    if constexpr (kPfSingleP<T>)
+                        ph[i] = pack_f16_rne(p[2 * i], p[2 * i + 1]);
+                    else
+                        Ops::split(p[2 * i], p[2 * i + 1], ph[i], pl[i]);
+                }
                 bh[rb] = u32x4{ph[0], ph[1], ph[2], ph[3]};
-                bl[rb] = u32x4{pl[0], pl[1], pl[2], pl[3]};
+                if constexpr (!kPfSingleP<T>) bl[rb] = u32x4{pl[0], pl[1], pl[2], pl[3]};
             }
 
-            // Value rows of keys 16 sub + 4 g + j, channels E c .. E c + E - 1.
-            uint32_t vr[8][NW];
-#pragma unroll
-            for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) lds_read_words<NW>(&sV[buf][16 * sub + 4 * g + j][E * c], vr[4 * sub + j]);
+            // A operand of output tile t (channels 16 t .. 16 t + 15): lane
+            // (c, g) needs channel 16 t + c of keys 4 g + j and 16 + 4 g + j
+            // (j = 0..3, the contraction order of the probabilities); two
+            // transposing reads, lanes 4 r + q of a group pointing at key
+            // row 4 g + r (+ 16), channels 16 t + 4 q .. 16 t + 4 q + 3.
+            const int tr_row = 4 * g + (c >> 2), tr_col = 4 * (c & 3);
 #pragma unroll
             for (int t = 0; t < E; ++t) {
-                const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
-                const int w = t / 2;
-                const u32x4 a = u32x4{__builtin_amdgcn_perm(vr[1][w], vr[0][w], sel),
-                                      __builtin_amdgcn_perm(vr[3][w], vr[2][w], sel),
-                                      __builtin_amdgcn_perm(vr[5][w], vr[4][w], sel),
-                                      __builtin_amdgcn_perm(vr[7][w], vr[6][w], sel)};
+                const u32x2 lo4 = lds_read_tr16(&sV[buf][tr_row][16 * t + tr_col]);
+                const u32x2 hi4 = lds_read_tr16(&sV[buf][16 + tr_row][16 * t + tr_col]);
+                const u32x4 a = u32x4{lo4.x, lo4.y, hi4.x, hi4.y};
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb) {
                     acc[rb][t] = Ops::qk(a, bh[rb], acc[rb][t]);
-                    acc[rb][t] = Ops::qk(a, bl[rb], acc[rb][t]);
+                    if constexpr (!kPfSingleP<T>) acc[rb][t] = Ops::qk(a, bl[rb], acc[rb][t]);
                 }
             }
         }
@@ -304,7 +362,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(
     }
     bad = __syncthreads_or(bad);
 
-    // Lane (c, g) holds row wr0 + 16 rb + c, channels D/4 g .. D/4 g + D/4 - 1.
+    // Lane (c, g) holds row wr0 + 16 rb + c: acc[rb][t][j] is channel
+    // 16 t + 4 g + j (transposing reads) or D/4 g + E j + t (row reads).
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         float lt = l[rb];
@@ -313,19 +372,15 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(
         const int row = wr0 + 16 * rb + c;
         if (row < n) {
             const float inv = bad ? __builtin_nanf("") : 1.0f / lt;
-            uint16_t* op = out + (static_cast<int64_t>(q0 + row) * num_heads + h) * D + (D / 4) * g;
-            uint32_t packed[D / 8];
+            uint16_t* op = out + (static_cast<int64_t>(q0 + row) * num_heads + h) * D + 4 * g;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int t = 0; t < E; ++t) {
+                uint32_t w[4];
 #pragma unroll
-                for (int t = 0; t < E; t += 2) {
-                    const uint32_t lo = narrow<T>(acc[rb][t][j] * inv), hi = narrow<T>(acc[rb][t + 1][j] * inv);
-                    packed[(E * j + t) / 2] = lo | (hi << 16);
-                }
-#pragma unroll
-            for (int i = 0; i < D / 32; ++i)
-                reinterpret_cast<uint4*>(op)[i] =
-                    uint4{packed[4 * i + 0], packed[4 * i + 1], packed[4 * i + 2], packed[4 * i + 3]};
+                for (int j = 0; j < 4; ++j) w[j] = narrow<T>(acc[rb][t][j] * inv);
+                const uint32_t w0 = w[0] | (w[1] << 16), w1 = w[2] | (w[3] << 16);
+                *reinterpret_cast<uint2*>(op + 16 * t) = uint2{w0, w1};
+            }
         }
     }
 }
@@ -335,13 +390,16 @@ hipError_t launch_prefill_t(const PrefillArgs& a) {
     const int log2_bs = __builtin_ctz(static_cast<unsigned>(a.block_size));
     const float qscale = a.scale * 1.4426950408889634f;  // log2(e)
     const int n_qtiles = (a.max_query_len + kPfRows - 1) / kPfRows;
-    dim3 grid(a.num_heads, a.num_seqs, n_qtiles);
+    const int num_units = a.num_seqs * a.num_kv_heads;
+    const int64_t items = static_cast<int64_t>(a.num_heads / a.num_kv_heads) * n_qtiles;
+    const int64_t groups = (num_units + kXcds - 1) / kXcds;
+    dim3 grid(static_cast<unsigned>(groups * kXcds * items));
     const size_t lds = static_cast<size_t>(a.staged_ids) * sizeof(int);
     hipLaunchKernelGGL((prefill_kernel<T, D>), grid, dim3(kPfThreads), lds, a.stream, static_cast<uint16_t*>(a.out),
                        static_cast<const uint16_t*>(a.query), static_cast<const uint16_t*>(a.k_cache),
                        static_cast<const uint16_t*>(a.v_cache), a.block_tables, a.context_lens, a.query_start,
                        a.num_heads, a.num_kv_heads, log2_bs, a.max_blocks_per_seq, a.num_blocks, a.max_context_len,
-                       n_qtiles, qscale);
+                       n_qtiles, num_units, qscale);
     return hipGetLastError();
 }
 

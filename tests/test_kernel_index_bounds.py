@@ -239,8 +239,11 @@ def check_prefill_bounds(case, max_query_len=None):
     """Grid (H, S, ceil(max_query_len / 128)); wavefront w of a workgroup owns
     chunk rows r0 + 32 w + 16 rb + c (rb = 0, 1); query loads read row min(row, n - 1), channels
     32 ks + 8 g .. +7; block ids of keys 0 .. kv_end - 1 are staged; tile
-    loads read key kp < kv_end at chunk 8 cc of its row; LDS reads stay in
-    the [2][32][D + 8] tiles; output rows < n, channels D/4 g .. +D/4."""
+    loads read key min(kp, kv_end - 1), CPT adjacent 16-byte chunks of one
+    row per thread; LDS reads stay in
+    the [2][32][D + 16] tiles (K rows 16 sub + c at 32 ks + 8 g .. +7;
+    transposing V reads at rows 4 g + c // 4 (+ 16), channels 16 t + 4 (c % 4)
+    .. +3, 8-byte aligned); output rows < n, channels 16 t + 4 g .. +3."""
     T, H, D = case.q.shape
     N, Hk, B, _ = case.k_cache.shape
     S = case.num_seqs
@@ -259,8 +262,14 @@ def check_prefill_bounds(case, max_query_len=None):
     G = H // Hk
     c = np.arange(16)
     g = np.arange(4)
-    # Channel extents inside a row.
-    assert (32 * (KS - 1) + 8 * g.max() + 8) <= D and E * c.max() + E <= D
+    # Channel extents inside a row (K operand reads, transposing V reads,
+    # output writes), and the 8-byte alignment of the transposing reads.
+    LD = D + 16
+    assert (32 * (KS - 1) + 8 * g.max() + 8) <= D
+    tr_cols = 16 * (E - 1) + 4 * (c % 4)
+    assert tr_cols.max() + 4 <= D and (16 + 4 * g.max() + c.max() // 4) < PF_KEYS
+    assert (LD * 2) % 8 == 0 and all(((2 * (16 * t + 4 * (c % 4))) % 8 == 0).all() for t in range(E))
+    assert 16 * (E - 1) + 4 * g.max() + 4 <= D
     cache_elems = N * Hk * B * D
     for s in range(S):
         n, ctx = int(n_all[s]), int(case.context_lens[s])
@@ -281,24 +290,45 @@ def check_prefill_bounds(case, max_query_len=None):
             assert int(qs[s]) + rows.max() < T
             # tile loads
             tid = np.arange(PF_THREADS)
+            assert CPR % cpt == 0
+            ld_row, ld_chunk = tid // (CPR // cpt), cpt * (tid % (CPR // cpt))
+            assert ld_row.max() < PF_KEYS and ld_chunk.max() + cpt <= CPR
+            # every (key row, chunk) of a tile is moved exactly once
+            assert len({(r, c_ + u) for r, c_ in zip(ld_row, ld_chunk) for u in range(cpt)}) == PF_KEYS * CPR
             for kt in range(ntiles):
+                kp = np.minimum(kt * PF_KEYS + ld_row, kv_end - 1)  # tail keys re-read the last one
+                idx = kp // B
+                assert idx.min() >= 0 and idx.max() < nids
+                b = case.block_tables[s, idx]
+                b = np.where((b >= 0) & (b < N), b, 0).astype(np.int64)
                 for u in range(cpt):
-                    ci = tid + u * PF_THREADS
-                    kk, cc = ci // CPR, ci % CPR
-                    assert kk.max() < PF_KEYS
-                    kp = kt * PF_KEYS + kk
-                    live = kp < kv_end
-                    idx = kp[live] // B
-                    assert idx.size == 0 or idx.max() < nids
-                    b = case.block_tables[s, idx]
-                    b = np.where((b >= 0) & (b < N), b, 0).astype(np.int64)
-                    e = b * Hk * B * D + (Hk - 1) * B * D + (kp[live] % B) * D + 8 * cc[live]
-                    assert e.size == 0 or (e.min() >= 0 and e.max() + 8 <= cache_elems)
+                    e = b * Hk * B * D + (Hk - 1) * B * D + (kp % B) * D + 8 * (ld_chunk + u)
+                    assert e.min() >= 0 and e.max() + 8 <= cache_elems
             # LDS rows read by the compute: keys 16 sub + c and 16 sub + 4 g + j < 32
             assert 16 + 15 < PF_KEYS and 16 + 4 * 3 + 3 < PF_KEYS
         # output rows
         assert int(qs[s]) + n - 1 < T
     assert (H - 1) // G < Hk
+    # XCD-aware 1-D grid: linear id -> (query tile, unit, head) covers every
+    # (sequence, head, query tile) exactly once; padding units exit.
+    units = S * Hk
+    groups = -(-units // 8)
+    grid = groups * 8 * G * n_qt
+    assert grid <= 0x7FFFFFFF
+    per_tile = grid // (8 * n_qt)
+    seen = set()
+    for lin in range(grid):
+        xcd, r8 = lin % 8, lin // 8
+        qt = n_qt - 1 - r8 // per_tile
+        unit = ((r8 % per_tile) // G) * 8 + xcd
+        if unit >= units:
+            continue
+        s_, hk = unit // Hk, unit % Hk
+        h = hk * G + r8 % G
+        assert 0 <= s_ < S and 0 <= h < H and 0 <= qt < n_qt and h // G == hk
+        assert unit % 8 == lin % 8  # a unit's workgroups share one XCD
+        seen.add((s_, h, qt))
+    assert len(seen) == S * H * n_qt
 
 
 PF_CASES = [
