@@ -221,9 +221,11 @@ __global__ __launch_bounds__(kPfThreads, kPfWavesPerSimd) void prefill_kernel(
     int bad = 0;
 
     uint4 kreg[CPT], vreg[CPT];
-    // Thread tid moves CPT adjacent 16-byte chunks of one key row: row
-    // tid / (CPR / CPT), chunks CPT * (tid % (CPR / CPT)) + u.
-    const int ld_row = tid / (CPR / CPT), ld_chunk = CPT * (tid % (CPR / CPT));
+    // Thread tid moves CPT 16-byte chunks of one key row (one block-table
+    // lookup per tile): row tid / (CPR / CPT), chunks tid % (CPR / CPT) +
+    // u CPR / CPT, so each LDS store instruction writes whole row halves
+    // (no bank conflicts).
+    const int ld_row = tid / (CPR / CPT), ld_chunk = tid % (CPR / CPT);
     auto load_tile = [&](int kt) {
         // Keys past kv_end (the last tile's tail) re-read key kv_end - 1:
         // they are masked out of every row, and the value row read is a real
@@ -235,15 +237,15 @@ __global__ __launch_bounds__(kPfThreads, kPfWavesPerSimd) void prefill_kernel(
                            static_cast<uint32_t>(kp & bmask) * D + 8 * ld_chunk;
 #pragma unroll
         for (int u = 0; u < CPT; ++u) {
-            kreg[u] = load16(kc + e + 8 * u);
-            vreg[u] = load16(vc + e + 8 * u);
+            kreg[u] = load16(kc + e + 8 * (CPR / CPT) * u);
+            vreg[u] = load16(vc + e + 8 * (CPR / CPT) * u);
         }
     };
     auto store_tile = [&](int buf) {
 #pragma unroll
         for (int u = 0; u < CPT; ++u) {
-            *reinterpret_cast<uint4*>(&sK[buf][ld_row][8 * (ld_chunk + u)]) = kreg[u];
-            *reinterpret_cast<uint4*>(&sV[buf][ld_row][8 * (ld_chunk + u)]) = vreg[u];
+            *reinterpret_cast<uint4*>(&sK[buf][ld_row][8 * (ld_chunk + (CPR / CPT) * u)]) = kreg[u];
+            *reinterpret_cast<uint4*>(&sV[buf][ld_row][8 * (ld_chunk + (CPR / CPT) * u)]) = vreg[u];
         }
     };
 

@@ -239,8 +239,8 @@ def check_prefill_bounds(case, max_query_len=None):
     """Grid (H, S, ceil(max_query_len / 128)); wavefront w of a workgroup owns
     chunk rows r0 + 32 w + 16 rb + c (rb = 0, 1); query loads read row min(row, n - 1), channels
     32 ks + 8 g .. +7; block ids of keys 0 .. kv_end - 1 are staged; tile
-    loads read key min(kp, kv_end - 1), CPT adjacent 16-byte chunks of one
-    row per thread; LDS reads stay in
+    loads read key min(kp, kv_end - 1), CPT 16-byte chunks of one row per
+    thread (CPR / CPT apart); LDS reads stay in
     the [2][32][D + 16] tiles (K rows 16 sub + c at 32 ks + 8 g .. +7;
     transposing V reads at rows 4 g + c // 4 (+ 16), channels 16 t + 4 (c % 4)
     .. +3, 8-byte aligned); output rows < n, channels 16 t + 4 g .. +3."""
@@ -291,10 +291,11 @@ def check_prefill_bounds(case, max_query_len=None):
             # tile loads
             tid = np.arange(PF_THREADS)
             assert CPR % cpt == 0
-            ld_row, ld_chunk = tid // (CPR // cpt), cpt * (tid % (CPR // cpt))
-            assert ld_row.max() < PF_KEYS and ld_chunk.max() + cpt <= CPR
+            ld_row, ld_chunk = tid // (CPR // cpt), tid % (CPR // cpt)
+            chunks = [ld_chunk + (CPR // cpt) * u for u in range(cpt)]
+            assert ld_row.max() < PF_KEYS and max(ch.max() for ch in chunks) < CPR
             # every (key row, chunk) of a tile is moved exactly once
-            assert len({(r, c_ + u) for r, c_ in zip(ld_row, ld_chunk) for u in range(cpt)}) == PF_KEYS * CPR
+            assert len({(r, int(ch[i])) for ch in chunks for i, r in enumerate(ld_row)}) == PF_KEYS * CPR
             for kt in range(ntiles):
                 kp = np.minimum(kt * PF_KEYS + ld_row, kv_end - 1)  # tail keys re-read the last one
                 idx = kp // B
@@ -302,7 +303,7 @@ def check_prefill_bounds(case, max_query_len=None):
                 b = case.block_tables[s, idx]
                 b = np.where((b >= 0) & (b < N), b, 0).astype(np.int64)
                 for u in range(cpt):
-                    e = b * Hk * B * D + (Hk - 1) * B * D + (kp % B) * D + 8 * (ld_chunk + u)
+                    e = b * Hk * B * D + (Hk - 1) * B * D + (kp % B) * D + 8 * chunks[u]
                     assert e.min() >= 0 and e.max() + 8 <= cache_elems
             # LDS rows read by the compute: keys 16 sub + c and 16 sub + 4 g + j < 32
             assert 16 + 15 < PF_KEYS and 16 + 4 * 3 + 3 < PF_KEYS
