@@ -3,6 +3,8 @@
 // frees or synchronises.
 #include <math.h>
 
+#include <atomic>
+
 #include "../../include/pa.h"
 #include "pa_internal.h"
 
@@ -26,14 +28,43 @@ int resolve_partition(int32_t partition_size, int32_t num_seqs, int32_t num_head
         .part_tokens;
 }
 
-int64_t parts_for(int32_t max_context_len, int part) {
-    return max_context_len <= 0 ? 1 : (static_cast<int64_t>(max_context_len) + part - 1) / part;
+// Partials per query head: one per partition; under a balanced plan a
+// head's run can straddle one more workgroup boundary than it has
+// kBalancedMinChunk-token pieces.
+int64_t parts_for(int32_t max_context_len, int part, bool balanced) {
+    const int64_t p = max_context_len <= 0 ? 1 : (static_cast<int64_t>(max_context_len) + part - 1) / part;
+    return balanced ? p + 1 : p;
 }
 
-// Workspace bytes for the split path, or 0 when one partition always suffices.
-size_t workspace_bytes_for(int64_t num_seqs, int64_t num_heads, int64_t head_dim, int64_t parts) {
+// Workspace bytes for the split path (partials, then the balanced plan's
+// int32 [S + 2] share table), or 0 when one partition always suffices.
+size_t workspace_bytes_for(int64_t num_seqs, int64_t num_heads, int64_t head_dim, int64_t parts, bool balanced) {
     if (parts <= 1) return 0;
-    return static_cast<size_t>(num_seqs * num_heads * parts * (head_dim + 2)) * sizeof(float);
+    return static_cast<size_t>(num_seqs * num_heads * parts * (head_dim + 2)) * sizeof(float) +
+           (balanced ? static_cast<size_t>(num_seqs + 2) * sizeof(int32_t) : 0);
+}
+
+// Workgroups of a balanced split on the current device: kBalancedWgsPerCu
+// per compute unit, half that for head_dim 256 (whose kernel fits 2
+// wavefronts per SIMD, not 4).  The CU count is queried once per device.
+int balanced_workgroups(int32_t head_dim) {
+    static std::atomic<int> cached_cus[64];
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
+        int n = cached_cus[dev].load(std::memory_order_relaxed);
+        if (n == 0) {
+            if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+                (void)hipGetLastError();
+                n = 256;
+            }
+            cached_cus[dev].store(n, std::memory_order_relaxed);
+        }
+        cus = n;
+    } else {
+        (void)hipGetLastError();
+    }
+    const int per_cu = head_dim <= 128 ? pa::kBalancedWgsPerCu : (pa::kBalancedWgsPerCu + 1) / 2;
+    return cus * per_cu;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
@@ -80,8 +111,10 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads || head_dim <= 0 ||
         max_context_len < 0 || partition_size < 0)
         return 0;
-    const int part = resolve_partition(partition_size, num_seqs, num_heads, num_kv_heads, max_context_len);
-    return workspace_bytes_for(num_seqs, num_heads, head_dim, parts_for(max_context_len, part));
+    const pa::DecodePlan plan =
+        pa::plan_decode(num_seqs, num_kv_heads, num_heads / num_kv_heads, max_context_len, partition_size);
+    return workspace_bytes_for(num_seqs, num_heads, head_dim,
+                               parts_for(max_context_len, plan.part_tokens, plan.balanced), plan.balanced);
 }
 
 }  // extern "C"
@@ -122,9 +155,9 @@ int decode_common(void* out, const void* query, const void* key, const void* val
     // A partition may start mid-block, so it touches at most ceil(P/B) + 1 blocks.
     const int64_t staged = pa::partition_blocks(part, block_size);
     if (staged > pa::kMaxPartitionBlocks) return PA_ERR_INVALID;
-    const int64_t parts = parts_for(max_context_len, part);
+    const int64_t parts = parts_for(max_context_len, part, plan.balanced);
     if (parts > 65535) return PA_ERR_INVALID;  // grid dimension limit
-    const size_t need = workspace_bytes_for(num_seqs, num_heads, head_dim, parts);
+    const size_t need = workspace_bytes_for(num_seqs, num_heads, head_dim, parts, plan.balanced);
     if (need) {
         if (!workspace) return PA_ERR_NULL;
         if (workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 3u)) return PA_ERR_INVALID;
@@ -153,6 +186,19 @@ int decode_common(void* out, const void* query, const void* key, const void* val
     a.max_parts = static_cast<int>(parts);
     a.staged_blocks = static_cast<int>(staged);
     a.longest_first = plan.longest_first;
+    a.balanced = plan.balanced;
+    a.balanced_wgs = 0;
+    a.staged_balanced = 0;
+    if (plan.balanced) {
+        // A workgroup's run covers at most min(its share, the context) tokens.
+        a.balanced_wgs = balanced_workgroups(head_dim);
+        const int64_t total = static_cast<int64_t>(num_seqs) * num_kv_heads * max_context_len;
+        int64_t share = (total + a.balanced_wgs - 1) / a.balanced_wgs;
+        share = (share + 15) / 16 * 16;
+        if (share < part) share = part;
+        if (share > max_context_len) share = max_context_len;
+        a.staged_balanced = static_cast<int>(pa::partition_blocks(share, block_size));
+    }
     a.cached_loads = (flags & PA_DECODE_SHARED_BLOCKS) != 0;
     a.workspace = need ? workspace : nullptr;
     a.stream = static_cast<hipStream_t>(stream);

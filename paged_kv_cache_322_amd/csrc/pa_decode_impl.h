@@ -370,16 +370,31 @@ template <class T, int D>
 __global__ __launch_bounds__(kWave) void decode_merge_kernel(
     typename T::bits* __restrict__ out, const float* __restrict__ ws_o, const float* __restrict__ ws_m,
     const float* __restrict__ ws_l, const int32_t* __restrict__ context_lens, int num_heads, int max_context_len,
-    int part_tokens, int max_parts) {
+    int part_tokens, int max_parts, int num_kv_heads, const int32_t* __restrict__ meta) {
     __shared__ float s_w[kMergeMaxParts];
     const int h = blockIdx.x, s = blockIdx.y;
     const int ctx = context_lens[s];
-    if (ctx <= part_tokens || ctx > max_context_len) return;  // written by the partition kernel
-    const int np = (ctx + part_tokens - 1) / part_tokens;
     const int64_t sh = static_cast<int64_t>(s) * num_heads + h;
+    const int lane = threadIdx.x;
+    int np;
+    if (meta) {
+        // Balanced split: the decode kernel skipped empty and invalid
+        // contexts, and wrote whole (sequence, K/V head) runs itself.
+        if (ctx <= 0 || ctx > max_context_len) {
+            const float v = (ctx == 0) ? 0.0f : __builtin_nanf("");
+            for (int d = lane; d < D; d += kWave) out[sh * D + d] = narrow<T>(v);
+            return;
+        }
+        const int64_t C = meta[0];
+        const int64_t F = static_cast<int64_t>(num_kv_heads) * meta[1 + s] + static_cast<int64_t>(h / (num_heads / num_kv_heads)) * ctx;
+        np = static_cast<int>((F + ctx - 1) / C - F / C + 1);
+        if (np == 1) return;
+    } else {
+        if (ctx <= part_tokens || ctx > max_context_len) return;  // written by the partition kernel
+        np = (ctx + part_tokens - 1) / part_tokens;
+    }
     const float* wm = ws_m + sh * max_parts;
     const float* wl = ws_l + sh * max_parts;
-    const int lane = threadIdx.x;
     float M = -INFINITY;
     for (int p = lane; p < np; p += kWave) M = fmaxf(M, wm[p]);
     M = group_reduce<1, kWave>(M, OpMax{});
@@ -427,17 +442,35 @@ hipError_t launch_decode_t(const DecodeArgs& a) {
     const size_t n_sh = static_cast<size_t>(a.num_seqs) * a.num_heads * a.max_parts;
     float* ws_m = ws_o ? ws_o + n_sh * D : nullptr;
     float* ws_l = ws_o ? ws_m + n_sh : nullptr;
+    int32_t* meta = ws_o ? reinterpret_cast<int32_t*>(ws_l + n_sh) : nullptr;
     dim3 grid(a.num_kv_heads, a.num_seqs, a.max_parts);
     const size_t lds = static_cast<size_t>(a.staged_blocks) * sizeof(int);
     if constexpr (kUseMfma<T, D, G>) {
+        if (a.balanced && a.staged_balanced <= kMfmaMaxStaged) {
+            hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, APPEND, NT, true>), dim3(a.balanced_wgs), dim3(kMfmaThreads),
+                               static_cast<size_t>(a.staged_balanced) * sizeof(int), a.stream, out, ws_o, ws_m, ws_l,
+                               static_cast<const bits*>(a.query), static_cast<bits*>(a.k_cache),
+                               static_cast<bits*>(a.v_cache), static_cast<const bits*>(a.key_new),
+                               static_cast<const bits*>(a.value_new), a.block_tables, a.context_lens, a.num_seqs,
+                               a.num_kv_heads, log2_bs, a.max_blocks_per_seq, a.max_context_len, a.num_blocks,
+                               a.part_tokens, a.max_parts, kPlanBalanced, a.balanced_wgs, meta, qscale);
+            hipError_t err = hipGetLastError();
+            if (err != hipSuccess) return err;
+            hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(a.num_heads, a.num_seqs), dim3(kWave), 0, a.stream,
+                               out, ws_o, ws_m, ws_l, a.context_lens, a.num_heads, a.max_context_len, a.part_tokens,
+                               a.max_parts, a.num_kv_heads, static_cast<const int32_t*>(meta));
+            return hipGetLastError();
+        }
+        // Otherwise (and for a balanced plan whose runs would stage too many
+        // block ids): partitions of part_tokens.
         if (a.staged_blocks <= kMfmaMaxStaged) {
-            hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, APPEND, NT>), grid, dim3(kMfmaThreads), lds, a.stream,
+            hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, APPEND, NT, false>), grid, dim3(kMfmaThreads), lds, a.stream,
                                out, ws_o, ws_m, ws_l, static_cast<const bits*>(a.query),
                                static_cast<bits*>(a.k_cache), static_cast<bits*>(a.v_cache),
                                static_cast<const bits*>(a.key_new), static_cast<const bits*>(a.value_new),
                                a.block_tables, a.context_lens, a.num_seqs, a.num_kv_heads, log2_bs,
                                a.max_blocks_per_seq, a.max_context_len, a.num_blocks, a.part_tokens, a.max_parts,
-                               a.longest_first ? 1 : 0, qscale);
+                               a.longest_first ? kPlanLongestFirst : kPlanPartitions, 0, nullptr, qscale);
         } else {
             hipLaunchKernelGGL((decode_partition_kernel<T, D, G, APPEND, NT>), grid, dim3(kThreads), lds, a.stream,
                                out, ws_o, ws_m, ws_l, static_cast<const bits*>(a.query),
@@ -459,7 +492,7 @@ hipError_t launch_decode_t(const DecodeArgs& a) {
     if (err != hipSuccess || a.max_parts <= 1) return err;
     hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(a.num_heads, a.num_seqs), dim3(kWave), 0, a.stream, out,
                        ws_o, ws_m, ws_l, a.context_lens, a.num_heads, a.max_context_len, a.part_tokens,
-                       a.max_parts);
+                       a.max_parts, a.num_kv_heads, static_cast<const int32_t*>(nullptr));
     return hipGetLastError();
 }
 

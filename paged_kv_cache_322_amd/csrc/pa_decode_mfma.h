@@ -68,6 +68,14 @@ constexpr int kMfmaThreads = kMfmaWaves * kWave;
 constexpr int kMfmaTile = 16;            // tokens per wavefront step
 constexpr int kMfmaMergeFloats = 8192;   // LDS floats for the cross-wave merge (32 KB)
 
+// Register budget of the kernel: wavefronts per SIMD it must fit (4, i.e.
+// <= 128 VGPRs and 2 resident 8-wavefront workgroups per CU, for D <= 128;
+// 2 for D = 256).  The balanced split launches that many workgroups per CU.
+#ifndef PA_MFMA_WAVES_PER_SIMD
+#define PA_MFMA_WAVES_PER_SIMD 4  // for D <= 128
+#endif
+constexpr int mfma_waves_per_simd(int D) { return D <= 128 ? PA_MFMA_WAVES_PER_SIMD : 2; }
+
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -172,15 +180,15 @@ __device__ __forceinline__ int longest_first_seq(const int32_t* __restrict__ con
     return __builtin_amdgcn_readfirstlane(s_pick);
 }
 
-template <class T, int D, int G, bool APPEND, bool NT>
-__global__ __launch_bounds__(kMfmaThreads) void decode_mfma_kernel(
+template <class T, int D, int G, bool APPEND, bool NT, bool BALANCED>
+__global__ __launch_bounds__(kMfmaThreads, mfma_waves_per_simd(D)) void decode_mfma_kernel(
     typename T::bits* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_m,
     float* __restrict__ ws_l, const typename T::bits* __restrict__ q, typename T::bits* __restrict__ kc,
     typename T::bits* __restrict__ vc, const typename T::bits* __restrict__ knew,
     const typename T::bits* __restrict__ vnew, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, int num_seqs, int num_kv_heads, int log2_bs,
-    int max_blocks_per_seq, int max_context_len, int64_t num_blocks, int part_tokens, int max_parts,
-    int longest_first, float qscale) {
+    int max_blocks_per_seq, int max_context_len, int64_t num_blocks, int part_tokens, int max_parts, int mode,
+    int num_wgs, int32_t* __restrict__ meta, float qscale) {
     static_assert(sizeof(typename T::bits) == 2, "16-bit caches only");
     static_assert(D == 64 || D == 128 || D == 256, "head_dim");
     static_assert(G >= 1 && G <= 16, "group size");
@@ -198,25 +206,16 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma_kernel(
     __shared__ float s_m[kMfmaWaves][16], s_l[kMfmaWaves][16];
     __shared__ float s_o[kMfmaWaves][HC][DP];
 
-    const int hk = blockIdx.x, srow = blockIdx.y, part = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const int c = lane & 15, g = lane >> 4;
-    const int s = longest_first ? longest_first_seq<kMfmaThreads>(context_lens, num_seqs, srow, tid) : srow;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int num_heads = num_kv_heads * G;
-    const int64_t sh0 = static_cast<int64_t>(s) * num_heads + static_cast<int64_t>(hk) * G;
-    const int ctx = __builtin_amdgcn_readfirstlane(context_lens[s]);
 
-    if (ctx <= 0 || ctx > max_context_len) {
-        if (part == 0) {
-            const float v = (ctx == 0) ? 0.0f : __builtin_nanf("");
-            for (int d = tid; d < G * D; d += kMfmaThreads) out[sh0 * D + d] = narrow<T>(v);
-        }
-        return;
-    }
-    const int t_begin = part * part_tokens;
-    if (t_begin >= ctx) return;
-    const int t_end = min(ctx, t_begin + part_tokens);
+    // One pass over tokens [t_begin, t_end) of K/V head hk of sequence s
+    // (context ctx): the G heads' partial softmax state, merged across the
+    // wavefronts, goes to `out` (single) or to workspace slot `slot`.
+    auto run_segment = [&](int s, int hk, int ctx, int t_begin, int t_end, bool single, int slot) {
+    const int64_t sh0 = static_cast<int64_t>(s) * num_heads + static_cast<int64_t>(hk) * G;
     const int bmask = (1 << log2_bs) - 1;
     const int j0 = t_begin >> log2_bs;
     const int nblk = ((t_end - 1) >> log2_bs) - j0 + 1;
@@ -377,7 +376,6 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma_kernel(
     bad = __syncthreads_or(bad);
 
     // Merge the wavefronts through LDS, HC heads per pass.
-    const bool single = ctx <= part_tokens;
     if (g == 0) {
         s_m[wave][c] = m;
         s_l[wave][c] = l;
@@ -408,14 +406,109 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma_kernel(
             if (single) {
                 out[sh * D + d] = narrow<T>(O / L);
             } else {
-                ws_o[(sh * max_parts + part) * D + d] = O;
+                ws_o[(sh * max_parts + slot) * D + d] = O;
                 if (d == 0) {
-                    ws_m[sh * max_parts + part] = M;
-                    ws_l[sh * max_parts + part] = L;
+                    ws_m[sh * max_parts + slot] = M;
+                    ws_l[sh * max_parts + slot] = L;
                 }
             }
         }
         if (c0 + HC < G) __syncthreads();  // s_o is reused by the next pass
+    }
+    };
+
+    // Classic plans: one workgroup per (K/V head, sequence row, partition),
+    // one run.  Balanced split: the work is the flat sequence of (sequence
+    // s, K/V head hk, token t) in that order, sequence s contributing n_s =
+    // ctx_s tokens per K/V head (0 for an empty or invalid context, whose
+    // output the merge kernel writes).  Workgroup w takes the C consecutive
+    // items [w C, (w + 1) C), C = max(part_tokens, ceil(total / num_wgs))
+    // rounded up to a whole tile, and makes one run per (s, hk) inside it.
+    // A run that is a whole (s, hk) writes the output; otherwise its partial
+    // goes to slot w - floor(F / C) of that head's partials, F being the flat
+    // index of the pair's first token, and the merge kernel combines the
+    // floor((F + n_s - 1) / C) - floor(F / C) + 1 partials.
+    __shared__ int s_pre[kMaxLptSeqs + 1];  // balanced: s_pre[i] = n_0 + ... + n_{i-1}
+    constexpr bool balanced = BALANCED;  // (mode == kPlanBalanced)
+    int s = 0, hk = 0, ctx = 0, t_begin = 0, t_end = 0, slot = 0;
+    bool single = false;
+    int64_t x = 0, x_end = 0, C = 1;
+    const int w = blockIdx.x;
+    if constexpr (!balanced) {
+        hk = blockIdx.x;
+        const int srow = blockIdx.y, part = blockIdx.z;
+        s = mode == kPlanLongestFirst ? longest_first_seq<kMfmaThreads>(context_lens, num_seqs, srow, tid) : srow;
+        ctx = __builtin_amdgcn_readfirstlane(context_lens[s]);
+        if (ctx <= 0 || ctx > max_context_len) {
+            if (part == 0) {
+                const int64_t sh0 = static_cast<int64_t>(s) * num_heads + static_cast<int64_t>(hk) * G;
+                const float v = (ctx == 0) ? 0.0f : __builtin_nanf("");
+                for (int d = tid; d < G * D; d += kMfmaThreads) out[sh0 * D + d] = narrow<T>(v);
+            }
+            return;
+        }
+        t_begin = part * part_tokens;
+        if (t_begin >= ctx) return;
+        t_end = min(ctx, t_begin + part_tokens);
+        single = ctx <= part_tokens;
+        slot = part;
+    } else {
+        for (int i = tid; i < num_seqs; i += kMfmaThreads) {
+            const int n = context_lens[i];
+            s_pre[i + 1] = (n > 0 && n <= max_context_len) ? n : 0;
+        }
+        if (tid == 0) s_pre[0] = 0;
+        __syncthreads();
+        for (int off = 1; off <= num_seqs; off <<= 1) {  // inclusive scan of s_pre[1..S] (Hillis-Steele)
+            int v[kMaxLptSeqs / kMfmaThreads + 1];
+            int k = 0;
+            for (int i = tid + 1; i <= num_seqs; i += kMfmaThreads, ++k) v[k] = (i > off) ? s_pre[i - off] : 0;
+            __syncthreads();
+            k = 0;
+            for (int i = tid + 1; i <= num_seqs; i += kMfmaThreads, ++k) s_pre[i] += v[k];
+            __syncthreads();
+        }
+        // (Values read from LDS are made scalar: they are uniform, and the
+        // per-run state then costs no vector registers.)
+        const int64_t total = static_cast<int64_t>(num_kv_heads) * __builtin_amdgcn_readfirstlane(s_pre[num_seqs]);
+        int64_t chunk = (total + num_wgs - 1) / num_wgs;
+        chunk = (chunk + kMfmaTile - 1) / kMfmaTile * kMfmaTile;
+        C = chunk > part_tokens ? chunk : part_tokens;
+        if (w == 0) {  // for the merge kernel
+            if (tid == 0) meta[0] = static_cast<int32_t>(C);
+            for (int i = tid; i <= num_seqs; i += kMfmaThreads) meta[1 + i] = s_pre[i];
+        }
+        x = static_cast<int64_t>(w) * C;
+        x_end = min(total, x + C);
+        if (x >= x_end) return;
+    }
+    while (true) {
+        int64_t seg_end = 0;
+        if constexpr (balanced) {
+            // The sequence holding flat index x: the last s with Hk * pre[s] <= x.
+            int lo = 0, hi = num_seqs - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (static_cast<int64_t>(num_kv_heads) * s_pre[mid] <= x) lo = mid;
+                else hi = mid - 1;
+            }
+            s = __builtin_amdgcn_readfirstlane(lo);
+            const int pre_s = __builtin_amdgcn_readfirstlane(s_pre[s]);
+            ctx = __builtin_amdgcn_readfirstlane(s_pre[s + 1]) - pre_s;  // > 0: x lies in sequence s's range
+            const int64_t off = x - static_cast<int64_t>(num_kv_heads) * pre_s;
+            hk = __builtin_amdgcn_readfirstlane(static_cast<int>(off / ctx));
+            t_begin = __builtin_amdgcn_readfirstlane(static_cast<int>(off % ctx));
+            const int64_t F = x - t_begin;  // flat index of (s, hk, 0)
+            seg_end = min(x_end, F + ctx);
+            t_end = __builtin_amdgcn_readfirstlane(t_begin + static_cast<int>(seg_end - x));
+            const int64_t first = F / C, last = (F + ctx - 1) / C;
+            single = __builtin_amdgcn_readfirstlane(static_cast<int>(first == last)) != 0;
+            slot = __builtin_amdgcn_readfirstlane(static_cast<int>(w - first));
+        }
+        run_segment(s, hk, ctx, t_begin, t_end, single, slot);
+        if constexpr (!balanced) break;
+        x = seg_end;
+        if (x >= x_end) break;
     }
 }
 

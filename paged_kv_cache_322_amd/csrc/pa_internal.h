@@ -16,6 +16,12 @@ constexpr int kMaxPartitionBlocks = 8192;
 // Work items are (sequence, K/V head, KV partition).  The hardware
 // dispatches workgroups in grid order, so the order of the items decides how
 // evenly the 256 compute units finish.
+//  * Grouped heads (G >= 2, the matrix-core kernel), fewer pairs than the
+//    longest-first threshold (512), no caller-given partition length:
+//    balanced split.  One workgroup per resident slot (kBalancedWgsPerCu per
+//    CU); each takes an equal share (at least kBalancedMinChunk tokens) of
+//    the flat (sequence, K/V head, token) work, whatever the length mix, and
+//    a merge launch combines the heads split across workgroups.
 //  * Many (sequence, K/V head) pairs (>= kManyPairs): whole contexts up to
 //    4096 tokens per item, in batch order (the items are many and short
 //    enough).
@@ -50,9 +56,21 @@ constexpr int64_t kLptPairs = PA_LPT_PAIRS;
 constexpr int64_t kLptGroupedPairs = 512;
 constexpr int kMaxLptSeqs = 512;
 
+// Work decompositions of the decode kernels.
+constexpr int kPlanPartitions = 0;    // one workgroup per (K/V head, sequence, partition)
+constexpr int kPlanLongestFirst = 1;  // whole contexts, longest sequences dispatched first
+constexpr int kPlanBalanced = 2;      // equal shares of the flat (sequence, K/V head, token) work
+
+#ifndef PA_BALANCED_WGS_PER_CU
+#define PA_BALANCED_WGS_PER_CU 2  // resident matrix-core decode workgroups per CU (8 waves, <= 128 VGPRs)
+#endif
+constexpr int kBalancedWgsPerCu = PA_BALANCED_WGS_PER_CU;
+constexpr int kBalancedMinChunk = 256;  // fewest tokens a balanced-split workgroup takes
+
 struct DecodePlan {
     int part_tokens;
     bool longest_first;
+    bool balanced;  // the matrix-core kernel splits the flat work evenly (part_tokens = smallest share)
 };
 
 inline DecodePlan plan_decode(int64_t num_seqs, int64_t num_kv_heads, int64_t group, int64_t max_context_len,
@@ -62,8 +80,17 @@ inline DecodePlan plan_decode(int64_t num_seqs, int64_t num_kv_heads, int64_t gr
     const int64_t lpt_pairs = group >= 2 ? kLptGroupedPairs : kLptPairs;
     int whole = min_part;
     while (whole < kMaxDefaultPartition && whole < max_context_len) whole *= 2;
-    DecodePlan p{whole, false};
+    DecodePlan p{whole, false, false};
     const bool can_sort = num_seqs <= kMaxLptSeqs;
+    // Grouped heads (the matrix-core kernel) with few (sequence, K/V head)
+    // pairs: split the flat work evenly over the resident workgroups.  The
+    // flat index must fit 31 bits.
+    if (group >= 2 && partition_size == 0 && pairs < lpt_pairs && can_sort &&
+        pairs * max_context_len < (int64_t{1} << 31)) {
+        p.part_tokens = kBalancedMinChunk;
+        p.balanced = true;
+        return p;
+    }
     if (pairs >= kManyPairs) {
         p.part_tokens = whole;
     } else if (pairs >= lpt_pairs && can_sort) {
@@ -101,8 +128,13 @@ struct DecodeArgs {
     int part_tokens, max_parts;
     int staged_blocks;  // LDS entries for a partition's block ids
     bool longest_first; // map grid rows to sequences in decreasing context length
+    bool balanced;      // balanced split (matrix-core kernel); else partitions of part_tokens
+    int balanced_wgs;   // workgroups of the balanced split
+    int staged_balanced;  // LDS entries for a balanced-split run's block ids
     bool cached_loads;  // ordinary (cached) K/V loads instead of non-temporal ones
-    void* workspace;  // float [S*H*max_parts*D] then [S*H*max_parts] x 2; NULL when max_parts == 1
+    // float [S*H*max_parts*D] then [S*H*max_parts] x 2, then (balanced plan)
+    // int32 [S + 2]; NULL when max_parts == 1
+    void* workspace;
     hipStream_t stream;
 };
 

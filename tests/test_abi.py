@@ -58,13 +58,17 @@ def test_default_partition_heuristic():
 
 
 def test_default_partition_heuristic_grouped():
-    # G >= 2 (matrix-core kernel): longest first from 512 pairs, partitions of
-    # at least 512 tokens.
+    # G >= 2 (matrix-core kernel) with fewer than 512 pairs: balanced split,
+    # shares of at least 256 tokens.  Otherwise the G >= 2 rules: longest
+    # first from 512 pairs, partitions of >= 512 tokens.
     assert pa.partition_tokens(64, 32, 2048, num_kv_heads=8) == 2048  # LLaMA-3-8B shape: 512 pairs, whole
-    assert pa.partition_tokens(64, 32, 2048, num_kv_heads=32) == 2048  # 2048 multi-head pairs: whole too
+    assert pa.partition_tokens(60, 32, 2048, num_kv_heads=8) == 256  # 480 pairs: balanced
+    assert pa.partition_tokens(64, 32, 2048, num_kv_heads=32) == 2048  # 2048 multi-head pairs: whole
     assert pa.partition_tokens(16, 32, 2048) == 256  # 512 multi-head pairs: split to 256 tokens
-    assert pa.partition_tokens(128, 8, 4096, num_kv_heads=1) == 512  # 128 pairs, minimum 512
-    assert pa.partition_tokens(128, 8, 300, num_kv_heads=1) == 512  # whole context rounds up to 512
+    assert pa.partition_tokens(128, 8, 4096, num_kv_heads=1) == 256  # 128 pairs: balanced
+    assert pa.partition_tokens(128, 8, 300, num_kv_heads=1) == 256
+    assert pa.partition_tokens(600, 8, 4096, num_kv_heads=1) == 512  # 600 pairs, too many to rank: split
+    assert pa.partition_tokens(4096, 32, 2048, num_kv_heads=4) == 2048  # 16384 pairs: whole contexts
     assert pa.partition_tokens(2, 30, 100, num_kv_heads=8) == 0  # 30 heads over 8 K/V heads: invalid
     assert pa.partition_tokens(2, 8, 100, 64, num_kv_heads=1) == 64  # explicit sizes pass through
 
@@ -91,9 +95,12 @@ def test_workspace_size():
     assert pa.decode_workspace_size(3, 1, 8, 37, 16) == 3 * 1 * 3 * 10 * 4
     assert pa.decode_workspace_size(-1, 1, 8, 37, 16) == 0
     # One K/V head serving 8 query heads, 128 sequences up to 4096 tokens:
-    # partitions of 512 tokens, 8 of them.
-    assert pa.decode_workspace_size(128, 8, 128, 4096, num_kv_heads=1) == 128 * 8 * 8 * 130 * 4
+    # balanced split, up to 4096 / 256 + 1 = 17 partials per head, and the
+    # int32 [S + 2] share table.
+    assert pa.decode_workspace_size(128, 8, 128, 4096, num_kv_heads=1) == 128 * 8 * 17 * 130 * 4 + 130 * 4
     assert pa.decode_workspace_size(64, 32, 128, 2048, num_kv_heads=8) == 0  # whole contexts, longest first
+    assert pa.decode_workspace_size(60, 32, 128, 2048, num_kv_heads=8) == 60 * 32 * 9 * 130 * 4 + 62 * 4
+    assert pa.decode_workspace_size(4, 8, 64, 100, num_kv_heads=1) == 4 * 8 * 2 * 66 * 4 + 6 * 4
     assert pa.decode_workspace_size(2, 30, 128, 100, num_kv_heads=8) == 0  # invalid grouping
 
 

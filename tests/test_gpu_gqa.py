@@ -41,6 +41,11 @@ SWEEP = [
     ("bf16", 8, 1, 128, 16, [1, 4000], 0),
     ("f32", 4, 2, 8, 4, [5, 16, 37], 4),
     ("f16", 32, 4, 64, 1, [1, 2, 129], 16),
+    # Default plans of grouped heads: the balanced split (16-bit, D >= 64), or
+    # for fp32 / D = 32 its fallback, 256-token partitions on the vector kernel.
+    ("f32", 8, 2, 64, 16, [5, 300, 1000], 0),
+    ("f16", 8, 2, 32, 8, [3, 260, 513], 0),
+    ("bf16", 16, 8, 64, 4, [1, 2, 3, 700, 33, 257], 0),
 ]
 
 
@@ -76,3 +81,39 @@ def test_gqa_append_decode(Hk):
     assert_pool_equal(g.kc, kc, "f16", f"K Hk={Hk}")
     assert_pool_equal(g.vc, vc, "f16", f"V Hk={Hk}")
     assert_close(out, ref, "f16", f"gqa append_decode Hk={Hk}", strict=False)
+
+
+def test_balanced_split_empty_invalid_and_tiny_contexts():
+    """Balanced split over 200 sequences of 0..40 tokens (many (sequence,
+    K/V head) runs per workgroup), one empty context (output 0) and one past
+    max_context_len (output NaN, nothing read)."""
+    rng = np.random.default_rng(77)
+    ctx = rng.integers(1, 41, 200)
+    ctx[5] = 0
+    case = wl.random_case(540, 200, 8, 128, 16, "f16", ctx=ctx.tolist(), num_kv_heads=2, spare_blocks=3)
+    assert pa().partition_tokens(200, 8, case.max_context_len, num_kv_heads=2) == 256  # balanced plan
+    g = GpuCase(case)
+    bad = case.context_lens.copy()
+    bad[7] = case.max_context_len + 1
+    out = g.decode(out=torch.full_like(g.q, 7.0), ctx=to_gpu(bad))
+    torch.cuda.synchronize()
+    seqs = [s for s in range(200) if s not in (5, 7)]
+    ref = oracle_decode(case, case.k_cache, case.v_cache, seqs)
+    assert_close(out, ref, "f16", "balanced tiny contexts", seqs=seqs)
+    o = out.float().cpu()
+    assert torch.all(o[5] == 0) and torch.all(torch.isnan(o[7]))
+    log("empty context -> 0, invalid context -> NaN")
+
+
+@pytest.mark.parametrize("H,Hk,D", [(8, 1, 128), (32, 8, 64), (16, 4, 256)])
+def test_balanced_split_matches_partitions(H, Hk, D):
+    """The balanced split and fixed 256-token partitions both match the
+    oracle on a ragged batch with long and short contexts."""
+    ctx = [1, 15, 16, 17, 255, 256, 257, 1000, 2500, 40]
+    case = wl.random_case(550 + H + D, len(ctx), H, D, 16, "bf16", ctx=ctx, num_kv_heads=Hk, spare_blocks=3)
+    g = GpuCase(case)
+    ref = oracle_decode(case, case.k_cache, case.v_cache)
+    for part in (0, 256):
+        out = g.decode(partition=part, out=torch.empty_like(g.q))
+        torch.cuda.synchronize()
+        assert_close(out, ref, "bf16", f"H={H} Hk={Hk} D={D} partition={part}", strict=False)

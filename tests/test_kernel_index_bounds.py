@@ -18,8 +18,20 @@ import workloads as wl
 MAX_PART_BLOCKS = 8192
 
 
+BALANCED_MIN_CHUNK = 256
+
+
+def balanced_plan(S, Hk, max_ctx, G=1, partition=0):
+    """Mirror of plan_decode's choice of the balanced split."""
+    pairs = S * Hk
+    return G >= 2 and partition == 0 and pairs < 512 and S <= 512 and pairs * max_ctx < (1 << 31)
+
+
 def default_partition(S, Hk, max_ctx, G=1):
-    """Mirror of the library's default partition rule (plan_decode)."""
+    """Mirror of the library's default partition rule (plan_decode): the
+    partition length, or under a balanced plan its smallest share."""
+    if balanced_plan(S, Hk, max_ctx, G):
+        return BALANCED_MIN_CHUNK
     pmin, lpt = (512, 512) if G >= 2 else (256, 1024)
     whole = pmin
     while whole < 4096 and whole < max_ctx:
@@ -117,10 +129,7 @@ def check_mfma_bounds(S, Hk, G, D, B, N, W, ctx, bt, max_ctx, part):
     col = E * (4 * g[:, None, None] + np.arange(4)[None, :, None]) + np.arange(E)[None, None, :]
     assert col.min() >= 0 and col.max() < D
     assert MFMA_WAVES * hc * (D + 4) <= MFMA_MERGE_FLOATS or hc == 1
-    log2b = B.bit_length() - 1
     staged = (part + B - 1) // B + 1
-    blk_stride = Hk * B * D
-    cache_elems = N * Hk * B * D
     max_parts = max(1, math.ceil(max_ctx / part))
     for s in range(S):
         cl = int(ctx[s])
@@ -130,26 +139,91 @@ def check_mfma_bounds(S, Hk, G, D, B, N, W, ctx, bt, max_ctx, part):
             t_begin = p * part
             if t_begin >= cl:
                 continue
-            t_end = min(cl, t_begin + part)
-            j0 = t_begin >> log2b
-            nblk = ((t_end - 1) >> log2b) - j0 + 1
-            assert 1 <= nblk <= staged and j0 + nblk - 1 < W
-            ntile = (t_end - t_begin + MFMA_TILE - 1) // MFMA_TILE
-            tb = t_begin + np.arange(ntile)[:, None] * MFMA_TILE
-            tk = np.minimum(tb + c[None, :], t_end - 1).ravel()
-            tv = np.minimum(tb + (4 * g[:, None] + np.arange(4)[None, :]).ravel()[None, :], t_end - 1).ravel()
-            for t, lo, width in ((tk, k_lo, 8), (tv, v_lo, E)):
-                assert t.min() >= t_begin
-                lds = (t >> log2b) - j0
-                assert lds.min() >= 0 and lds.max() < nblk
-                b = bt[s, j0 + lds]
-                b = np.where((b >= 0) & (b < N), b, 0)
-                e = b.astype(np.int64) * blk_stride + (Hk - 1) * B * D + (t & (B - 1)).astype(np.int64) * D
-                assert e.min() >= 0 and e.max() + lo.max() + width <= cache_elems
-            # The newest token (append) is token cl - 1, covered by the last tile.
-            if t_end == cl:
-                last = tb[-1, 0]
-                assert last <= cl - 1 < last + MFMA_TILE
+            mfma_run_checks(s, cl, t_begin, min(cl, t_begin + part), staged, Hk, D, B, N, W, bt)
+
+
+def mfma_run_checks(s, cl, t_begin, t_end, staged, Hk, D, B, N, W, bt):
+    """One run of the matrix-core kernel over tokens [t_begin, t_end) of
+    sequence s (context cl): staged block ids, clamped K/V addresses."""
+    E, KS = D // 16, D // 32
+    c, g = np.arange(16), np.arange(4)
+    k_lo = (32 * np.arange(KS)[:, None] + 8 * g[None, :]).ravel()
+    v_lo = E * c
+    log2b = B.bit_length() - 1
+    blk_stride = Hk * B * D
+    cache_elems = N * Hk * B * D
+    assert 0 <= t_begin < t_end <= cl
+    j0 = t_begin >> log2b
+    nblk = ((t_end - 1) >> log2b) - j0 + 1
+    assert 1 <= nblk <= staged and j0 + nblk - 1 < W
+    ntile = (t_end - t_begin + MFMA_TILE - 1) // MFMA_TILE
+    tb = t_begin + np.arange(ntile)[:, None] * MFMA_TILE
+    tk = np.minimum(tb + c[None, :], t_end - 1).ravel()
+    tv = np.minimum(tb + (4 * g[:, None] + np.arange(4)[None, :]).ravel()[None, :], t_end - 1).ravel()
+    for t, lo, width in ((tk, k_lo, 8), (tv, v_lo, E)):
+        assert t.min() >= t_begin
+        lds = (t >> log2b) - j0
+        assert lds.min() >= 0 and lds.max() < nblk
+        b = bt[s, j0 + lds]
+        b = np.where((b >= 0) & (b < N), b, 0)
+        e = b.astype(np.int64) * blk_stride + (Hk - 1) * B * D + (t & (B - 1)).astype(np.int64) * D
+        assert e.min() >= 0 and e.max() + lo.max() + width <= cache_elems
+    # The newest token (append) is token cl - 1, covered by the last tile.
+    if t_end == cl:
+        last = tb[-1, 0]
+        assert last <= cl - 1 < last + MFMA_TILE
+
+
+def check_balanced_bounds(S, Hk, G, D, B, N, W, ctx, bt, max_ctx, num_wgs):
+    """The balanced split: workgroup w takes flat items [w C, (w + 1) C) of
+    the (sequence, K/V head, token) sequence; every run's reads stay in
+    bounds, every valid (sequence, K/V head) is covered exactly once, its
+    partial slots are 0 .. np - 1 with np the merge kernel's count, and the
+    workspace and share table hold every slot."""
+    P = BALANCED_MIN_CHUNK
+    max_parts = -(-max_ctx // P) + 1 if max_ctx > 0 else 2
+    n = np.array([int(x) if 0 < int(x) <= max_ctx else 0 for x in ctx], dtype=np.int64)
+    pre = np.concatenate([[0], np.cumsum(n)])
+    total = Hk * int(pre[-1])
+    C = max(P, -(-(-(-total // num_wgs)) // MFMA_TILE) * MFMA_TILE)
+    assert C < (1 << 31)
+    share = -(-(S * Hk * max_ctx) // num_wgs)
+    share = min(max(P, -(-share // 16) * 16), max_ctx)
+    staged = -(-share // B) + 1
+    H = Hk * G
+    ws_rows = S * H * max_parts
+    runs = {}
+    for w in range(num_wgs):
+        x, x_end = w * C, min(total, w * C + C)
+        while x < x_end:
+            s = int(np.searchsorted(Hk * pre[:S], x, side="right")) - 1
+            cn = int(n[s])
+            assert cn > 0
+            off = x - Hk * int(pre[s])
+            hk, t0 = off // cn, off % cn
+            F = x - t0
+            seg_end = min(x_end, F + cn)
+            t1 = t0 + (seg_end - x)
+            first, last = F // C, (F + cn - 1) // C
+            slot = w - first
+            assert 0 <= slot <= last - first and slot < max_parts
+            mfma_run_checks(s, cn, t0, t1, staged, Hk, D, B, N, W, bt)
+            for h in range(hk * G, hk * G + G):  # workspace rows of the group's query heads
+                assert (s * H + h) * max_parts + slot < ws_rows
+            runs.setdefault((s, hk), []).append((slot, t0, t1, first == last))
+            x = seg_end
+    assert 1 + S < S + 2  # share table: C, then pre[0..S]
+    for s in range(S):
+        for hk in range(Hk):
+            if n[s] == 0:
+                assert (s, hk) not in runs  # the merge kernel writes 0 or NaN
+                continue
+            r = sorted(runs[(s, hk)], key=lambda v: v[1])
+            assert r[0][1] == 0 and r[-1][2] == n[s] and all(a[2] == b[1] for a, b in zip(r, r[1:]))
+            F = Hk * int(pre[s]) + hk * int(n[s])
+            np_merge = (F + int(n[s]) - 1) // C - F // C + 1
+            assert sorted(v[0] for v in r) == list(range(np_merge))
+            assert all(v[3] == (np_merge == 1) for v in r)
 
 
 CASES = [
@@ -205,6 +279,11 @@ def test_mfma_index_bounds(name, make, part):
     B = case.block_size
     max_ctx = case.max_context_len
     G = case.num_heads // case.num_kv_heads
+    if part == 0 and balanced_plan(case.num_seqs, case.num_kv_heads, max_ctx, G):
+        for wgs in (512, 256, 7, 1):
+            check_balanced_bounds(case.num_seqs, case.num_kv_heads, G, case.head_dim, B, case.num_blocks,
+                                  case.block_tables.shape[1], case.context_lens, case.block_tables, max_ctx, wgs)
+        return
     p = default_partition(case.num_seqs, case.num_kv_heads, max_ctx, G) if part == 0 else part
     if p == 1 << 30:
         p = max(1, max_ctx)
@@ -218,6 +297,32 @@ def test_mfma_gqa70b_bounds():
     case = wl.gqa_config("llama2-70b-tp8")
     check_mfma_bounds(case.num_seqs, case.num_kv_heads, 8, case.head_dim, case.block_size, case.num_blocks,
                       case.block_tables.shape[1], case.context_lens, case.block_tables, case.max_context_len, 256)
+
+
+@pytest.mark.parametrize("wgs", [512, 333, 64])
+def test_balanced_gqa70b_bounds(wgs):
+    case = wl.gqa_config("llama2-70b-tp8")
+    assert balanced_plan(case.num_seqs, case.num_kv_heads, case.max_context_len, 8)
+    check_balanced_bounds(case.num_seqs, case.num_kv_heads, 8, case.head_dim, case.block_size, case.num_blocks,
+                          case.block_tables.shape[1], case.context_lens, case.block_tables, case.max_context_len, wgs)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_balanced_random_lengths(seed):
+    """Empty, invalid, tiny and long contexts mixed; shares smaller and
+    larger than a context."""
+    rng = np.random.default_rng([29, seed])
+    S = int(rng.integers(1, 40))
+    Hk, G, B = int(rng.choice([1, 2, 4])), int(rng.choice([2, 4, 8])), int(rng.choice([1, 4, 16]))
+    ctx = rng.integers(1, 300, S)
+    ctx[rng.random(S) < 0.2] = 0
+    case = wl.random_case(30 + seed, S, Hk * G, 64, B, "f16", ctx=ctx.tolist(), num_kv_heads=Hk)
+    ctx2 = case.context_lens.copy()
+    if S > 2:
+        ctx2[1] = case.max_context_len + 5  # invalid: skipped, the merge kernel writes NaN
+    for wgs in (1, 3, 16, 512):
+        check_balanced_bounds(S, Hk, G, 64, B, case.num_blocks, case.block_tables.shape[1], ctx2,
+                              case.block_tables, case.max_context_len, wgs)
 
 
 @pytest.mark.parametrize("D", [64, 128, 256])
