@@ -85,12 +85,12 @@ typedef enum {
  * G = num_heads / num_kv_heads.
  *
  * Balanced split (G >= 2, R < 512, R * max_context_len < 2^31): returns
- * 256, the smallest share.  The matrix-core kernel then runs
- * 2 workgroups per compute unit (one per CU for head_dim 256), and each takes
- * an equal share (a multiple of 16 tokens, at least 256) of the batch's
- * (sequence, K/V head, token) work laid end to end, whatever the mix of
- * context lengths; a head whose tokens straddle shares is merged by a second
- * launch.  (For caches the matrix-core kernel does not serve, fp32 or
+ * 256, the smallest piece.  The matrix-core kernel then cuts each (sequence,
+ * K/V head) context into n = ceil(ctx / C) equal pieces, with C (>= 256)
+ * chosen on the device from the batch's total so that the pieces about fill
+ * the resident workgroups (2 per compute unit, 1 for head_dim 256),
+ * whatever the mix of context lengths; heads cut into several pieces are
+ * merged by a second launch.  (For caches the matrix-core kernel does not serve, fp32 or
  * head_dim below 64, and when a share would stage more than 6144 block ids,
  * pa_decode uses partitions of 256 tokens instead.)
  *
@@ -117,8 +117,8 @@ int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_heads, int32_t 
  * When a context spans several partitions, each partition's unnormalised
  * partial result (fp32 accumulator, maximum, sum) goes to the workspace and a
  * second kernel merges them.  Under a balanced split the workspace holds
- * ceil(max_context_len / 256) + 1 partials per query head and a table of
- * num_seqs + 2 int32 values.  Returns 0 when no sequence can span two
+ * ceil(max_context_len / 256) + 1 partials per query head and one int32
+ * (the piece length).  Returns 0 when no sequence can span two
  * partitions (then pa_decode accepts a NULL workspace), and 0 for invalid
  * sizes.  `partition_size` as for pa_decode_partition_tokens.
  */

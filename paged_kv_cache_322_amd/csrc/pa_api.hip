@@ -3,6 +3,7 @@
 // frees or synchronises.
 #include <math.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "../../include/pa.h"
@@ -28,20 +29,20 @@ int resolve_partition(int32_t partition_size, int32_t num_seqs, int32_t num_head
         .part_tokens;
 }
 
-// Partials per query head: one per partition; under a balanced plan a
-// head's run can straddle one more workgroup boundary than it has
-// kBalancedMinChunk-token pieces.
+// Partials per query head: one per partition (under a balanced plan, at
+// most one per kBalancedMinChunk tokens, plus one so that the workspace is
+// never empty: the piece length is stored after the partials).
 int64_t parts_for(int32_t max_context_len, int part, bool balanced) {
     const int64_t p = max_context_len <= 0 ? 1 : (static_cast<int64_t>(max_context_len) + part - 1) / part;
     return balanced ? p + 1 : p;
 }
 
 // Workspace bytes for the split path (partials, then the balanced plan's
-// int32 [S + 2] share table), or 0 when one partition always suffices.
+// int32 piece length), or 0 when one partition always suffices.
 size_t workspace_bytes_for(int64_t num_seqs, int64_t num_heads, int64_t head_dim, int64_t parts, bool balanced) {
     if (parts <= 1) return 0;
     return static_cast<size_t>(num_seqs * num_heads * parts * (head_dim + 2)) * sizeof(float) +
-           (balanced ? static_cast<size_t>(num_seqs + 2) * sizeof(int32_t) : 0);
+           (balanced ? sizeof(int32_t) : 0);
 }
 
 // Workgroups of a balanced split on the current device: kBalancedWgsPerCu
@@ -190,11 +191,12 @@ int decode_common(void* out, const void* query, const void* key, const void* val
     a.balanced_wgs = 0;
     a.staged_balanced = 0;
     if (plan.balanced) {
-        // A workgroup's run covers at most min(its share, the context) tokens.
+        // A workgroup's piece has at most min(C, the context) tokens, C as
+        // the kernel computes it (its total is at most pairs * max_context_len).
         a.balanced_wgs = balanced_workgroups(head_dim);
-        const int64_t total = static_cast<int64_t>(num_seqs) * num_kv_heads * max_context_len;
-        int64_t share = (total + a.balanced_wgs - 1) / a.balanced_wgs;
-        share = (share + 15) / 16 * 16;
+        const int64_t pairs = static_cast<int64_t>(num_seqs) * num_kv_heads;
+        const int64_t slots = std::max<int64_t>(1, a.balanced_wgs - pairs / 2);
+        int64_t share = (pairs * max_context_len + slots - 1) / slots;
         if (share < part) share = part;
         if (share > max_context_len) share = max_context_len;
         a.staged_balanced = static_cast<int>(pa::partition_blocks(share, block_size));

@@ -385,9 +385,8 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(
             for (int d = lane; d < D; d += kWave) out[sh * D + d] = narrow<T>(v);
             return;
         }
-        const int64_t C = meta[0];
-        const int64_t F = static_cast<int64_t>(num_kv_heads) * meta[1 + s] + static_cast<int64_t>(h / (num_heads / num_kv_heads)) * ctx;
-        np = static_cast<int>((F + ctx - 1) / C - F / C + 1);
+        const int C = meta[0];  // longest piece of the balanced split
+        np = (ctx + C - 1) / C;
         if (np == 1) return;
     } else {
         if (ctx <= part_tokens || ctx > max_context_len) return;  // written by the partition kernel
@@ -427,10 +426,12 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(
 template <class T, int D, int G>
 constexpr bool kUseMfma = sizeof(typename T::bits) == 2 && (D == 64 || D == 128 || D == 256) && G >= PA_MFMA_MIN_G;
 
-// Its static LDS is at most ~36 KB; partitions staging more block ids than
-// this (tiny blocks with very long forced partitions) keep the total within
-// 64 KB by taking the vector kernel.
-constexpr int kMfmaMaxStaged = 6144;
+// Its static LDS (per-wavefront K/V tiles) is ~44 KB for D = 64, ~77 KB for
+// D = 128 and ~143 KB for D = 256; partitions staging more block ids than
+// this (tiny blocks with very long partitions) take the vector kernel, so
+// that static plus staged ids stay within the CU's 160 KB.
+template <int D>
+constexpr int kMfmaMaxStaged = D == 256 ? 4096 : 6144;
 
 template <class T, int D, int G, bool APPEND, bool NT>
 hipError_t launch_decode_t(const DecodeArgs& a) {
@@ -446,8 +447,9 @@ hipError_t launch_decode_t(const DecodeArgs& a) {
     dim3 grid(a.num_kv_heads, a.num_seqs, a.max_parts);
     const size_t lds = static_cast<size_t>(a.staged_blocks) * sizeof(int);
     if constexpr (kUseMfma<T, D, G>) {
-        if (a.balanced && a.staged_balanced <= kMfmaMaxStaged) {
-            hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, APPEND, NT, true>), dim3(a.balanced_wgs), dim3(kMfmaThreads),
+        if (a.balanced && a.staged_balanced <= kMfmaMaxStaged<D>) {
+            const unsigned grid_b = static_cast<unsigned>(a.balanced_wgs + a.num_seqs * a.num_kv_heads);
+            hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, APPEND, NT, true>), dim3(grid_b), dim3(kMfmaThreads),
                                static_cast<size_t>(a.staged_balanced) * sizeof(int), a.stream, out, ws_o, ws_m, ws_l,
                                static_cast<const bits*>(a.query), static_cast<bits*>(a.k_cache),
                                static_cast<bits*>(a.v_cache), static_cast<const bits*>(a.key_new),
@@ -463,7 +465,7 @@ hipError_t launch_decode_t(const DecodeArgs& a) {
         }
         // Otherwise (and for a balanced plan whose runs would stage too many
         // block ids): partitions of part_tokens.
-        if (a.staged_blocks <= kMfmaMaxStaged) {
+        if (a.staged_blocks <= kMfmaMaxStaged<D>) {
             hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, APPEND, NT, false>), grid, dim3(kMfmaThreads), lds, a.stream,
                                out, ws_o, ws_m, ws_l, static_cast<const bits*>(a.query),
                                static_cast<bits*>(a.k_cache), static_cast<bits*>(a.v_cache),

@@ -58,12 +58,8 @@ namespace pa {
 #define PA_MFMA_WAVES 8  // wavefronts per workgroup of the matrix-core kernel
 #endif
 
-#ifndef PA_MFMA_PREFETCH
-#define PA_MFMA_PREFETCH 0  // keep the next tile's loads in flight while computing (measured slower: +36 VGPRs cost a wave of occupancy)
-#endif
 
 constexpr int kMfmaWaves = PA_MFMA_WAVES;
-constexpr bool kMfmaPrefetch = PA_MFMA_PREFETCH;
 constexpr int kMfmaThreads = kMfmaWaves * kWave;
 constexpr int kMfmaTile = 16;            // tokens per wavefront step
 constexpr int kMfmaMergeFloats = 8192;   // LDS floats for the cross-wave merge (32 KB)
@@ -74,7 +70,15 @@ constexpr int kMfmaMergeFloats = 8192;   // LDS floats for the cross-wave merge 
 #ifndef PA_MFMA_WAVES_PER_SIMD
 #define PA_MFMA_WAVES_PER_SIMD 4  // for D <= 128
 #endif
-constexpr int mfma_waves_per_simd(int D) { return D <= 128 ? PA_MFMA_WAVES_PER_SIMD : 2; }
+#ifndef PA_BAL_WAVES_PER_SIMD
+#define PA_BAL_WAVES_PER_SIMD 4  // balanced split, D <= 128
+#endif
+#ifndef PA_BAL_PREFETCH
+#define PA_BAL_PREFETCH 1
+#endif
+constexpr int mfma_waves_per_simd(int D, bool balanced) {
+    return D <= 128 ? (balanced ? PA_BAL_WAVES_PER_SIMD : PA_MFMA_WAVES_PER_SIMD) : 2;
+}
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -82,6 +86,19 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// gfx950 transposing LDS read (ds_read_b64_tr_b16).  In each group of 16
+// lanes, lanes 4r .. 4r + 3 each point at 4 consecutive 16-bit elements, the
+// four together a 16-element row segment r (r = 0..3); lane i of the group
+// receives column i of the 4 x 16 block, i.e. element i of segments 0..3.
+// p must be 8-byte aligned and point into LDS.
+__device__ __forceinline__ u32x2 lds_read_tr16_b64(const uint16_t* p) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    typedef __attribute__((address_space(3))) uint16_t lds_u16;
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_u16*)p));
+    return __builtin_bit_cast(u32x2, v);
+}
 
 // Matrix-core operations per 16-bit element type.
 template <class T>
@@ -181,7 +198,7 @@ __device__ __forceinline__ int longest_first_seq(const int32_t* __restrict__ con
 }
 
 template <class T, int D, int G, bool APPEND, bool NT, bool BALANCED>
-__global__ __launch_bounds__(kMfmaThreads, mfma_waves_per_simd(D)) void decode_mfma_kernel(
+__global__ __launch_bounds__(kMfmaThreads, mfma_waves_per_simd(D, BALANCED)) void decode_mfma_kernel(
     typename T::bits* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_m,
     float* __restrict__ ws_l, const typename T::bits* __restrict__ q, typename T::bits* __restrict__ kc,
     typename T::bits* __restrict__ vc, const typename T::bits* __restrict__ knew,
@@ -194,17 +211,25 @@ __global__ __launch_bounds__(kMfmaThreads, mfma_waves_per_simd(D)) void decode_m
     static_assert(G >= 1 && G <= 16, "group size");
     constexpr int KS = D / 32;  // q.k k-steps (8 channels per lane each)
     constexpr int E = D / 16;   // channels per lane of a V row = output tiles
-    constexpr int NW = E / 2;   // 32-bit words per lane of a V row
     constexpr int DP = D + 4;   // padded LDS row
     constexpr int HC0 = kMfmaMergeFloats / (kMfmaWaves * DP);
     constexpr int HC = HC0 >= G ? G : (HC0 >= 8 ? 8 : (HC0 >= 4 ? 4 : (HC0 >= 2 ? 2 : 1)));  // heads per merge pass
     static_assert(HC >= 1 && G % HC == 0, "merge chunk");
-    using bits = typename T::bits;
     using Ops = MfmaOps<T>;
 
+    // Per-wavefront K and V tiles (16 token rows each, rows padded by 32
+    // bytes); after the token loop the same LDS holds the merge rows s_o.
+    constexpr int LDW = D + 16;                      // tile row pitch (16-bit elements)
+    constexpr int TILE_ELEMS = 2 * kMfmaTile * LDW;  // K then V
+    constexpr int RPI = kWave * 8 / D;               // token rows per 16-byte-per-lane load
+    constexpr int NLD = kMfmaTile / RPI;             // loads per lane per tile, each of K and V
+    static_assert(kMfmaTile % RPI == 0, "tile rows per load");
+    constexpr size_t kTileBytes = sizeof(uint16_t) * TILE_ELEMS * kMfmaWaves;
+    constexpr size_t kMergeBytes = sizeof(float) * kMfmaWaves * HC * DP;
     extern __shared__ int s_blk[];  // this partition's block ids (dynamic size)
     __shared__ float s_m[kMfmaWaves][16], s_l[kMfmaWaves][16];
-    __shared__ float s_o[kMfmaWaves][HC][DP];
+    __shared__ __align__(16) unsigned char s_raw[kTileBytes > kMergeBytes ? kTileBytes : kMergeBytes];
+    auto s_o = reinterpret_cast<float (*)[HC][DP]>(s_raw);
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const int c = lane & 15, g = lane >> 4;
@@ -247,65 +272,74 @@ __global__ __launch_bounds__(kMfmaThreads, mfma_waves_per_simd(D)) void decode_m
 
     const int ntile = (t_end - t_begin + kMfmaTile - 1) / kMfmaTile;
 
-    struct Tile {
-        uint4 k[KS];         // key row of token tb + c, channels 32 ks + 8 g .. +7
-        uint32_t v[4][NW];   // value rows of tokens tb + 4 g + i, channels E c .. E c + E - 1
-    };
+    // This wavefront's tile buffers.
+    uint16_t* const sK = reinterpret_cast<uint16_t*>(s_raw) + wave * TILE_ELEMS;
+    uint16_t* const sV = sK + kMfmaTile * LDW;
 
-    // Issue the loads of tile `it`.  Tokens past the partition re-read its
-    // last token (always in bounds; masked out of the softmax).  In the
-    // newest tile t_end == ctx, and every lane whose clamped token is ctx - 1
-    // (the newest token and the masked lanes past it) reads the newest rows
-    // from knew/vnew, never the not-yet-written cache slot, whose contents
-    // may be anything (a masked token still multiplies its V row by p = 0,
-    // and 0 * NaN is NaN).
-    auto load_tile = [&](int it, Tile& tl) {
+    // Global loads of tile `it`, coalesced: load i of lane L reads 16 bytes
+    // (chunk L % (D / 8)) of token row RPI i + L / (D / 8), for K and for V.
+    // Tokens past the partition re-read its last token (always in bounds;
+    // masked out of the softmax).  In the newest tile t_end == ctx, rows
+    // whose clamped token is ctx - 1 (the newest token and the masked rows
+    // past it) come from knew/vnew, never from the not-yet-written cache
+    // slot, whose contents may be anything (a masked token still multiplies
+    // its V row by p = 0, and 0 * NaN is NaN).
+    const int ld_row = lane / (D / 8), ld_ch = lane % (D / 8);
+    uint4 kreg[NLD], vreg[NLD];
+    auto load_tile = [&](int it) {
         const int tb = t_begin + it * kMfmaTile;
         const bool newest = APPEND && newest_here && it == ntile - 1;  // wave-uniform
-        const int tk = min(tb + c, t_end - 1);
-        const int bk = s_blk[(tk >> log2_bs) - j0];
-        bad |= (bk < 0);
-        const uint64_t ek = static_cast<uint64_t>(static_cast<uint32_t>(max(bk, 0))) * blk_stride + head_off +
-                            static_cast<uint32_t>(tk & bmask) * D + 8 * g;
-        const bits* kp = (newest && tk == ctx - 1) ? knew + kv_row + 8 * g : kc + ek;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) tl.k[ks] = load16<NT>(kp + 32 * ks);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int tv = min(tb + 4 * g + i, t_end - 1);
-            const int bv = s_blk[(tv >> log2_bs) - j0];
-            bad |= (bv < 0);
-            const uint64_t ev = static_cast<uint64_t>(static_cast<uint32_t>(max(bv, 0))) * blk_stride + head_off +
-                                static_cast<uint32_t>(tv & bmask) * D + E * c;
-            load_words<NW, NT>((newest && tv == ctx - 1) ? vnew + kv_row + E * c : vc + ev, tl.v[i]);
+        for (int i = 0; i < NLD; ++i) {
+            const int t = min(tb + RPI * i + ld_row, t_end - 1);
+            const int b = s_blk[(t >> log2_bs) - j0];
+            bad |= (b < 0);
+            const uint64_t e = static_cast<uint64_t>(static_cast<uint32_t>(max(b, 0))) * blk_stride + head_off +
+                               static_cast<uint32_t>(t & bmask) * D + 8 * ld_ch;
+            const bool nw = newest && t == ctx - 1;
+            kreg[i] = load16<NT>(nw ? knew + kv_row + 8 * ld_ch : kc + e);
+            vreg[i] = load16<NT>(nw ? vnew + kv_row + 8 * ld_ch : vc + e);
         }
     };
-
-    auto compute_tile = [&](int it, const Tile& tl) {
-        const int tb = t_begin + it * kMfmaTile;
+    // Registers -> this wavefront's LDS tile; in append mode the lanes holding
+    // the newest token's rows (read from knew/vnew) also store them to the
+    // cache.
+    auto store_tile = [&](int it) {
+        // LDS accesses of one wavefront execute in order; the compiler must
+        // not move this tile's stores above the previous tile's reads.
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            *reinterpret_cast<uint4*>(sK + (RPI * i + ld_row) * LDW + 8 * ld_ch) = kreg[i];
+            *reinterpret_cast<uint4*>(sV + (RPI * i + ld_row) * LDW + 8 * ld_ch) = vreg[i];
+        }
         if constexpr (APPEND) {
             if (newest_here && it == ntile - 1) {
-                // The lanes whose own (unclamped) token is ctx - 1 store the
-                // newest rows they read from knew/vnew.
                 const int t = ctx - 1;
                 const int b = s_blk[(t >> log2_bs) - j0];
+                const int tb = t_begin + it * kMfmaTile;
                 const uint64_t e = static_cast<uint64_t>(static_cast<uint32_t>(max(b, 0))) * blk_stride + head_off +
-                                   static_cast<uint32_t>(t & bmask) * D;
-                if (b >= 0 && tb + c == t) {
+                                   static_cast<uint32_t>(t & bmask) * D + 8 * ld_ch;
 #pragma unroll
-                    for (int ks = 0; ks < KS; ++ks)
-                        *reinterpret_cast<uint4*>(kc + e + 8 * g + 32 * ks) = tl.k[ks];
+                for (int i = 0; i < NLD; ++i) {
+                    if (b >= 0 && tb + RPI * i + ld_row == t) {
+                        *reinterpret_cast<uint4*>(kc + e) = kreg[i];
+                        *reinterpret_cast<uint4*>(vc + e) = vreg[i];
+                    }
                 }
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (b >= 0 && tb + 4 * g + i == t) store_words<NW>(vc + e + E * c, tl.v[i]);
             }
         }
+        asm volatile("" ::: "memory");
+    };
 
-        // Scores S^T: lane (c, g) gets tokens tb + 4 g + j of head c.
+    auto compute_tile = [&](int it) {
+        const int tb = t_begin + it * kMfmaTile;
+        // Scores S^T: lane (c, g) gets tokens tb + 4 g + j of head c; its K
+        // operand is token c's channels 32 ks + 8 g .. +7.
         f32x4 sc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) sc = Ops::qk(as_u32x4(tl.k[ks]), qv[ks], sc);
+        for (int ks = 0; ks < KS; ++ks)
+            sc = Ops::qk(as_u32x4(*reinterpret_cast<const uint4*>(sK + c * LDW + 32 * ks + 8 * g)), qv[ks], sc);
 
         float x[4];
         float mx = -INFINITY;
@@ -335,38 +369,35 @@ __global__ __launch_bounds__(kMfmaThreads, mfma_waves_per_simd(D)) void decode_m
         Ops::split(p[2], p[3], ph1, pl1);
         const u32x2 bh = u32x2{ph0, ph1}, bl = u32x2{pl0, pl1};
 
-        // O^T += V^T P^T, one output tile per channel offset t.
+        // O^T += V^T P^T, output tile t = channels 16 t .. 16 t + 15.  The A
+        // operand (channel 16 t + c of tokens 4 g .. 4 g + 3) is one
+        // transposing LDS read: lanes 4 r + q of group g point at token row
+        // 4 g + r, channels 16 t + 4 q .. +3.
+        const uint16_t* vt = sV + (4 * g + (c >> 2)) * LDW + 4 * (c & 3);
 #pragma unroll
         for (int t = 0; t < E; ++t) {
-            const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
-            const u32x2 a = u32x2{__builtin_amdgcn_perm(tl.v[1][t / 2], tl.v[0][t / 2], sel),
-                                  __builtin_amdgcn_perm(tl.v[3][t / 2], tl.v[2][t / 2], sel)};
+            const u32x2 a = lds_read_tr16_b64(vt + 16 * t);
             acc[t] = Ops::pv(a, bh, acc[t]);
             acc[t] = Ops::pv(a, bl, acc[t]);
         }
     };
 
+    // Software pipeline: the next tile's global loads are in flight while
+    // the current tile is computed from LDS.
     int it = wave;
-    if constexpr (!kMfmaPrefetch) {
+    if (BALANCED && !PA_BAL_PREFETCH) {
         for (; it < ntile; it += kMfmaWaves) {
-            Tile ta;
-            load_tile(it, ta);
-            compute_tile(it, ta);
+            load_tile(it);
+            store_tile(it);
+            compute_tile(it);
         }
     } else if (it < ntile) {
-        // Software pipeline: the next tile's loads are in flight while the
-        // current one is computed.
-        Tile ta, tb2;
-        load_tile(it, ta);
+        load_tile(it);
         while (true) {
-            int nx = it + kMfmaWaves;
-            if (nx < ntile) load_tile(nx, tb2);
-            compute_tile(it, ta);
-            if (nx >= ntile) break;
-            it = nx;
-            nx = it + kMfmaWaves;
-            if (nx < ntile) load_tile(nx, ta);
-            compute_tile(it, tb2);
+            store_tile(it);
+            const int nx = it + kMfmaWaves;
+            if (nx < ntile) load_tile(nx);
+            compute_tile(it);
             if (nx >= ntile) break;
             it = nx;
         }
@@ -386,7 +417,7 @@ __global__ __launch_bounds__(kMfmaThreads, mfma_waves_per_simd(D)) void decode_m
 #pragma unroll
             for (int t = 0; t < E; ++t)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) s_o[wave][c - c0][E * (4 * g + j) + t] = acc[t][j];
+                for (int j = 0; j < 4; ++j) s_o[wave][c - c0][16 * t + 4 * g + j] = acc[t][j];
         }
         __syncthreads();
         for (int idx = tid; idx < HC * D; idx += kMfmaThreads) {
@@ -417,24 +448,21 @@ __global__ __launch_bounds__(kMfmaThreads, mfma_waves_per_simd(D)) void decode_m
     }
     };
 
-    // Classic plans: one workgroup per (K/V head, sequence row, partition),
-    // one run.  Balanced split: the work is the flat sequence of (sequence
-    // s, K/V head hk, token t) in that order, sequence s contributing n_s =
-    // ctx_s tokens per K/V head (0 for an empty or invalid context, whose
-    // output the merge kernel writes).  Workgroup w takes the C consecutive
-    // items [w C, (w + 1) C), C = max(part_tokens, ceil(total / num_wgs))
-    // rounded up to a whole tile, and makes one run per (s, hk) inside it.
-    // A run that is a whole (s, hk) writes the output; otherwise its partial
-    // goes to slot w - floor(F / C) of that head's partials, F being the flat
-    // index of the pair's first token, and the merge kernel combines the
-    // floor((F + n_s - 1) / C) - floor(F / C) + 1 partials.
-    __shared__ int s_pre[kMaxLptSeqs + 1];  // balanced: s_pre[i] = n_0 + ... + n_{i-1}
-    constexpr bool balanced = BALANCED;  // (mode == kPlanBalanced)
-    int s = 0, hk = 0, ctx = 0, t_begin = 0, t_end = 0, slot = 0;
-    bool single = false;
-    int64_t x = 0, x_end = 0, C = 1;
-    const int w = blockIdx.x;
-    if constexpr (!balanced) {
+    // Classic plans: one workgroup per (K/V head, sequence row, partition).
+    // Balanced split: every (sequence s, K/V head) pair with a valid
+    // context of ctx_s tokens is cut into n_s = ceil(ctx_s / C) pieces of
+    // ceil(ctx_s / n_s) <= C tokens (the last one shorter, never empty),
+    // C = max(part_tokens, ceil(total / (num_wgs - pairs / 2))), total the
+    // batch's tokens over all K/V heads: with ceil's half piece of slack per
+    // pair, the pieces about fill the num_wgs resident workgroups.  The grid
+    // has num_wgs + pairs workgroups (an upper bound); workgroup w takes the
+    // w-th piece in (sequence, K/V head, piece) order, found from prefix sums
+    // of Hk n_s.  A pair cut into one piece writes the output; otherwise
+    // piece k is partial slot k and the merge kernel combines n_s of them.
+    __shared__ int s_pre[kMaxLptSeqs + 1];
+    int s, hk, ctx, t_begin, t_end, slot;
+    bool single;
+    if constexpr (!BALANCED) {
         hk = blockIdx.x;
         const int srow = blockIdx.y, part = blockIdx.z;
         s = mode == kPlanLongestFirst ? longest_first_seq<kMfmaThreads>(context_lens, num_seqs, srow, tid) : srow;
@@ -453,63 +481,60 @@ __global__ __launch_bounds__(kMfmaThreads, mfma_waves_per_simd(D)) void decode_m
         single = ctx <= part_tokens;
         slot = part;
     } else {
+        // Inclusive scan of s_pre[1..S] (Hillis-Steele); s_pre[0] = 0.
+        auto scan = [&]() {
+            for (int off = 1; off <= num_seqs; off <<= 1) {
+                int v[kMaxLptSeqs / kMfmaThreads + 1];
+                int k = 0;
+                for (int i = tid + 1; i <= num_seqs; i += kMfmaThreads, ++k) v[k] = (i > off) ? s_pre[i - off] : 0;
+                __syncthreads();
+                k = 0;
+                for (int i = tid + 1; i <= num_seqs; i += kMfmaThreads, ++k) s_pre[i] += v[k];
+                __syncthreads();
+            }
+        };
         for (int i = tid; i < num_seqs; i += kMfmaThreads) {
             const int n = context_lens[i];
             s_pre[i + 1] = (n > 0 && n <= max_context_len) ? n : 0;
         }
         if (tid == 0) s_pre[0] = 0;
         __syncthreads();
-        for (int off = 1; off <= num_seqs; off <<= 1) {  // inclusive scan of s_pre[1..S] (Hillis-Steele)
-            int v[kMaxLptSeqs / kMfmaThreads + 1];
-            int k = 0;
-            for (int i = tid + 1; i <= num_seqs; i += kMfmaThreads, ++k) v[k] = (i > off) ? s_pre[i - off] : 0;
-            __syncthreads();
-            k = 0;
-            for (int i = tid + 1; i <= num_seqs; i += kMfmaThreads, ++k) s_pre[i] += v[k];
-            __syncthreads();
-        }
-        // (Values read from LDS are made scalar: they are uniform, and the
-        // per-run state then costs no vector registers.)
+        scan();
         const int64_t total = static_cast<int64_t>(num_kv_heads) * __builtin_amdgcn_readfirstlane(s_pre[num_seqs]);
-        int64_t chunk = (total + num_wgs - 1) / num_wgs;
-        chunk = (chunk + kMfmaTile - 1) / kMfmaTile * kMfmaTile;
-        C = chunk > part_tokens ? chunk : part_tokens;
-        if (w == 0) {  // for the merge kernel
-            if (tid == 0) meta[0] = static_cast<int32_t>(C);
-            for (int i = tid; i <= num_seqs; i += kMfmaThreads) meta[1 + i] = s_pre[i];
+        const int pairs = num_seqs * num_kv_heads;
+        const int64_t slots = max(1, num_wgs - pairs / 2);
+        const int C = __builtin_amdgcn_readfirstlane(
+            static_cast<int>(max(static_cast<int64_t>(part_tokens), (total + slots - 1) / slots)));
+        if (blockIdx.x == 0 && tid == 0) meta[0] = C;  // for the merge kernel
+        __syncthreads();  // every thread has read s_pre[num_seqs]
+        for (int i = tid; i < num_seqs; i += kMfmaThreads) {
+            const int n = context_lens[i];
+            s_pre[i + 1] = (n > 0 && n <= max_context_len) ? (n + C - 1) / C : 0;  // pieces per K/V head
         }
-        x = static_cast<int64_t>(w) * C;
-        x_end = min(total, x + C);
-        if (x >= x_end) return;
-    }
-    while (true) {
-        int64_t seg_end = 0;
-        if constexpr (balanced) {
-            // The sequence holding flat index x: the last s with Hk * pre[s] <= x.
-            int lo = 0, hi = num_seqs - 1;
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (static_cast<int64_t>(num_kv_heads) * s_pre[mid] <= x) lo = mid;
-                else hi = mid - 1;
-            }
-            s = __builtin_amdgcn_readfirstlane(lo);
-            const int pre_s = __builtin_amdgcn_readfirstlane(s_pre[s]);
-            ctx = __builtin_amdgcn_readfirstlane(s_pre[s + 1]) - pre_s;  // > 0: x lies in sequence s's range
-            const int64_t off = x - static_cast<int64_t>(num_kv_heads) * pre_s;
-            hk = __builtin_amdgcn_readfirstlane(static_cast<int>(off / ctx));
-            t_begin = __builtin_amdgcn_readfirstlane(static_cast<int>(off % ctx));
-            const int64_t F = x - t_begin;  // flat index of (s, hk, 0)
-            seg_end = min(x_end, F + ctx);
-            t_end = __builtin_amdgcn_readfirstlane(t_begin + static_cast<int>(seg_end - x));
-            const int64_t first = F / C, last = (F + ctx - 1) / C;
-            single = __builtin_amdgcn_readfirstlane(static_cast<int>(first == last)) != 0;
-            slot = __builtin_amdgcn_readfirstlane(static_cast<int>(w - first));
+        __syncthreads();
+        scan();
+        const int w = blockIdx.x;
+        if (w >= num_kv_heads * __builtin_amdgcn_readfirstlane(s_pre[num_seqs])) return;
+        // The sequence of piece w: the last s with Hk * pre[s] <= w.
+        int lo = 0, hi = num_seqs - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (num_kv_heads * s_pre[mid] <= w) lo = mid;
+            else hi = mid - 1;
         }
-        run_segment(s, hk, ctx, t_begin, t_end, single, slot);
-        if constexpr (!balanced) break;
-        x = seg_end;
-        if (x >= x_end) break;
+        s = __builtin_amdgcn_readfirstlane(lo);
+        const int pre_s = __builtin_amdgcn_readfirstlane(s_pre[s]);
+        const int n = __builtin_amdgcn_readfirstlane(s_pre[s + 1]) - pre_s;  // > 0
+        const int r = w - num_kv_heads * pre_s;
+        hk = r / n;
+        slot = r % n;
+        ctx = __builtin_amdgcn_readfirstlane(context_lens[s]);
+        const int len = (ctx + n - 1) / n;
+        t_begin = slot * len;
+        t_end = min(ctx, t_begin + len);
+        single = n == 1;
     }
+    run_segment(s, hk, ctx, t_begin, t_end, single, slot);
 }
 
 }  // namespace pa

@@ -96,11 +96,11 @@ def test_workspace_size():
     assert pa.decode_workspace_size(-1, 1, 8, 37, 16) == 0
     # One K/V head serving 8 query heads, 128 sequences up to 4096 tokens:
     # balanced split, up to 4096 / 256 + 1 = 17 partials per head, and the
-    # int32 [S + 2] share table.
-    assert pa.decode_workspace_size(128, 8, 128, 4096, num_kv_heads=1) == 128 * 8 * 17 * 130 * 4 + 130 * 4
+    # int32 piece length.
+    assert pa.decode_workspace_size(128, 8, 128, 4096, num_kv_heads=1) == 128 * 8 * 17 * 130 * 4 + 4
     assert pa.decode_workspace_size(64, 32, 128, 2048, num_kv_heads=8) == 0  # whole contexts, longest first
-    assert pa.decode_workspace_size(60, 32, 128, 2048, num_kv_heads=8) == 60 * 32 * 9 * 130 * 4 + 62 * 4
-    assert pa.decode_workspace_size(4, 8, 64, 100, num_kv_heads=1) == 4 * 8 * 2 * 66 * 4 + 6 * 4
+    assert pa.decode_workspace_size(60, 32, 128, 2048, num_kv_heads=8) == 60 * 32 * 9 * 130 * 4 + 4
+    assert pa.decode_workspace_size(4, 8, 64, 100, num_kv_heads=1) == 4 * 8 * 2 * 66 * 4 + 4
     assert pa.decode_workspace_size(2, 30, 128, 100, num_kv_heads=8) == 0  # invalid grouping
 
 

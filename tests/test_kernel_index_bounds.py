@@ -126,8 +126,8 @@ def check_mfma_bounds(S, Hk, G, D, B, N, W, ctx, bt, max_ctx, part):
     # Merge buffer indices.
     hc = mfma_merge_heads(D, G)
     assert G % hc == 0
-    col = E * (4 * g[:, None, None] + np.arange(4)[None, :, None]) + np.arange(E)[None, None, :]
-    assert col.min() >= 0 and col.max() < D
+    col = 16 * np.arange(E)[None, None, :] + 4 * g[:, None, None] + np.arange(4)[None, :, None]
+    assert col.min() >= 0 and col.max() < D and len(np.unique(col)) == D
     assert MFMA_WAVES * hc * (D + 4) <= MFMA_MERGE_FLOATS or hc == 1
     staged = (part + B - 1) // B + 1
     max_parts = max(1, math.ceil(max_ctx / part))
@@ -144,30 +144,46 @@ def check_mfma_bounds(S, Hk, G, D, B, N, W, ctx, bt, max_ctx, part):
 
 def mfma_run_checks(s, cl, t_begin, t_end, staged, Hk, D, B, N, W, bt):
     """One run of the matrix-core kernel over tokens [t_begin, t_end) of
-    sequence s (context cl): staged block ids, clamped K/V addresses."""
+    sequence s (context cl): staged block ids; coalesced K/V loads (load i of
+    lane L: token row RPI i + L // (D / 8) of the 16-token tile, clamped to
+    t_end - 1, 16-byte chunk L % (D / 8)); the wavefront's LDS tiles (16
+    rows of D + 16 elements; K operand rows c, channels 32 ks + 8 g .. +7;
+    transposing V reads at rows 4 g + c // 4, channels 16 t + 4 (c % 4) .. +3,
+    8-byte aligned)."""
     E, KS = D // 16, D // 32
     c, g = np.arange(16), np.arange(4)
-    k_lo = (32 * np.arange(KS)[:, None] + 8 * g[None, :]).ravel()
-    v_lo = E * c
+    lane = np.arange(64)
+    rpi = 64 * 8 // D
+    nld = MFMA_TILE // rpi
+    ld_row, ld_ch = lane // (D // 8), lane % (D // 8)
     log2b = B.bit_length() - 1
     blk_stride = Hk * B * D
     cache_elems = N * Hk * B * D
+    ldw = D + 16
     assert 0 <= t_begin < t_end <= cl
     j0 = t_begin >> log2b
     nblk = ((t_end - 1) >> log2b) - j0 + 1
     assert 1 <= nblk <= staged and j0 + nblk - 1 < W
     ntile = (t_end - t_begin + MFMA_TILE - 1) // MFMA_TILE
     tb = t_begin + np.arange(ntile)[:, None] * MFMA_TILE
-    tk = np.minimum(tb + c[None, :], t_end - 1).ravel()
-    tv = np.minimum(tb + (4 * g[:, None] + np.arange(4)[None, :]).ravel()[None, :], t_end - 1).ravel()
-    for t, lo, width in ((tk, k_lo, 8), (tv, v_lo, E)):
-        assert t.min() >= t_begin
-        lds = (t >> log2b) - j0
-        assert lds.min() >= 0 and lds.max() < nblk
-        b = bt[s, j0 + lds]
-        b = np.where((b >= 0) & (b < N), b, 0)
-        e = b.astype(np.int64) * blk_stride + (Hk - 1) * B * D + (t & (B - 1)).astype(np.int64) * D
-        assert e.min() >= 0 and e.max() + lo.max() + width <= cache_elems
+    rows = (rpi * np.arange(nld)[:, None] + ld_row[None, :]).ravel()
+    assert rows.min() >= 0 and rows.max() < MFMA_TILE and 8 * ld_ch.max() + 8 <= D
+    t = np.minimum(tb + rows[None, :], t_end - 1).ravel()
+    assert t.min() >= t_begin
+    lds = (t >> log2b) - j0
+    assert lds.min() >= 0 and lds.max() < nblk
+    b = bt[s, j0 + lds]
+    b = np.where((b >= 0) & (b < N), b, 0)
+    e = b.astype(np.int64) * blk_stride + (Hk - 1) * B * D + (t & (B - 1)).astype(np.int64) * D
+    assert e.min() >= 0 and e.max() + 8 * ld_ch.max() + 8 <= cache_elems
+    # LDS tile reads and writes stay inside the wavefront's 2 x 16 x ldw tile.
+    assert (MFMA_TILE - 1) * ldw + 8 * ld_ch.max() + 8 <= MFMA_TILE * ldw
+    k_hi = (MFMA_TILE - 1) * ldw + 32 * (KS - 1) + 8 * 3 + 8
+    assert k_hi <= MFMA_TILE * ldw
+    tr = (4 * g[:, None] + c[None, :] // 4) * ldw + 4 * (c[None, :] % 4)
+    tr_all = tr[..., None] + 16 * np.arange(E)
+    assert tr_all.max() + 4 <= MFMA_TILE * ldw and (tr_all % 4 == 0).all() and (ldw * 2) % 8 == 0
+    assert (16 * (E - 1) + 4 * 3 + 4) <= D  # a row's channels only
     # The newest token (append) is token cl - 1, covered by the last tile.
     if t_end == cl:
         last = tb[-1, 0]
@@ -175,55 +191,56 @@ def mfma_run_checks(s, cl, t_begin, t_end, staged, Hk, D, B, N, W, bt):
 
 
 def check_balanced_bounds(S, Hk, G, D, B, N, W, ctx, bt, max_ctx, num_wgs):
-    """The balanced split: workgroup w takes flat items [w C, (w + 1) C) of
-    the (sequence, K/V head, token) sequence; every run's reads stay in
-    bounds, every valid (sequence, K/V head) is covered exactly once, its
-    partial slots are 0 .. np - 1 with np the merge kernel's count, and the
-    workspace and share table hold every slot."""
+    """The balanced split: each valid (sequence, K/V head) context is cut
+    into n = ceil(ctx / C) pieces of ceil(ctx / n) tokens, C = max(256,
+    ceil(total / (num_wgs - pairs // 2))); workgroup w (of num_wgs + pairs)
+    takes the w-th piece in (sequence, K/V head, piece) order.  Every piece's
+    reads stay in bounds, every token is covered exactly once, pieces are
+    never empty, the partial slots 0 .. n - 1 match the merge kernel's count
+    ceil(ctx / C), and the workspace holds every slot."""
     P = BALANCED_MIN_CHUNK
     max_parts = -(-max_ctx // P) + 1 if max_ctx > 0 else 2
-    n = np.array([int(x) if 0 < int(x) <= max_ctx else 0 for x in ctx], dtype=np.int64)
-    pre = np.concatenate([[0], np.cumsum(n)])
-    total = Hk * int(pre[-1])
-    C = max(P, -(-(-(-total // num_wgs)) // MFMA_TILE) * MFMA_TILE)
+    pairs = S * Hk
+    valid = np.array([0 < int(x) <= max_ctx for x in ctx])
+    n_tok = np.where(valid, np.asarray(ctx, dtype=np.int64), 0)
+    total = Hk * int(n_tok.sum())
+    slots = max(1, num_wgs - pairs // 2)
+    C = max(P, -(-total // slots))
     assert C < (1 << 31)
-    share = -(-(S * Hk * max_ctx) // num_wgs)
-    share = min(max(P, -(-share // 16) * 16), max_ctx)
+    share = min(max(P, -(-(pairs * max_ctx) // slots)), max_ctx)  # host bound of the staged ids
+    assert C <= share or C > max_ctx
     staged = -(-share // B) + 1
+    pieces = np.where(valid, -(-n_tok // C), 0)
+    pre = np.concatenate([[0], np.cumsum(pieces)])
+    assert Hk * int(pre[-1]) <= num_wgs + pairs  # the grid covers every piece
     H = Hk * G
     ws_rows = S * H * max_parts
     runs = {}
-    for w in range(num_wgs):
-        x, x_end = w * C, min(total, w * C + C)
-        while x < x_end:
-            s = int(np.searchsorted(Hk * pre[:S], x, side="right")) - 1
-            cn = int(n[s])
-            assert cn > 0
-            off = x - Hk * int(pre[s])
-            hk, t0 = off // cn, off % cn
-            F = x - t0
-            seg_end = min(x_end, F + cn)
-            t1 = t0 + (seg_end - x)
-            first, last = F // C, (F + cn - 1) // C
-            slot = w - first
-            assert 0 <= slot <= last - first and slot < max_parts
-            mfma_run_checks(s, cn, t0, t1, staged, Hk, D, B, N, W, bt)
-            for h in range(hk * G, hk * G + G):  # workspace rows of the group's query heads
-                assert (s * H + h) * max_parts + slot < ws_rows
-            runs.setdefault((s, hk), []).append((slot, t0, t1, first == last))
-            x = seg_end
-    assert 1 + S < S + 2  # share table: C, then pre[0..S]
+    for w in range(num_wgs + pairs):
+        if w >= Hk * int(pre[-1]):
+            continue
+        s = int(np.searchsorted(Hk * pre[:S], w, side="right")) - 1
+        n = int(pieces[s])
+        assert n > 0
+        r = w - Hk * int(pre[s])
+        hk, slot = r // n, r % n
+        cl = int(ctx[s])
+        ln = -(-cl // n)
+        t0, t1 = slot * ln, min(cl, slot * ln + ln)
+        assert t0 < t1 and t1 - t0 <= min(C, share)
+        assert slot < max_parts and n == -(-cl // C)  # the merge kernel's count
+        mfma_run_checks(s, cl, t0, t1, staged, Hk, D, B, N, W, bt)
+        for h in range(hk * G, hk * G + G):
+            assert (s * H + h) * max_parts + slot < ws_rows
+        runs.setdefault((s, hk), []).append((slot, t0, t1))
     for s in range(S):
         for hk in range(Hk):
-            if n[s] == 0:
+            if not valid[s]:
                 assert (s, hk) not in runs  # the merge kernel writes 0 or NaN
                 continue
             r = sorted(runs[(s, hk)], key=lambda v: v[1])
-            assert r[0][1] == 0 and r[-1][2] == n[s] and all(a[2] == b[1] for a, b in zip(r, r[1:]))
-            F = Hk * int(pre[s]) + hk * int(n[s])
-            np_merge = (F + int(n[s]) - 1) // C - F // C + 1
-            assert sorted(v[0] for v in r) == list(range(np_merge))
-            assert all(v[3] == (np_merge == 1) for v in r)
+            assert r[0][1] == 0 and r[-1][2] == int(ctx[s]) and all(a[2] == b[1] for a, b in zip(r, r[1:]))
+            assert sorted(v[0] for v in r) == list(range(int(pieces[s])))
 
 
 CASES = [
@@ -287,7 +304,7 @@ def test_mfma_index_bounds(name, make, part):
     p = default_partition(case.num_seqs, case.num_kv_heads, max_ctx, G) if part == 0 else part
     if p == 1 << 30:
         p = max(1, max_ctx)
-    if (p + B - 1) // B + 1 > 6144:
+    if (p + B - 1) // B + 1 > (4096 if case.head_dim == 256 else 6144):
         pytest.skip("such partitions take the vector kernel")
     check_mfma_bounds(case.num_seqs, case.num_kv_heads, case.num_heads // case.num_kv_heads, case.head_dim, B,
                       case.num_blocks, case.block_tables.shape[1], case.context_lens, case.block_tables, max_ctx, p)
