@@ -129,6 +129,16 @@ def test_16bit_partition_beyond_matrix_core_staging():
     full_parity(case, partitions=(6300, 0), strict=False)
 
 
+def test_head_dim_256_staging_limit():
+    # At head_dim 256 the matrix-core kernel's per-wavefront tiles take
+    # 143 KB of LDS, so it stages at most 4096 block ids: a 4000-token
+    # partition of 1-token blocks runs on the matrix cores (159 KB of LDS in
+    # all), a 5000-token one on the vector kernel; both match the oracle, as
+    # does the default plan (a balanced split).
+    case = wl.random_case(304, 2, 8, 256, 1, "f16", ctx=[5200, 300], spare_blocks=3, num_kv_heads=2)
+    full_parity(case, partitions=(4000, 5000, 0), strict=False)
+
+
 def test_empty_calls_are_no_ops():
     case = wl.random_case(302, 2, 2, 64, 8, "f16", ctx=[3, 9])
     g = GpuCase(case)
