@@ -67,18 +67,7 @@ constexpr int kMfmaMergeFloats = 8192;   // LDS floats for the cross-wave merge 
 // Register budget of the kernel: wavefronts per SIMD it must fit (4, i.e.
 // <= 128 VGPRs and 2 resident 8-wavefront workgroups per CU, for D <= 128;
 // 2 for D = 256).  The balanced split launches that many workgroups per CU.
-#ifndef PA_MFMA_WAVES_PER_SIMD
-#define PA_MFMA_WAVES_PER_SIMD 4  // for D <= 128
-#endif
-#ifndef PA_BAL_WAVES_PER_SIMD
-#define PA_BAL_WAVES_PER_SIMD 4  // balanced split, D <= 128
-#endif
-#ifndef PA_BAL_PREFETCH
-#define PA_BAL_PREFETCH 1
-#endif
-constexpr int mfma_waves_per_simd(int D, bool balanced) {
-    return D <= 128 ? (balanced ? PA_BAL_WAVES_PER_SIMD : PA_MFMA_WAVES_PER_SIMD) : 2;
-}
+constexpr int mfma_waves_per_simd(int D) { return D <= 128 ? 4 : 2; }
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -198,7 +187,7 @@ __device__ __forceinline__ int longest_first_seq(const int32_t* __restrict__ con
 }
 
 template <class T, int D, int G, bool APPEND, bool NT, bool BALANCED>
-__global__ __launch_bounds__(kMfmaThreads, mfma_waves_per_simd(D, BALANCED)) void decode_mfma_kernel(
+__global__ __launch_bounds__(kMfmaThreads, mfma_waves_per_simd(D)) void decode_mfma_kernel(
     typename T::bits* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_m,
     float* __restrict__ ws_l, const typename T::bits* __restrict__ q, typename T::bits* __restrict__ kc,
     typename T::bits* __restrict__ vc, const typename T::bits* __restrict__ knew,
@@ -385,13 +374,7 @@ __global__ __launch_bounds__(kMfmaThreads, mfma_waves_per_simd(D, BALANCED)) voi
     // Software pipeline: the next tile's global loads are in flight while
     // the current tile is computed from LDS.
     int it = wave;
-    if (BALANCED && !PA_BAL_PREFETCH) {
-        for (; it < ntile; it += kMfmaWaves) {
-            load_tile(it);
-            store_tile(it);
-            compute_tile(it);
-        }
-    } else if (it < ntile) {
+    if (it < ntile) {
         load_tile(it);
         while (true) {
             store_tile(it);
