@@ -63,6 +63,15 @@ def test_config5_opt175b_shape_sampled():
     full_parity(case, partitions=(0,), seqs=seqs)
 
 
+def test_config5_tp8_share_sampled():
+    # One tensor-parallel rank's share of the OPT-175B-shaped layer: 96 heads
+    # over 8 GPUs leave 12 per GPU, with the same block tables and lengths.
+    case = wl.config5(num_heads=12)
+    order = np.argsort(case.context_lens)
+    seqs = sorted(set(order[:: max(1, case.num_seqs // 16)].tolist() + [int(order[-1]), int(order[0])]))
+    full_parity(case, partitions=(0, 512), seqs=seqs)
+
+
 SWEEP = [
     # dtype, head_dim, block_size, ctx, partition
     ("f32", 128, 16, [1, 17, 300, 1299], 0),
