@@ -120,6 +120,14 @@ __device__ __forceinline__ uint32_t pack_f16_rne(float p0, float p1) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{p0, p1}), f16x2_t));
 }
 
+// acc + x.lo + x.hi for a packed pair of fp16 values x (v_dot2_f32_f16
+// against (1, 1)): one instruction for two terms of a row sum.
+__device__ __forceinline__ float dot2_f16_ones(uint32_t x, float acc) {
+    typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+    const f16x2_t one = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, x), one, acc, false);
+}
+
 constexpr int kPfWavesPerSimd = 3;  // register budget: <= 168 VGPRs, 3 workgroups per CU
 
 // gfx950 transposing LDS read (ds_read_b64_tr_b16).  In each group of 16
@@ -290,52 +298,74 @@ __global__ __launch_bounds__(kPfThreads, kPfWavesPerSimd) void prefill_kernel(
             u32x4 bh[RB], bl[RB];
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
-                // Keys above the diagonal exist only in tiles reaching past
-                // the block's first row (wave-uniform test).
-                const bool full = k0 + kPfKeys - 1 <= wpos0 + 16 * rb;
                 float raw[8];
 #pragma unroll
                 for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) raw[4 * sub + j] = sc[rb][sub][j];
+                // Exponent arguments against the current reference m.
+                float t[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) t[i] = fmaf(raw[i], sc_mul, -m[rb]);
+                // Keys above the diagonal exist only in tiles reaching past
+                // the block's first row (wave-uniform test).  Key k0 + 16 sub
+                // + 4 g + j is visible to this lane's row iff 16 sub + j <=
+                // pos - k0 - 4 g; a hidden key gets exponent -inf (p = 0),
+                // whatever the scale (also 0).
+                const bool full = k0 + kPfKeys - 1 <= wpos0 + 16 * rb;
+                const int lim = full ? kPfKeys : pos[rb] - k0 - 4 * g;
                 if (!full) {
-                    // Diagonal tile: key k0 + 16 sub + 4 g + j is visible to
-                    // this lane's row iff 16 sub + j <= pos - k0 - 4 g.  (The
-                    // empty asm keeps this a branch around the tile instead
-                    // of selects executed on every tile.)
+                    // (The empty asm keeps this a branch around the tile
+                    // instead of selects executed on every tile.)
                     asm volatile("");
-                    const int lim = pos[rb] - k0 - 4 * g;
 #pragma unroll
                     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
                         for (int j = 0; j < 4; ++j)
-                            if (16 * sub + j > lim) raw[4 * sub + j] = -INFINITY;
+                            if (16 * sub + j > lim) t[4 * sub + j] = -INFINITY;
                 }
-                float mx = -INFINITY;
+                float tmax = t[0];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) mx = fmaxf(mx, raw[i]);
-                mx = max_over_groups(mx) * sc_mul;  // every row has a valid key here: finite (tile 0 holds key 0)
-                if (__builtin_amdgcn_ballot_w64(mx > m[rb] + kPfRescaleSlack)) {
-                    const float m_new = fmaxf(m[rb], mx);
+                for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, t[i]);
+                // The reference moves only when some key of the wavefront's
+                // rows exceeds it by more than the slack (always on the
+                // first tile, where m = -inf); then the row maximum over
+                // the visible keys becomes the reference.
+                if (__builtin_amdgcn_ballot_w64(tmax > kPfRescaleSlack)) {
+                    float mr = -INFINITY;
+#pragma unroll
+                    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            if (16 * sub + j <= lim) mr = fmaxf(mr, raw[4 * sub + j]);
+                    // Every row sees key 0 on tile 0, so m is finite from then on.
+                    const float m_new = fmaxf(m[rb], max_over_groups(mr) * sc_mul);
                     const float alpha = fast_exp2(m[rb] - m_new);  // 0 on the first tile (m = -inf)
                     l[rb] *= alpha;
 #pragma unroll
-                    for (int t = 0; t < E; ++t) acc[rb][t] *= alpha;
+                    for (int t2 = 0; t2 < E; ++t2) acc[rb][t2] *= alpha;
                     m[rb] = m_new;
+#pragma unroll
+                    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            t[4 * sub + j] = 16 * sub + j <= lim ? fmaf(raw[4 * sub + j], sc_mul, -m_new) : -INFINITY;
                 }
                 float p[8];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    p[i] = fast_exp2(fmaf(raw[i], sc_mul, -m[rb]));  // masked: exp2(-inf) = 0
-                    l[rb] += p[i];
-                }
+                for (int i = 0; i < 8; ++i) p[i] = fast_exp2(t[i]);  // <= 2^slack
                 uint32_t ph[4], pl[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    if constexpr (kPfSingleP<T>)
+                    if constexpr (kPfSingleP<T>) {
+                        // The row sum takes the rounded fp16 probabilities the
+                        // product uses, two per dot instruction.
                         ph[i] = pack_f16_rne(p[2 * i], p[2 * i + 1]);
-                    else
+                        l[rb] = dot2_f16_ones(ph[i], l[rb]);
+                    } else {
                         Ops::split(p[2 * i], p[2 * i + 1], ph[i], pl[i]);
+                        l[rb] += p[2 * i] + p[2 * i + 1];
+                    }
                 }
                 bh[rb] = u32x4{ph[0], ph[1], ph[2], ph[3]};
                 if constexpr (!kPfSingleP<T>) bl[rb] = u32x4{pl[0], pl[1], pl[2], pl[3]};

@@ -7,6 +7,8 @@ whole prompts, block sizes 1..256, groups 1..8), and the invariants:
 chunked == whole-prompt rows, single-row chunks == pa_decode, guards.
 The oracle runs on sampled sequences for the large batches.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -118,6 +120,16 @@ def test_prefill_sweep(dtype, H, Hk, D, B, prefix, chunk):
     mq = min(int(max(chunk)) + 130, case.max_context_len)
     if mq > max(chunk):
         check(case, strict=False, max_query_len=mq)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("scale", [0.0, -0.25])
+def test_prefill_zero_and_negative_scale(dtype, scale):
+    """Scale 0 makes every row the plain mean of the V rows it may see (keys
+    past its position must weigh exactly 0, not 0 * inf); a negative scale is
+    an ordinary softmax of the negated scores."""
+    base = wl.random_prefill_case(91, [0, 37, 5], [40, 70, 1], 4, 128, 16, dtype, num_kv_heads=2)
+    check(dataclasses.replace(base, scale=scale), strict=False)
 
 
 def test_prefill_chunks_match_whole_prompt():
