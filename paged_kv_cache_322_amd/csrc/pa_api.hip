@@ -45,10 +45,9 @@ size_t workspace_bytes_for(int64_t num_seqs, int64_t num_heads, int64_t head_dim
            (balanced ? sizeof(int32_t) : 0);
 }
 
-// Workgroups of a balanced split on the current device: kBalancedWgsPerCu
-// per compute unit, half that for head_dim 256 (whose kernel fits 2
-// wavefronts per SIMD, not 4).  The CU count is queried once per device.
-int balanced_workgroups(int32_t head_dim) {
+// Compute units of the current device, queried once per device (256 if the
+// query fails).
+int device_cus() {
     static std::atomic<int> cached_cus[64];
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
@@ -64,8 +63,15 @@ int balanced_workgroups(int32_t head_dim) {
     } else {
         (void)hipGetLastError();
     }
+    return cus;
+}
+
+// Workgroups of a balanced split on the current device: kBalancedWgsPerCu
+// per compute unit, half that for head_dim 256 (whose kernel fits 2
+// wavefronts per SIMD, not 4).
+int balanced_workgroups(int32_t head_dim) {
     const int per_cu = head_dim <= 128 ? pa::kBalancedWgsPerCu : (pa::kBalancedWgsPerCu + 1) / 2;
-    return cus * per_cu;
+    return device_cus() * per_cu;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
@@ -187,6 +193,10 @@ int decode_common(void* out, const void* query, const void* key, const void* val
     a.max_parts = static_cast<int>(parts);
     a.staged_blocks = static_cast<int>(staged);
     a.longest_first = plan.longest_first;
+    // Grouped heads under longest-first order: pair long and short contexts
+    // in the CUs' first two workgroup slots (grid rows hold num_kv_heads
+    // workgroups each).
+    a.pair_rows = (plan.longest_first && num_heads > num_kv_heads) ? std::max(1, device_cus() / num_kv_heads) : 0;
     a.balanced = plan.balanced;
     a.balanced_wgs = 0;
     a.staged_balanced = 0;

@@ -472,7 +472,8 @@ hipError_t launch_decode_t(const DecodeArgs& a) {
                                static_cast<const bits*>(a.key_new), static_cast<const bits*>(a.value_new),
                                a.block_tables, a.context_lens, a.num_seqs, a.num_kv_heads, log2_bs,
                                a.max_blocks_per_seq, a.max_context_len, a.num_blocks, a.part_tokens, a.max_parts,
-                               a.longest_first ? kPlanLongestFirst : kPlanPartitions, 0, nullptr, qscale);
+                               a.longest_first ? kPlanLongestFirst : kPlanPartitions,
+                               a.longest_first ? a.pair_rows : 0, nullptr, qscale);
         } else {
             hipLaunchKernelGGL((decode_partition_kernel<T, D, G, APPEND, NT>), grid, dim3(kThreads), lds, a.stream,
                                out, ws_o, ws_m, ws_l, static_cast<const bits*>(a.query),

@@ -166,9 +166,21 @@ __device__ __forceinline__ u32x4 as_u32x4(const uint4& v) { return u32x4{v.x, v.
 // Sequence handled by grid row `row` under longest-first order: the one of
 // rank `row` in decreasing context length, ties by index.  Needs
 // num_seqs <= kMaxLptSeqs (host check); every thread returns the same value.
+//
+// pair_rows > 0: the grid rows of the first round of one workgroup per CU
+// (rows < pair_rows) take the longest sequences, and the rows of the second
+// round (pair_rows <= row < 2 pair_rows), which land in the CUs' second
+// slots in dispatch order, take the next ones in increasing length, so a CU
+// that holds one of the longest contexts gets one of the shorter ones
+// beside it.  Later rows stay longest first.  The map is a permutation of
+// the ranks.
 template <int THREADS>
 __device__ __forceinline__ int longest_first_seq(const int32_t* __restrict__ context_lens, int num_seqs, int row,
-                                                 int tid) {
+                                                 int tid, int pair_rows) {
+    if (pair_rows > 0 && row >= pair_rows && row < 2 * pair_rows) {
+        const int hi = min(2 * pair_rows, num_seqs);
+        row = pair_rows + (hi - 1 - row);
+    }
     __shared__ int s_len[kMaxLptSeqs];
     __shared__ int s_pick;
     for (int i = tid; i < num_seqs; i += THREADS) s_len[i] = context_lens[i];
@@ -448,7 +460,8 @@ __global__ __launch_bounds__(kMfmaThreads, mfma_waves_per_simd(D)) void decode_m
     if constexpr (!BALANCED) {
         hk = blockIdx.x;
         const int srow = blockIdx.y, part = blockIdx.z;
-        s = mode == kPlanLongestFirst ? longest_first_seq<kMfmaThreads>(context_lens, num_seqs, srow, tid) : srow;
+        s = mode == kPlanLongestFirst ? longest_first_seq<kMfmaThreads>(context_lens, num_seqs, srow, tid, num_wgs)
+                                      : srow;
         ctx = __builtin_amdgcn_readfirstlane(context_lens[s]);
         if (ctx <= 0 || ctx > max_context_len) {
             if (part == 0) {

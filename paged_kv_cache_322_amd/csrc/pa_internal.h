@@ -128,6 +128,7 @@ struct DecodeArgs {
     int part_tokens, max_parts;
     int staged_blocks;  // LDS entries for a partition's block ids
     bool longest_first; // map grid rows to sequences in decreasing context length
+    int pair_rows;      // matrix-core longest-first: grid rows per round of one workgroup per CU (0 = none)
     bool balanced;      // balanced split (matrix-core kernel); else partitions of part_tokens
     int balanced_wgs;   // workgroups of the balanced split
     int staged_balanced;  // LDS entries for a balanced-split run's block ids

@@ -117,3 +117,19 @@ def test_balanced_split_matches_partitions(H, Hk, D):
         out = g.decode(partition=part, out=torch.empty_like(g.q))
         torch.cuda.synchronize()
         assert_close(out, ref, "bf16", f"H={H} Hk={Hk} D={D} partition={part}", strict=False)
+
+
+@pytest.mark.parametrize("dtype,S,H,Hk", [("f16", 50, 32, 16), ("bf16", 20, 128, 32), ("f16", 70, 32, 8)])
+def test_gqa_longest_first_pairing(dtype, S, H, Hk):
+    """Grouped-head batches of 512+ (sequence, K/V head) pairs run whole
+    contexts longest first, with the second round of grid rows in increasing
+    length (paired with the longest in the CUs' first slots): every sequence
+    must still be computed exactly once, with its own context.  The batches
+    span the paired rows and rows past them."""
+    case = wl.random_case(900 + S + Hk, S, H, 128, 16, dtype, ctx_range=(1, 300), num_kv_heads=Hk, spare_blocks=5)
+    assert S * Hk >= 512
+    g = GpuCase(case)
+    ref = oracle_decode(case, case.k_cache, case.v_cache)
+    out = g.decode(out=torch.full_like(g.q, float("nan")))
+    torch.cuda.synchronize()
+    assert_close(out, ref, dtype, f"{case.name} S={S} H={H} Hk={Hk}", strict=False)

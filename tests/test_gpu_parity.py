@@ -96,6 +96,18 @@ def test_shape_sweep(dtype, D, B, ctx, part):
     full_parity(case, partitions=(part,), strict=False)
 
 
+@pytest.mark.parametrize("dtype,G", [("f32", 1), ("f16", 1), ("bf16", 1), ("f16", 4), ("bf16", 8)])
+@pytest.mark.parametrize("scale", [0.0, -0.3])
+def test_zero_and_negative_scale(dtype, G, scale):
+    """Scale 0 gives the plain mean of each context's V rows (tail slots of
+    the last block, NaN-poisoned, must weigh exactly 0); a negative scale is
+    an ordinary softmax of the negated scores.  Both decode kernels (vector
+    for G = 1, matrix-core for grouped heads) and a forced split."""
+    case = wl.random_case(77 + G, 4, 2 * G, 128, 16, dtype, ctx=[1, 15, 100, 700], spare_blocks=5, scale=scale,
+                          num_kv_heads=2)
+    full_parity(case, partitions=(0, 64), strict=False)
+
+
 def test_append_sweep():
     for dtype, D, B in (("f32", 64, 4), ("bf16", 128, 16), ("f16", 256, 32)):
         case = wl.random_case(200 + D, 5, 4, D, B, dtype, ctx_range=(3, 90), n_append=3, spare_blocks=6)
