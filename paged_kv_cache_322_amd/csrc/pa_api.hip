@@ -345,6 +345,7 @@ extern "C" int pa_prefill(void* out, const void* query, const void* k_cache, con
     a.max_blocks_per_seq = max_blocks_per_seq;
     a.max_query_len = max_query_len;
     a.max_context_len = max_context_len;
+    a.num_tokens = num_tokens;
     a.num_blocks = num_blocks;
     a.scale = scale;
     a.dtype = dtype;

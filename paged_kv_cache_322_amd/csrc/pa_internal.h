@@ -161,6 +161,7 @@ struct PrefillArgs {
     const int32_t* query_start;
     int num_seqs, num_heads, num_kv_heads, head_dim, block_size;
     int max_blocks_per_seq, max_query_len, max_context_len;
+    int num_tokens;  // query rows of the call (sum of the chunk lengths)
     int64_t num_blocks;
     float scale;
     int dtype;

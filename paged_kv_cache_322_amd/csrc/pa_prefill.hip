@@ -49,9 +49,16 @@
 //     round-robin by linear id, each XCD with its own L2.  Every workgroup of
 //     one (sequence, K/V head) unit gets a linear id congruent to the unit
 //     mod 8, so the unit's G query heads and query tiles read its K/V through
-//     one L2; in dispatch order the last query tile (most keys) of every
-//     unit comes first, then the second last, and so on, and the G heads of
-//     a unit and tile are adjacent.
+//     one L2.  Two orders per XCD:
+//       - unit-major (most launched tiles hold rows: chunked prefill): the
+//         units in decreasing context length (sequences ranked in LDS), and
+//         all tiles and heads of a unit adjacent, last tile first, so they
+//         run together and share each K/V tile through the L2 instead of
+//         re-reading it from memory;
+//       - tile-major (mixed whole prompts, many empty tiles): the last query
+//         tile (most keys) of every unit first, then the second last, and
+//         so on, the G heads of a unit and tile adjacent: longest work
+//         first, and the empty tiles of short prompts exit early.
 #include <math.h>
 
 #include "pa_decode_mfma.h"  // MfmaOps, vector types
@@ -73,6 +80,8 @@ constexpr int kPfPad = 16;                          // LDS row padding (elements
 // rescaled rarely; probabilities stay below 2^8 (no overflow in f16/bf16 or
 // fp32).
 constexpr float kPfRescaleSlack = 8.0f;
+constexpr int kPfMaxRankedSeqs = 64;  // unit-major order ranks at most this many sequences
+static_assert(kPfMaxRankedSeqs <= kPfThreads, "one thread ranks one sequence");
 
 template <int D>
 struct PfShape {
@@ -149,7 +158,7 @@ __global__ __launch_bounds__(kPfThreads, kPfWavesPerSimd) void prefill_kernel(
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ query_start, int num_heads,
     int num_kv_heads, int log2_bs, int max_blocks_per_seq, int64_t num_blocks, int max_context_len, int n_qtiles,
-    int num_units, float qscale) {
+    int num_units, int unit_major, float qscale) {
     using Sh = PfShape<D>;
     constexpr int KS = Sh::KS, E = Sh::E, LD = Sh::LD, CPR = Sh::CPR, CPT = Sh::CPT;
     constexpr int RB = kPfBlocks;
@@ -159,21 +168,55 @@ __global__ __launch_bounds__(kPfThreads, kPfWavesPerSimd) void prefill_kernel(
     __shared__ __align__(16) uint16_t sK[2][kPfKeys][LD];
     __shared__ __align__(16) uint16_t sV[2][kPfKeys][LD];
 
-    // Linear id -> (query tile, unit, head): unit u = (sequence, K/V head)
-    // runs on XCD u % 8.  Per XCD, ids r8 = lin / 8 run through the query
-    // tiles last first; within a tile, through the XCD's units and, within a
-    // unit, its G query heads.  The grid holds ceil(units / 8) * 8 * G *
-    // n_qtiles workgroups; those of padding units return at once.
+    // Linear id -> (query tile, unit, head): unit u runs on XCD u % 8, and
+    // per XCD the ids r8 = lin / 8 run
+    //   unit-major: through the XCD's units, within a unit through its query
+    //     tiles last first and, within a tile, its G query heads; unit u is
+    //     (sequence of rank u / Hk in decreasing context length, K/V head
+    //     u % Hk);
+    //   tile-major: through the query tiles last first, within a tile
+    //     through the XCD's units and, within a unit, its G query heads;
+    //     unit u is (sequence u / Hk, K/V head u % Hk).
+    // The grid holds ceil(units / 8) * 8 * G * n_qtiles workgroups; those of
+    // padding units return at once.
     const int G = num_heads / num_kv_heads;
     const int lin = static_cast<int>(blockIdx.x);
     const int xcd = lin % kXcds, r8 = lin / kXcds;
-    const int per_tile = static_cast<int>(gridDim.x) / (kXcds * n_qtiles);  // units per XCD x G
-    const int qt = n_qtiles - 1 - r8 / per_tile;
-    const int unit = ((r8 % per_tile) / G) * kXcds + xcd;
-    if (unit >= num_units) return;
-    const int s = unit / num_kv_heads, hk = unit % num_kv_heads;
-    const int h = hk * G + r8 % G;
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    int qt, unit;
+    if (unit_major) {
+        const int per_unit = n_qtiles * G;
+        qt = n_qtiles - 1 - (r8 % per_unit) / G;
+        unit = (r8 / per_unit) * kXcds + xcd;
+    } else {
+        const int per_tile = static_cast<int>(gridDim.x) / (kXcds * n_qtiles);  // units per XCD x G
+        qt = n_qtiles - 1 - r8 / per_tile;
+        unit = ((r8 % per_tile) / G) * kXcds + xcd;
+    }
+    if (unit >= num_units) return;
+    const int hk = unit % num_kv_heads;
+    const int h = hk * G + r8 % G;
+    int s = unit / num_kv_heads;
+    if (unit_major) {
+        // Sequence of rank s in decreasing context length, ties by index
+        // (num_seqs <= kPfMaxRankedSeqs: host check).
+        __shared__ int s_len[kPfMaxRankedSeqs];
+        __shared__ int s_pick;
+        const int num_seqs = num_units / num_kv_heads;
+        if (tid < num_seqs) s_len[tid] = context_lens[tid];
+        __syncthreads();
+        if (tid < num_seqs) {
+            const int c0 = s_len[tid];
+            int rank = 0;
+            for (int j = 0; j < num_seqs; ++j) {
+                const int cj = s_len[j];
+                rank += (cj > c0) || (cj == c0 && j < tid);
+            }
+            if (rank == s) s_pick = tid;
+        }
+        __syncthreads();
+        s = __builtin_amdgcn_readfirstlane(s_pick);
+    }
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int c = lane & 15, g = lane >> 4;
 
@@ -426,12 +469,16 @@ hipError_t launch_prefill_t(const PrefillArgs& a) {
     const int64_t items = static_cast<int64_t>(a.num_heads / a.num_kv_heads) * n_qtiles;
     const int64_t groups = (num_units + kXcds - 1) / kXcds;
     dim3 grid(static_cast<unsigned>(groups * kXcds * items));
+    // Unit-major order when at least half of the launched query tiles hold
+    // rows (the chunks fill their tiles); tile-major otherwise.
+    const int unit_major = a.num_seqs <= kPfMaxRankedSeqs &&
+                           2 * static_cast<int64_t>(a.num_tokens) >= static_cast<int64_t>(a.num_seqs) * n_qtiles * kPfRows;
     const size_t lds = static_cast<size_t>(a.staged_ids) * sizeof(int);
     hipLaunchKernelGGL((prefill_kernel<T, D>), grid, dim3(kPfThreads), lds, a.stream, static_cast<uint16_t*>(a.out),
                        static_cast<const uint16_t*>(a.query), static_cast<const uint16_t*>(a.k_cache),
                        static_cast<const uint16_t*>(a.v_cache), a.block_tables, a.context_lens, a.query_start,
                        a.num_heads, a.num_kv_heads, log2_bs, a.max_blocks_per_seq, a.num_blocks, a.max_context_len,
-                       n_qtiles, num_units, qscale);
+                       n_qtiles, num_units, unit_major, qscale);
     return hipGetLastError();
 }
 

@@ -132,6 +132,27 @@ def test_prefill_zero_and_negative_scale(dtype, scale):
     check(dataclasses.replace(base, scale=scale), strict=False)
 
 
+@pytest.mark.parametrize("dtype,H,Hk", [("f16", 8, 8), ("bf16", 16, 4)])
+def test_prefill_dispatch_orders_agree_bitwise(dtype, H, Hk):
+    """The launch order of the query tiles (unit-major with sequences ranked
+    by context length when the chunks fill the launched tiles, tile-major
+    otherwise) changes no row's arithmetic: a generous max_query_len, which
+    launches mostly empty tiles and so flips the order, gives identical bits."""
+    case = wl.random_prefill_case(1234 + H, [700, 0, 300, 1500, 64], [256, 250, 130, 200, 256], H, 128, 16, dtype,
+                                  num_kv_heads=Hk)
+    run = PrefillRun(case)
+    mq = int(np.diff(case.query_start).max())
+    assert 2 * case.num_tokens >= case.num_seqs * ((mq + 127) // 128) * 128  # unit-major
+    a = run.run().clone()
+    big = 4 * 128 * ((mq + 127) // 128)
+    assert big <= case.max_context_len and 2 * case.num_tokens < case.num_seqs * big  # tile-major
+    b = run.run(max_query_len=big).clone()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    kc, vc = oracle_pools(case)
+    ref, rows = oracle_rows(case, kc, vc, range(case.num_seqs))
+    assert_close(a[torch.from_numpy(rows).cuda()], ref, dtype, f"{case.name} prefill", strict=False)
+
+
 def test_prefill_chunks_match_whole_prompt():
     """Prefilling a prompt in three chunks gives the rows the whole-prompt
     prefill gives (within one output ulp)."""
