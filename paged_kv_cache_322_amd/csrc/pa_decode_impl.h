@@ -67,6 +67,7 @@ constexpr int kWgWaves = PA_WG_WAVES;  // wavefronts per workgroup
 constexpr int kThreads = kWgWaves * kWave;
 static_assert(kMaxLptSeqs <= kThreads || kWgWaves < 8, "one thread ranks one sequence");
 constexpr int kMergeMaxParts = 256;  // partition weights cached in LDS by the merge kernel
+constexpr int kMergePre = 8;         // partitions whose accumulators the merge kernel loads up front
 
 template <class T, int D, int G>
 struct DecodeShape {
@@ -394,6 +395,19 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(
     }
     const float* wm = ws_m + sh * max_parts;
     const float* wl = ws_l + sh * max_parts;
+    const float* wo = ws_o + sh * max_parts * D;
+    // The accumulators of the first kMergePre partitions are loaded before
+    // the statistics are reduced, so they arrive in the same memory round
+    // trip as the maxima and sums (a split context usually has a few pieces).
+    constexpr int DPL = (D + kWave - 1) / kWave;  // channels per lane
+    float o_pre[kMergePre][DPL];
+#pragma unroll
+    for (int p = 0; p < kMergePre; ++p)
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) {
+            const int d = lane + i * kWave;
+            o_pre[p][i] = (p < np && d < D) ? wo[p * D + d] : 0.0f;
+        }
     float M = -INFINITY;
     for (int p = lane; p < np; p += kWave) M = fmaxf(M, wm[p]);
     M = group_reduce<1, kWave>(M, OpMax{});
@@ -405,10 +419,15 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(
     }
     L = group_reduce<1, kWave>(L, OpAdd{});
     __syncthreads();
-    const float* wo = ws_o + sh * max_parts * D;
-    for (int d = lane; d < D; d += kWave) {
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) {
+        const int d = lane + i * kWave;
+        if (d >= D) break;
         float O = 0.0f;
-        for (int p = 0; p < np; ++p) {
+#pragma unroll
+        for (int p = 0; p < kMergePre; ++p)
+            if (p < np) O = fmaf(s_w[p], o_pre[p][i], O);
+        for (int p = kMergePre; p < np; ++p) {
             const float w = p < kMergeMaxParts ? s_w[p] : fast_exp2(wm[p] - M);
             O = fmaf(w, wo[p * D + d], O);
         }
