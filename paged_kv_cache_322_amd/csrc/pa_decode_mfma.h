@@ -477,38 +477,51 @@ __global__ __launch_bounds__(kMfmaThreads, mfma_waves_per_simd(D)) void decode_m
         single = ctx <= part_tokens;
         slot = part;
     } else {
-        // Inclusive scan of s_pre[1..S] (Hillis-Steele); s_pre[0] = 0.
-        auto scan = [&]() {
-            for (int off = 1; off <= num_seqs; off <<= 1) {
-                int v[kMaxLptSeqs / kMfmaThreads + 1];
-                int k = 0;
-                for (int i = tid + 1; i <= num_seqs; i += kMfmaThreads, ++k) v[k] = (i > off) ? s_pre[i - off] : 0;
-                __syncthreads();
-                k = 0;
-                for (int i = tid + 1; i <= num_seqs; i += kMfmaThreads, ++k) s_pre[i] += v[k];
-                __syncthreads();
+        // Wave 0 reads the S <= kMaxLptSeqs context lengths (PER consecutive
+        // sequences per lane), finds the piece length C from their total,
+        // and writes the inclusive prefix sums of the pieces per K/V head to
+        // s_pre[1..S] with a wavefront scan; one barrier publishes them.
+        if (tid < kWave) {
+            constexpr int PER = kMaxLptSeqs / kWave;
+            int nv[PER];
+            int tot = 0;
+#pragma unroll
+            for (int k = 0; k < PER; ++k) {
+                const int i = tid * PER + k;
+                const int n = i < num_seqs ? context_lens[i] : 0;
+                nv[k] = (n > 0 && n <= max_context_len) ? n : 0;
+                tot += nv[k];
             }
-        };
-        for (int i = tid; i < num_seqs; i += kMfmaThreads) {
-            const int n = context_lens[i];
-            s_pre[i + 1] = (n > 0 && n <= max_context_len) ? n : 0;
+#pragma unroll
+            for (int off = kWave / 2; off > 0; off >>= 1) tot += __shfl_xor(tot, off);
+            const int64_t total = static_cast<int64_t>(num_kv_heads) * tot;
+            const int pairs = num_seqs * num_kv_heads;
+            const int64_t slots = max(1, num_wgs - pairs / 2);
+            const int C = static_cast<int>(max(static_cast<int64_t>(part_tokens), (total + slots - 1) / slots));
+            int run = 0;
+#pragma unroll
+            for (int k = 0; k < PER; ++k) {
+                run += nv[k] > 0 ? (nv[k] + C - 1) / C : 0;  // pieces per K/V head
+                nv[k] = run;
+            }
+            int incl = run;  // inclusive scan of the lane totals
+#pragma unroll
+            for (int off = 1; off < kWave; off <<= 1) {
+                const int v = __shfl_up(incl, off);
+                if (tid >= off) incl += v;
+            }
+            const int excl = incl - run;
+#pragma unroll
+            for (int k = 0; k < PER; ++k) {
+                const int i = tid * PER + k;
+                if (i < num_seqs) s_pre[i + 1] = excl + nv[k];
+            }
+            if (tid == 0) {
+                s_pre[0] = 0;
+                if (blockIdx.x == 0) meta[0] = C;  // for the merge kernel
+            }
         }
-        if (tid == 0) s_pre[0] = 0;
         __syncthreads();
-        scan();
-        const int64_t total = static_cast<int64_t>(num_kv_heads) * __builtin_amdgcn_readfirstlane(s_pre[num_seqs]);
-        const int pairs = num_seqs * num_kv_heads;
-        const int64_t slots = max(1, num_wgs - pairs / 2);
-        const int C = __builtin_amdgcn_readfirstlane(
-            static_cast<int>(max(static_cast<int64_t>(part_tokens), (total + slots - 1) / slots)));
-        if (blockIdx.x == 0 && tid == 0) meta[0] = C;  // for the merge kernel
-        __syncthreads();  // every thread has read s_pre[num_seqs]
-        for (int i = tid; i < num_seqs; i += kMfmaThreads) {
-            const int n = context_lens[i];
-            s_pre[i + 1] = (n > 0 && n <= max_context_len) ? (n + C - 1) / C : 0;  // pieces per K/V head
-        }
-        __syncthreads();
-        scan();
         const int w = blockIdx.x;
         if (w >= num_kv_heads * __builtin_amdgcn_readfirstlane(s_pre[num_seqs])) return;
         // The sequence of piece w: the last s with Hk * pre[s] <= w.
