@@ -348,6 +348,8 @@ def main():
         if ev is not None:
             ev[2].record()
 
+    medians = []  # per run: median over the steps of each event-pair span
+
     def run(step, nev):
         """Step time from an uninstrumented pass; per-launch times from a
         second pass with HIP events around each launch."""
@@ -366,6 +368,7 @@ def main():
             step(i, evs[i])
         torch.cuda.synchronize()
         spans = [float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j in range(nev - 1)]
+        medians.append([float(np.median([e[j].elapsed_time(e[j + 1]) for e in evs])) for j in range(nev - 1)])
         return ms, spans
 
     log(f"warmup {args.warmup} steps, then {args.steps} timed steps")
@@ -482,6 +485,7 @@ def main():
             "algorithmic_bytes_per_launch": int(decode_bytes),
             "avg_launch_us": round(rot_ms * 1e3, 2),
             "event_pair_per_launch_us": round(launch_ms * 1e3, 2),
+            "event_pair_median_us": round(medians[0][1] * 1e3, 2),
         },
         "append_us": round(append_ms * 1e3, 2) if fused else None,
         "fused": ({"entry_point": "pa_append_decode", "ms_per_step": round(fused_ms, 5),
