@@ -151,7 +151,8 @@ def unique_kv_bytes(case):
 COUNTER_FILES = {"2": "decode_llama7b_counters.txt", "3": "decode_opt13b_counters.txt",
                  "4": "decode_parallel_sampling_b16_counters.txt", "5": "decode_opt175b_counters.txt",
                  "gqa8b": "decode_gqa_llama3_8b_counters.txt", "gqa70b": "decode_gqa_llama2_70b_tp8_counters.txt",
-                 "prefill-llama7b": "prefill_llama7b_counters.txt"}
+                 "prefill-llama7b": "prefill_llama7b_counters.txt", "prefill-gqa8b": "prefill_gqa_llama3_8b_counters.txt",
+                 "prefill-prompts": "prefill_prompts_bf16_counters.txt"}
 DECODE_SOURCES = ("pa_decode_impl.h", "pa_decode_mfma.h", "pa_device.h", "pa_internal.h")
 PREFILL_SOURCES = ("pa_prefill.hip", "pa_decode_mfma.h", "pa_device.h", "pa_internal.h")
 
