@@ -40,6 +40,8 @@
 //     (and the accumulators are rescaled) only when a tile exceeds it by more
 //     than 2^8, so the rescale is rare; the score scale is one fused
 //     multiply-add;
+//   * wavefront priority raised while a wavefront issues its products
+//     (s_setprio), so the other wavefronts' softmax work fills in under them;
 //   * register budget for 3 wavefronts per SIMD (<= 168 VGPRs, 3 workgroups
 //     per CU), accumulators in VGPRs (MFMA with VGPR C/D); LDS rows padded
 //     by 32 bytes;
@@ -329,6 +331,10 @@ __global__ __launch_bounds__(kPfThreads, kPfWavesPerSimd) void prefill_kernel(
             for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                 for (int sub = 0; sub < 2; ++sub) sc[rb][sub] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            // Issue priority: a wavefront issuing matrix-core products goes
+            // first, so other wavefronts' softmax instructions fill the
+            // cycles under its products instead of delaying them.
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
@@ -338,6 +344,7 @@ __global__ __launch_bounds__(kPfThreads, kPfWavesPerSimd) void prefill_kernel(
                     for (int rb = 0; rb < RB; ++rb) sc[rb][sub] = Ops::qk(kop, qv[rb][ks], sc[rb][sub]);
                 }
             }
+            __builtin_amdgcn_s_setprio(0);
             u32x4 bh[RB], bl[RB];
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
@@ -420,6 +427,7 @@ __global__ __launch_bounds__(kPfThreads, kPfWavesPerSimd) void prefill_kernel(
             // transposing reads, lanes 4 r + q of a group pointing at key
             // row 4 g + r (+ 16), channels 16 t + 4 q .. 16 t + 4 q + 3.
             const int tr_row = 4 * g + (c >> 2), tr_col = 4 * (c & 3);
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int t = 0; t < E; ++t) {
                 const u32x2 lo4 = lds_read_tr16(&sV[buf][tr_row][16 * t + tr_col]);
@@ -432,6 +440,7 @@ __global__ __launch_bounds__(kPfThreads, kPfWavesPerSimd) void prefill_kernel(
                 }
             }
         }
+        __builtin_amdgcn_s_setprio(0);
         if (kt + 1 < ntiles) store_tile(buf ^ 1);
         __syncthreads();
     }
