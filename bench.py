@@ -520,6 +520,7 @@ def main():
                     kc, vc = oracle.copy_blocks(kc, vc, st.pairs)
             setup_pools = (kc, vc)
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds, timed_steps, setup_pools)
+        result["cpu_baseline"]["gpu_over_oracle"] = round(value / result["cpu_baseline"]["value"], 1)
     print(json.dumps(result), flush=True)
 
 
@@ -688,6 +689,7 @@ def bench_prefill(args, case, pa, torch, dev):
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample of the batch")
         result["cpu_baseline"] = cpu_baseline_prefill(case, args.cpu_seconds)
+        result["cpu_baseline"]["gpu_over_oracle"] = round(value / result["cpu_baseline"]["value"], 1)
     print(json.dumps(result), flush=True)
 
 
