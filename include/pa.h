@@ -100,6 +100,9 @@ typedef enum {
  *               clamped to [Pmin, 4096]) per workgroup, in batch order;
  *   Rlpt <= R < 8192 and num_seqs <= 512:  whole contexts as above,
  *               dispatched longest context first (no split, no merge launch);
+ *               with G >= 2 the second round of one workgroup per compute
+ *               unit takes its sequences in increasing length, so each
+ *               unit's two slots pair a long and a short context;
  *   otherwise:  the largest power of two in [Pmin, 4096] (not above the
  *               next power of two of max_context_len) that still gives
  *               R * ceil(max_context_len / P) >= 8192 work items, in batch
