@@ -363,11 +363,11 @@ __global__ __launch_bounds__(kPfThreads, kPfWavesPerSimd) void prefill_kernel(
                 // pos - k0 - 4 g; a hidden key gets exponent -inf (p = 0),
                 // whatever the scale (also 0).
                 const bool full = k0 + kPfKeys - 1 <= wpos0 + 16 * rb;
-                const int lim = full ? kPfKeys : pos[rb] - k0 - 4 * g;
                 if (!full) {
                     // (The empty asm keeps this a branch around the tile
                     // instead of selects executed on every tile.)
                     asm volatile("");
+                    const int lim = pos[rb] - k0 - 4 * g;
 #pragma unroll
                     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
@@ -382,12 +382,12 @@ __global__ __launch_bounds__(kPfThreads, kPfWavesPerSimd) void prefill_kernel(
                 // first tile, where m = -inf); then the row maximum over
                 // the visible keys becomes the reference.
                 if (__builtin_amdgcn_ballot_w64(tmax > kPfRescaleSlack)) {
+                    // Visible keys are those whose exponent argument is not
+                    // -inf (finite scores give a finite or +inf argument).
                     float mr = -INFINITY;
 #pragma unroll
-                    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            if (16 * sub + j <= lim) mr = fmaxf(mr, raw[4 * sub + j]);
+                    for (int i = 0; i < 8; ++i)
+                        if (t[i] > -INFINITY) mr = fmaxf(mr, raw[i]);
                     // Every row sees key 0 on tile 0, so m is finite from then on.
                     const float m_new = fmaxf(m[rb], max_over_groups(mr) * sc_mul);
                     const float alpha = fast_exp2(m[rb] - m_new);  // 0 on the first tile (m = -inf)
@@ -396,10 +396,7 @@ __global__ __launch_bounds__(kPfThreads, kPfWavesPerSimd) void prefill_kernel(
                     for (int t2 = 0; t2 < E; ++t2) acc[rb][t2] *= alpha;
                     m[rb] = m_new;
 #pragma unroll
-                    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            t[4 * sub + j] = 16 * sub + j <= lim ? fmaf(raw[4 * sub + j], sc_mul, -m_new) : -INFINITY;
+                    for (int i = 0; i < 8; ++i) t[i] = t[i] > -INFINITY ? fmaf(raw[i], sc_mul, -m_new) : -INFINITY;
                 }
                 float p[8];
 #pragma unroll
