@@ -1,0 +1,77 @@
+"""Seeded random shapes through the C ABI against the oracle: decode
+(multi-head and grouped heads, every dtype, forced and default partitions,
+with and without the fused append) and chunked prefill.  Each case is small
+enough for the oracle to check every output; together they cross the plan
+thresholds, block sizes and ragged tails the hand-written cases pick one at
+a time."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from gpu_helpers import GpuCase, assert_close, assert_pool_equal, log, oracle_decode, oracle_steps, pa, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+HEAD_DIMS = {"f32": [8, 32, 64, 128], "f16": [64, 128, 256], "bf16": [64, 128, 256]}
+
+
+def _decode_case(seed: int):
+    rng = np.random.default_rng([322, 9001, seed])
+    dtype = ["f32", "f16", "bf16"][seed % 3]
+    D = int(rng.choice(HEAD_DIMS[dtype]))
+    B = int(rng.choice([1, 2, 4, 8, 16, 32, 64]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    Hk = int(rng.choice([1, 2, 3]))
+    S = int(rng.integers(1, 9))
+    ctx = rng.integers(1, 700, S)
+    part = int(rng.choice([0, 0, 16, 64, 256]))
+    return dtype, D, B, G, Hk, S, ctx, part
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_decode(seed):
+    case, part = random_decode_case(seed)
+    dtype = case.dtype
+    log(f"seed {seed}: {dtype} D={case.head_dim} B={case.block_size} H={case.num_heads} Hk={case.num_kv_heads} "
+        f"part={part} ctx={case.context_lens.tolist()}")
+    g = GpuCase(case)
+    kc, vc = case.k_cache, case.v_cache
+    for i, (kc, vc) in enumerate(oracle_steps(case)):
+        g.run_step(i)
+        assert_pool_equal(g.kc, kc, dtype, f"seed {seed} K after step {i}")
+        assert_pool_equal(g.vc, vc, dtype, f"seed {seed} V after step {i}")
+    ref = oracle_decode(case, kc, vc)
+    out = g.decode(partition=part, out=torch.empty_like(g.q))
+    torch.cuda.synchronize()
+    assert_close(out, ref, dtype, f"seed {seed} decode", strict=False)
+
+
+def random_decode_case(seed: int) -> tuple:
+    """(case, forced partition or 0) of random decode seed `seed`."""
+    dtype, D, B, G, Hk, S, ctx, part = _decode_case(seed)
+    case = wl.random_case(5000 + seed, S, G * Hk, D, B, dtype, ctx=ctx, spare_blocks=4, n_append=1, num_kv_heads=Hk)
+    return case, part
+
+
+def random_prefill_case(seed: int) -> wl.Case:
+    rng = np.random.default_rng([322, 9002, seed])
+    dtype = ["f16", "bf16"][seed % 2]
+    D = int(rng.choice([64, 128]))
+    B = int(rng.choice([1, 4, 16, 32, 128]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    Hk = int(rng.choice([1, 2]))
+    S = int(rng.integers(1, 6))
+    prefix = rng.integers(0, 400, S).tolist()
+    chunk = rng.integers(1, 300, S).tolist()
+    return wl.random_prefill_case(7000 + seed, prefix, chunk, G * Hk, D, B, dtype, num_kv_heads=Hk)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_prefill(seed):
+    from test_gpu_prefill import check
+
+    case = random_prefill_case(seed)
+    log(f"seed {seed}: {case.dtype} D={case.head_dim} B={case.block_size} H={case.num_heads} "
+        f"Hk={case.num_kv_heads} ctx={case.context_lens.tolist()} rows={np.diff(case.query_start).tolist()}")
+    check(case, strict=False)

@@ -452,6 +452,24 @@ def check_prefill_bounds(case, max_query_len=None):
         assert unit % 8 == lin % 8  # a unit's workgroups share one XCD
         seen.add((s_, h, qt))
     assert len(seen) == S * H * n_qt
+    # Unit-major order (sequences ranked by decreasing context length, ties
+    # by index; at most 64 sequences): the same coverage.
+    if S <= 64:
+        ctx_all = [int(x) for x in case.context_lens]
+        rank_to_seq = sorted(range(S), key=lambda i: (-ctx_all[i], i))
+        per_unit = n_qt * G
+        seen = set()
+        for lin in range(grid):
+            xcd, r8 = lin % 8, lin // 8
+            qt = n_qt - 1 - (r8 % per_unit) // G
+            unit = (r8 // per_unit) * 8 + xcd
+            if unit >= units:
+                continue
+            s_, hk = rank_to_seq[unit // Hk], unit % Hk
+            h = hk * G + r8 % G
+            assert 0 <= s_ < S and 0 <= h < H and 0 <= qt < n_qt and h // G == hk
+            seen.add((s_, h, qt))
+        assert len(seen) == S * H * n_qt
 
 
 PF_CASES = [
@@ -468,3 +486,40 @@ def test_prefill_index_bounds(name, make):
     case = make()
     check_prefill_bounds(case)
     check_prefill_bounds(case, max_query_len=int(np.diff(case.query_start).max()) + 100)
+
+
+# ---------------------------------------------------------------------------
+# The seeded random shapes of tests/test_gpu_random_cases.py, checked here
+# before they run on the GPU.
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_decode_case_bounds(seed):
+    from test_gpu_random_cases import random_decode_case
+
+    case, part = random_decode_case(seed)
+    B, D = case.block_size, case.head_dim
+    S, Hk = case.num_seqs, case.num_kv_heads
+    G = case.num_heads // Hk
+    max_ctx = case.max_context_len
+    W = case.block_tables.shape[1]
+    p = default_partition(S, Hk, max_ctx, G) if part == 0 else part
+    assert (p + B - 1) // B + 1 <= MAX_PART_BLOCKS
+    check_decode_bounds(S, Hk, D, B, case.num_blocks, W, case.elem_bytes, case.context_lens, case.block_tables,
+                        max_ctx, p, G=G)
+    if case.elem_bytes == 2 and D in (64, 128, 256) and G >= 2:
+        if part == 0 and balanced_plan(S, Hk, max_ctx, G):
+            for wgs in (512, 256, 7):
+                check_balanced_bounds(S, Hk, G, D, B, case.num_blocks, W, case.context_lens, case.block_tables,
+                                      max_ctx, wgs)
+        else:
+            check_mfma_bounds(S, Hk, G, D, B, case.num_blocks, W, case.context_lens, case.block_tables, max_ctx, p)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_prefill_case_bounds(seed):
+    from test_gpu_random_cases import random_prefill_case
+
+    case = random_prefill_case(seed)
+    check_prefill_bounds(case)
