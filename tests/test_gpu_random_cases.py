@@ -29,7 +29,7 @@ def _decode_case(seed: int):
     return dtype, D, B, G, Hk, S, ctx, part
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(48))
 def test_random_decode(seed):
     case, part = random_decode_case(seed)
     dtype = case.dtype
@@ -67,7 +67,7 @@ def random_prefill_case(seed: int) -> wl.Case:
     return wl.random_prefill_case(7000 + seed, prefix, chunk, G * Hk, D, B, dtype, num_kv_heads=Hk)
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(24))
 def test_random_prefill(seed):
     from test_gpu_prefill import check
 

@@ -494,7 +494,7 @@ def test_prefill_index_bounds(name, make):
 # ---------------------------------------------------------------------------
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(48))
 def test_random_decode_case_bounds(seed):
     from test_gpu_random_cases import random_decode_case
 
@@ -517,7 +517,7 @@ def test_random_decode_case_bounds(seed):
             check_mfma_bounds(S, Hk, G, D, B, case.num_blocks, W, case.context_lens, case.block_tables, max_ctx, p)
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(24))
 def test_random_prefill_case_bounds(seed):
     from test_gpu_random_cases import random_prefill_case
 
