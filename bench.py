@@ -38,15 +38,15 @@ import numpy as np
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, vendor figure
 METRIC = "paged decode attention: KV-read GB/s and % of HBM peak; decode tokens/s"
-SWAP_WORKLOAD = ("swap-llama7b: preempt 16 of the 64 LLaMA-7B-shaped decode sequences (config 2): swap their "
+SWAP_WORKLOAD = ("swap-llama7b: preempt 16 of the 64 LLaMA-7B-shaped decode sequences: swap their "
                  "K/V blocks out to a pinned host pool and back in under new ids; H=32, D=128, f16, B=16")
 LINK_PEAK_GBPS = 64.0  # PCIe 5.0 x16, one direction, nominal
 WORKLOADS = {
-    "2": "llama7b-decode-layer: 64 seqs, ctx U[128,2048], H=32, D=128, f16, B=16, 8192-block pool",
-    "3": "opt13b-decode-layer: 256 seqs, ctx lognormal(median 300, sigma 0.9) in [16,2048], H=40, D=128, f16, B=16",
-    "4": "parallel-sampling-cow: 64 prompts x 4 samples, prompt 500, suffix U[0,256], H=40, D=128, f16",
-    "5": "opt175b-decode-layer: 128 seqs, ctx U[1024,2048], H=96, D=128, bf16, B=16, 16384-block pool",
-    "5tp8": "opt175b-decode-tp8-share: config 5 with the 12 of its 96 heads one of 8 tensor-parallel GPUs holds; "
+    "llama7b": "llama7b-decode-layer: 64 seqs, ctx U[128,2048], H=32, D=128, f16, B=16, 8192-block pool",
+    "opt13b": "opt13b-decode-layer: 256 seqs, ctx lognormal(median 300, sigma 0.9) in [16,2048], H=40, D=128, f16, B=16",
+    "sampling": "parallel-sampling-cow: 64 prompts x 4 samples, prompt 500, suffix U[0,256], H=40, D=128, f16",
+    "opt175b": "opt175b-decode-layer: 128 seqs, ctx U[1024,2048], H=96, D=128, bf16, B=16, 16384-block pool",
+    "opt175b-tp8": "opt175b-decode-tp8-share: the OPT-175B-shaped layer with the 12 of its 96 heads one of 8 tensor-parallel GPUs holds; "
             "128 seqs, ctx U[1024,2048], D=128, bf16, B=16, 16384-block pool",
     "gqa8b": "llama3-8b-gqa-decode-layer: 64 seqs, ctx U[128,2048], 32 query / 8 K/V heads, D=128, f16, B=16",
     "gqa70b": "llama2-70b-gqa-tp8-share: 128 seqs, ctx U[512,4096], 8 query / 1 K/V head, D=128, bf16, B=16",
@@ -57,7 +57,7 @@ WORKLOADS = {
     "prefill-prompts": "llama7b-prompt-prefill: 32 whole prompts, lognormal(median 300, sigma 0.9) lengths in "
                        "[16,2048], H=32, D=128, bf16, B=16",
     "swap": SWAP_WORKLOAD,
-    "block-manager": "block-manager: host bookkeeping of a decode step for config 3's 256 sequences "
+    "block-manager": "block-manager: host bookkeeping of a decode step for the OPT-13B-shaped batch's 256 sequences "
                      "(lognormal(300, 0.9) contexts, B=16) and prefix-cached admission of 256 prompts sharing a "
                      "512-token system prompt",
 }
@@ -73,11 +73,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed warmup steps (default 10; 100 for the prefill workloads, about 30 ms: sustained "
                          "matrix-core load slows the clocks for the first ~15 ms after an idle period)")
-    ap.add_argument("--config", default="2", choices=sorted(WORKLOADS))
+    ap.add_argument("--config", default="llama7b", choices=sorted(WORKLOADS))
     ap.add_argument("--partition", type=int, default=0, help="KV partition tokens (0 = library default)")
-    ap.add_argument("--block-size", type=int, default=16, help="block size for config 4 (8, 16 or 32)")
+    ap.add_argument("--block-size", type=int, default=16, help="block size of the parallel-sampling workload (8, 16 or 32)")
     ap.add_argument("--shared-blocks", choices=["auto", "on", "off"], default="auto",
-                    help="PA_DECODE_SHARED_BLOCKS (cached K/V loads); auto = on for config 4, whose samples share "
+                    help="PA_DECODE_SHARED_BLOCKS (cached K/V loads); auto = on for the parallel-sampling workload, whose samples share "
                          "prompt blocks")
     ap.add_argument("--rotate", type=int, default=2, help="independent pool copies cycled across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -95,12 +95,12 @@ def log(msg):
 def make_case(cfg, block_size=16):
     import workloads as wl
 
-    if cfg == "2":
-        return wl.config2(n_append=1)
-    if cfg == "3":
-        return wl.config3()
-    if cfg == "4":
-        return wl.config4(block_size=block_size)
+    if cfg == "llama7b":
+        return wl.llama7b_decode(n_append=1)
+    if cfg == "opt13b":
+        return wl.opt13b_decode()
+    if cfg == "sampling":
+        return wl.parallel_sampling(block_size=block_size)
     if cfg == "gqa8b":
         return wl.gqa_config("llama3-8b", n_append=1)
     if cfg == "gqa70b":
@@ -108,12 +108,12 @@ def make_case(cfg, block_size=16):
     if cfg in PREFILL_KINDS:
         return wl.prefill_config(PREFILL_KINDS[cfg])
     if cfg == "swap":
-        return wl.config2()
+        return wl.llama7b_decode()
     if cfg == "block-manager":
         return None
-    if cfg == "5tp8":
-        return wl.config5(num_heads=12, n_append=1)
-    return wl.config5(n_append=1)
+    if cfg == "opt175b-tp8":
+        return wl.opt175b_decode(num_heads=12, n_append=1)
+    return wl.opt175b_decode(n_append=1)
 
 
 def algorithmic_bytes(case, timed_steps):
@@ -148,8 +148,8 @@ def unique_kv_bytes(case):
 
 # Committed HBM counter summaries (rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled
 # by a copy kernel of known size), per workload at its default plan.
-COUNTER_FILES = {"2": "decode_llama7b_counters.txt", "3": "decode_opt13b_counters.txt",
-                 "4": "decode_parallel_sampling_b16_counters.txt", "5": "decode_opt175b_counters.txt",
+COUNTER_FILES = {"llama7b": "decode_llama7b_counters.txt", "opt13b": "decode_opt13b_counters.txt",
+                 "sampling": "decode_parallel_sampling_b16_counters.txt", "opt175b": "decode_opt175b_counters.txt",
                  "gqa8b": "decode_gqa_llama3_8b_counters.txt", "gqa70b": "decode_gqa_llama2_70b_tp8_counters.txt",
                  "prefill-llama7b": "prefill_llama7b_counters.txt", "prefill-gqa8b": "prefill_gqa_llama3_8b_counters.txt",
                  "prefill-prompts": "prefill_prompts_bf16_counters.txt"}
@@ -289,9 +289,10 @@ def main():
         return bench_swap(args, case, pa, torch, dev)
     import workloads as wl
 
-    # Config 4's prompt write, fork copies and suffix writes are set-up; the
-    # other configs time their one-token-per-sequence append with the decode.
-    if args.config == "4":
+    # The parallel-sampling workload's prompt write, fork copies and suffix
+    # writes are set-up; the other workloads time their one-token-per-sequence
+    # append with the decode.
+    if args.config == "sampling":
         setup_steps, timed_steps = list(case.steps), []
     else:
         setup_steps, timed_steps = [], list(case.steps)
@@ -321,7 +322,7 @@ def main():
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
-    shared = args.shared_blocks == "on" or (args.shared_blocks == "auto" and args.config == "4")
+    shared = args.shared_blocks == "on" or (args.shared_blocks == "auto" and args.config == "sampling")
     fused = bool(timed_steps)
     if fused:
         assert len(timed_steps) == 1 and timed_steps[0].slot_mapping.size == S  # one newest row per sequence
@@ -438,8 +439,8 @@ def main():
     achieved = decode_bytes / (rot_ms * 1e-3) / 1e9
     # The committed counters cover each profiled workload at its default partition.
     default_part = pa.partition_tokens(S, H, max_ctx, num_kv_heads=case.num_kv_heads)
-    # Config 4's counters were taken at its default 16-token blocks.
-    profiled = args.partition in (0, default_part) and (args.config != "4" or B == 16)
+    # The parallel-sampling counters were taken at its default 16-token blocks.
+    profiled = args.partition in (0, default_part) and (args.config != "sampling" or B == 16)
     traffic = traffic_from_profiles(args.config, kernel_source_sha()) if profiled else None
 
     result = {
@@ -501,7 +502,7 @@ def main():
         "copy_blocks": cow,
         "hbm_copy_probe": probe,
     }
-    if args.config == "4":
+    if args.config == "sampling":
         ub = unique_kv_bytes(case)
         result["unique_kv_bytes"] = int(ub)
         result["unique_kv_GBps"] = round(ub / (rot_ms * 1e-3) / 1e9, 1)
@@ -697,7 +698,7 @@ def bench_block_manager(args):
     """Host-side cost of the library's C++ block manager, against the Python
     reference model doing the same operations.
 
-    Decode step: config 3's 256 sequences (contexts lognormal(300, 0.9) in
+    Decode step: the OPT-13B-shaped batch's 256 sequences (contexts lognormal(300, 0.9) in
     [16, 2048], B = 16) each take one token (pa_bm_append_batch: slots and
     copy pairs), then the step's block tables are exported
     (pa_bm_block_tables).  Admission: 256 prompts of a 512-token shared system
@@ -707,7 +708,7 @@ def bench_block_manager(args):
     from oracle.block_manager import BlockManagerModel
     import workloads as wl
 
-    lens = wl.config3_lengths()
+    lens = wl.opt13b_context_lengths()
     S, B = len(lens), 16
     steps = max(20, args.steps)
     grow = -(-(steps + B) // B)  # blocks a sequence can gain over the timed steps
@@ -774,7 +775,7 @@ def bench_block_manager(args):
         "admission_us_per_prompt": round(cpp_admit_us, 2),
         "prefix_blocks_shared_by_all": reused,
         "roofline": None,
-        "note": "host-side bookkeeping (no GPU kernel); for scale, config 3's decode kernel takes ~355 us per step",
+        "note": "host-side bookkeeping (no GPU kernel); for scale, the OPT-13B-shaped batch's decode kernel takes ~355 us per step",
         "cpu_baseline": {"value": round(model_step_us, 2), "unit": "us/step", "cores": 1, "kind": "oracle",
                          "sample": f"the Python reference model on the same decode step ({msteps} steps) and "
                                    f"admissions ({model_admit_us:.1f} us/prompt)"},
@@ -783,7 +784,7 @@ def bench_block_manager(args):
 
 
 def bench_swap(args, case, pa, torch, dev):
-    """Preemption by swapping: the blocks of 16 of config 2's 64 sequences
+    """Preemption by swapping: the blocks of 16 of the LLaMA-7B-shaped batch's 64 sequences
     move to a pinned host pool (swap-out) and back under new device ids
     (swap-in), one pa_swap_blocks launch each.  Reference: one DMA copy of
     the same number of bytes between a contiguous device buffer and pinned

@@ -24,8 +24,8 @@ GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
 @functools.lru_cache(None)
-def _config3():
-    return wl.config3()
+def _opt13b():
+    return wl.opt13b_decode()
 
 
 def _golden(name):
@@ -100,7 +100,7 @@ def _decode(orc, case: wl.Case, q=None, kc=None, vc=None, bt=None, ctx=None, sca
 
 
 def _small_cases():
-    yield wl.config1()
+    yield wl.tiny_f32()
     yield wl.random_case(1, 4, 2, 8, 4, "f32", ctx_range=(1, 21))
     yield wl.random_case(2, 3, 2, 4, 2, "f16", ctx_range=(1, 13))
     yield wl.random_case(3, 3, 1, 8, 3, "bf16", ctx_range=(1, 17))
@@ -170,7 +170,7 @@ def pin_permutation(orc):
     """Relabelling physical blocks (moving them and rewriting the tables)
     leaves the result bit-for-bit unchanged."""
     rng = np.random.default_rng(13)
-    for case in (wl.config1(), wl.random_case(6, 4, 2, 8, 4, "f16", ctx_range=(1, 30)), wl.random_case(7, 3, 2, 8, 2, "bf16")):
+    for case in (wl.tiny_f32(), wl.random_case(6, 4, 2, 8, 4, "f16", ctx_range=(1, 30)), wl.random_case(7, 3, 2, 8, 2, "bf16")):
         base = _decode(orc, case)
         pi = rng.permutation(case.num_blocks)
         kc = np.empty_like(case.k_cache)
@@ -342,7 +342,7 @@ def pin_cow(orc):
     """Block copies: destination equals source bit-for-bit, other blocks are
     untouched, reading through a copy gives the same attention as through the
     original, and a write into one sample's block does not reach the others."""
-    case = wl.config4(block_size=4, num_prompts=3, samples=4, prompt_len=10, num_heads=2, head_dim=8, pool_tokens=4096)
+    case = wl.parallel_sampling(block_size=4, num_prompts=3, samples=4, prompt_len=10, num_heads=2, head_dim=8, pool_tokens=4096)
     ap0, cp, ap1 = case.steps
     kc, vc = orc.reshape_and_cache(ap0.key, ap0.value, case.k_cache, case.v_cache, ap0.slot_mapping)
     kc2, vc2 = orc.copy_blocks(kc, vc, cp.pairs)
@@ -408,10 +408,10 @@ def pin_split_merge(orc):
 
 def pin_newest_token_slots(orc):
     """The newest token's slot agrees with the slots the host block pool
-    handed out when that token was appended (configs built independently of
+    handed out when that token was appended (workloads built independently of
     the oracle), with the Digest flowchart's tables, and with ctx <= 0 -> -1;
     append_decode equals append followed by decode."""
-    case = _config3()
+    case = _opt13b()
     st = case.steps[0]
     assert np.array_equal(orc.newest_token_slots(case.block_tables, case.context_lens, 16), st.slot_mapping)
     g = _golden("digest_flowchart_layout.json")

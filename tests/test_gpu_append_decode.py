@@ -34,15 +34,15 @@ def fused_vs_oracle(case, seqs=None, partition=0, strict=True):
 
 
 def test_append_decode_llama7b_shape():
-    fused_vs_oracle(wl.config2(n_append=1))
+    fused_vs_oracle(wl.llama7b_decode(n_append=1))
 
 
 def test_append_decode_opt13b_shape():
-    fused_vs_oracle(wl.config3())
+    fused_vs_oracle(wl.opt13b_decode())
 
 
 def test_append_decode_opt175b_shape_sampled():
-    case = wl.config5(n_append=1)
+    case = wl.opt175b_decode(n_append=1)
     order = np.argsort(case.context_lens)
     fused_vs_oracle(case, seqs=sorted(set(order[::12].tolist() + [int(order[-1])])))
 

@@ -34,21 +34,21 @@ def full_parity(case: wl.Case, partitions=(0,), seqs=None, strict=True):
     return g, ref
 
 
-def test_config1_tiny_f32():
-    full_parity(wl.config1(), partitions=(0, 4, 8, 12, 37))
+def test_tiny_f32():
+    full_parity(wl.tiny_f32(), partitions=(0, 4, 8, 12, 37))
 
 
-def test_config2_llama7b_shape():
-    full_parity(wl.config2(), partitions=(0, 256))
+def test_llama7b_decode_shape():
+    full_parity(wl.llama7b_decode(), partitions=(0, 256))
 
 
-def test_config3_append_then_decode():
-    full_parity(wl.config3())
+def test_opt13b_append_then_decode():
+    full_parity(wl.opt13b_decode())
 
 
 @pytest.mark.parametrize("B", [8, 16, 32])
-def test_config4_parallel_sampling_cow(B):
-    g, ref = full_parity(wl.config4(block_size=B))
+def test_parallel_sampling_cow(B):
+    g, ref = full_parity(wl.parallel_sampling(block_size=B))
     # Cached loads for shared blocks: a cache policy only, results bit-identical.
     streamed = g.decode(out=torch.empty_like(g.q)).clone()
     cached = g.decode(out=torch.empty_like(g.q), shared_blocks=True)
@@ -56,17 +56,17 @@ def test_config4_parallel_sampling_cow(B):
     assert torch.equal(cached.view(torch.int16), streamed.view(torch.int16))
 
 
-def test_config5_opt175b_shape_sampled():
-    case = wl.config5()
+def test_opt175b_shape_sampled():
+    case = wl.opt175b_decode()
     order = np.argsort(case.context_lens)
     seqs = sorted(set(order[:: max(1, case.num_seqs // 12)].tolist() + [int(order[-1]), int(order[0])]))
     full_parity(case, partitions=(0,), seqs=seqs)
 
 
-def test_config5_tp8_share_sampled():
+def test_opt175b_tp8_share_sampled():
     # One tensor-parallel rank's share of the OPT-175B-shaped layer: 96 heads
     # over 8 GPUs leave 12 per GPU, with the same block tables and lengths.
-    case = wl.config5(num_heads=12)
+    case = wl.opt175b_decode(num_heads=12)
     order = np.argsort(case.context_lens)
     seqs = sorted(set(order[:: max(1, case.num_seqs // 16)].tolist() + [int(order[-1]), int(order[0])]))
     full_parity(case, partitions=(0, 512), seqs=seqs)
@@ -206,7 +206,7 @@ def test_split_partitions_agree():
 
 
 def test_fork_reads_through_copy_bitwise():
-    case = wl.config4(block_size=16, num_prompts=4, num_heads=8, head_dim=128, pool_tokens=16384)
+    case = wl.parallel_sampling(block_size=16, num_prompts=4, num_heads=8, head_dim=128, pool_tokens=16384)
     g = GpuCase(case)
     g.run_step(0)
     g.run_step(1)

@@ -244,12 +244,12 @@ def check_balanced_bounds(S, Hk, G, D, B, N, W, ctx, bt, max_ctx, num_wgs):
 
 
 CASES = [
-    ("config1", functools.lru_cache(None)(lambda: wl.config1())),
-    ("config2", functools.lru_cache(None)(lambda: wl.config2())),
-    ("config3", functools.lru_cache(None)(lambda: wl.config3())),
-    ("config4-B8", functools.lru_cache(None)(lambda: wl.config4(block_size=8, num_heads=1, head_dim=128))),
-    ("config4-B32", functools.lru_cache(None)(lambda: wl.config4(block_size=32, num_heads=1, head_dim=128))),
-    ("config5", functools.lru_cache(None)(lambda: wl.config5(num_heads=2))),
+    ("tiny-f32", functools.lru_cache(None)(lambda: wl.tiny_f32())),
+    ("llama7b-decode", functools.lru_cache(None)(lambda: wl.llama7b_decode())),
+    ("opt13b-decode", functools.lru_cache(None)(lambda: wl.opt13b_decode())),
+    ("sampling-B8", functools.lru_cache(None)(lambda: wl.parallel_sampling(block_size=8, num_heads=1, head_dim=128))),
+    ("sampling-B32", functools.lru_cache(None)(lambda: wl.parallel_sampling(block_size=32, num_heads=1, head_dim=128))),
+    ("opt175b-decode", functools.lru_cache(None)(lambda: wl.opt175b_decode(num_heads=2))),
     ("edge", functools.lru_cache(None)(lambda: wl.random_case(21, 5, 2, 64, 1, "bf16", ctx=[0, 1, 2, 513, 700]))),
     ("gqa-llama3-8b", functools.lru_cache(None)(lambda: wl.gqa_config("llama3-8b"))),
 ]
@@ -283,8 +283,8 @@ def test_invalid_ids_are_clamped_in_the_model():
     check_decode_bounds(2, 1, 8, 4, case.num_blocks, bt.shape[1], 4, case.context_lens, bt, 9, 4)
 
 
-MFMA_CASES = [c for c in CASES if c[0] in ("config2", "config3", "config5", "edge", "gqa-llama3-8b",
-                                            "config4-B8", "config4-B32")]
+MFMA_CASES = [c for c in CASES if c[0] in ("llama7b-decode", "opt13b-decode", "opt175b-decode", "edge", "gqa-llama3-8b",
+                                            "sampling-B8", "sampling-B32")]
 
 
 @pytest.mark.parametrize("name,make", MFMA_CASES, ids=[c[0] for c in MFMA_CASES])

@@ -48,11 +48,12 @@ def _check_case(case: wl.Case):
     return seen
 
 
-@pytest.mark.parametrize("n", [1, 2, 3])
-def test_config_block_tables_are_well_formed(n):
-    case = wl.config(n)
+@pytest.mark.parametrize("make", [wl.tiny_f32, wl.llama7b_decode, wl.opt13b_decode],
+                         ids=["tiny-f32", "llama7b", "opt13b"])
+def test_block_tables_are_well_formed(make):
+    case = make()
     used = _check_case(case)
-    # No two sequences share a block in configs without forking.
+    # No two sequences share a block in workloads without forking.
     assert len(used) == sum(math.ceil(int(c) / case.block_size) for c in case.context_lens)
     # Every slot outside the valid tokens holds the canary; valid slots do not.
     bits = wl.bits_view(case.k_cache)
@@ -67,15 +68,15 @@ def test_config_block_tables_are_well_formed(n):
     assert (per_slot[valid] != canary).all()
 
 
-def test_config1_shape():
-    c = wl.config1()
+def test_tiny_f32_shape():
+    c = wl.tiny_f32()
     assert c.context_lens.tolist() == [5, 16, 37]
     assert c.num_blocks == 16 and c.meta["blocks_used"] == 16
     assert c.q.dtype == np.float32 and c.scale == pytest.approx(1 / math.sqrt(8))
 
 
-def test_config3_append_slots():
-    c = wl.config3()
+def test_opt13b_append_slots():
+    c = wl.opt13b_decode()
     st = c.steps[0]
     assert st.key.shape == (256, 40, 128)
     assert np.unique(st.slot_mapping).size == 256
@@ -86,8 +87,8 @@ def test_config3_append_slots():
 
 
 @pytest.mark.parametrize("B", [8, 16, 32])
-def test_config4_cow_structure(B):
-    c = wl.config4(block_size=B, num_prompts=8, num_heads=2, head_dim=8, pool_tokens=65536)
+def test_parallel_sampling_cow_structure(B):
+    c = wl.parallel_sampling(block_size=B, num_prompts=8, num_heads=2, head_dim=8, pool_tokens=65536)
     ap0, cp, ap1 = c.steps
     assert cp.pairs.shape == (8 * 3, 2)
     src, dst = cp.pairs[:, 0], cp.pairs[:, 1]

@@ -6,19 +6,17 @@ attention, cache-write or block-copy computation lives here.
 """
 from .blockpool import BlockPool, PoolExhausted, SeqBlocks, append_tokens, cow_last_block, fork, tables_array
 from .cases import (
-    CONFIG_NAMES,
     GQA_NAMES,
     PREFILL_NAMES,
     AppendStep,
     Case,
     CopyStep,
-    config,
-    config1,
-    config2,
-    config3,
-    config3_lengths,
-    config4,
-    config5,
+    tiny_f32,
+    llama7b_decode,
+    opt13b_decode,
+    opt13b_context_lengths,
+    parallel_sampling,
+    opt175b_decode,
     gqa_config,
     normal_storage,
     prefill_config,

@@ -231,26 +231,17 @@ def _prefill_case(name, dtype, H, D, B, N, prefix, chunk, seed, perm, Hk=None, s
 
 
 # --------------------------------------------------------------------------
-# The five workload configurations.
+# The decode workloads: a tiny fp32 case and four model-shaped layers.
 # --------------------------------------------------------------------------
 
-CONFIG_NAMES = {
-    1: "tiny-f32: 3 seqs ctx 5/16/37, H=1, D=8, B=4",
-    2: "llama7b-decode: 64 seqs ctx U[128,2048], H=32, D=128, f16, B=16",
-    3: "opt13b-decode: 256 seqs lognormal(300, 0.9) ctx, H=40, D=128, f16, B=16, +1 appended token",
-    4: "parallel-sampling-cow: 64 prompts x 4 samples, prompt 500, suffix U[0,256], H=40, D=128, f16",
-    5: "opt175b-decode: 128 seqs ctx U[1024,2048], H=96, D=128, bf16, B=16",
-}
-
-
-def config1() -> Case:
+def tiny_f32() -> Case:
     seed = BASE_SEED + 1
     rng = np.random.default_rng(seed)
     perm = rng.permutation(16)
-    return _paged_case("config1", "f32", 1, 8, 4, 16, [5, 16, 37], seed, perm, 0, scale=1.0 / math.sqrt(8.0))
+    return _paged_case("tiny-f32", "f32", 1, 8, 4, 16, [5, 16, 37], seed, perm, 0, scale=1.0 / math.sqrt(8.0))
 
 
-def config2(num_seqs: int = 64, n_append: int = 0) -> Case:
+def llama7b_decode(num_seqs: int = 64, n_append: int = 0) -> Case:
     """LLaMA-7B-shaped decode layer.  With ``n_append`` = 1 the last context
     token of every sequence is written by an append step (a serving decode
     step: store the current token's K/V, then attend)."""
@@ -258,31 +249,31 @@ def config2(num_seqs: int = 64, n_append: int = 0) -> Case:
     rng = np.random.default_rng(seed)
     ctx = rng.integers(128, 2049, 64)[:num_seqs]
     perm = rng.permutation(8192)
-    return _paged_case("config2", "f16", 32, 128, 16, 8192, ctx, seed, perm, n_append)
+    return _paged_case("llama7b-decode", "f16", 32, 128, 16, 8192, ctx, seed, perm, n_append)
 
 
-def config3_lengths() -> np.ndarray:
+def opt13b_context_lengths() -> np.ndarray:
     rng = np.random.default_rng(BASE_SEED + 3)
     return np.clip(np.round(rng.lognormal(math.log(300.0), 0.9, 256)), 16, 2048).astype(np.int64)
 
 
-def config3() -> Case:
+def opt13b_decode() -> Case:
     seed = BASE_SEED + 3
-    ctx = config3_lengths()
+    ctx = opt13b_context_lengths()
     rng = np.random.default_rng([seed, 1])
     perm = rng.permutation(16384)
-    return _paged_case("config3", "f16", 40, 128, 16, 16384, ctx, seed, perm, 1)
+    return _paged_case("opt13b-decode", "f16", 40, 128, 16, 16384, ctx, seed, perm, 1)
 
 
-def config5(num_heads: int = 96, n_append: int = 0) -> Case:
+def opt175b_decode(num_heads: int = 96, n_append: int = 0) -> Case:
     seed = BASE_SEED + 5
     rng = np.random.default_rng(seed)
     ctx = rng.integers(1024, 2049, 128)
     perm = rng.permutation(16384)
-    return _paged_case("config5", "bf16", num_heads, 128, 16, 16384, ctx, seed, perm, n_append)
+    return _paged_case("opt175b-decode", "bf16", num_heads, 128, 16, 16384, ctx, seed, perm, n_append)
 
 
-def config4(
+def parallel_sampling(
     block_size: int = 16,
     num_prompts: int = 64,
     samples: int = 4,
@@ -343,7 +334,7 @@ def config4(
         ),
     ]
     return Case(
-        name=f"config4-B{B}",
+        name=f"parallel-sampling-B{B}",
         dtype=dtype,
         num_heads=H,
         head_dim=D,
@@ -375,7 +366,7 @@ GQA_NAMES = {
 def gqa_config(kind: str = "llama3-8b", n_append: int = 0) -> Case:
     """Grouped-query decode layers (query heads share K/V heads).
 
-    llama3-8b: the LLaMA-7B-shaped batch of config 2 with 32 query heads over
+    llama3-8b: the LLaMA-7B-shaped decode batch with 32 query heads over
     8 K/V heads (groups of 4).  llama2-70b-tp8: one tensor-parallel rank's
     share of a 64-query / 8-K/V-head layer (8 query heads over 1 K/V head,
     groups of 8), 128 sequences of 512..4096 tokens.
@@ -410,7 +401,7 @@ def prefill_config(kind: str = "llama7b") -> Case:
     512-token chunk; the LLaMA-7B-shaped layer (32 heads) and the
     LLaMA-3-8B-shaped one (32 query over 8 K/V heads).
     prompts: whole-prompt prefill of 32 prompts with the chat-like lognormal
-    length mix of config 3 (no cached prefix), bf16.
+    length mix of the OPT-13B-shaped batch (no cached prefix), bf16.
     """
     if kind in ("llama7b", "llama3-8b"):
         seed = BASE_SEED + 8
@@ -446,10 +437,6 @@ def random_prefill_case(
     perm = rng.permutation(N)
     return _prefill_case(f"prefill-random-{seed}", dtype, num_heads, head_dim, block_size, N, prefix, chunk,
                          BASE_SEED * 1000 + seed, perm, Hk=num_kv_heads)
-
-
-def config(n: int, **kw) -> Case:
-    return {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}[n](**kw)
 
 
 # --------------------------------------------------------------------------
