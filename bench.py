@@ -81,6 +81,8 @@ def parse():
                          "prompt blocks")
     ap.add_argument("--rotate", type=int, default=2, help="independent pool copies cycled across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-second-config", action="store_true",
+                    help="with the default workload, skip timing the OPT-13B-shaped batch beside it")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle baseline")
     args = ap.parse_args()
     if args.warmup is None:
@@ -287,12 +289,65 @@ def main():
         return bench_prefill(args, case, pa, torch, dev)
     if args.config == "swap":
         return bench_swap(args, case, pa, torch, dev)
+    result = bench_decode(args, args.config, case, pa, torch, dev, full=True)
+    del case
+    if args.config == "llama7b" and not args.no_second_config:
+        # The OPT-13B-shaped batch (chat-like lengths, one appended token
+        # per sequence) timed the same way in the same run, with its own
+        # pools (freed after).
+        log("building workload config opt13b")
+        second = bench_decode(args, "opt13b", make_case("opt13b"), pa, torch, dev, full=False)
+        result["configs"] = {"opt13b": second}
+    probe = hbm_read_probe(pa, torch, dev)
+    result["hbm_read_probe"] = probe
+    best = probe["best_GB/s"]
+    result["roofline"]["frac_of_read_probe"] = round(result["roofline"]["achieved"] / best, 4)
+    for extra in result.get("configs", {}).values():
+        extra["roofline_frac_of_read_probe"] = round(extra["roofline_achieved"] / best, 4)
+    print(json.dumps(result), flush=True)
+
+
+def hbm_read_probe(pa, torch, dev, gib=4, reps=10):
+    """Achievable streaming-read rate (``pa_hbm_read_probe``): one 4 GiB
+    buffer read once per launch, 16-byte loads, non-temporal and cached, over
+    a few grid sizes; the best is the measured read ceiling decode is quoted
+    against beside the vendor peak."""
+    buf = torch.empty(gib << 30, dtype=torch.uint8, device=dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.zeros(cus * 8, dtype=torch.int32, device=dev)
+    runs = []
+    for nt in (True, False):
+        for per_cu in (2, 4, 8):
+            wgs = cus * per_cu
+            for _ in range(3):
+                pa.hbm_read_probe(buf, sink, wgs, nontemporal=nt)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record()
+            for _ in range(reps):
+                pa.hbm_read_probe(buf, sink, wgs, nontemporal=nt)
+            b.record()
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) / reps * 1e3
+            runs.append({"nontemporal": nt, "workgroups": wgs, "us": round(us, 1),
+                         "GB/s": round(buf.numel() / us / 1e3, 1)})
+    del buf
+    best = max(runs, key=lambda r: r["GB/s"])
+    log(f"HBM read probe: best {best}")
+    return {"bytes": gib << 30, "best_GB/s": best["GB/s"], "best": best, "runs": runs,
+            "note": "pa_hbm_read_probe: every byte of a 4 GiB buffer read once per launch (512-thread "
+                    "workgroups, 16-byte loads, four in flight per lane); HIP events around 10 launches"}
+
+
+def bench_decode(args, config, case, pa, torch, dev, full=True):
+    """The decode step of one workload.  full: the complete JSON record (copy
+    probe, CPU baseline); otherwise a summary for the record's `configs`."""
     import workloads as wl
 
     # The parallel-sampling workload's prompt write, fork copies and suffix
     # writes are set-up; the other workloads time their one-token-per-sequence
     # append with the decode.
-    if args.config == "sampling":
+    if config == "sampling":
         setup_steps, timed_steps = list(case.steps), []
     else:
         setup_steps, timed_steps = [], list(case.steps)
@@ -322,7 +377,7 @@ def main():
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
-    shared = args.shared_blocks == "on" or (args.shared_blocks == "auto" and args.config == "sampling")
+    shared = args.shared_blocks == "on" or (args.shared_blocks == "auto" and config == "sampling")
     fused = bool(timed_steps)
     if fused:
         assert len(timed_steps) == 1 and timed_steps[0].slot_mapping.size == S  # one newest row per sequence
@@ -404,6 +459,34 @@ def main():
     b2b_ms = decode_loop(args.steps, False)
     log(f"decode loop: rotated {rot_ms*1e3:.1f} us, back-to-back {b2b_ms*1e3:.1f} us")
 
+    decode_bytes, store_bytes = algorithmic_bytes(case, timed_steps)
+    step_bytes = decode_bytes + store_bytes
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    # The dominant kernel's average duration: a loop of pa_decode launches on
+    # the rotated pool copies, bracketed by HIP events on the launch stream
+    # (per-launch event pairs add their own ~2-4 us to each launch).
+    achieved = decode_bytes / (rot_ms * 1e-3) / 1e9
+    if not full:
+        return {
+            "workload": WORKLOADS[config],
+            "step": "pa_reshape_and_cache (1 new token per sequence) + pa_decode" if fused else "pa_decode",
+            "GB/s": round(value, 1),
+            "ms_per_step": round(ms_step, 5),
+            "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+            "decode_tokens_per_s": round(S / (ms_step * 1e-3), 1),
+            "step_bytes": int(step_bytes),
+            "roofline_achieved": round(achieved, 1),
+            "roofline_frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "avg_launch_us": round(rot_ms * 1e3, 2),
+            "back_to_back_us": round(b2b_ms * 1e3, 2),
+            "fused_ms_per_step": round(fused_ms, 5) if fused else None,
+            "fused_GB/s": round(step_bytes / (fused_ms * 1e-3) / 1e9, 1) if fused else None,
+            "dtype": case.dtype,
+            "num_seqs": S,
+            "sum_context_len": int(case.context_lens.sum()),
+            "partition_tokens": pa.partition_tokens(S, H, max_ctx, args.partition, num_kv_heads=case.num_kv_heads),
+        }
+
     # Copy-on-write block copies, timed beside the step on the first pool:
     # a fork-sized batch (192 pairs) and a large batch used as the HBM copy probe.
     used = np.unique(case.block_tables[case.block_tables >= 0])
@@ -430,18 +513,11 @@ def main():
     probe = time_copies(4096)
     log(f"copy_blocks: {cow}; copy probe: {probe}")
 
-    decode_bytes, store_bytes = algorithmic_bytes(case, timed_steps)
-    step_bytes = decode_bytes + store_bytes
-    value = step_bytes / (ms_step * 1e-3) / 1e9
-    # The dominant kernel's average duration: a loop of pa_decode launches on
-    # the rotated pool copies, bracketed by HIP events on the launch stream
-    # (per-launch event pairs add their own ~2-4 us to each launch).
-    achieved = decode_bytes / (rot_ms * 1e-3) / 1e9
     # The committed counters cover each profiled workload at its default partition.
     default_part = pa.partition_tokens(S, H, max_ctx, num_kv_heads=case.num_kv_heads)
     # The parallel-sampling counters were taken at its default 16-token blocks.
-    profiled = args.partition in (0, default_part) and (args.config != "sampling" or B == 16)
-    traffic = traffic_from_profiles(args.config, kernel_source_sha()) if profiled else None
+    profiled = args.partition in (0, default_part) and (config != "sampling" or B == 16)
+    traffic = traffic_from_profiles(config, kernel_source_sha()) if profiled else None
 
     result = {
         "metric": METRIC,
@@ -457,7 +533,7 @@ def main():
         "dtype": case.dtype,
         "data": "synthetic",
         "config": {
-            "workload": WORKLOADS[args.config],
+            "workload": WORKLOADS[config],
             "step": ("pa_reshape_and_cache (1 new token per sequence) + pa_decode" if fused else
                      "pa_decode (prompt write, copy-on-write fork and suffix writes done before timing)"),
             "num_seqs": S,
@@ -502,7 +578,7 @@ def main():
         "copy_blocks": cow,
         "hbm_copy_probe": probe,
     }
-    if args.config == "sampling":
+    if config == "sampling":
         ub = unique_kv_bytes(case)
         result["unique_kv_bytes"] = int(ub)
         result["unique_kv_GBps"] = round(ub / (rot_ms * 1e-3) / 1e9, 1)
@@ -522,7 +598,7 @@ def main():
             setup_pools = (kc, vc)
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds, timed_steps, setup_pools)
         result["cpu_baseline"]["gpu_over_oracle"] = round(value / result["cpu_baseline"]["value"], 1)
-    print(json.dumps(result), flush=True)
+    return result
 
 
 def prefill_flops(case, seqs=None):

@@ -265,9 +265,21 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pairs, int
  *
  * with r = query_start[s] + i, t over 0 .. ctx_s - n_s + i, and token t at
  * block block_tables[s][t / B], offset t % B.  G = num_heads / num_kv_heads
- * (any divisor).  Arithmetic as pa_decode: q.k products and p.v products of
- * the stored 16-bit values accumulated in fp32, out rounded to `dtype`
- * (nearest-even).
+ * (any divisor).  Arithmetic: q.k products of the stored 16-bit values
+ * accumulated in fp32; softmax in fp32 (base 2); the probabilities enter
+ * the p.v products as 16-bit matrix-core operands, accumulated in fp32:
+ *   - bf16: each probability p as a truncated bf16 hi part plus the bf16
+ *     rounding of the remainder (about 16 significant bits);
+ *   - f16: each probability as one round-to-nearest-even fp16 value p~
+ *     (relative error <= 2^-11, or 2^-25 absolute where p~ is subnormal),
+ *     and the row sum adds the same rounded values, so the output is the
+ *     exact softmax average under perturbed weights: its error is at most
+ *     2^-11 * sum_t w_t |V_t - out| + 2^-25 * sum_t |V_t - out| (w the
+ *     softmax weights) plus fp32 accumulation and the final rounding.
+ *     With N(0,1) values that is far below 2e-3; where V rows are large and
+ *     cancel (e.g. +-64) it can exceed 2e-3 (pa_decode keeps fp32
+ *     probabilities there).
+ * out is rounded to `dtype` (nearest-even).
  *
  *   out, query     [num_tokens, num_heads, head_dim], packed by sequence
  *   query_start    int32 [num_seqs + 1], device: rising from 0 to num_tokens;
@@ -281,10 +293,18 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pairs, int
  *
  * Built for dtype PA_F16 and PA_BF16 with head_dim 64 or 128 (others:
  * PA_ERR_UNSUPPORTED).  query, out and the caches 16-byte aligned.  Ownership,
- * streams and host-side errors as for pa_decode.  Device-side guards: a
- * sequence with n_s <= 0 is skipped; n_s > ctx_s or ctx_s > max_context_len
- * gives NaN rows; a needed block id outside [0, num_blocks) gives NaN for
- * the rows of that (128-row tile, head) without reading outside the caches.
+ * streams and host-side errors as for pa_decode.  Device-side guards (the
+ * kernel checks what it reads from device memory, nothing faults):
+ *   - a chunk whose rows are not inside [0, num_tokens) (query_start[s] < 0,
+ *     query_start[s+1] <= query_start[s], or query_start[s+1] > num_tokens)
+ *     is skipped: nothing read or written for it (an empty chunk, n_s = 0,
+ *     is the ordinary case of this);
+ *   - n_s > ctx_s, ctx_s > max_context_len or n_s > max_query_len gives NaN
+ *     in every row of that chunk;
+ *   - a needed block id outside [0, num_blocks) gives NaN for the rows of
+ *     that (128-row tile, head) without reading outside the caches.
+ * Chunks of a query_start that is not non-decreasing may overlap; their
+ * rows are then undefined (some may be left unwritten).
  */
 int pa_prefill(void* out, const void* query, const void* k_cache, const void* v_cache,
                const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start,

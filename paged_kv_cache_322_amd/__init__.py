@@ -30,6 +30,7 @@ __all__ = [
     "partition_tokens",
     "prefill",
     "swap_blocks",
+    "hbm_read_probe",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
@@ -68,6 +69,9 @@ lib.pa_swap_blocks.argtypes = [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i64,
 lib.pa_prefill.restype = ctypes.c_int
 lib.pa_prefill.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                            _i64, ctypes.c_float, _i32, _p]
+
+lib.pa_hbm_read_probe.restype = ctypes.c_int
+lib.pa_hbm_read_probe.argtypes = [_p, ctypes.c_size_t, _p, _i32, ctypes.c_uint32, ctypes.c_uint32, _p]
 
 _DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 SHARED_BLOCKS = 1  # PA_DECODE_SHARED_BLOCKS
@@ -324,3 +328,19 @@ def swap_blocks(dst_k: torch.Tensor, dst_v: torch.Tensor, src_k: torch.Tensor, s
                             block_pairs.data_ptr(), block_pairs.numel() // 2, H, D, B, Ns, Nd, _code(dt),
                             _stream_handle(dev, stream))
     _check(st, "pa_swap_blocks")
+
+
+def hbm_read_probe(buf: torch.Tensor, sink: torch.Tensor, num_workgroups: int, nontemporal: bool = True,
+                   magic: int = 0x5A17C0DE, stream=None) -> None:
+    """Read every byte of ``buf`` once (``pa_hbm_read_probe``, a measurement
+    aid): the achievable streaming-read rate.  ``sink`` is a uint32-sized
+    device tensor of ``num_workgroups`` elements, written only where a
+    workgroup's data XOR to ``magic``."""
+    _dev(buf, "buf")
+    _dev(sink, "sink")
+    if sink.numel() * sink.element_size() < 4 * num_workgroups:
+        raise ValueError("sink must hold num_workgroups uint32 values")
+    st = lib.pa_hbm_read_probe(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(),
+                               int(num_workgroups), int(magic) & 0xFFFFFFFF, 1 if nontemporal else 0,
+                               _stream_handle(buf.device, stream))
+    _check(st, "pa_hbm_read_probe")

@@ -23,7 +23,7 @@ OBJDIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
 SOURCES = ["pa_decode.hip", "pa_decode_f32.hip", "pa_decode_f16.hip", "pa_decode_bf16.hip", "pa_prefill.hip",
-           "pa_cache.hip", "pa_api.hip", "pa_block_manager.cpp"]
+           "pa_cache.hip", "pa_api.hip", "pa_probe.hip", "pa_block_manager.cpp"]
 
 # Host-only C++ (the block manager): built by the host compiler.
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Werror", f"-I{os.path.join(ROOT, 'include')}"]

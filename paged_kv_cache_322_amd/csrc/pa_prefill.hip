@@ -51,17 +51,24 @@
 //     round-robin by linear id, each XCD with its own L2.  Every workgroup of
 //     one (sequence, K/V head) unit gets a linear id congruent to the unit
 //     mod 8, so the unit's G query heads and query tiles read its K/V through
-//     one L2.  Two orders per XCD:
+//     one L2.  Three orders per XCD:
 //       - unit-major (most launched tiles hold rows: chunked prefill): the
 //         units in decreasing context length (sequences ranked in LDS), and
 //         all tiles and heads of a unit adjacent, last tile first, so they
 //         run together and share each K/V tile through the L2 instead of
 //         re-reading it from memory;
-//       - tile-major (mixed whole prompts, many empty tiles): the last query
-//         tile (most keys) of every unit first, then the second last, and
-//         so on, the G heads of a unit and tile adjacent: longest work
-//         first, and the empty tiles of short prompts exit early.
+//       - packed (mixed whole prompts, where most of a padded grid's tiles
+//         would be empty; at most 64 sequences): the last query tile (most
+//         keys) of every chunk first, then the second last, and so on,
+//         chunks in decreasing length within a level, the G heads of a unit
+//         and tile adjacent: longest work first, and only tiles holding
+//         rows are enumerated (each workgroup finds its tile from the chunk
+//         lengths in LDS);
+//       - tile-major (more sequences than can be ranked): the same level
+//         order over every unit's padded tiles; empty tiles exit at once.
 #include <math.h>
+
+#include <algorithm>
 
 #include "pa_decode_mfma.h"  // MfmaOps, vector types
 #include "pa_device.h"
@@ -82,7 +89,7 @@ constexpr int kPfPad = 16;                          // LDS row padding (elements
 // rescaled rarely; probabilities stay below 2^8 (no overflow in f16/bf16 or
 // fp32).
 constexpr float kPfRescaleSlack = 8.0f;
-constexpr int kPfMaxRankedSeqs = 64;  // unit-major order ranks at most this many sequences
+constexpr int kPfMaxRankedSeqs = 64;  // the ranked orders rank at most this many sequences
 static_assert(kPfMaxRankedSeqs <= kPfThreads, "one thread ranks one sequence");
 
 template <int D>
@@ -154,13 +161,27 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
     return __builtin_bit_cast(u32x2, v);
 }
 
+// Dispatch orders of the prefill grid (chosen on the host).
+constexpr int kPfOrderTileMajor = 0;  // query tiles last first, every unit's tiles launched (padded)
+constexpr int kPfOrderUnitMajor = 1;  // units by decreasing context, all of a unit's tiles adjacent
+constexpr int kPfOrderPacked = 2;     // tile levels last first, only tiles that hold rows
+constexpr int kPfMaxLevels = 64;      // packed order: at most this many 128-row tiles per chunk
+static_assert(kPfMaxLevels <= kPfThreads, "one thread counts one tile level");
+
+// Rows of sequence s whose chunk lies inside the call's rows [0, num_tokens):
+// n >= 1, or 0 for an empty chunk or one outside the call's rows (skipped).
+__device__ __forceinline__ int chunk_rows(const int32_t* __restrict__ query_start, int s, int num_tokens) {
+    const int q0 = query_start[s], q1 = query_start[s + 1];
+    return (q0 >= 0 && q1 > q0 && q1 <= num_tokens) ? q1 - q0 : 0;
+}
+
 template <class T, int D>
 __global__ __launch_bounds__(kPfThreads, kPfWavesPerSimd) void prefill_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ query_start, int num_heads,
     int num_kv_heads, int log2_bs, int max_blocks_per_seq, int64_t num_blocks, int max_context_len, int n_qtiles,
-    int num_units, int unit_major, float qscale) {
+    int num_units, int num_tokens, int max_query_len, int order, float qscale) {
     using Sh = PfShape<D>;
     constexpr int KS = Sh::KS, E = Sh::E, LD = Sh::LD, CPR = Sh::CPR, CPT = Sh::CPT;
     constexpr int RB = kPfBlocks;
@@ -170,73 +191,119 @@ __global__ __launch_bounds__(kPfThreads, kPfWavesPerSimd) void prefill_kernel(
     __shared__ __align__(16) uint16_t sK[2][kPfKeys][LD];
     __shared__ __align__(16) uint16_t sV[2][kPfKeys][LD];
 
-    // Linear id -> (query tile, unit, head): unit u runs on XCD u % 8, and
-    // per XCD the ids r8 = lin / 8 run
+    // Linear id -> (query tile, unit, head).  A unit is a (sequence, K/V
+    // head); unit u runs on XCD u % 8, and per XCD the ids r8 = lin / 8 run
+    //   tile-major: through the query tiles last first, within a tile
+    //     through the XCD's units and, within a unit, its G query heads;
+    //     unit u is (sequence u / Hk, K/V head u % Hk).  The grid holds
+    //     ceil(units / 8) * 8 * G * n_qtiles workgroups; those of padding
+    //     units and of tiles past a chunk return at once;
     //   unit-major: through the XCD's units, within a unit through its query
     //     tiles last first and, within a tile, its G query heads; unit u is
     //     (sequence of rank u / Hk in decreasing context length, K/V head
-    //     u % Hk);
-    //   tile-major: through the query tiles last first, within a tile
-    //     through the XCD's units and, within a unit, its G query heads;
-    //     unit u is (sequence u / Hk, K/V head u % Hk).
-    // The grid holds ceil(units / 8) * 8 * G * n_qtiles workgroups; those of
-    // padding units return at once.
+    //     u % Hk).  Same grid;
+    //   packed: through tile levels j = 0, 1, ... (level j is the j-th tile
+    //     from a chunk's end), within a level through the XCD's units that
+    //     have a tile there and, within a unit, its G heads; unit u is
+    //     (sequence of rank u / Hk in decreasing chunk length, K/V head
+    //     u % Hk), so level j holds the first c_j * Hk units, c_j the number
+    //     of chunks with more than j tiles.  Only tiles holding rows are
+    //     enumerated; the grid is an upper bound and the ids past the last
+    //     level return at once.
+    // Ranks break ties by sequence index (num_seqs <= kPfMaxRankedSeqs:
+    // host check for both ranked orders).
     const int G = num_heads / num_kv_heads;
     const int lin = static_cast<int>(blockIdx.x);
     const int xcd = lin % kXcds, r8 = lin / kXcds;
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
-    int qt, unit;
-    if (unit_major) {
-        const int per_unit = n_qtiles * G;
-        qt = n_qtiles - 1 - (r8 % per_unit) / G;
-        unit = (r8 / per_unit) * kXcds + xcd;
-    } else {
+    const int num_seqs = num_units / num_kv_heads;
+    int qt, s, hk, h;
+    if (order == kPfOrderTileMajor) {
         const int per_tile = static_cast<int>(gridDim.x) / (kXcds * n_qtiles);  // units per XCD x G
         qt = n_qtiles - 1 - r8 / per_tile;
-        unit = ((r8 % per_tile) / G) * kXcds + xcd;
-    }
-    if (unit >= num_units) return;
-    const int hk = unit % num_kv_heads;
-    const int h = hk * G + r8 % G;
-    int s = unit / num_kv_heads;
-    if (unit_major) {
-        // Sequence of rank s in decreasing context length, ties by index
-        // (num_seqs <= kPfMaxRankedSeqs: host check).
-        __shared__ int s_len[kPfMaxRankedSeqs];
-        __shared__ int s_pick;
-        const int num_seqs = num_units / num_kv_heads;
-        if (tid < num_seqs) s_len[tid] = context_lens[tid];
-        __syncthreads();
-        if (tid < num_seqs) {
-            const int c0 = s_len[tid];
-            int rank = 0;
-            for (int j = 0; j < num_seqs; ++j) {
-                const int cj = s_len[j];
-                rank += (cj > c0) || (cj == c0 && j < tid);
+        const int unit = ((r8 % per_tile) / G) * kXcds + xcd;
+        if (unit >= num_units) return;
+        s = unit / num_kv_heads;
+        hk = unit % num_kv_heads;
+        h = hk * G + r8 % G;
+    } else {
+        __shared__ int s_key[kPfMaxRankedSeqs];
+        __shared__ int s_lvl[kPfMaxLevels];
+        __shared__ int s_pick, s_level, s_off;
+        int rank, level = 0;
+        if (order == kPfOrderUnitMajor) {
+            const int per_unit = n_qtiles * G;
+            qt = n_qtiles - 1 - (r8 % per_unit) / G;
+            const int unit = (r8 / per_unit) * kXcds + xcd;
+            if (unit >= num_units) return;
+            rank = unit / num_kv_heads;
+            hk = unit % num_kv_heads;
+            h = hk * G + r8 % G;
+            if (tid < num_seqs) s_key[tid] = context_lens[tid];
+            __syncthreads();
+        } else {
+            // Rank key: the chunk's rows (0 when skipped), capped at the
+            // launched tiles.  Tiles of sequence i: ceil(key / 128).
+            if (tid < num_seqs) s_key[tid] = min(chunk_rows(query_start, tid, num_tokens), n_qtiles * kPfRows);
+            __syncthreads();
+            if (tid < n_qtiles) {
+                int cnt = 0;
+                for (int i = 0; i < num_seqs; ++i) cnt += s_key[i] > tid * kPfRows;
+                const int units_j = cnt * num_kv_heads;
+                s_lvl[tid] = units_j > xcd ? (units_j - xcd + kXcds - 1) / kXcds * G : 0;
             }
-            if (rank == s) s_pick = tid;
+            __syncthreads();
+            if (tid == 0) {
+                int base = 0, j = 0;
+                while (j < n_qtiles && r8 >= base + s_lvl[j]) base += s_lvl[j++];
+                s_level = j;
+                s_off = r8 - base;
+            }
+            __syncthreads();
+            level = __builtin_amdgcn_readfirstlane(s_level);
+            if (level >= n_qtiles) return;  // past the last level (uniform)
+            const int off = __builtin_amdgcn_readfirstlane(s_off);
+            const int unit = (off / G) * kXcds + xcd;
+            rank = unit / num_kv_heads;
+            hk = unit % num_kv_heads;
+            h = hk * G + off % G;
+        }
+        if (tid < num_seqs) {
+            const int c0 = s_key[tid];
+            int r = 0;
+            for (int j = 0; j < num_seqs; ++j) {
+                const int cj = s_key[j];
+                r += (cj > c0) || (cj == c0 && j < tid);
+            }
+            if (r == rank) s_pick = tid;
         }
         __syncthreads();
         s = __builtin_amdgcn_readfirstlane(s_pick);
+        if (order == kPfOrderPacked) qt = (__builtin_amdgcn_readfirstlane(s_key[s]) + kPfRows - 1) / kPfRows - 1 - level;
     }
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int c = lane & 15, g = lane >> 4;
 
+    // Guards on the device-side row bounds: a chunk whose rows are not inside
+    // [0, num_tokens) (query_start falling, negative or past num_tokens) is
+    // skipped, nothing read or written.
     const int q0 = __builtin_amdgcn_readfirstlane(query_start[s]);
-    const int n = __builtin_amdgcn_readfirstlane(query_start[s + 1]) - q0;
+    const int q1 = __builtin_amdgcn_readfirstlane(query_start[s + 1]);
+    if (q0 < 0 || q1 <= q0 || q1 > num_tokens) return;
+    const int n = q1 - q0;
     const int r0 = qt * kPfRows;  // first row of this workgroup within the chunk
-    if (n <= 0 || r0 >= n) return;
+    if (r0 >= n) return;
     const int ctx = __builtin_amdgcn_readfirstlane(context_lens[s]);
     const int wr0 = r0 + 16 * RB * wave;  // first row of this wavefront
-    if (ctx < n || ctx > max_context_len) {
-        // Impossible lengths: NaN rows, nothing read.
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            const int row = wr0 + 16 * rb + c;
-            if (row < n) {
-                for (int d = g; d < D; d += 4)
-                    out[(static_cast<int64_t>(q0 + row) * num_heads + h) * D + d] = narrow<T>(__builtin_nanf(""));
-            }
+    if (ctx < n || ctx > max_context_len || n > max_query_len) {
+        // Impossible lengths: NaN rows, nothing read.  A chunk longer than
+        // max_query_len has tiles only up to n_qtiles; the last of them
+        // writes every row past its start.
+        const int row_end = (n > max_query_len && qt == n_qtiles - 1) ? n : min(r0 + kPfRows, n);
+        const uint16_t nan_bits = narrow<T>(__builtin_nanf(""));
+        for (int row = r0 + tid / (D / 2); row < row_end; row += kPfThreads / (D / 2)) {
+            uint32_t* op = reinterpret_cast<uint32_t*>(out + (static_cast<int64_t>(q0 + row) * num_heads + h) * D);
+            op[tid % (D / 2)] = nan_bits * 0x10001u;
         }
         return;
     }
@@ -472,19 +539,35 @@ hipError_t launch_prefill_t(const PrefillArgs& a) {
     const float qscale = a.scale * 1.4426950408889634f;  // log2(e)
     const int n_qtiles = (a.max_query_len + kPfRows - 1) / kPfRows;
     const int num_units = a.num_seqs * a.num_kv_heads;
-    const int64_t items = static_cast<int64_t>(a.num_heads / a.num_kv_heads) * n_qtiles;
+    const int G = a.num_heads / a.num_kv_heads;
     const int64_t groups = (num_units + kXcds - 1) / kXcds;
-    dim3 grid(static_cast<unsigned>(groups * kXcds * items));
+    const int64_t padded = groups * kXcds * G * n_qtiles;  // every unit's n_qtiles tiles
     // Unit-major order when at least half of the launched query tiles hold
-    // rows (the chunks fill their tiles); tile-major otherwise.
-    const int unit_major = a.num_seqs <= kPfMaxRankedSeqs &&
-                           2 * static_cast<int64_t>(a.num_tokens) >= static_cast<int64_t>(a.num_seqs) * n_qtiles * kPfRows;
+    // rows (the chunks fill their tiles); otherwise the packed order, which
+    // launches only tiles holding rows, when the sequences can be ranked;
+    // tile-major beyond that.
+    const bool rankable = a.num_seqs <= kPfMaxRankedSeqs;
+    int order = kPfOrderTileMajor;
+    int64_t wgs = padded;
+    if (rankable && 2 * static_cast<int64_t>(a.num_tokens) >= static_cast<int64_t>(a.num_seqs) * n_qtiles * kPfRows) {
+        order = kPfOrderUnitMajor;
+    } else if (rankable && n_qtiles <= kPfMaxLevels) {
+        // Chunks inside [0, num_tokens) hold at most (num_tokens + 127 S) /
+        // 128 tiles in all; an XCD's share of level j is at most
+        // ceil(c_j Hk / 8) units, so per XCD at most that total * Hk / 8 +
+        // n_qtiles units (G workgroups each).
+        order = kPfOrderPacked;
+        const int64_t tiles = (static_cast<int64_t>(a.num_tokens) + (kPfRows - 1) * int64_t{a.num_seqs}) / kPfRows;
+        const int64_t per_xcd = (tiles * a.num_kv_heads + kXcds - 1) / kXcds + n_qtiles;
+        wgs = std::min(padded, per_xcd * kXcds * G);
+    }
+    dim3 grid(static_cast<unsigned>(wgs));
     const size_t lds = static_cast<size_t>(a.staged_ids) * sizeof(int);
     hipLaunchKernelGGL((prefill_kernel<T, D>), grid, dim3(kPfThreads), lds, a.stream, static_cast<uint16_t*>(a.out),
                        static_cast<const uint16_t*>(a.query), static_cast<const uint16_t*>(a.k_cache),
                        static_cast<const uint16_t*>(a.v_cache), a.block_tables, a.context_lens, a.query_start,
                        a.num_heads, a.num_kv_heads, log2_bs, a.max_blocks_per_seq, a.num_blocks, a.max_context_len,
-                       n_qtiles, num_units, unit_major, qscale);
+                       n_qtiles, num_units, a.num_tokens, a.max_query_len, order, qscale);
     return hipGetLastError();
 }
 

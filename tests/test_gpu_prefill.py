@@ -5,7 +5,7 @@ Chunked-prefill batches shaped like a LLaMA-7B layer and a LLaMA-3-8B
 mix, a sweep of ragged shapes (chunks of 1 row, chunks crossing 64-row tiles,
 whole prompts, block sizes 1..256, groups 1..8), and the invariants:
 chunked == whole-prompt rows, single-row chunks == pa_decode, guards.
-The oracle runs on sampled sequences for the large batches.
+Every batch is compared with the oracle on every row of every sequence.
 """
 import dataclasses
 
@@ -15,7 +15,7 @@ import torch
 
 import oracle
 import workloads as wl
-from gpu_helpers import assert_close, log, pa, to_gpu
+from gpu_helpers import assert_close, log, out_ulp, pa, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -73,28 +73,19 @@ def check(case, seqs=None, strict=True, max_query_len=None):
     return run
 
 
-def _sample(case, k=3):
-    lens = case.context_lens
-    order = np.argsort(lens, kind="stable")
-    return sorted({int(order[0]), int(order[len(order) // 2]), int(order[-1])})
-
-
 def test_prefill_llama7b_chunked():
-    case = wl.prefill_config("llama7b")
-    check(case, seqs=_sample(case))
+    check(wl.prefill_config("llama7b"))
 
 
 def test_prefill_llama3_8b_gqa_chunked():
-    case = wl.prefill_config("llama3-8b")
-    check(case, seqs=_sample(case))
+    check(wl.prefill_config("llama3-8b"))
 
 
 def test_prefill_whole_prompts_bf16():
     # A whole prompt's first rows attend to a handful of tokens, so |out|
     # reaches ~3 there, where bf16's half-ulp (2^-7 on [2, 4)) exceeds 2e-3:
     # the bound is 2e-3 or one output ulp, as for the short decode contexts.
-    case = wl.prefill_config("prompts")
-    check(case, seqs=_sample(case), strict=False)
+    check(wl.prefill_config("prompts"), strict=False)
 
 
 SWEEP = [
@@ -135,9 +126,10 @@ def test_prefill_zero_and_negative_scale(dtype, scale):
 @pytest.mark.parametrize("dtype,H,Hk", [("f16", 8, 8), ("bf16", 16, 4)])
 def test_prefill_dispatch_orders_agree_bitwise(dtype, H, Hk):
     """The launch order of the query tiles (unit-major with sequences ranked
-    by context length when the chunks fill the launched tiles, tile-major
-    otherwise) changes no row's arithmetic: a generous max_query_len, which
-    launches mostly empty tiles and so flips the order, gives identical bits."""
+    by context length when the chunks fill the launched tiles, the packed
+    level order otherwise) changes no row's arithmetic: a generous
+    max_query_len, which would launch mostly empty tiles and so flips the
+    order, gives identical bits."""
     case = wl.random_prefill_case(1234 + H, [700, 0, 300, 1500, 64], [256, 250, 130, 200, 256], H, 128, 16, dtype,
                                   num_kv_heads=Hk)
     run = PrefillRun(case)
@@ -145,7 +137,7 @@ def test_prefill_dispatch_orders_agree_bitwise(dtype, H, Hk):
     assert 2 * case.num_tokens >= case.num_seqs * ((mq + 127) // 128) * 128  # unit-major
     a = run.run().clone()
     big = 4 * 128 * ((mq + 127) // 128)
-    assert big <= case.max_context_len and 2 * case.num_tokens < case.num_seqs * big  # tile-major
+    assert big <= case.max_context_len and 2 * case.num_tokens < case.num_seqs * big  # packed
     b = run.run(max_query_len=big).clone()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     kc, vc = oracle_pools(case)
@@ -224,3 +216,146 @@ def test_prefill_guards():
     pa().prefill(run.out, run.q, run.kc, run.vc, run.bt, run.ctx, run.qs, case.scale, 70, case.max_context_len)
     torch.cuda.synchronize()
     assert (run.out[qs[2]:qs[3]].float() == 7.0).all()
+
+
+def test_prefill_tile_major_many_sequences():
+    """More than 64 sequences (too many to rank in the kernel) take the
+    padded tile-major order; the same chunks prefilled in two calls of at
+    most 64 sequences (ranked orders) give identical bits, and every row
+    matches the oracle."""
+    S = 70
+    rng = np.random.default_rng(70)
+    prefix = rng.integers(0, 300, S).tolist()
+    chunk = rng.integers(1, 200, S).tolist()
+    case = wl.random_prefill_case(7070, prefix, chunk, 4, 64, 16, "f16", num_kv_heads=2)
+    run = PrefillRun(case)
+    whole = run.run().clone()
+    kc, vc = oracle_pools(case)
+    ref, rows = oracle_rows(case, kc, vc, range(S))
+    assert_close(whole[torch.from_numpy(rows).cuda()], ref, "f16", "70-sequence prefill", strict=False)
+    qs = case.query_start
+    for lo, hi in ((0, 35), (35, 70)):
+        r0, r1 = int(qs[lo]), int(qs[hi])
+        sub_qs = torch.from_numpy((qs[lo:hi + 1] - r0).astype(np.int32)).cuda()
+        out = torch.full_like(run.q[r0:r1], float("nan"))
+        pa().prefill(out, run.q[r0:r1].contiguous(), run.kc, run.vc, run.bt[lo:hi].contiguous(),
+                     run.ctx[lo:hi].contiguous(), sub_qs, case.scale, int(np.diff(qs).max()), case.max_context_len)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), whole[r0:r1].view(torch.int16)), (lo, hi)
+
+
+def test_prefill_query_start_guards():
+    """Row bounds read from device memory are guarded: a chunk that starts
+    below 0 or ends past num_tokens is skipped (its rows keep their old
+    contents, nothing faults), and a chunk longer than max_query_len gets
+    NaN rows; the other chunks are unaffected."""
+    case = wl.random_prefill_case(44, [10, 0, 4, 30], [40, 70, 3, 20], 4, 64, 8, "f16", num_kv_heads=2)
+    run = PrefillRun(case)
+    kc, vc = oracle_pools(case)
+    qs = case.query_start.copy()
+    T = case.num_tokens
+
+    def with_qs(new_qs, max_query_len=70):
+        run.qs = to_gpu(np.asarray(new_qs, dtype=np.int32))
+        run.out.fill_(7.0)
+        return run.run(max_query_len=max_query_len)
+
+    def others_match(out, seqs, what):
+        ref, rows = oracle_rows(case, kc, vc, seqs)
+        assert_close(out[torch.from_numpy(rows).cuda()], ref, case.dtype, what, strict=False)
+
+    # Chunk 0 starts below 0: skipped.
+    bad = qs.copy()
+    bad[0] = -8
+    out = with_qs(bad)
+    assert (out[0:qs[1]].float() == 7.0).all()
+    others_match(out, [1, 2, 3], "guard: negative start")
+    # The last chunk ends past num_tokens: skipped.
+    bad = qs.copy()
+    bad[-1] = T + 9
+    out = with_qs(bad)
+    assert (out[qs[3]:T].float() == 7.0).all()
+    others_match(out, [0, 1, 2], "guard: end past num_tokens")
+    # Chunk 1 (70 rows) is longer than max_query_len = 50: NaN rows.
+    out = with_qs(qs, max_query_len=50)
+    assert torch.isnan(out[qs[1]:qs[2]].float()).all()
+    others_match(out, [0, 2, 3], "guard: chunk longer than max_query_len")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_prefill_large_v_rows(dtype):
+    """Large V rows.  (a) A common offset of 300 plus small noise under a
+    peaked softmax: the offset cancels exactly against the row sum, so every
+    element is within 2e-3 or one output ulp.  (b) Rows of +-64 that cancel:
+    fp16 probabilities are rounded once to fp16 (relative error <= 2^-11
+    each, the row sum taken over the same rounded values), which bounds the
+    error by 2^-11 * sum_t w_t |V_t - out| (w the softmax weights); bf16
+    probabilities keep a hi/lo split, within 2e-3 or one ulp."""
+    base = wl.random_prefill_case(45, [0, 100, 700], [160, 130, 200], 4, 128, 16, dtype, num_kv_heads=2)
+    rng = np.random.default_rng(46)
+    nb, Hk, B, D = base.v_cache.shape
+
+    def store(x):
+        return wl.to_storage(x.astype(np.float32), dtype)
+
+    def prefill_with_v(v_fn, q_gain, strict_ok):
+        v = v_fn((nb, Hk, B, D))
+        c = dataclasses.replace(base, v_cache=store(v), q=store(oracle.widen(base.q, dtype) * q_gain))
+        c.steps = list(c.steps)
+        st = c.steps[0]
+        st_v = store(v_fn(st.value.shape))
+        c.steps[0] = dataclasses.replace(st, value=st_v)
+        run = PrefillRun(c)
+        out = run.run()
+        kc2, vc2 = oracle_pools(c)
+        ref, rows = oracle_rows(c, kc2, vc2, range(c.num_seqs))
+        got = out[torch.from_numpy(rows).cuda()]
+        if strict_ok:
+            assert_close(got, ref, dtype, f"{dtype} large V", strict=False)
+            return
+        # Proven bound for one rounded fp16 probability operand: each
+        # probability p (<= 2^8, relative to a reference that makes the row's
+        # sum >= 1) is off by at most 2^-11 p, or 2^-25 where fp16 is
+        # subnormal; the output moves by sum_t (p~_t - p_t)(V_t - out) / sum_t p_t.
+        wdev, adev = oracle_v_spread(c, kc2, vc2)
+        bound = wdev * 2.0 ** -11 + adev * 2.0 ** -25
+        err = np.abs(got.double().cpu().numpy() - ref)
+        ulp = out_ulp(ref, dtype)
+        log(f"{dtype} cancelling V: max err {err.max():.3e}, max err / bound {(err / (bound + ulp)).max():.3f}")
+        assert (err <= bound + ulp).all()
+
+    # (a) offset 300 + N(0, 0.25) noise, peaked softmax (queries x 4).
+    prefill_with_v(lambda shp: 300.0 + 0.5 * rng.standard_normal(shp), 4.0, True)
+    # (b) +-64 rows that cancel, moderately peaked softmax.
+    signs = lambda shp: 64.0 * np.where(rng.random(shp) < 0.5, -1.0, 1.0) + rng.standard_normal(shp)
+    prefill_with_v(signs, 2.0, dtype == "bf16")
+
+
+def oracle_v_spread(case, kc, vc):
+    """Per (row, head, channel): sum_t w_t |V_t - out| (the weighted mean
+    deviation of the attended V rows from the output, w the softmax
+    weights) and sum_t |V_t - out|, in float64."""
+    qs = case.query_start
+    T, H, D = case.q.shape
+    Hk = case.k_cache.shape[1]
+    G = H // Hk
+    spread = np.zeros((T, H, D))
+    total = np.zeros((T, H, D))
+    for s in range(case.num_seqs):
+        r0, r1 = int(qs[s]), int(qs[s + 1])
+        n, ctx = r1 - r0, int(case.context_lens[s])
+        K = oracle.widen(oracle.logical_kv(kc, case.block_tables[s], ctx), case.dtype)
+        V = oracle.widen(oracle.logical_kv(vc, case.block_tables[s], ctx), case.dtype)
+        Q = oracle.widen(case.q[r0:r1], case.dtype)
+        for h in range(H):
+            for i in range(n):
+                p = ctx - n + i
+                sc = case.scale * (K[h // G, : p + 1] @ Q[i, h])
+                w = np.exp(sc - sc.max())
+                w /= w.sum()
+                o = w @ V[h // G, : p + 1]
+                dev = np.abs(V[h // G, : p + 1] - o)
+                spread[r0 + i, h] = w @ dev
+                total[r0 + i, h] = dev.sum(axis=0)
+    return spread, total
+

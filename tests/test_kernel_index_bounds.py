@@ -432,44 +432,116 @@ def check_prefill_bounds(case, max_query_len=None):
         # output rows
         assert int(qs[s]) + n - 1 < T
     assert (H - 1) // G < Hk
-    # XCD-aware 1-D grid: linear id -> (query tile, unit, head) covers every
-    # (sequence, head, query tile) exactly once; padding units exit.
+    # Every order's linear id -> (sequence, head, query tile) map covers each
+    # tile that holds rows exactly once; padding ids exit.
+    rows = [prefill_chunk_rows(qs, s, T) for s in range(S)]
+    want = {(s_, h, qt) for s_ in range(S) for h in range(H) for qt in range(min(-(-rows[s_] // PF_ROWS), n_qt))}
+    for order in ("tile", "unit", "packed"):
+        if order != "tile" and S > PF_MAX_RANKED:
+            continue
+        if order == "packed" and n_qt > PF_MAX_LEVELS:
+            continue
+        grid = prefill_grid(S, Hk, G, n_qt, T, order)
+        assert grid <= 0x7FFFFFFF
+        got = [w for w in prefill_items(qs, case.context_lens, S, Hk, G, n_qt, T, grid, order)]
+        got = [w for w in got if w[2] * PF_ROWS < rows[w[0]]]  # tiles past a chunk exit
+        assert len(got) == len(set(got)), order
+        assert set(got) == want, order
+
+
+PF_MAX_RANKED, PF_MAX_LEVELS = 64, 64
+
+
+def prefill_chunk_rows(qs, s, T):
+    """Rows of chunk s the kernel serves: 0 when its rows are not inside [0, T)."""
+    q0, q1 = int(qs[s]), int(qs[s + 1])
+    return q1 - q0 if (q0 >= 0 and q1 > q0 and q1 <= T) else 0
+
+
+def prefill_order(S, n_qt, T):
+    """The host's choice of dispatch order (launch_prefill_t)."""
+    if S <= PF_MAX_RANKED and 2 * T >= S * n_qt * PF_ROWS:
+        return "unit"
+    if S <= PF_MAX_RANKED and n_qt <= PF_MAX_LEVELS:
+        return "packed"
+    return "tile"
+
+
+def prefill_grid(S, Hk, G, n_qt, T, order):
+    padded = -(-(S * Hk) // 8) * 8 * G * n_qt
+    if order != "packed":
+        return padded
+    tiles = (T + (PF_ROWS - 1) * S) // PF_ROWS
+    per_xcd = -(-(tiles * Hk) // 8) + n_qt
+    return min(padded, per_xcd * 8 * G)
+
+
+def prefill_items(qs, ctx, S, Hk, G, n_qt, T, grid, order):
+    """(sequence, head, query tile) of every workgroup that does not exit at
+    once, as the kernel maps linear ids (XCD = lin % 8 = unit % 8)."""
     units = S * Hk
-    groups = -(-units // 8)
-    grid = groups * 8 * G * n_qt
-    assert grid <= 0x7FFFFFFF
-    per_tile = grid // (8 * n_qt)
-    seen = set()
+    if order == "unit":
+        rank_to_seq = sorted(range(S), key=lambda i: (-int(ctx[i]), i))
+    if order == "packed":
+        key = [min(prefill_chunk_rows(qs, i, T), n_qt * PF_ROWS) for i in range(S)]
+        rank_to_seq = sorted(range(S), key=lambda i: (-key[i], i))
+        cnt = [sum(k > j * PF_ROWS for k in key) for j in range(n_qt)]
     for lin in range(grid):
         xcd, r8 = lin % 8, lin // 8
-        qt = n_qt - 1 - r8 // per_tile
-        unit = ((r8 % per_tile) // G) * 8 + xcd
-        if unit >= units:
-            continue
-        s_, hk = unit // Hk, unit % Hk
-        h = hk * G + r8 % G
-        assert 0 <= s_ < S and 0 <= h < H and 0 <= qt < n_qt and h // G == hk
-        assert unit % 8 == lin % 8  # a unit's workgroups share one XCD
-        seen.add((s_, h, qt))
-    assert len(seen) == S * H * n_qt
-    # Unit-major order (sequences ranked by decreasing context length, ties
-    # by index; at most 64 sequences): the same coverage.
-    if S <= 64:
-        ctx_all = [int(x) for x in case.context_lens]
-        rank_to_seq = sorted(range(S), key=lambda i: (-ctx_all[i], i))
-        per_unit = n_qt * G
-        seen = set()
-        for lin in range(grid):
-            xcd, r8 = lin % 8, lin // 8
+        if order == "tile":
+            per_tile = grid // (8 * n_qt)
+            qt = n_qt - 1 - r8 // per_tile
+            unit = ((r8 % per_tile) // G) * 8 + xcd
+            if unit >= units:
+                continue
+            s_, hk, h = unit // Hk, unit % Hk, (unit % Hk) * G + r8 % G
+        elif order == "unit":
+            per_unit = n_qt * G
             qt = n_qt - 1 - (r8 % per_unit) // G
             unit = (r8 // per_unit) * 8 + xcd
             if unit >= units:
                 continue
-            s_, hk = rank_to_seq[unit // Hk], unit % Hk
-            h = hk * G + r8 % G
-            assert 0 <= s_ < S and 0 <= h < H and 0 <= qt < n_qt and h // G == hk
-            seen.add((s_, h, qt))
-        assert len(seen) == S * H * n_qt
+            s_, hk, h = rank_to_seq[unit // Hk], unit % Hk, (unit % Hk) * G + r8 % G
+        else:
+            lvl = [(-(-(c * Hk - xcd) // 8)) * G if c * Hk > xcd else 0 for c in cnt]
+            base, j = 0, 0
+            while j < n_qt and r8 >= base + lvl[j]:
+                base += lvl[j]
+                j += 1
+            if j >= n_qt:
+                continue
+            off = r8 - base
+            unit = (off // G) * 8 + xcd
+            assert unit < cnt[j] * Hk  # a unit that has a tile at level j
+            s_ = rank_to_seq[unit // Hk]
+            hk, h = unit % Hk, (unit % Hk) * G + off % G
+            qt = -(-key[s_] // PF_ROWS) - 1 - j
+            assert qt >= 0
+        assert 0 <= s_ < S and 0 <= h < H_of(Hk, G) and 0 <= qt < n_qt and h // G == hk
+        assert unit % 8 == lin % 8  # a unit's workgroups share one XCD
+        yield (s_, h, qt)
+
+
+def H_of(Hk, G):
+    return Hk * G
+
+
+def test_prefill_row_guards_in_the_model():
+    """query_start entries that fall, go negative or pass num_tokens leave
+    that chunk without rows (skipped); every other chunk's tiles are still
+    enumerated by every order, and no served row lies outside [0, T)."""
+    T, S, Hk, G = 300, 6, 2, 2
+    qs = np.array([0, 50, 40, 120, -5, 200, 400])  # chunk 1 falls, 3 falls, 4 starts below 0, 5 ends past T
+    rows = [prefill_chunk_rows(qs, s, T) for s in range(S)]
+    assert rows == [50, 0, 80, 0, 0, 0]
+    ctx = np.array([60, 10, 80, 90, 200, 500])
+    n_qt = 2
+    for order in ("tile", "unit", "packed"):
+        grid = prefill_grid(S, Hk, G, n_qt, T, order)
+        got = {w for w in prefill_items(qs, ctx, S, Hk, G, n_qt, T, grid, order) if w[2] * PF_ROWS < rows[w[0]]}
+        assert got == {(s, h, 0) for s in (0, 2) for h in range(Hk * G)}
+        for s, _, qt in got:
+            assert 0 <= int(qs[s]) and int(qs[s]) + rows[s] <= T
 
 
 PF_CASES = [
