@@ -309,34 +309,38 @@ def main():
 
 def hbm_read_probe(pa, torch, dev, gib=4, reps=10):
     """Achievable streaming-read rate (``pa_hbm_read_probe``): one 4 GiB
-    buffer read once per launch, 16-byte loads, non-temporal and cached, over
-    a few grid sizes; the best is the measured read ceiling decode is quoted
+    buffer read once per launch with 16-byte loads, over a few shapes
+    (non-temporal or cached loads, grid size, grid-stride or contiguous runs
+    per workgroup); the best is the measured read ceiling decode is quoted
     against beside the vendor peak."""
     buf = torch.empty(gib << 30, dtype=torch.uint8, device=dev)
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     sink = torch.zeros(cus * 8, dtype=torch.int32, device=dev)
     runs = []
-    for nt in (True, False):
-        for per_cu in (2, 4, 8):
-            wgs = cus * per_cu
-            for _ in range(3):
-                pa.hbm_read_probe(buf, sink, wgs, nontemporal=nt)
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            a.record()
-            for _ in range(reps):
-                pa.hbm_read_probe(buf, sink, wgs, nontemporal=nt)
-            b.record()
-            torch.cuda.synchronize()
-            us = a.elapsed_time(b) / reps * 1e3
-            runs.append({"nontemporal": nt, "workgroups": wgs, "us": round(us, 1),
-                         "GB/s": round(buf.numel() / us / 1e3, 1)})
+    # (non-temporal, workgroups per CU, contiguous run bytes; 0 = grid-stride)
+    shapes = [(True, 8, 0), (False, 8, 0), (True, 2, 65536), (True, 4, 65536), (True, 8, 65536),
+              (True, 4, 8192), (True, 8, 8192), (True, 4, 262144), (False, 4, 65536)]
+    for nt, per_cu, run in shapes:
+        wgs = cus * per_cu
+        for _ in range(3):
+            pa.hbm_read_probe(buf, sink, wgs, nontemporal=nt, run_bytes=run)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            pa.hbm_read_probe(buf, sink, wgs, nontemporal=nt, run_bytes=run)
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) / reps * 1e3
+        runs.append({"nontemporal": nt, "workgroups": wgs, "run_bytes": run, "us": round(us, 1),
+                     "GB/s": round(buf.numel() / us / 1e3, 1)})
     del buf
     best = max(runs, key=lambda r: r["GB/s"])
     log(f"HBM read probe: best {best}")
     return {"bytes": gib << 30, "best_GB/s": best["GB/s"], "best": best, "runs": runs,
             "note": "pa_hbm_read_probe: every byte of a 4 GiB buffer read once per launch (512-thread "
-                    "workgroups, 16-byte loads, four in flight per lane); HIP events around 10 launches"}
+                    "workgroups, 16-byte loads, four in flight per lane; grid-stride or contiguous runs per "
+                    "workgroup); HIP events around 10 launches; the best shape is the ceiling"}
 
 
 def bench_decode(args, config, case, pa, torch, dev, full=True):

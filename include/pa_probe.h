@@ -29,16 +29,22 @@ extern "C" {
  *                  writes its slot only when its running XOR of the data equals
  *                  `magic` (so the loads cannot be optimised away while the
  *                  writes stay negligible); contents otherwise untouched
- *   num_workgroups 1 .. 65535 workgroups of 512 threads, each striding over
- *                  the buffer in 16-byte lanes, four loads in flight per lane
+ *   num_workgroups 1 .. 65535 workgroups of 512 threads, four 16-byte loads
+ *                  in flight per lane
+ *   run_bytes      0: the workgroups stride over the whole buffer together
+ *                  (consecutive lanes on consecutive 16-byte chunks); else a
+ *                  multiple of 8192: the buffer is cut into runs of this many
+ *                  bytes and workgroup w reads runs w, w + num_workgroups, ...
+ *                  each from start to end, as a decode workgroup reads whole
+ *                  K/V blocks
  *   flags          0 or PA_PROBE_NONTEMPORAL (other bits: PA_ERR_INVALID)
  *
  * Enqueued on `stream` (a hipStream_t); nothing allocated or synchronised.
- * Returns PA_OK, PA_ERR_NULL, PA_ERR_INVALID (sizes, alignment, flags) or
+ * Returns PA_OK, PA_ERR_NULL, PA_ERR_INVALID (sizes, alignment, run length, flags) or
  * PA_ERR_HIP.
  */
-int pa_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, int32_t num_workgroups, uint32_t magic,
-                      uint32_t flags, void* stream);
+int pa_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, int32_t num_workgroups, size_t run_bytes,
+                      uint32_t magic, uint32_t flags, void* stream);
 
 #ifdef __cplusplus
 }

@@ -71,7 +71,7 @@ lib.pa_prefill.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _
                            _i64, ctypes.c_float, _i32, _p]
 
 lib.pa_hbm_read_probe.restype = ctypes.c_int
-lib.pa_hbm_read_probe.argtypes = [_p, ctypes.c_size_t, _p, _i32, ctypes.c_uint32, ctypes.c_uint32, _p]
+lib.pa_hbm_read_probe.argtypes = [_p, ctypes.c_size_t, _p, _i32, ctypes.c_size_t, ctypes.c_uint32, ctypes.c_uint32, _p]
 
 _DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 SHARED_BLOCKS = 1  # PA_DECODE_SHARED_BLOCKS
@@ -331,16 +331,18 @@ def swap_blocks(dst_k: torch.Tensor, dst_v: torch.Tensor, src_k: torch.Tensor, s
 
 
 def hbm_read_probe(buf: torch.Tensor, sink: torch.Tensor, num_workgroups: int, nontemporal: bool = True,
-                   magic: int = 0x5A17C0DE, stream=None) -> None:
+                   run_bytes: int = 0, magic: int = 0x5A17C0DE, stream=None) -> None:
     """Read every byte of ``buf`` once (``pa_hbm_read_probe``, a measurement
-    aid): the achievable streaming-read rate.  ``sink`` is a uint32-sized
-    device tensor of ``num_workgroups`` elements, written only where a
-    workgroup's data XOR to ``magic``."""
+    aid): the achievable streaming-read rate.  ``run_bytes`` 0 strides the
+    workgroups over the whole buffer; a multiple of 8192 gives each workgroup
+    whole contiguous runs of that size.  ``sink`` is a uint32-sized device
+    tensor of ``num_workgroups`` elements, written only where a workgroup's
+    data XOR to ``magic``."""
     _dev(buf, "buf")
     _dev(sink, "sink")
     if sink.numel() * sink.element_size() < 4 * num_workgroups:
         raise ValueError("sink must hold num_workgroups uint32 values")
     st = lib.pa_hbm_read_probe(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(),
-                               int(num_workgroups), int(magic) & 0xFFFFFFFF, 1 if nontemporal else 0,
+                               int(num_workgroups), int(run_bytes), int(magic) & 0xFFFFFFFF, 1 if nontemporal else 0,
                                _stream_handle(buf.device, stream))
     _check(st, "pa_hbm_read_probe")

@@ -276,11 +276,13 @@ def test_swap_binding_rejects_pageable_host_tensors():
 def test_hbm_read_probe_host_checks():
     lib = pa.lib
     f = lib.pa_hbm_read_probe
-    assert f(None, 64, P, 4, 0, 0, None) == NULL
-    assert f(P, 64, None, 4, 0, 0, None) == NULL
-    assert f(P, 0, P, 4, 0, 0, None) == INVALID  # nothing to read
-    assert f(P, 24, P, 4, 0, 0, None) == INVALID  # not a multiple of 16
-    assert f(P + 8, 64, P, 4, 0, 0, None) == INVALID  # misaligned
-    assert f(P, 64, P, 0, 0, 0, None) == INVALID
-    assert f(P, 64, P, 65536, 0, 0, None) == INVALID
-    assert f(P, 64, P, 4, 0, 2, None) == INVALID  # unknown flag
+    assert f(None, 64, P, 4, 0, 0, 0, None) == NULL
+    assert f(P, 64, None, 4, 0, 0, 0, None) == NULL
+    assert f(P, 0, P, 4, 0, 0, 0, None) == INVALID  # nothing to read
+    assert f(P, 24, P, 4, 0, 0, 0, None) == INVALID  # not a multiple of 16
+    assert f(P + 8, 64, P, 4, 0, 0, 0, None) == INVALID  # misaligned
+    assert f(P, 64, P, 0, 0, 0, 0, None) == INVALID
+    assert f(P, 64, P, 65536, 0, 0, 0, None) == INVALID
+    assert f(P, 64, P, 4, 4096, 0, 0, None) == INVALID  # runs not a multiple of 8192 bytes
+    assert f(P, 64, P, 4, 0, 0, 2, None) == INVALID  # unknown flag
+
