@@ -61,7 +61,8 @@ typedef enum {
     PA_ERR_UNSUPPORTED = 2, /* dtype, head_dim or block_size outside the built kernels */
     PA_ERR_INVALID = 3,     /* sizes, alignment, scale or workspace out of range */
     PA_ERR_HIP = 4,         /* the HIP runtime rejected a launch */
-    PA_ERR_OUT_OF_BLOCKS = 5 /* block manager: not enough free blocks (nothing changed) */
+    PA_ERR_OUT_OF_BLOCKS = 5, /* block manager: not enough free blocks (nothing changed) */
+    PA_ERR_SCRATCH = 6        /* pa_decode_static: more scratch needed than PA_STATIC_SCRATCH_BYTES */
 } pa_status;
 
 /* pa_decode / pa_append_decode flags. */
@@ -203,6 +204,31 @@ int pa_append_decode(void* out, const void* query, const void* key, const void* 
                      int32_t max_context_len, int64_t num_blocks, float scale, int32_t dtype,
                      int32_t partition_size, uint32_t flags, void* workspace, size_t workspace_bytes,
                      void* stream);
+
+/*
+ * pa_decode_static - pa_decode without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, serving loops
+ * that must not call the allocator, harnesses that forbid it).
+ *
+ * Same arguments (minus workspace and workspace_bytes), results, guards and
+ * errors as pa_decode; it runs the same kernels.  When the call's plan splits
+ * contexts, the partial results go to a scratch buffer the library holds in
+ * device memory: a file-scope array of PA_STATIC_SCRATCH_BYTES, one copy per
+ * GPU the library runs on, kept until the process ends.  Nothing is
+ * allocated or freed by the call.  A call whose plan needs more than
+ * PA_STATIC_SCRATCH_BYTES (pa_decode_workspace_size of the same arguments)
+ * returns PA_ERR_SCRATCH before anything is enqueued.  The scratch needs no
+ * initialisation (every partial is written before it is read).
+ * Every call on one GPU shares that GPU's scratch: calls that overlap in time
+ * on one GPU (different streams, or host threads racing) race on it and give
+ * undefined results; calls on one stream are ordered and safe.
+ */
+#define PA_STATIC_SCRATCH_BYTES (32u << 20) /* 32 MiB per GPU */
+int pa_decode_static(void* out, const void* query, const void* k_cache, const void* v_cache,
+                     const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                     int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                     int32_t max_blocks_per_seq, int32_t max_context_len, int64_t num_blocks, float scale,
+                     int32_t dtype, int32_t partition_size, uint32_t flags, void* stream);
 
 /*
  * pa_reshape_and_cache - store new tokens' keys and values in their slots.

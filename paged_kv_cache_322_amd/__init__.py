@@ -31,6 +31,8 @@ __all__ = [
     "prefill",
     "swap_blocks",
     "hbm_read_probe",
+    "decode_static",
+    "STATIC_SCRATCH_BYTES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
@@ -70,6 +72,10 @@ lib.pa_prefill.restype = ctypes.c_int
 lib.pa_prefill.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                            _i64, ctypes.c_float, _i32, _p]
 
+lib.pa_decode_static.restype = ctypes.c_int
+lib.pa_decode_static.argtypes = [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i64,
+                                 ctypes.c_float, _i32, _i32, _u32, _p]
+STATIC_SCRATCH_BYTES = 32 << 20  # PA_STATIC_SCRATCH_BYTES
 lib.pa_hbm_read_probe.restype = ctypes.c_int
 lib.pa_hbm_read_probe.argtypes = [_p, ctypes.c_size_t, _p, _i32, ctypes.c_size_t, ctypes.c_uint32, ctypes.c_uint32, _p]
 
@@ -134,7 +140,7 @@ def decode_workspace_size(num_seqs: int, num_heads: int, head_dim: int, max_cont
 
 
 def _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, max_context_len,
-                 partition_size, workspace, stream):
+                 partition_size, workspace, stream, allocate=True):
     _dev(query, "query", ndim=3)
     dt = query.dtype
     _dev(out, "out", dt, 3)
@@ -151,7 +157,7 @@ def _decode_args(out, query, key_cache, value_cache, block_tables, context_lens,
                          "(query heads must be a multiple of K/V heads)")
     if block_tables.shape[0] != S or context_lens.shape[0] != S:
         raise ValueError("block_tables / context_lens must have one row per sequence")
-    need = decode_workspace_size(S, H, D, max_context_len, partition_size, Hk)
+    need = decode_workspace_size(S, H, D, max_context_len, partition_size, Hk) if allocate else 0
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
     ws_ptr, ws_bytes = 0, 0
@@ -183,6 +189,21 @@ def decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor, valu
                        float(scale), _code(dt), int(partition_size), SHARED_BLOCKS if shared_blocks else 0,
                        ws_ptr, ws_bytes, _stream_handle(query.device, stream))
     _check(st, "pa_decode")
+    return out
+
+
+def decode_static(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                  block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float, max_context_len: int,
+                  partition_size: int = 0, stream=None, shared_blocks: bool = False) -> torch.Tensor:
+    """``decode`` through ``pa_decode_static``: no workspace, none allocated;
+    split-K partials go to the library's static per-GPU scratch
+    (``STATIC_SCRATCH_BYTES``).  Calls overlapping on one GPU race on it."""
+    dt, tail, _, _ = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, max_context_len,
+                                  partition_size, None, stream, allocate=False)
+    st = lib.pa_decode_static(out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+                              *tail, float(scale), _code(dt), int(partition_size),
+                              SHARED_BLOCKS if shared_blocks else 0, _stream_handle(query.device, stream))
+    _check(st, "pa_decode_static")
     return out
 
 

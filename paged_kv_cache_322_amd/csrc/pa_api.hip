@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "../../include/pa.h"
 #include "pa_internal.h"
@@ -101,6 +102,8 @@ const char* pa_status_string(int status) {
         case PA_ERR_INVALID: return "PA_ERR_INVALID: size, alignment, scale or workspace out of range";
         case PA_ERR_HIP: return "PA_ERR_HIP: the HIP runtime rejected a launch";
         case PA_ERR_OUT_OF_BLOCKS: return "PA_ERR_OUT_OF_BLOCKS: not enough free KV blocks";
+        case PA_ERR_SCRATCH:
+            return "PA_ERR_SCRATCH: the call needs more scratch than the library's static buffer holds";
         default: return "PA_ERR_UNKNOWN";
     }
 }
@@ -126,6 +129,46 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num
 
 }  // extern "C"
 
+// ---------------------------------------------------------------------------
+// pa_decode_static: pa_decode whose split-K scratch is a file-scope device
+// array instead of a caller workspace, for callers that cannot allocate.
+// ---------------------------------------------------------------------------
+
+namespace {
+
+// The scratch: each GPU the library runs on holds its own copy, for the life
+// of the process.  Its name is a host-side stand-in in host code: kernels get
+// the per-device address hipGetSymbolAddress returns, never the name.
+static __device__ __align__(256) unsigned char scratch[PA_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// Device address of the current device's scratch, looked up once per device
+// (with that device current); NULL if the lookup fails.
+void* device_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+
+}  // namespace
+
 namespace {
 
 // Shared by pa_decode and pa_append_decode.  key/value are NULL for a plain
@@ -136,7 +179,7 @@ int decode_common(void* out, const void* query, const void* key, const void* val
                   int32_t max_blocks_per_seq,
                   int32_t max_context_len, int64_t num_blocks, float scale, int32_t dtype,
                   int32_t partition_size, uint32_t flags, void* workspace, size_t workspace_bytes, void* stream,
-                  bool append) {
+                  bool append, bool static_scratch = false) {
     if (!supported_dtype(dtype) || !supported_head_dim(head_dim) || !supported_block_size(block_size))
         return PA_ERR_UNSUPPORTED;
     if (num_seqs == 0) return PA_OK;  // nothing to read or write
@@ -165,6 +208,13 @@ int decode_common(void* out, const void* query, const void* key, const void* val
     const int64_t parts = parts_for(max_context_len, part, plan.balanced);
     if (parts > 65535) return PA_ERR_INVALID;  // grid dimension limit
     const size_t need = workspace_bytes_for(num_seqs, num_heads, head_dim, parts, plan.balanced);
+    if (need && static_scratch) {
+        // pa_decode_static: the library's per-GPU scratch stands in for the workspace.
+        if (need > static_cast<size_t>(PA_STATIC_SCRATCH_BYTES)) return PA_ERR_SCRATCH;
+        workspace = device_scratch();
+        if (!workspace) return PA_ERR_HIP;
+        workspace_bytes = PA_STATIC_SCRATCH_BYTES;
+    }
     if (need) {
         if (!workspace) return PA_ERR_NULL;
         if (workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 3u)) return PA_ERR_INVALID;
@@ -352,4 +402,17 @@ extern "C" int pa_prefill(void* out, const void* query, const void* k_cache, con
     a.staged_ids = static_cast<int>(ids < 1 ? 1 : ids);
     a.stream = static_cast<hipStream_t>(stream);
     return hip_status(pa::launch_prefill(a));
+}
+
+
+extern "C" int pa_decode_static(void* out, const void* query, const void* k_cache, const void* v_cache,
+                                const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                                int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                int32_t max_blocks_per_seq, int32_t max_context_len, int64_t num_blocks,
+                                float scale, int32_t dtype, int32_t partition_size, uint32_t flags,
+                                void* stream) {
+    return decode_common(out, query, nullptr, nullptr, const_cast<void*>(k_cache), const_cast<void*>(v_cache),
+                         block_tables, context_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                         max_blocks_per_seq, max_context_len, num_blocks, scale, dtype, partition_size, flags,
+                         nullptr, 0, stream, false, true);
 }

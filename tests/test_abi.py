@@ -286,3 +286,16 @@ def test_hbm_read_probe_host_checks():
     assert f(P, 64, P, 4, 4096, 0, 0, None) == INVALID  # runs not a multiple of 8192 bytes
     assert f(P, 64, P, 4, 0, 0, 2, None) == INVALID  # unknown flag
 
+
+def test_decode_static_rejects_what_the_scratch_cannot_hold():
+    """pa_decode_static refuses, before touching any device, a plan whose
+    split-K partials exceed its static scratch (PA_ERR_SCRATCH = 6)."""
+    f = pa.lib.pa_decode_static
+    S, H, D, B, maxc = 128, 96, 128, 16, 2048
+    assert pa.decode_workspace_size(S, H, D, maxc, 16) > pa.STATIC_SCRATCH_BYTES
+    assert f(P, P, P, P, P, P, S, H, H, D, B, 128, maxc, 16384, 0.1, 1, 16, 0, None) == 6
+    assert pa.status_string(6).startswith("PA_ERR_SCRATCH")
+    # Plans within the scratch go on to pa_decode's own checks.
+    assert pa.decode_workspace_size(S, H, D, maxc, 512) <= pa.STATIC_SCRATCH_BYTES
+    assert f(None, P, P, P, P, P, S, H, H, D, B, 128, maxc, 16384, 0.1, 1, 512, 0, None) == NULL
+    assert f(P, P, P, P, P, P, S, H, H, D, B, 64, maxc, 16384, 0.1, 1, 512, 0, None) == INVALID  # table too narrow
