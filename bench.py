@@ -77,8 +77,11 @@ def parse():
     ap.add_argument("--partition", type=int, default=0, help="KV partition tokens (0 = library default)")
     ap.add_argument("--block-size", type=int, default=16, help="block size of the parallel-sampling workload (8, 16 or 32)")
     ap.add_argument("--shared-blocks", choices=["auto", "on", "off"], default="auto",
-                    help="PA_DECODE_SHARED_BLOCKS (cached K/V loads); auto = on for the parallel-sampling workload, whose samples share "
-                         "prompt blocks")
+                    help="PA_DECODE_SHARED_BLOCKS (cached K/V loads); auto = on for the parallel-sampling workload "
+                         "decoded without sibling groups (its samples then re-read the shared prompt blocks)")
+    ap.add_argument("--siblings", default="auto",
+                    help="PA_DECODE_SIBLINGS group size (0 = off); auto = the samples per prompt (4) for the "
+                         "parallel-sampling workload, off otherwise")
     ap.add_argument("--rotate", type=int, default=2, help="independent pool copies cycled across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-second-config", action="store_true",
@@ -155,7 +158,7 @@ COUNTER_FILES = {"llama7b": "decode_llama7b_counters.txt", "opt13b": "decode_opt
                  "gqa8b": "decode_gqa_llama3_8b_counters.txt", "gqa70b": "decode_gqa_llama2_70b_tp8_counters.txt",
                  "prefill-llama7b": "prefill_llama7b_counters.txt", "prefill-gqa8b": "prefill_gqa_llama3_8b_counters.txt",
                  "prefill-prompts": "prefill_prompts_bf16_counters.txt"}
-DECODE_SOURCES = ("pa_decode_impl.h", "pa_decode_mfma.h", "pa_device.h", "pa_internal.h")
+DECODE_SOURCES = ("pa_decode_impl.h", "pa_decode_mfma.h", "pa_decode_siblings.h", "pa_device.h", "pa_internal.h")
 PREFILL_SOURCES = ("pa_prefill.hip", "pa_decode_mfma.h", "pa_device.h", "pa_internal.h")
 
 
@@ -180,12 +183,16 @@ def traffic_from_profiles(config, kernel_src_sha):
         return None
 
 
-def decode_kernel_name(case):
-    """The decode kernel the library runs for this shape: the matrix-core
-    kernel for 16-bit caches with D in {64, 128, 256} and grouped heads, else
-    the vector-ALU kernel."""
+def decode_kernel_name(case, siblings=0):
+    """The decode kernel the library runs for this shape: the sibling-group
+    kernel when siblings are named and it is built for the shape, the
+    matrix-core kernel for 16-bit caches with D in {64, 128, 256} and grouped
+    heads, else the vector-ALU kernel."""
     G = case.num_heads // case.num_kv_heads
-    if case.elem_bytes == 2 and case.head_dim in (64, 128, 256) and G >= 2:
+    mfma_shape = case.elem_bytes == 2 and case.head_dim in (64, 128, 256)
+    if mfma_shape and G == 1 and siblings >= 2:
+        return "decode_siblings_kernel"
+    if mfma_shape and G >= 2:
         return "decode_mfma_kernel"
     return "decode_partition_kernel"
 
@@ -381,7 +388,12 @@ def bench_decode(args, config, case, pa, torch, dev, full=True):
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
-    shared = args.shared_blocks == "on" or (args.shared_blocks == "auto" and config == "sampling")
+    siblings = (4 if config == "sampling" else 0) if args.siblings == "auto" else int(args.siblings)
+    # Cached K/V loads pay off when several workgroups read the same blocks:
+    # the parallel-sampling workload decoded without sibling groups.  With
+    # them, each shared block is read once per (group, head) and the
+    # non-temporal loads are faster (measured: 229 -> 206 us at B = 16).
+    shared = args.shared_blocks == "on" or (args.shared_blocks == "auto" and config == "sampling" and siblings < 2)
     fused = bool(timed_steps)
     if fused:
         assert len(timed_steps) == 1 and timed_steps[0].slot_mapping.size == S  # one newest row per sequence
@@ -405,7 +417,7 @@ def bench_decode(args, config, case, pa, torch, dev, full=True):
         if ev is not None:
             ev[1].record()
         pa.decode(out, q, kc, vc, bt, ctx, case.scale, max_ctx, partition_size=args.partition, workspace=ws,
-                  shared_blocks=shared)
+                  shared_blocks=shared, siblings=siblings)
         if ev is not None:
             ev[2].record()
 
@@ -447,7 +459,7 @@ def bench_decode(args, config, case, pa, torch, dev, full=True):
         def one(i):
             kc, vc = pools[i % len(pools)] if rotate else pools[0]
             pa.decode(out, q, kc, vc, bt, ctx, case.scale, max_ctx, partition_size=args.partition, workspace=ws,
-                      shared_blocks=shared)
+                      shared_blocks=shared, siblings=siblings)
         for i in range(3):
             one(i)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -551,12 +563,13 @@ def bench_decode(args, config, case, pa, torch, dev, full=True):
             "partition_tokens": pa.partition_tokens(S, H, max_ctx, args.partition, num_kv_heads=case.num_kv_heads),
             "pool_copies_rotated": len(pools),
             "shared_blocks_flag": shared,
+            "siblings_flag": siblings,
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "decode_tokens_per_s": round(S / (ms_step * 1e-3), 1),
         "step_bytes": int(step_bytes),
         "roofline": {
-            "kernel": f"pa_decode ({decode_kernel_name(case)}, plus decode_merge_kernel when a context is "
+            "kernel": f"pa_decode ({decode_kernel_name(case, siblings)}, plus decode_merge_kernel when a context is "
                       "split): HIP events around a loop of launches on the rotated pool copies",
             "bound": "hbm",
             "achieved": round(achieved, 1),

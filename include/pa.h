@@ -71,6 +71,26 @@ typedef enum {
                                       caches so sibling sequences hit in L2.  Without it, K/V
                                       are streamed with non-temporal loads, the faster choice
                                       when every block is read once.  Results are identical. */
+#define PA_DECODE_SIBLINGS(n) ((uint32_t)(n) << 8)
+                                   /* pa_decode: consecutive groups of n (2 .. 16) sequences are
+                                      siblings (samples forked from one prompt, beam candidates):
+                                      sequences n*k .. n*k+n-1 form group k (the last group may be
+                                      smaller).  The library compares the members' block tables and
+                                      reads the leading blocks they all hold (the same physical ids)
+                                      once per group and head, for all members together; each
+                                      member's other tokens are read from its own blocks.  A hint:
+                                      nothing is assumed that the tables do not show.  Taken for
+                                      16-bit caches, head_dim 64, 128 or 256, num_kv_heads ==
+                                      num_heads and n * ceil(max_context_len / B) <= 4096, with one
+                                      workgroup per (group, head) over whole contexts
+                                      (partition_size is then not used); otherwise ignored.  The
+                                      arithmetic (fp32 products and softmax, probabilities as hi and
+                                      lo 16-bit parts) differs from the multi-head kernel's only by
+                                      fp32 rounding.  Each block shared within a group is then
+                                      read once per (group, head): PA_DECODE_SHARED_BLOCKS is not
+                                      needed for it (the streaming loads are faster).  n = 0 or 1:
+                                      no grouping; n > 16: PA_ERR_INVALID.  Ignored by
+                                      pa_append_decode. */
 
 /* Supported shapes: head_dim in {8, 16, 32, 64, 128, 256}; block_size a power
  * of two in [1, 256]; num_seqs and num_heads at most 65535. */
@@ -160,7 +180,8 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num
  *   scale          finite softmax scale (1/sqrt(D) for standard attention)
  *   partition_size tokens per KV partition, 0 = default (see
  *                  pa_decode_partition_tokens); ceil(P / B) + 1 <= 8192
- *   flags          0 or PA_DECODE_SHARED_BLOCKS (other bits: PA_ERR_INVALID)
+ *   flags          PA_DECODE_SHARED_BLOCKS and/or PA_DECODE_SIBLINGS(n) (other bits:
+ *                  PA_ERR_INVALID)
  *   workspace      device scratch of at least pa_decode_workspace_size(...)
  *                  bytes, 4-byte aligned; contents need no initialisation
  *

@@ -172,7 +172,7 @@ def _decode_args(out, query, key_cache, value_cache, block_tables, context_lens,
 def decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
            block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float, max_context_len: int,
            partition_size: int = 0, workspace: Optional[torch.Tensor] = None, stream=None,
-           shared_blocks: bool = False) -> torch.Tensor:
+           shared_blocks: bool = False, siblings: int = 0) -> torch.Tensor:
     """Paged single-query attention (``pa_decode``); writes and returns ``out``.
 
     out, query [S, H, D]; key_cache, value_cache [N, Hk, B, D] (Hk divides H:
@@ -182,12 +182,16 @@ def decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor, valu
     allocated from torch's caching allocator when not given.
     ``shared_blocks``: some blocks are read by several sequences (forked
     samples, shared prefixes): load K/V through the caches.
+    ``siblings`` (2 .. 16): consecutive groups of that many sequences are
+    forked siblings; their common leading blocks are read once per group
+    (``PA_DECODE_SIBLINGS``).
     """
     dt, tail, ws_ptr, ws_bytes = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens,
                                               max_context_len, partition_size, workspace, stream)
+    flags = (SHARED_BLOCKS if shared_blocks else 0) | (int(siblings) << 8)
     st = lib.pa_decode(out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(), *tail,
-                       float(scale), _code(dt), int(partition_size), SHARED_BLOCKS if shared_blocks else 0,
-                       ws_ptr, ws_bytes, _stream_handle(query.device, stream))
+                       float(scale), _code(dt), int(partition_size), flags, ws_ptr, ws_bytes,
+                       _stream_handle(query.device, stream))
     _check(st, "pa_decode")
     return out
 

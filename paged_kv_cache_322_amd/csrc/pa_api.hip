@@ -193,7 +193,9 @@ int decode_common(void* out, const void* query, const void* key, const void* val
     if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
         return PA_ERR_INVALID;
     if (!isfinite(scale)) return PA_ERR_INVALID;
-    if (flags & ~static_cast<uint32_t>(PA_DECODE_SHARED_BLOCKS)) return PA_ERR_INVALID;
+    if (flags & ~static_cast<uint32_t>(PA_DECODE_SHARED_BLOCKS | PA_DECODE_SIBLINGS(0xFF))) return PA_ERR_INVALID;
+    const int siblings = static_cast<int>((flags >> 8) & 0xFFu);
+    if (siblings > pa::kMaxSiblings) return PA_ERR_INVALID;
     // One block of one cache must be addressable with 32-bit element offsets.
     if (static_cast<int64_t>(num_kv_heads) * block_size * head_dim > 0x7FFFFFFF) return PA_ERR_INVALID;
     if (!aligned16(out) || !aligned16(query) || !aligned16(k_cache) || !aligned16(v_cache))
@@ -262,6 +264,19 @@ int decode_common(void* out, const void* query, const void* key, const void* val
         a.staged_balanced = static_cast<int>(pa::partition_blocks(share, block_size));
     }
     a.cached_loads = (flags & PA_DECODE_SHARED_BLOCKS) != 0;
+    // Sibling groups: a hint the sibling-group kernel takes where it is built
+    // (16-bit caches, head_dim 64..256, one query head per K/V head, plain
+    // decode) and the members' block ids fit its LDS; otherwise ignored.
+    a.siblings = 0;
+    a.sibling_ids = 0;
+    if (siblings >= 2 && !append && (dtype == PA_F16 || dtype == PA_BF16) && head_dim >= 64 &&
+        num_heads == num_kv_heads) {
+        const int64_t ids = std::max<int64_t>(1, (static_cast<int64_t>(max_context_len) + block_size - 1) / block_size);
+        if (siblings * ids <= pa::kMaxSiblingIds) {
+            a.siblings = siblings;
+            a.sibling_ids = static_cast<int>(ids);
+        }
+    }
     a.workspace = need ? workspace : nullptr;
     a.stream = static_cast<hipStream_t>(stream);
     return hip_status(pa::launch_decode(a));

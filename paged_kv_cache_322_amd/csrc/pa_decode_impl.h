@@ -48,6 +48,7 @@
 #include <math.h>
 
 #include "pa_decode_mfma.h"
+#include "pa_decode_siblings.h"
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -452,6 +453,11 @@ constexpr bool kUseMfma = sizeof(typename T::bits) == 2 && (D == 64 || D == 128 
 template <int D>
 constexpr int kMfmaMaxStaged = D == 256 ? 4096 : 6144;
 
+// Sibling-group decode: 16-bit caches, head_dim 64..256, one query head per
+// K/V head (the group's members take the matrix columns).
+template <class T, int D, int G>
+constexpr bool kUseSiblings = sizeof(typename T::bits) == 2 && (D == 64 || D == 128 || D == 256) && G == 1;
+
 template <class T, int D, int G, bool APPEND, bool NT>
 hipError_t launch_decode_t(const DecodeArgs& a) {
     const int log2_bs = __builtin_ctz(static_cast<unsigned>(a.block_size));
@@ -465,6 +471,19 @@ hipError_t launch_decode_t(const DecodeArgs& a) {
     int32_t* meta = ws_o ? reinterpret_cast<int32_t*>(ws_l + n_sh) : nullptr;
     dim3 grid(a.num_kv_heads, a.num_seqs, a.max_parts);
     const size_t lds = static_cast<size_t>(a.staged_blocks) * sizeof(int);
+    if constexpr (kUseSiblings<T, D, G> && !APPEND) {
+        if (a.siblings >= 2) {
+            // One workgroup per (head, group of siblings), whole contexts.
+            const unsigned groups = static_cast<unsigned>((a.num_seqs + a.siblings - 1) / a.siblings);
+            hipLaunchKernelGGL((decode_siblings_kernel<T, D, NT>), dim3(a.num_heads, groups), dim3(kMfmaThreads),
+                               static_cast<size_t>(a.siblings) * a.sibling_ids * sizeof(int), a.stream, out,
+                               static_cast<const bits*>(a.query), static_cast<const bits*>(a.k_cache),
+                               static_cast<const bits*>(a.v_cache), a.block_tables, a.context_lens, a.num_seqs,
+                               a.num_heads, a.siblings, a.sibling_ids, log2_bs, a.max_blocks_per_seq,
+                               a.max_context_len, a.num_blocks, qscale);
+            return hipGetLastError();
+        }
+    }
     if constexpr (kUseMfma<T, D, G>) {
         if (a.balanced && a.staged_balanced <= kMfmaMaxStaged<D>) {
             const unsigned grid_b = static_cast<unsigned>(a.balanced_wgs + a.num_seqs * a.num_kv_heads);

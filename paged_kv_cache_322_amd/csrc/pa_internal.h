@@ -133,6 +133,11 @@ struct DecodeArgs {
     int balanced_wgs;   // workgroups of the balanced split
     int staged_balanced;  // LDS entries for a balanced-split run's block ids
     bool cached_loads;  // ordinary (cached) K/V loads instead of non-temporal ones
+    // Sibling groups (pa_decode with PA_DECODE_SIBLINGS(n)): consecutive
+    // groups of `siblings` sequences read their common leading blocks once;
+    // 0 = no grouping.  sibling_ids: block ids staged per member.
+    int siblings;
+    int sibling_ids;
     // float [S*H*max_parts*D] then [S*H*max_parts] x 2, then (balanced plan)
     // int32 [S + 2]; NULL when max_parts == 1
     void* workspace;
@@ -143,6 +148,11 @@ hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_decode_f32(const DecodeArgs& a);
 hipError_t launch_decode_f16(const DecodeArgs& a);
 hipError_t launch_decode_bf16(const DecodeArgs& a);
+
+// Sibling-group decode: at most this many members per group (the columns of
+// one 16x16 matrix product) and staged block ids per workgroup.
+constexpr int kMaxSiblings = 16;
+constexpr int kMaxSiblingIds = 4096;
 
 // Query heads per K/V head with built kernels.
 inline bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }

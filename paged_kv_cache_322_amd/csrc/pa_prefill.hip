@@ -202,14 +202,13 @@ __global__ __launch_bounds__(kPfThreads, kPfWavesPerSimd) void prefill_kernel(
     //     tiles last first and, within a tile, its G query heads; unit u is
     //     (sequence of rank u / Hk in decreasing context length, K/V head
     //     u % Hk).  Same grid;
-    //   packed: through tile levels j = 0, 1, ... (level j is the j-th tile
-    //     from a chunk's end), within a level through the XCD's units that
-    //     have a tile there and, within a unit, its G heads; unit u is
-    //     (sequence of rank u / Hk in decreasing chunk length, K/V head
-    //     u % Hk), so level j holds the first c_j * Hk units, c_j the number
-    //     of chunks with more than j tiles.  Only tiles holding rows are
-    //     enumerated; the grid is an upper bound and the ids past the last
-    //     level return at once.
+    //   packed: as tile-major (query tiles last first), but through only
+    //     the units whose chunk reaches the tile: unit u is (sequence of
+    //     rank u / Hk in decreasing chunk length, K/V head u % Hk), so tile
+    //     qt is held by the first c_qt * Hk units, c_qt the number of chunks
+    //     longer than 128 qt rows.  Only tiles holding rows are enumerated;
+    //     the grid is an upper bound and the ids past the last tile return
+    //     at once.
     // Ranks break ties by sequence index (num_seqs <= kPfMaxRankedSeqs:
     // host check for both ranked orders).
     const int G = num_heads / num_kv_heads;
@@ -247,8 +246,10 @@ __global__ __launch_bounds__(kPfThreads, kPfWavesPerSimd) void prefill_kernel(
             if (tid < num_seqs) s_key[tid] = min(chunk_rows(query_start, tid, num_tokens), n_qtiles * kPfRows);
             __syncthreads();
             if (tid < n_qtiles) {
+                // Level tid: query tile n_qtiles - 1 - tid (tiles with the
+                // most keys first), held by the chunks longer than its start.
                 int cnt = 0;
-                for (int i = 0; i < num_seqs; ++i) cnt += s_key[i] > tid * kPfRows;
+                for (int i = 0; i < num_seqs; ++i) cnt += s_key[i] > (n_qtiles - 1 - tid) * kPfRows;
                 const int units_j = cnt * num_kv_heads;
                 s_lvl[tid] = units_j > xcd ? (units_j - xcd + kXcds - 1) / kXcds * G : 0;
             }
@@ -279,7 +280,7 @@ __global__ __launch_bounds__(kPfThreads, kPfWavesPerSimd) void prefill_kernel(
         }
         __syncthreads();
         s = __builtin_amdgcn_readfirstlane(s_pick);
-        if (order == kPfOrderPacked) qt = (__builtin_amdgcn_readfirstlane(s_key[s]) + kPfRows - 1) / kPfRows - 1 - level;
+        if (order == kPfOrderPacked) qt = n_qtiles - 1 - level;
     }
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int c = lane & 15, g = lane >> 4;

@@ -299,3 +299,10 @@ def test_decode_static_rejects_what_the_scratch_cannot_hold():
     assert pa.decode_workspace_size(S, H, D, maxc, 512) <= pa.STATIC_SCRATCH_BYTES
     assert f(None, P, P, P, P, P, S, H, H, D, B, 128, maxc, 16384, 0.1, 1, 512, 0, None) == NULL
     assert f(P, P, P, P, P, P, S, H, H, D, B, 64, maxc, 16384, 0.1, 1, 512, 0, None) == INVALID  # table too narrow
+
+
+def test_decode_sibling_flag_host_checks():
+    f = pa.lib.pa_decode
+    args = (P, P, P, P, P, P, 4, 2, 2, 128, 16, 8, 100, 64, 0.1, 1, 0)
+    assert f(*args, 17 << 8, P, 0, None) == INVALID  # more than 16 members
+    assert f(*args, 1 << 16, P, 0, None) == INVALID  # unknown bit

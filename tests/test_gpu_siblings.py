@@ -1,0 +1,130 @@
+"""Sibling-group decode (pa_decode with PA_DECODE_SIBLINGS(n)): the shared
+leading blocks of forked samples read once per group, against the oracle on
+every sequence, and against the ungrouped decode (same definition; the two
+differ by fp32 rounding only).  Unrelated sequences, empty, impossible and
+out-of-pool entries, and the cases where the hint is not taken."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from gpu_helpers import GpuCase, assert_close, log, oracle_decode, oracle_steps, pa
+
+pytestmark = pytest.mark.gpu
+
+
+def run_case(case, group, strict=True, shared_blocks=False):
+    g = GpuCase(case)
+    g.run_steps()
+    kc, vc = case.k_cache, case.v_cache
+    for kc, vc in oracle_steps(case):
+        pass
+    ref = oracle_decode(case, kc, vc)
+    out = torch.full_like(g.q, float("nan"))
+    pa().decode(out, g.q, g.kc, g.vc, g.bt, g.ctx, case.scale, case.max_context_len, shared_blocks=shared_blocks,
+                siblings=group)
+    plain = g.decode(out=torch.empty_like(g.q), shared_blocks=shared_blocks)
+    torch.cuda.synchronize()
+    assert_close(out, ref, case.dtype, f"{case.name} siblings={group}", strict=strict)
+    diff = (out.float() - plain.float()).abs().max().item()
+    log(f"{case.name}: max |grouped - ungrouped| = {diff:.3e}")
+    return g, out, ref
+
+
+@pytest.mark.parametrize("B", [8, 16, 32])
+def test_parallel_sampling_siblings(B):
+    # 64 prompts x 4 samples: prompt blocks shared, the partly filled last
+    # prompt block copied for samples 0-2 at the fork.
+    case = wl.parallel_sampling(block_size=B)
+    g, out, ref = run_case(case, 4)
+    # Cached instead of streaming loads: a cache policy only, identical bits.
+    cached = torch.empty_like(g.q)
+    pa().decode(cached, g.q, g.kc, g.vc, g.bt, g.ctx, case.scale, case.max_context_len, shared_blocks=True,
+                siblings=4)
+    torch.cuda.synchronize()
+    assert torch.equal(cached.view(torch.int16), out.view(torch.int16))
+
+
+SIB_CASES = [
+    # seed, group, dtype, D, B, prompts, samples, prompt_len, max_suffix
+    (1, 2, "f16", 64, 1, 3, 2, 37, 20),
+    (2, 3, "bf16", 128, 8, 4, 3, 100, 40),
+    (3, 16, "f16", 128, 16, 2, 16, 70, 30),
+    (4, 4, "bf16", 256, 32, 3, 4, 65, 64),
+    (5, 5, "f16", 128, 256, 3, 4, 300, 10),  # groups cut across prompts
+]
+
+
+@pytest.mark.parametrize("seed,group,dtype,D,B,prompts,samples,plen,msuf", SIB_CASES,
+                         ids=[f"n{c[1]}-{c[2]}-D{c[3]}-B{c[4]}" for c in SIB_CASES])
+def test_siblings_forked(seed, group, dtype, D, B, prompts, samples, plen, msuf):
+    case = wl.parallel_sampling(block_size=B, num_prompts=prompts, samples=samples, prompt_len=plen, num_heads=2,
+                                head_dim=D, pool_tokens=max(4096, 64 * B), dtype=dtype, max_suffix=msuf)
+    # Short contexts give |out| near 1-3: 2e-3 or one output ulp.
+    run_case(case, group, strict=False)
+
+
+def test_siblings_unrelated_sequences_and_guards():
+    """Sequences that share nothing (every token read privately), an empty
+    context (zeros), an impossible context (NaN for that member only) and an
+    out-of-pool id in one member's own blocks (NaN for that member only)."""
+    case = wl.random_case(77, 7, 2, 128, 16, "f16", ctx=[1, 300, 0, 17, 64, 65, 900], spare_blocks=4)
+    g, out, ref = run_case(case, 4, strict=False)
+    assert (out[2].float() == 0).all()
+    run_case(case, 3, strict=False)
+    # Impossible context for sequence 1 (group 0 of 4): NaN there only.
+    ctx = case.context_lens.copy()
+    ctx[1] = case.max_context_len + 5
+    out = torch.full_like(g.q, 0.0)
+    pa().decode(out, g.q, g.kc, g.vc, g.bt, torch.from_numpy(ctx).cuda(), case.scale, case.max_context_len,
+                siblings=4)
+    torch.cuda.synchronize()
+    assert torch.isnan(out[1].float()).all()
+    keep = [0, 2, 3, 4, 5, 6]
+    assert_close(out[keep], ref[keep], "f16", "siblings: other members", strict=False)
+    # Out-of-pool id in sequence 6's last block.
+    bt = case.block_tables.copy()
+    bt[6, (int(case.context_lens[6]) - 1) // case.block_size] = case.num_blocks + 3
+    out = torch.full_like(g.q, 0.0)
+    pa().decode(out, g.q, g.kc, g.vc, torch.from_numpy(bt).cuda(), g.ctx, case.scale, case.max_context_len,
+                siblings=4)
+    torch.cuda.synchronize()
+    assert torch.isnan(out[6].float()).all()
+    keep = [0, 1, 2, 3, 4, 5]
+    assert_close(out[keep], ref[keep], "f16", "siblings: bad id elsewhere", strict=False)
+
+
+def test_siblings_bad_id_in_the_shared_prefix():
+    """An out-of-pool id in the blocks a whole group shares gives NaN for
+    every member of that group and nothing else."""
+    case = wl.parallel_sampling(block_size=16, num_prompts=3, samples=4, prompt_len=100, num_heads=2, head_dim=128,
+                                pool_tokens=8192, max_suffix=30)
+    g, out, ref = run_case(case, 4, strict=False)
+    bt = case.block_tables.copy()
+    bt[4:8, 1] = case.num_blocks + 1  # group 1, a shared prompt block
+    out = torch.full_like(g.q, 0.0)
+    pa().decode(out, g.q, g.kc, g.vc, torch.from_numpy(bt).cuda(), g.ctx, case.scale, case.max_context_len,
+                siblings=4)
+    torch.cuda.synchronize()
+    assert torch.isnan(out[4:8].float()).all()
+    keep = [0, 1, 2, 3, 8, 9, 10, 11]
+    assert_close(out[keep], ref[keep], "f16", "siblings: other groups", strict=False)
+
+
+@pytest.mark.parametrize("what", ["f32", "gqa", "d32"])
+def test_siblings_hint_ignored_where_not_built(what):
+    """Where the sibling kernel is not built (fp32 caches, grouped-query
+    heads, head_dim below 64) the hint changes nothing: identical bits."""
+    if what == "f32":
+        case = wl.random_case(81, 6, 2, 64, 8, "f32", ctx=[5, 40, 41, 9, 100, 3], spare_blocks=2)
+    elif what == "gqa":
+        case = wl.random_case(82, 6, 4, 128, 16, "f16", ctx=[5, 40, 41, 9, 100, 3], spare_blocks=2, num_kv_heads=2)
+    else:
+        case = wl.random_case(83, 6, 2, 32, 16, "bf16", ctx=[5, 40, 41, 9, 100, 3], spare_blocks=2)
+    g = GpuCase(case)
+    a = g.decode(out=torch.empty_like(g.q)).clone()
+    b = torch.empty_like(g.q)
+    pa().decode(b, g.q, g.kc, g.vc, g.bt, g.ctx, case.scale, case.max_context_len, siblings=3)
+    torch.cuda.synchronize()
+    iv = torch.int32 if case.dtype == "f32" else torch.int16
+    assert torch.equal(a.view(iv), b.view(iv))

@@ -485,7 +485,7 @@ def prefill_items(qs, ctx, S, Hk, G, n_qt, T, grid, order):
     if order == "packed":
         key = [min(prefill_chunk_rows(qs, i, T), n_qt * PF_ROWS) for i in range(S)]
         rank_to_seq = sorted(range(S), key=lambda i: (-key[i], i))
-        cnt = [sum(k > j * PF_ROWS for k in key) for j in range(n_qt)]
+        cnt = [sum(k > (n_qt - 1 - j) * PF_ROWS for k in key) for j in range(n_qt)]  # level j = tile n_qt-1-j
     for lin in range(grid):
         xcd, r8 = lin % 8, lin // 8
         if order == "tile":
@@ -515,8 +515,8 @@ def prefill_items(qs, ctx, S, Hk, G, n_qt, T, grid, order):
             assert unit < cnt[j] * Hk  # a unit that has a tile at level j
             s_ = rank_to_seq[unit // Hk]
             hk, h = unit % Hk, (unit % Hk) * G + off % G
-            qt = -(-key[s_] // PF_ROWS) - 1 - j
-            assert qt >= 0
+            qt = n_qt - 1 - j
+            assert qt >= 0 and key[s_] > qt * PF_ROWS
         assert 0 <= s_ < S and 0 <= h < H_of(Hk, G) and 0 <= qt < n_qt and h // G == hk
         assert unit % 8 == lin % 8  # a unit's workgroups share one XCD
         yield (s_, h, qt)
@@ -595,3 +595,115 @@ def test_random_prefill_case_bounds(seed):
 
     case = random_prefill_case(seed)
     check_prefill_bounds(case)
+
+
+# ---------------------------------------------------------------------------
+# Sibling-group decode kernel (csrc/pa_decode_siblings.h)
+# ---------------------------------------------------------------------------
+
+SIB_MAX, SIB_MAX_IDS, SIB_TILE = 16, 4096, 16
+
+
+def check_siblings_bounds(case, group):
+    """Grid (H, ceil(S / group)); members m < n of group k are sequences
+    group * k + m.  Staged ids s_blk[m * ids + j] for j <= (ctx_m - 1) / B;
+    the shared prefix covers the leading entries all usable members hold in
+    common, capped at the shortest context; tiles of 16 tokens per segment
+    (shared, then each member's own tokens) load token min(t, end - 1) from
+    the segment's member's ids.  Every staged, loaded and written index is
+    in bounds, and each usable member's tokens 0 .. ctx - 1 are each read
+    exactly once, from the physical block its own table names."""
+    S, H, D = case.q.shape
+    N, Hk, B, _ = case.k_cache.shape
+    assert Hk == H and 2 <= group <= SIB_MAX
+    W = case.block_tables.shape[1]
+    maxc = case.max_context_len
+    assert maxc <= W * B
+    ids = max(1, -(-maxc // B))
+    assert group * ids <= SIB_MAX_IDS
+    cache_elems = N * H * B * D
+    RPI = 64 * 8 // D
+    # Longest-first dispatch: grid row r takes the group of rank r in
+    # decreasing total usable context (ties by index): a permutation.
+    G_n = -(-S // group)
+    tot = [sum(int(c) for c in case.context_lens[k * group:(k + 1) * group] if 0 < int(c) <= maxc)
+           for k in range(G_n)]
+    if G_n <= 512:
+        ranks = [sum((tot[j] > tot[k]) or (tot[j] == tot[k] and j < k) for j in range(G_n)) for k in range(G_n)]
+        assert sorted(ranks) == list(range(G_n))
+    for k in range(G_n):
+        s0 = k * group
+        n = min(group, S - s0)
+        ctx = [int(case.context_lens[s0 + m]) for m in range(n)]
+        usable = [0 < c <= maxc for c in ctx]
+        blk = np.full((n, ids), -1, dtype=np.int64)
+        for m in range(n):
+            if usable[m]:
+                nb = (ctx[m] - 1) // B + 1
+                assert nb <= ids and nb <= W and (s0 + m) * W + nb - 1 < S * W
+                row = case.block_tables[s0 + m, :nb].astype(np.int64)
+                blk[m, :nb] = np.where((row >= 0) & (row < N), row, -1)
+        members = [m for m in range(n) if usable[m]]
+        if len(members) >= 2:
+            minctx = min(ctx[m] for m in members)
+            jmax = (minctx - 1) // B + 1
+            common = jmax
+            for j in range(jmax):
+                if any(blk[m, j] != blk[members[0], j] for m in members):
+                    common = j
+                    break
+            shared_end = min(common * B, minctx)
+        else:
+            shared_end = 0
+        segs = [(0, shared_end, members[0] if members else 0, set(members))]
+        segs += [(shared_end, ctx[m], m, {m}) for m in members]
+        seen = {m: np.zeros(ctx[m], dtype=np.int64) for m in members}
+        for tb0, tend, mid, cols in segs:
+            for tb in range(tb0, tend, SIB_TILE):
+                for i in range(SIB_TILE // RPI):
+                    t = np.minimum(tb + RPI * i + np.arange(RPI), tend - 1)
+                    assert (t >> int(np.log2(B))).max() < ids
+                    b = np.maximum(blk[mid, t // B], 0)
+                    e = b * H * B * D + (H - 1) * B * D + (t % B) * D + D - 8
+                    assert e.max() + 8 <= cache_elems
+                # tokens this tile weighs (unmasked: tb + 4 g + j < tend)
+                for t in range(tb, min(tb + SIB_TILE, tend)):
+                    for m in cols:
+                        seen[m][t] += 1
+                        # the block read is the member's own block for t
+                        assert blk[mid, t // B] == blk[m, t // B]
+        for m in members:
+            assert (seen[m] == 1).all(), (k, m)
+        assert s0 + n - 1 < S  # output rows
+
+
+@pytest.mark.parametrize("B", [8, 16, 32])
+def test_siblings_parallel_sampling_bounds(B):
+    case = wl.parallel_sampling(block_size=B)
+    check_siblings_bounds(case, 4)
+
+
+SIB_CASES = [
+    # seed, group, dtype, D, B, prompts, samples, prompt_len, max_suffix
+    (1, 2, "f16", 64, 1, 3, 2, 37, 20),
+    (2, 3, "bf16", 128, 8, 4, 3, 100, 40),
+    (3, 16, "f16", 128, 16, 2, 16, 70, 30),
+    (4, 4, "bf16", 256, 32, 3, 4, 65, 64),
+    (5, 5, "f16", 128, 256, 3, 4, 300, 10),  # groups cut across prompts
+]
+
+
+@pytest.mark.parametrize("seed,group,dtype,D,B,prompts,samples,plen,msuf", SIB_CASES)
+def test_siblings_forked_bounds(seed, group, dtype, D, B, prompts, samples, plen, msuf):
+    case = wl.parallel_sampling(block_size=B, num_prompts=prompts, samples=samples, prompt_len=plen, num_heads=2,
+                                head_dim=D, pool_tokens=max(4096, 64 * B), dtype=dtype, max_suffix=msuf)
+    check_siblings_bounds(case, group)
+
+
+def test_siblings_unrelated_and_guarded_bounds():
+    """Unrelated sequences (nothing shared), empty and impossible contexts,
+    and an out-of-pool id in the shared region: still in bounds."""
+    case = wl.random_case(77, 7, 2, 128, 16, "f16", ctx=[1, 300, 0, 17, 64, 65, 900], spare_blocks=4)
+    check_siblings_bounds(case, 4)
+    case.context_lens[2] = case.max_context_len + 5  # impossible: not staged
+    check_siblings_bounds(case, 3)

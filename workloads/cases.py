@@ -281,6 +281,8 @@ def parallel_sampling(
     num_heads: int = 40,
     head_dim: int = 128,
     pool_tokens: int = 262144,
+    dtype: str = "f16",
+    max_suffix: int = 256,
 ) -> Case:
     """Parallel sampling with copy-on-write of the shared partial prompt block.
 
@@ -289,12 +291,19 @@ def parallel_sampling(
     samples 0..n-2 take private copies of the partially filled last prompt
     block (one batched block copy), sample n-1 keeps the original; each sample
     then appends its own suffix tokens; decode attends to prompt + suffix.
+    Suffix lengths are uniform in [0, max_suffix]; with the defaults (at most
+    64 prompts of at most 4 samples, f16) the draws are those of the
+    parallel-sampling workload.
     """
     seed = BASE_SEED + 4
-    D, dtype, B = head_dim, "f16", block_size
+    D, B = head_dim, block_size
     H = num_heads
     rng = np.random.default_rng(seed)
-    suffix = rng.integers(0, 257, (64, 4))[:num_prompts, :samples]
+    if num_prompts <= 64 and samples <= 4 and max_suffix == 256:
+        suffix = rng.integers(0, 257, (64, 4))[:num_prompts, :samples]
+    else:
+        suffix = np.random.default_rng([seed, samples, max_suffix]).integers(0, max_suffix + 1,
+                                                                             (num_prompts, samples))
     N = pool_tokens // B
     perm = np.random.default_rng([seed, B]).permutation(N)
     pool = BlockPool(N, B, perm)
@@ -334,7 +343,7 @@ def parallel_sampling(
         ),
     ]
     return Case(
-        name=f"parallel-sampling-B{B}",
+        name=f"parallel-sampling-B{B}" + ("" if dtype == "f16" else f"-{dtype}"),
         dtype=dtype,
         num_heads=H,
         head_dim=D,
