@@ -1,6 +1,7 @@
 """Seeded random shapes through the C ABI against the oracle: decode
 (multi-head and grouped heads, every dtype, forced and default partitions,
-with and without the fused append) and chunked prefill.  Each case is small
+with and without the fused append), sibling groups of forked samples, and
+chunked prefill.  Each case is small
 enough for the oracle to check every output; together they cross the plan
 thresholds, block sizes and ragged tails the hand-written cases pick one at
 a time."""
@@ -75,3 +76,41 @@ def test_random_prefill(seed):
     log(f"seed {seed}: {case.dtype} D={case.head_dim} B={case.block_size} H={case.num_heads} "
         f"Hk={case.num_kv_heads} ctx={case.context_lens.tolist()} rows={np.diff(case.query_start).tolist()}")
     check(case, strict=False)
+
+
+def random_siblings_case(seed: int) -> tuple:
+    """(case, group size) of random sibling seed `seed`: forked samples of a
+    few prompts (copy-on-write of the partly filled last prompt block), with
+    a group size that may or may not match the samples per prompt."""
+    rng = np.random.default_rng([322, 9003, seed])
+    dtype = ["f16", "bf16"][seed % 2]
+    D = int(rng.choice([64, 128, 256]))
+    B = int(rng.choice([1, 2, 8, 16, 32, 64, 256]))
+    samples = int(rng.integers(1, 9))
+    prompts = int(rng.integers(1, 5))
+    prompt_len = int(rng.integers(1, 400))
+    max_suffix = int(rng.integers(0, 200))
+    group = int(rng.choice([samples, samples, 2, 3, 16])) if samples >= 2 else int(rng.choice([2, 5]))
+    need = prompts * samples * ((prompt_len + max_suffix) // B + 3)
+    case = wl.parallel_sampling(block_size=B, num_prompts=prompts, samples=samples, prompt_len=prompt_len,
+                                num_heads=int(rng.choice([1, 2, 4])), head_dim=D, pool_tokens=max(4096, 2 * need * B),
+                                dtype=dtype, max_suffix=max_suffix)
+    return case, max(2, min(16, group))
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_siblings(seed):
+    case, group = random_siblings_case(seed)
+    log(f"seed {seed}: {case.dtype} D={case.head_dim} B={case.block_size} H={case.num_heads} group={group} "
+        f"ctx={case.context_lens.tolist()}")
+    g = GpuCase(case)
+    kc, vc = case.k_cache, case.v_cache
+    for i, (kc, vc) in enumerate(oracle_steps(case)):
+        g.run_step(i)
+        assert_pool_equal(g.kc, kc, case.dtype, f"seed {seed} K after step {i}")
+        assert_pool_equal(g.vc, vc, case.dtype, f"seed {seed} V after step {i}")
+    ref = oracle_decode(case, kc, vc)
+    out = torch.empty_like(g.q)
+    pa().decode(out, g.q, g.kc, g.vc, g.bt, g.ctx, case.scale, case.max_context_len, siblings=group)
+    torch.cuda.synchronize()
+    assert_close(out, ref, case.dtype, f"seed {seed} siblings", strict=False)

@@ -707,3 +707,12 @@ def test_siblings_unrelated_and_guarded_bounds():
     check_siblings_bounds(case, 4)
     case.context_lens[2] = case.max_context_len + 5  # impossible: not staged
     check_siblings_bounds(case, 3)
+
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_siblings_case_bounds(seed):
+    from test_gpu_random_cases import random_siblings_case
+
+    case, group = random_siblings_case(seed)
+    check_siblings_bounds(case, group)
