@@ -45,6 +45,8 @@ WORKLOADS = {
     "llama7b": "llama7b-decode-layer: 64 seqs, ctx U[128,2048], H=32, D=128, f16, B=16, 8192-block pool",
     "opt13b": "opt13b-decode-layer: 256 seqs, ctx lognormal(median 300, sigma 0.9) in [16,2048], H=40, D=128, f16, B=16",
     "sampling": "parallel-sampling-cow: 64 prompts x 4 samples, prompt 500, suffix U[0,256], H=40, D=128, f16",
+    "sampling-gqa": "parallel-sampling-cow-gqa: 64 prompts x 4 samples, prompt 500, suffix U[0,256], 32 query / 8 K/V "
+                    "heads (LLaMA-3-8B-shaped), D=128, f16",
     "opt175b": "opt175b-decode-layer: 128 seqs, ctx U[1024,2048], H=96, D=128, bf16, B=16, 16384-block pool",
     "opt175b-tp8": "opt175b-decode-tp8-share: the OPT-175B-shaped layer with the 12 of its 96 heads one of 8 tensor-parallel GPUs holds; "
             "128 seqs, ctx U[1024,2048], D=128, bf16, B=16, 16384-block pool",
@@ -61,6 +63,7 @@ WORKLOADS = {
                      "(lognormal(300, 0.9) contexts, B=16) and prefix-cached admission of 256 prompts sharing a "
                      "512-token system prompt",
 }
+SAMPLING_KINDS = ("sampling", "sampling-gqa")  # forked samples sharing prompt blocks
 PREFILL_KINDS = {"prefill-llama7b": "llama7b", "prefill-gqa8b": "llama3-8b", "prefill-prompts": "prompts"}
 MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak, vendor figure
 PREFILL_METRIC = "paged prefill attention: TFLOP/s and % of MFMA peak"
@@ -104,6 +107,8 @@ def make_case(cfg, block_size=16):
         return wl.opt13b_decode()
     if cfg == "sampling":
         return wl.parallel_sampling(block_size=block_size)
+    if cfg == "sampling-gqa":
+        return wl.parallel_sampling(block_size=block_size, num_heads=32, num_kv_heads=8)
     if cfg == "gqa8b":
         return wl.gqa_config("llama3-8b", n_append=1)
     if cfg == "gqa70b":
@@ -188,7 +193,7 @@ def decode_kernel_name(case, siblings=0):
     heads, else the vector-ALU kernel."""
     G = case.num_heads // case.num_kv_heads
     mfma_shape = case.elem_bytes == 2 and case.head_dim in (64, 128, 256)
-    if mfma_shape and G == 1 and siblings >= 2:
+    if mfma_shape and siblings >= 2 and siblings * G <= 16:
         return "decode_siblings_kernel"
     if mfma_shape and G >= 2:
         return "decode_mfma_kernel"
@@ -356,7 +361,7 @@ def bench_decode(args, config, case, pa, torch, dev, full=True):
     # The parallel-sampling workload's prompt write, fork copies and suffix
     # writes are set-up; the other workloads time their one-token-per-sequence
     # append with the decode.
-    if config == "sampling":
+    if config in SAMPLING_KINDS:
         setup_steps, timed_steps = list(case.steps), []
     else:
         setup_steps, timed_steps = [], list(case.steps)
@@ -386,12 +391,12 @@ def bench_decode(args, config, case, pa, torch, dev, full=True):
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
-    siblings = (4 if config == "sampling" else 0) if args.siblings == "auto" else int(args.siblings)
+    siblings = (4 if config in SAMPLING_KINDS else 0) if args.siblings == "auto" else int(args.siblings)
     # Cached K/V loads pay off when several workgroups read the same blocks:
     # the parallel-sampling workload decoded without sibling groups.  With
     # them, each shared block is read once per (group, head) and the
     # non-temporal loads are faster (measured: 229 -> 206 us at B = 16).
-    shared = args.shared_blocks == "on" or (args.shared_blocks == "auto" and config == "sampling" and siblings < 2)
+    shared = args.shared_blocks == "on" or (args.shared_blocks == "auto" and config in SAMPLING_KINDS and siblings < 2)
     fused = bool(timed_steps)
     if fused:
         assert len(timed_steps) == 1 and timed_steps[0].slot_mapping.size == S  # one newest row per sequence
@@ -593,7 +598,7 @@ def bench_decode(args, config, case, pa, torch, dev, full=True):
         "copy_blocks": cow,
         "hbm_copy_probe": probe,
     }
-    if config == "sampling":
+    if config in SAMPLING_KINDS:
         ub = unique_kv_bytes(case)
         result["unique_kv_bytes"] = int(ub)
         result["unique_kv_GBps"] = round(ub / (rot_ms * 1e-3) / 1e9, 1)

@@ -80,9 +80,10 @@ typedef enum {
                                       once per group and head, for all members together; each
                                       member's other tokens are read from its own blocks.  A hint:
                                       nothing is assumed that the tables do not show.  Taken for
-                                      16-bit caches, head_dim 64, 128 or 256, num_kv_heads ==
-                                      num_heads and n * ceil(max_context_len / B) <= 4096, with one
-                                      workgroup per (group, head) over whole contexts
+                                      16-bit caches, head_dim 64, 128 or 256, n * G <= 16 (G =
+                                      num_heads / num_kv_heads) and n * ceil(max_context_len / B)
+                                      <= 4096, with one workgroup per (group, K/V head) over whole
+                                      contexts
                                       (partition_size is then not used); otherwise ignored.  The
                                       arithmetic (fp32 products and softmax, probabilities as hi and
                                       lo 16-bit parts) differs from the multi-head kernel's only by

@@ -453,10 +453,11 @@ constexpr bool kUseMfma = sizeof(typename T::bits) == 2 && (D == 64 || D == 128 
 template <int D>
 constexpr int kMfmaMaxStaged = D == 256 ? 4096 : 6144;
 
-// Sibling-group decode: 16-bit caches, head_dim 64..256, one query head per
-// K/V head (the group's members take the matrix columns).
+// Sibling-group decode: 16-bit caches, head_dim 64..256 (the group's members
+// times the query heads of a K/V head take the matrix columns; the host
+// checks that they fit 16).
 template <class T, int D, int G>
-constexpr bool kUseSiblings = sizeof(typename T::bits) == 2 && (D == 64 || D == 128 || D == 256) && G == 1;
+constexpr bool kUseSiblings = sizeof(typename T::bits) == 2 && (D == 64 || D == 128 || D == 256);
 
 template <class T, int D, int G, bool APPEND, bool NT>
 hipError_t launch_decode_t(const DecodeArgs& a) {
@@ -473,13 +474,13 @@ hipError_t launch_decode_t(const DecodeArgs& a) {
     const size_t lds = static_cast<size_t>(a.staged_blocks) * sizeof(int);
     if constexpr (kUseSiblings<T, D, G> && !APPEND) {
         if (a.siblings >= 2) {
-            // One workgroup per (head, group of siblings), whole contexts.
+            // One workgroup per (K/V head, group of siblings), whole contexts.
             const unsigned groups = static_cast<unsigned>((a.num_seqs + a.siblings - 1) / a.siblings);
-            hipLaunchKernelGGL((decode_siblings_kernel<T, D, NT>), dim3(a.num_heads, groups), dim3(kMfmaThreads),
+            hipLaunchKernelGGL((decode_siblings_kernel<T, D, NT>), dim3(a.num_kv_heads, groups), dim3(kMfmaThreads),
                                static_cast<size_t>(a.siblings) * a.sibling_ids * sizeof(int), a.stream, out,
                                static_cast<const bits*>(a.query), static_cast<const bits*>(a.k_cache),
                                static_cast<const bits*>(a.v_cache), a.block_tables, a.context_lens, a.num_seqs,
-                               a.num_heads, a.siblings, a.sibling_ids, log2_bs, a.max_blocks_per_seq,
+                               a.num_kv_heads, G, a.siblings, a.sibling_ids, log2_bs, a.max_blocks_per_seq,
                                a.max_context_len, a.num_blocks, qscale);
             return hipGetLastError();
         }

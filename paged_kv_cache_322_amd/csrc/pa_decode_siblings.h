@@ -12,15 +12,16 @@
 // with the same physical blocks, and reading those blocks once per sample
 // moves the shared prompt through the memory system n times.
 //
-// Design: one workgroup per (group of n consecutive sequences, head).  The
+// Design: one workgroup per (group of n consecutive sequences, K/V head).  The
 // group's block-table rows are staged in LDS and compared entry by entry:
 // the leading entries every member holds in common (the same physical
 // block) cover the shared prefix, S = min(J * B, shortest context) tokens
 // (J the common entries).  The prefix is read once: each 16-token K/V tile
 // feeds the 16x16 matrix products of decode_mfma_kernel with the n members'
-// queries as the columns (where that kernel puts the G heads of a K/V
-// head).  Each member's remaining tokens S .. ctx - 1 are then read from its
-// own blocks with only its column unmasked.  The grouping is a hint: nothing
+// queries as the columns (where that kernel puts the G heads of a K/V head;
+// with grouped-query heads, member m takes columns m G .. m G + G - 1, n G
+// <= 16).  Each member's remaining tokens S .. ctx - 1 are then read from
+// its own blocks with only its columns unmasked.  The grouping is a hint: nothing
 // is assumed shared that the tables do not show (no common entries: every
 // token is read privately, the same result), and the arithmetic is
 // decode_mfma_kernel's (fp32 products and softmax, probabilities split into
@@ -44,7 +45,7 @@ __global__ __launch_bounds__(kMfmaThreads, mfma_waves_per_simd(D)) void decode_s
     typename T::bits* __restrict__ out, const typename T::bits* __restrict__ q,
     const typename T::bits* __restrict__ kc, const typename T::bits* __restrict__ vc,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens, int num_seqs,
-    int num_heads, int group, int ids_per_seq, int log2_bs, int max_blocks_per_seq, int max_context_len,
+    int num_kv_heads, int gq, int group, int ids_per_seq, int log2_bs, int max_blocks_per_seq, int max_context_len,
     int64_t num_blocks, float qscale) {
     static_assert(sizeof(typename T::bits) == 2, "16-bit caches only");
     static_assert(D == 64 || D == 128 || D == 256, "head_dim");
@@ -73,7 +74,8 @@ __global__ __launch_bounds__(kMfmaThreads, mfma_waves_per_simd(D)) void decode_s
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const int c = lane & 15, g = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int h = blockIdx.x;
+    const int hk = blockIdx.x;               // K/V head
+    const int num_heads = num_kv_heads * gq;  // query heads; column c is member c / gq, query head hk gq + c % gq
     const int s0 = blockIdx.y * group;
     const int n = min(group, num_seqs - s0);
 
@@ -93,6 +95,11 @@ __global__ __launch_bounds__(kMfmaThreads, mfma_waves_per_simd(D)) void decode_s
         }
     }
     const int nvalid = __builtin_popcount(vmask);
+    // Matrix columns: member m's gq query heads take columns m gq .. m gq + gq - 1.
+    const int ncols = n * gq;
+    int vcols = 0;
+    for (int m = 0; m < n; ++m)
+        if ((vmask >> m) & 1) vcols |= ((1 << gq) - 1) << (m * gq);
 
     // Stage every usable member's block ids (entries past its context: -1).
     for (int i = tid; i < n * ids_per_seq; i += kMfmaThreads) {
@@ -138,13 +145,14 @@ __global__ __launch_bounds__(kMfmaThreads, mfma_waves_per_simd(D)) void decode_s
     u32x4 qv[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-        qv[ks] = (c < n) ? as_u32x4(load16(q + (static_cast<int64_t>(s0 + c) * num_heads + h) * D + 32 * ks + 8 * g))
+        qv[ks] = (c < ncols) ? as_u32x4(load16(q + (static_cast<int64_t>(s0 + c / gq) * num_heads + hk * gq + c % gq) * D +
+                                                32 * ks + 8 * g))
                          : u32x4{0u, 0u, 0u, 0u};
     __syncthreads();  // s_seg published
     const int ntile = __builtin_amdgcn_readfirstlane(s_seg[n + 1]);
 
-    const uint32_t blk_stride = static_cast<uint32_t>(num_heads << log2_bs) * D;
-    const uint32_t head_off = (static_cast<uint32_t>(h) << log2_bs) * D;
+    const uint32_t blk_stride = static_cast<uint32_t>(num_kv_heads << log2_bs) * D;
+    const uint32_t head_off = (static_cast<uint32_t>(hk) << log2_bs) * D;
     const int bmask = (1 << log2_bs) - 1;
 
     // Tile `it`: its segment, first token, end token, the member whose ids
@@ -162,13 +170,13 @@ __global__ __launch_bounds__(kMfmaThreads, mfma_waves_per_simd(D)) void decode_s
             ti.tb = (it - first) * kMfmaTile;
             ti.tend = shared_end;
             ti.ids = m0 * ids_per_seq;
-            ti.cols = vmask;
+            ti.cols = vcols;
         } else {
             const int m = ti.seg - 1;
             ti.tb = shared_end + (it - first) * kMfmaTile;
             ti.tend = __builtin_amdgcn_readfirstlane(s_ctx[m]);
             ti.ids = m * ids_per_seq;
-            ti.cols = 1 << m;
+            ti.cols = ((1 << gq) - 1) << (m * gq);
         }
         return ti;
     };
@@ -297,7 +305,7 @@ __global__ __launch_bounds__(kMfmaThreads, mfma_waves_per_simd(D)) void decode_s
         s_m[wave][c] = m;
         s_l[wave][c] = l;
     }
-    for (int c0 = 0; c0 < n; c0 += HC) {
+    for (int c0 = 0; c0 < ncols; c0 += HC) {
         if (c >= c0 && c < c0 + HC) {
 #pragma unroll
             for (int t = 0; t < E; ++t)
@@ -307,12 +315,13 @@ __global__ __launch_bounds__(kMfmaThreads, mfma_waves_per_simd(D)) void decode_s
         __syncthreads();
         for (int idx = tid; idx < HC * D; idx += kMfmaThreads) {
             const int hl = idx / D, d = idx % D, col = c0 + hl;
-            if (col >= n) continue;
-            const int cm = s_ctx[col];
+            if (col >= ncols) continue;
+            const int mem = col / gq;
+            const int cm = s_ctx[mem];
             float v;
             if (cm == 0) {
                 v = 0.0f;
-            } else if (!((vmask >> col) & 1) || (bad_all & 1u) || ((bad_all >> (col + 1)) & 1u)) {
+            } else if (!((vmask >> mem) & 1) || (bad_all & 1u) || ((bad_all >> (mem + 1)) & 1u)) {
                 v = __builtin_nanf("");
             } else {
                 float M = s_m[0][col];
@@ -327,7 +336,7 @@ __global__ __launch_bounds__(kMfmaThreads, mfma_waves_per_simd(D)) void decode_s
                 }
                 v = O / L;
             }
-            out[(static_cast<int64_t>(s0 + col) * num_heads + h) * D + d] = narrow<T>(v);
+            out[(static_cast<int64_t>(s0 + mem) * num_heads + hk * gq + col % gq) * D + d] = narrow<T>(v);
         }
         __syncthreads();  // s_o is reused by the next pass
     }

@@ -92,16 +92,20 @@ def random_siblings_case(seed: int) -> tuple:
     max_suffix = int(rng.integers(0, 200))
     group = int(rng.choice([samples, samples, 2, 3, 16])) if samples >= 2 else int(rng.choice([2, 5]))
     need = prompts * samples * ((prompt_len + max_suffix) // B + 3)
+    Hk = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 1, 2, 4]))
+    group = max(2, min(16 // G, group))
     case = wl.parallel_sampling(block_size=B, num_prompts=prompts, samples=samples, prompt_len=prompt_len,
-                                num_heads=int(rng.choice([1, 2, 4])), head_dim=D, pool_tokens=max(4096, 2 * need * B),
-                                dtype=dtype, max_suffix=max_suffix)
-    return case, max(2, min(16, group))
+                                num_heads=Hk * G, head_dim=D, pool_tokens=max(4096, 2 * need * B), dtype=dtype,
+                                max_suffix=max_suffix, num_kv_heads=Hk)
+    return case, group
 
 
 @pytest.mark.parametrize("seed", range(16))
 def test_random_siblings(seed):
     case, group = random_siblings_case(seed)
-    log(f"seed {seed}: {case.dtype} D={case.head_dim} B={case.block_size} H={case.num_heads} group={group} "
+    log(f"seed {seed}: {case.dtype} D={case.head_dim} B={case.block_size} H={case.num_heads} "
+        f"Hk={case.num_kv_heads} group={group} "
         f"ctx={case.context_lens.tolist()}")
     g = GpuCase(case)
     kc, vc = case.k_cache, case.v_cache

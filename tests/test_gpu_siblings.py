@@ -1,8 +1,9 @@
 """Sibling-group decode (pa_decode with PA_DECODE_SIBLINGS(n)): the shared
 leading blocks of forked samples read once per group, against the oracle on
 every sequence, and against the ungrouped decode (same definition; the two
-differ by fp32 rounding only).  Unrelated sequences, empty, impossible and
-out-of-pool entries, and the cases where the hint is not taken."""
+differ by fp32 rounding only).  Multi-head and grouped-query heads,
+unrelated sequences, empty, impossible and out-of-pool entries, and the
+cases where the hint is not taken."""
 import numpy as np
 import pytest
 import torch
@@ -111,20 +112,40 @@ def test_siblings_bad_id_in_the_shared_prefix():
     assert_close(out[keep], ref[keep], "f16", "siblings: other groups", strict=False)
 
 
-@pytest.mark.parametrize("what", ["f32", "gqa", "d32"])
+@pytest.mark.parametrize("G,group,dtype", [(2, 4, "f16"), (4, 4, "bf16"), (8, 2, "f16"), (4, 3, "f16")])
+def test_siblings_grouped_query(G, group, dtype):
+    """Grouped-query heads: member m of a group takes matrix columns
+    m G .. m G + G - 1 (n G <= 16); each K/V tile of the shared prefix feeds
+    every member's G query heads at once."""
+    case = wl.parallel_sampling(block_size=16, num_prompts=3, samples=4, prompt_len=90, num_heads=2 * G,
+                                head_dim=128, pool_tokens=8192, max_suffix=40, num_kv_heads=2, dtype=dtype)
+    run_case(case, group, strict=False)
+
+
+def test_siblings_grouped_query_llama3_8b_shape():
+    """LLaMA-3-8B-shaped heads (32 query over 8 K/V heads) for 16 prompts x 4
+    samples: 4 members x 4 query heads fill the 16 columns."""
+    case = wl.parallel_sampling(block_size=16, num_prompts=16, samples=4, prompt_len=500, num_heads=32,
+                                head_dim=128, pool_tokens=65536, num_kv_heads=8)
+    run_case(case, 4)
+
+
+@pytest.mark.parametrize("what", ["f32", "wide", "d32"])
 def test_siblings_hint_ignored_where_not_built(what):
-    """Where the sibling kernel is not built (fp32 caches, grouped-query
-    heads, head_dim below 64) the hint changes nothing: identical bits."""
+    """Where the sibling kernel is not built or the group does not fit its
+    16 matrix columns (fp32 caches, members x query heads per K/V head > 16,
+    head_dim below 64) the hint changes nothing: identical bits."""
+    group = 3
     if what == "f32":
         case = wl.random_case(81, 6, 2, 64, 8, "f32", ctx=[5, 40, 41, 9, 100, 3], spare_blocks=2)
-    elif what == "gqa":
-        case = wl.random_case(82, 6, 4, 128, 16, "f16", ctx=[5, 40, 41, 9, 100, 3], spare_blocks=2, num_kv_heads=2)
+    elif what == "wide":
+        case = wl.random_case(82, 6, 16, 128, 16, "f16", ctx=[5, 40, 41, 9, 100, 3], spare_blocks=2, num_kv_heads=2)
     else:
         case = wl.random_case(83, 6, 2, 32, 16, "bf16", ctx=[5, 40, 41, 9, 100, 3], spare_blocks=2)
     g = GpuCase(case)
     a = g.decode(out=torch.empty_like(g.q)).clone()
     b = torch.empty_like(g.q)
-    pa().decode(b, g.q, g.kc, g.vc, g.bt, g.ctx, case.scale, case.max_context_len, siblings=3)
+    pa().decode(b, g.q, g.kc, g.vc, g.bt, g.ctx, case.scale, case.max_context_len, siblings=group)
     torch.cuda.synchronize()
     iv = torch.int32 if case.dtype == "f32" else torch.int16
     assert torch.equal(a.view(iv), b.view(iv))

@@ -615,13 +615,14 @@ def check_siblings_bounds(case, group):
     exactly once, from the physical block its own table names."""
     S, H, D = case.q.shape
     N, Hk, B, _ = case.k_cache.shape
-    assert Hk == H and 2 <= group <= SIB_MAX
+    G = H // Hk
+    assert H % Hk == 0 and 2 <= group and group * G <= SIB_MAX  # matrix columns: members x query heads
     W = case.block_tables.shape[1]
     maxc = case.max_context_len
     assert maxc <= W * B
     ids = max(1, -(-maxc // B))
     assert group * ids <= SIB_MAX_IDS
-    cache_elems = N * H * B * D
+    cache_elems = N * Hk * B * D
     RPI = 64 * 8 // D
     # Longest-first dispatch: grid row r takes the group of rank r in
     # decreasing total usable context (ties by index): a permutation.
@@ -664,7 +665,7 @@ def check_siblings_bounds(case, group):
                     t = np.minimum(tb + RPI * i + np.arange(RPI), tend - 1)
                     assert (t >> int(np.log2(B))).max() < ids
                     b = np.maximum(blk[mid, t // B], 0)
-                    e = b * H * B * D + (H - 1) * B * D + (t % B) * D + D - 8
+                    e = b * Hk * B * D + (Hk - 1) * B * D + (t % B) * D + D - 8
                     assert e.max() + 8 <= cache_elems
                 # tokens this tile weighs (unmasked: tb + 4 g + j < tend)
                 for t in range(tb, min(tb + SIB_TILE, tend)):
@@ -674,7 +675,11 @@ def check_siblings_bounds(case, group):
                         assert blk[mid, t // B] == blk[m, t // B]
         for m in members:
             assert (seen[m] == 1).all(), (k, m)
-        assert s0 + n - 1 < S  # output rows
+        # query operands and output rows: member c // G, query head hk G + c % G
+        for col in range(n * G):
+            row = (s0 + col // G) * H + (Hk - 1) * G + col % G
+            assert row < S * H
+        assert s0 + n - 1 < S
 
 
 @pytest.mark.parametrize("B", [8, 16, 32])
@@ -715,4 +720,12 @@ def test_random_siblings_case_bounds(seed):
     from test_gpu_random_cases import random_siblings_case
 
     case, group = random_siblings_case(seed)
+    check_siblings_bounds(case, group)
+
+
+
+@pytest.mark.parametrize("G,group", [(2, 4), (4, 4), (8, 2), (4, 3)])
+def test_siblings_grouped_query_bounds(G, group):
+    case = wl.parallel_sampling(block_size=16, num_prompts=3, samples=4, prompt_len=90, num_heads=2 * G, head_dim=128,
+                                pool_tokens=8192, max_suffix=40, num_kv_heads=2)
     check_siblings_bounds(case, group)

@@ -283,6 +283,7 @@ def parallel_sampling(
     pool_tokens: int = 262144,
     dtype: str = "f16",
     max_suffix: int = 256,
+    num_kv_heads: Optional[int] = None,
 ) -> Case:
     """Parallel sampling with copy-on-write of the shared partial prompt block.
 
@@ -293,11 +294,14 @@ def parallel_sampling(
     then appends its own suffix tokens; decode attends to prompt + suffix.
     Suffix lengths are uniform in [0, max_suffix]; with the defaults (at most
     64 prompts of at most 4 samples, f16) the draws are those of the
-    parallel-sampling workload.
+    parallel-sampling workload.  num_kv_heads (a divisor of num_heads, default
+    num_heads) gives grouped-query caches.
     """
     seed = BASE_SEED + 4
     D, B = head_dim, block_size
     H = num_heads
+    Hk = H if num_kv_heads is None else num_kv_heads
+    assert H % Hk == 0
     rng = np.random.default_rng(seed)
     if num_prompts <= 64 and samples <= 4 and max_suffix == 256:
         suffix = rng.integers(0, 257, (64, 4))[:num_prompts, :samples]
@@ -331,27 +335,27 @@ def parallel_sampling(
     T0, T1 = len(prompt_slots), len(suffix_slots)
     steps: List[Step] = [
         AppendStep(
-            normal_storage(seed, f"kp/{B}", (T0, H, D), dtype),
-            normal_storage(seed, f"vp/{B}", (T0, H, D), dtype),
+            normal_storage(seed, f"kp/{B}", (T0, Hk, D), dtype),
+            normal_storage(seed, f"vp/{B}", (T0, Hk, D), dtype),
             np.asarray(prompt_slots, dtype=np.int64),
         ),
         CopyStep(np.asarray(pairs, dtype=np.int64).reshape(-1, 2)),
         AppendStep(
-            normal_storage(seed, f"ks/{B}", (T1, H, D), dtype),
-            normal_storage(seed, f"vs/{B}", (T1, H, D), dtype),
+            normal_storage(seed, f"ks/{B}", (T1, Hk, D), dtype),
+            normal_storage(seed, f"vs/{B}", (T1, Hk, D), dtype),
             np.asarray(suffix_slots, dtype=np.int64),
         ),
     ]
     return Case(
-        name=f"parallel-sampling-B{B}" + ("" if dtype == "f16" else f"-{dtype}"),
+        name=f"parallel-sampling-B{B}" + ("" if dtype == "f16" else f"-{dtype}") + ("" if Hk == H else f"-Hk{Hk}"),
         dtype=dtype,
         num_heads=H,
         head_dim=D,
         block_size=B,
         num_blocks=N,
         q=normal_storage(seed, f"q/{B}", (len(kids), H, D), dtype),
-        k_cache=canary_fill((N, H, B, D), dtype),
-        v_cache=canary_fill((N, H, B, D), dtype),
+        k_cache=canary_fill((N, Hk, B, D), dtype),
+        v_cache=canary_fill((N, Hk, B, D), dtype),
         block_tables=tables_array(kids),
         context_lens=ctx,
         scale=1.0 / math.sqrt(D),
