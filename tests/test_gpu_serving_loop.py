@@ -3,7 +3,8 @@
 Requests sharing a system prompt are admitted through the prefix cache and
 prefilled (pa_reshape_and_cache + pa_prefill for the uncached part); one is
 forked (parallel sampling); decode steps take their slots and copy-on-write
-pairs from the manager (pa_copy_blocks, pa_reshape_and_cache, pa_decode);
+pairs from the manager (pa_copy_blocks, pa_reshape_and_cache, pa_decode, also
+with the fork decoded as a sibling group);
 one sequence is swapped out to pinned host memory and back mid-stream
 (pa_swap_blocks).  A token's K/V rows are a deterministic function of its
 token prefix (as in a real model), so shared prefixes really share data.
@@ -119,9 +120,15 @@ def test_block_manager_drives_prefill_decode_cow_and_swap():
         out = torch.empty((len(live), H, D), dtype=torch.float16, device=dev)
         pa().decode(out, to_gpu(np.stack([x[2] for x in new])), kc, vc, to_gpu(bt), to_gpu(lens), SCALE,
                     int(lens.max()))
+        # The same step with sibling groups of 2: the fork (sequences 0 and
+        # 10, adjacent in the batch) reads its common blocks once.
+        out_sib = torch.empty_like(out)
+        pa().decode(out_sib, to_gpu(np.stack([x[2] for x in new])), kc, vc, to_gpu(bt), to_gpu(lens), SCALE,
+                    int(lens.max()), siblings=2)
         torch.cuda.synchronize()
         ref = np.stack([expected_decode(new[i][2], hist[s]) for i, s in enumerate(live)])
         assert_close(out, ref, "f16", f"decode step {step} (copies {len(cow)})", strict=False)
+        assert_close(out_sib, ref, "f16", f"decode step {step}, sibling groups", strict=False)
     assert swapped_pairs is not None
     # At the fork, sequences 0 and 10 (70 tokens) shared 4 full blocks and a
     # partly filled one; the first decode write copied only the partial one.
