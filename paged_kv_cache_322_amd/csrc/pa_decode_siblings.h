@@ -17,15 +17,15 @@
 // the leading entries every member holds in common (the same physical
 // block) cover the shared prefix, S = min(J * B, shortest context) tokens
 // (J the common entries).  The prefix is read once: each 16-token K/V tile
-// feeds the 16x16 matrix products of decode_mfma_kernel with the n members'
+// feeds the 16x16 matrix products of decode_mfma_kernel with the members'
 // queries as the columns (where that kernel puts the G heads of a K/V head;
-// with grouped-query heads, member m takes columns m G .. m G + G - 1, n G
-// <= 16).  Each member's remaining tokens S .. ctx - 1 are then read from
-// its own blocks with only its columns unmasked.  The grouping is a hint: nothing
-// is assumed shared that the tables do not show (no common entries: every
-// token is read privately, the same result), and the arithmetic is
-// decode_mfma_kernel's (fp32 products and softmax, probabilities split into
-// hi and lo 16-bit parts).  Each member's softmax state is per column; the 8
+// member m takes columns m G .. m G + G - 1, n G <= 16).  Each member's
+// remaining tokens S .. ctx - 1 are then read from its own blocks with only
+// its columns unmasked.  The grouping is a hint: nothing is assumed shared
+// that the tables do not show (no common entries: every token is read
+// privately, the same result), and the arithmetic is decode_mfma_kernel's
+// (fp32 products and softmax, probabilities split into hi and lo 16-bit
+// parts).  Each member's softmax state is per column; the 8
 // wavefronts split the tiles of the whole token list and merge through LDS.
 // The members' K/V values must be finite: a masked column still multiplies
 // its zero probabilities with the tile's V rows, so a non-finite value in
@@ -75,7 +75,7 @@ __global__ __launch_bounds__(kMfmaThreads, mfma_waves_per_simd(D)) void decode_s
     const int c = lane & 15, g = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int hk = blockIdx.x;               // K/V head
-    const int num_heads = num_kv_heads * gq;  // query heads; column c is member c / gq, query head hk gq + c % gq
+    const int num_heads = num_kv_heads * gq;  // query heads (gq per K/V head)
     const int s0 = blockIdx.y * group;
     const int n = min(group, num_seqs - s0);
 
@@ -128,9 +128,9 @@ __global__ __launch_bounds__(kMfmaThreads, mfma_waves_per_simd(D)) void decode_s
     const int common = __builtin_amdgcn_readfirstlane(s_common);
     const int shared_end = nvalid >= 2 ? min(common << log2_bs, minctx) : 0;  // tokens 0 .. shared_end - 1
 
-    // Token segments: 0 = the shared prefix (every usable column), 1 + m =
-    // member m's tokens shared_end .. ctx_m - 1 (column m only); 16-token
-    // tiles numbered segment after segment.
+    // Token segments: 0 = the shared prefix (every usable member's columns),
+    // 1 + m = member m's tokens shared_end .. ctx_m - 1 (its columns only);
+    // 16-token tiles numbered segment after segment.
     if (tid == 0) {
         int t = (shared_end + kMfmaTile - 1) / kMfmaTile;
         s_seg[0] = 0;
@@ -141,13 +141,13 @@ __global__ __launch_bounds__(kMfmaThreads, mfma_waves_per_simd(D)) void decode_s
         s_seg[n + 1] = t;
     }
 
-    // B operand of q.k: member c's query (zero for columns past the group).
+    // B operand of q.k: column c's query, member c / gq's query head
+    // hk gq + c % gq (zero for columns past the group).
+    const int64_t q_row = static_cast<int64_t>(s0 + c / gq) * num_heads + hk * gq + c % gq;
     u32x4 qv[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-        qv[ks] = (c < ncols) ? as_u32x4(load16(q + (static_cast<int64_t>(s0 + c / gq) * num_heads + hk * gq + c % gq) * D +
-                                                32 * ks + 8 * g))
-                         : u32x4{0u, 0u, 0u, 0u};
+        qv[ks] = (c < ncols) ? as_u32x4(load16(q + q_row * D + 32 * ks + 8 * g)) : u32x4{0u, 0u, 0u, 0u};
     __syncthreads();  // s_seg published
     const int ntile = __builtin_amdgcn_readfirstlane(s_seg[n + 1]);
 
