@@ -47,6 +47,8 @@ WORKLOADS = {
     "sampling": "parallel-sampling-cow: 64 prompts x 4 samples, prompt 500, suffix U[0,256], H=40, D=128, f16",
     "sampling-gqa": "parallel-sampling-cow-gqa: 64 prompts x 4 samples, prompt 500, suffix U[0,256], 32 query / 8 K/V "
                     "heads (LLaMA-3-8B-shaped), D=128, f16",
+    "sampling-70b": "parallel-sampling-cow-70b: 64 prompts x 4 samples, prompt 500, suffix U[0,256], 64 query / 8 K/V "
+                    "heads (LLaMA-2-70B-shaped), D=128, f16",
     "opt175b": "opt175b-decode-layer: 128 seqs, ctx U[1024,2048], H=96, D=128, bf16, B=16, 16384-block pool",
     "opt175b-tp8": "opt175b-decode-tp8-share: the OPT-175B-shaped layer with the 12 of its 96 heads one of 8 tensor-parallel GPUs holds; "
             "128 seqs, ctx U[1024,2048], D=128, bf16, B=16, 16384-block pool",
@@ -63,7 +65,7 @@ WORKLOADS = {
                      "(lognormal(300, 0.9) contexts, B=16) and prefix-cached admission of 256 prompts sharing a "
                      "512-token system prompt",
 }
-SAMPLING_KINDS = ("sampling", "sampling-gqa")  # forked samples sharing prompt blocks
+SAMPLING_KINDS = ("sampling", "sampling-gqa", "sampling-70b")  # forked samples sharing prompt blocks
 PREFILL_KINDS = {"prefill-llama7b": "llama7b", "prefill-gqa8b": "llama3-8b", "prefill-prompts": "prompts"}
 MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak, vendor figure
 PREFILL_METRIC = "paged prefill attention: TFLOP/s and % of MFMA peak"
@@ -109,6 +111,8 @@ def make_case(cfg, block_size=16):
         return wl.parallel_sampling(block_size=block_size)
     if cfg == "sampling-gqa":
         return wl.parallel_sampling(block_size=block_size, num_heads=32, num_kv_heads=8)
+    if cfg == "sampling-70b":
+        return wl.parallel_sampling(block_size=block_size, num_heads=64, num_kv_heads=8)
     if cfg == "gqa8b":
         return wl.gqa_config("llama3-8b", n_append=1)
     if cfg == "gqa70b":
@@ -194,7 +198,7 @@ def decode_kernel_name(case, siblings=0):
     heads, else the vector-ALU kernel."""
     G = case.num_heads // case.num_kv_heads
     mfma_shape = case.elem_bytes == 2 and case.head_dim in (64, 128, 256)
-    if mfma_shape and siblings >= 2 and siblings * G <= 16:
+    if mfma_shape and siblings >= 2 and min(siblings, 16 // G) >= 2:
         return "decode_siblings_kernel"
     if mfma_shape and G >= 2:
         return "decode_mfma_kernel"

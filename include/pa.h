@@ -79,16 +79,18 @@ typedef enum {
                                       reads the leading blocks they all hold (the same physical ids)
                                       once per group and head, for all members together; each
                                       member's other tokens are read from its own blocks.  A hint:
-                                      nothing is assumed that the tables do not show.  Taken for
-                                      16-bit caches, head_dim 64, 128 or 256, n * G <= 16 (G =
-                                      num_heads / num_kv_heads) and n * ceil(max_context_len / B)
-                                      <= 4096, with one workgroup per (group, K/V head) over whole
-                                      contexts
+                                      nothing is assumed that the tables do not show.  One
+                                      workgroup per (group, K/V head) takes up to 16 / G members
+                                      (G = num_heads / num_kv_heads): a larger group is cut into
+                                      consecutive sub-groups of u = min(n, floor(16 / G)) members,
+                                      each reading the blocks its members share once.  Taken for
+                                      16-bit caches, head_dim 64, 128 or 256, u >= 2 (G <= 8) and
+                                      u * ceil(max_context_len / B) <= 4096, over whole contexts
                                       (partition_size is then not used); otherwise ignored.  The
                                       arithmetic (fp32 products and softmax, probabilities as hi and
                                       lo 16-bit parts) differs from the multi-head kernel's only by
                                       fp32 rounding.  Each block shared within a group is then
-                                      read once per (group, head): PA_DECODE_SHARED_BLOCKS is not
+                                      read once per (sub-group, head): PA_DECODE_SHARED_BLOCKS is not
                                       needed for it (the streaming loads are faster).  n = 0 or 1:
                                       no grouping; n > 16: PA_ERR_INVALID.  Ignored by
                                       pa_append_decode. */

@@ -266,15 +266,18 @@ int decode_common(void* out, const void* query, const void* key, const void* val
     a.cached_loads = (flags & PA_DECODE_SHARED_BLOCKS) != 0;
     // Sibling groups: a hint the sibling-group kernel takes where it is built
     // (16-bit caches, head_dim 64..256, plain decode), its matrix columns hold
-    // the group (members x query heads per K/V head <= 16) and the members'
-    // block ids fit its LDS; otherwise ignored.
+    // at least two members (members x query heads per K/V head <= 16; a
+    // larger group is cut into sub-groups of 16 / G members) and the
+    // members' block ids fit its LDS; otherwise ignored.
     a.siblings = 0;
+    a.sibling_sub = 0;
     a.sibling_ids = 0;
-    if (siblings >= 2 && !append && (dtype == PA_F16 || dtype == PA_BF16) && head_dim >= 64 &&
-        siblings * (num_heads / num_kv_heads) <= pa::kMaxSiblings) {
+    const int sub = std::min(siblings, pa::kMaxSiblings / (num_heads / num_kv_heads));
+    if (siblings >= 2 && sub >= 2 && !append && (dtype == PA_F16 || dtype == PA_BF16) && head_dim >= 64) {
         const int64_t ids = std::max<int64_t>(1, (static_cast<int64_t>(max_context_len) + block_size - 1) / block_size);
-        if (siblings * ids <= pa::kMaxSiblingIds) {
+        if (sub * ids <= pa::kMaxSiblingIds) {
             a.siblings = siblings;
+            a.sibling_sub = sub;
             a.sibling_ids = static_cast<int>(ids);
         }
     }

@@ -474,13 +474,17 @@ hipError_t launch_decode_t(const DecodeArgs& a) {
     const size_t lds = static_cast<size_t>(a.staged_blocks) * sizeof(int);
     if constexpr (kUseSiblings<T, D, G> && !APPEND) {
         if (a.siblings >= 2) {
-            // One workgroup per (K/V head, group of siblings), whole contexts.
-            const unsigned groups = static_cast<unsigned>((a.num_seqs + a.siblings - 1) / a.siblings);
-            hipLaunchKernelGGL((decode_siblings_kernel<T, D, NT>), dim3(a.num_kv_heads, groups), dim3(kMfmaThreads),
-                               static_cast<size_t>(a.siblings) * a.sibling_ids * sizeof(int), a.stream, out,
+            // One workgroup per (K/V head, sub-group of siblings), whole
+            // contexts.
+            const int64_t groups = (a.num_seqs + a.siblings - 1) / a.siblings;
+            const int64_t per_group = (a.siblings + a.sibling_sub - 1) / a.sibling_sub;
+            const unsigned rows = static_cast<unsigned>(groups * per_group);
+            hipLaunchKernelGGL((decode_siblings_kernel<T, D, NT>), dim3(a.num_kv_heads, rows), dim3(kMfmaThreads),
+                               static_cast<size_t>(a.sibling_sub) * a.sibling_ids * sizeof(int), a.stream, out,
                                static_cast<const bits*>(a.query), static_cast<const bits*>(a.k_cache),
                                static_cast<const bits*>(a.v_cache), a.block_tables, a.context_lens, a.num_seqs,
-                               a.num_kv_heads, G, a.siblings, a.sibling_ids, log2_bs, a.max_blocks_per_seq,
+                               a.num_kv_heads, G, a.siblings, a.sibling_sub, a.sibling_ids, log2_bs,
+                               a.max_blocks_per_seq,
                                a.max_context_len, a.num_blocks, qscale);
             return hipGetLastError();
         }

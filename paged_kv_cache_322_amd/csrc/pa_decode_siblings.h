@@ -12,21 +12,25 @@
 // with the same physical blocks, and reading those blocks once per sample
 // moves the shared prompt through the memory system n times.
 //
-// Design: one workgroup per (group of n consecutive sequences, K/V head).  The
-// group's block-table rows are staged in LDS and compared entry by entry:
-// the leading entries every member holds in common (the same physical
-// block) cover the shared prefix, S = min(J * B, shortest context) tokens
-// (J the common entries).  The prefix is read once: each 16-token K/V tile
-// feeds the 16x16 matrix products of decode_mfma_kernel with the members'
-// queries as the columns (where that kernel puts the G heads of a K/V head;
-// member m takes columns m G .. m G + G - 1, n G <= 16).  Each member's
-// remaining tokens S .. ctx - 1 are then read from its own blocks with only
-// its columns unmasked.  The grouping is a hint: nothing is assumed shared
-// that the tables do not show (no common entries: every token is read
-// privately, the same result), and the arithmetic is decode_mfma_kernel's
-// (fp32 products and softmax, probabilities split into hi and lo 16-bit
-// parts).  Each member's softmax state is per column; the 8
-// wavefronts split the tiles of the whole token list and merge through LDS.
+// Design: one workgroup per (group of n consecutive sequences, K/V head),
+// or per (sub-group, K/V head) where the group has more members than the
+// matrix columns hold: a group is then cut into consecutive sub-groups of
+// `sub` members, each its own workgroup, so a shared block is read once per
+// sub-group.  A workgroup's members' block-table rows are staged in LDS and
+// compared entry by entry: the leading entries every member holds in common
+// (the same physical block) cover the shared prefix, S = min(J * B,
+// shortest context) tokens (J the common entries).  The prefix is read
+// once: each 16-token K/V tile feeds the 16x16 matrix products of
+// decode_mfma_kernel with the members' queries as the columns (where that
+// kernel puts the G heads of a K/V head; member m takes columns
+// m G .. m G + G - 1, members x G <= 16).  Each member's remaining tokens
+// S .. ctx - 1 are then read from its own blocks with only its columns
+// unmasked.  The grouping is a hint: nothing is assumed shared that the
+// tables do not show (no common entries: every token is read privately,
+// the same result), and the arithmetic is decode_mfma_kernel's (fp32
+// products and softmax, probabilities split into hi and lo 16-bit parts).
+// Each member's softmax state is per column; the 8 wavefronts split the
+// tiles of the whole token list and merge through LDS.
 // The members' K/V values must be finite: a masked column still multiplies
 // its zero probabilities with the tile's V rows, so a non-finite value in
 // one member's own tokens can reach its siblings' results.
@@ -45,7 +49,8 @@ __global__ __launch_bounds__(kMfmaThreads, mfma_waves_per_simd(D)) void decode_s
     typename T::bits* __restrict__ out, const typename T::bits* __restrict__ q,
     const typename T::bits* __restrict__ kc, const typename T::bits* __restrict__ vc,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens, int num_seqs,
-    int num_kv_heads, int gq, int group, int ids_per_seq, int log2_bs, int max_blocks_per_seq, int max_context_len,
+    int num_kv_heads, int gq, int group, int sub, int ids_per_seq, int log2_bs, int max_blocks_per_seq,
+    int max_context_len,
     int64_t num_blocks, float qscale) {
     static_assert(sizeof(typename T::bits) == 2, "16-bit caches only");
     static_assert(D == 64 || D == 128 || D == 256, "head_dim");
@@ -63,7 +68,7 @@ __global__ __launch_bounds__(kMfmaThreads, mfma_waves_per_simd(D)) void decode_s
     static_assert(kMfmaTile % RPI == 0, "tile rows per load");
     constexpr size_t kTileBytes = sizeof(uint16_t) * TILE_ELEMS * kMfmaWaves;
     constexpr size_t kMergeBytes = sizeof(float) * kMfmaWaves * HC * DP;
-    extern __shared__ int s_blk[];  // [group][ids_per_seq]: the members' block ids (-1: unusable)
+    extern __shared__ int s_blk[];  // [sub][ids_per_seq]: the members' block ids (-1: unusable)
     __shared__ float s_m[kMfmaWaves][16], s_l[kMfmaWaves][16];
     __shared__ __align__(16) unsigned char s_raw[kTileBytes > kMergeBytes ? kTileBytes : kMergeBytes];
     __shared__ int s_ctx[kMaxSiblings];
@@ -76,8 +81,14 @@ __global__ __launch_bounds__(kMfmaThreads, mfma_waves_per_simd(D)) void decode_s
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int hk = blockIdx.x;               // K/V head
     const int num_heads = num_kv_heads * gq;  // query heads (gq per K/V head)
-    const int s0 = blockIdx.y * group;
-    const int n = min(group, num_seqs - s0);
+    // Grid row y: sub-group y % per_group of group y / per_group; members
+    // s0 .. s0 + n - 1 (a group's last sub-group, and the batch's last
+    // group, may be smaller; a sub-group past the batch's end has none).
+    const int per_group = (group + sub - 1) / sub;
+    const int gi = blockIdx.y / per_group, si = blockIdx.y % per_group;
+    const int s0 = gi * group + si * sub;
+    const int n = min(min(sub, group - si * sub), num_seqs - s0);
+    if (n <= 0) return;  // (workgroup-uniform)
 
     if (tid < n) s_ctx[tid] = context_lens[s0 + tid];
     if (tid == 0) s_bad = 0;

@@ -137,6 +137,7 @@ struct DecodeArgs {
     // groups of `siblings` sequences read their common leading blocks once;
     // 0 = no grouping.  sibling_ids: block ids staged per member.
     int siblings;
+    int sibling_sub;  // members per workgroup: min(siblings, 16 / G)
     int sibling_ids;
     // float [S*H*max_parts*D] then [S*H*max_parts] x 2, then (balanced plan)
     // int32 [S + 2]; NULL when max_parts == 1

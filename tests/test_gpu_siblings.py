@@ -2,8 +2,9 @@
 leading blocks of forked samples read once per group, against the oracle on
 every sequence, and against the ungrouped decode (same definition; the two
 differ by fp32 rounding only).  Multi-head and grouped-query heads,
-unrelated sequences, empty, impossible and out-of-pool entries, and the
-cases where the hint is not taken."""
+groups cut into sub-groups where members x query heads exceed the 16
+matrix columns, unrelated sequences, empty, impossible and out-of-pool
+entries, and the cases where the hint is not taken."""
 import numpy as np
 import pytest
 import torch
@@ -130,16 +131,37 @@ def test_siblings_grouped_query_llama3_8b_shape():
     run_case(case, 4)
 
 
-@pytest.mark.parametrize("what", ["f32", "wide", "d32"])
+@pytest.mark.parametrize("G,group,dtype", [(8, 4, "f16"), (8, 3, "bf16"), (4, 8, "f16"), (2, 16, "bf16"),
+                                           (8, 16, "f16")])
+def test_siblings_subgroups(G, group, dtype):
+    """Members x query heads above the 16 matrix columns: each group is cut
+    into consecutive sub-groups of min(n, 16 // G) members, one workgroup
+    each (a group's last sub-group may be smaller, down to one member)."""
+    case = wl.parallel_sampling(block_size=16, num_prompts=3, samples=max(group, 4), prompt_len=90,
+                                num_heads=2 * G, head_dim=128, pool_tokens=16384, max_suffix=40, num_kv_heads=2,
+                                dtype=dtype)
+    g, out, ref = run_case(case, group, strict=False)
+    sub = 16 // G
+    if group % sub == 0:
+        # Sub-groups of an aligned larger group are the groups of size
+        # `sub`: the same workgroups, the same bits.
+        small = torch.empty_like(g.q)
+        pa().decode(small, g.q, g.kc, g.vc, g.bt, g.ctx, case.scale, case.max_context_len, siblings=sub)
+        torch.cuda.synchronize()
+        assert torch.equal(small.view(torch.int16), out.view(torch.int16))
+
+
+@pytest.mark.parametrize("what", ["f32", "ids", "d32"])
 def test_siblings_hint_ignored_where_not_built(what):
-    """Where the sibling kernel is not built or the group does not fit its
-    16 matrix columns (fp32 caches, members x query heads per K/V head > 16,
-    head_dim below 64) the hint changes nothing: identical bits."""
+    """Where the sibling kernel is not built or the members' block ids do
+    not fit its LDS (fp32 caches, more than 4096 ids per workgroup, head_dim
+    below 64) the hint changes nothing: identical bits."""
     group = 3
     if what == "f32":
         case = wl.random_case(81, 6, 2, 64, 8, "f32", ctx=[5, 40, 41, 9, 100, 3], spare_blocks=2)
-    elif what == "wide":
-        case = wl.random_case(82, 6, 16, 128, 16, "f16", ctx=[5, 40, 41, 9, 100, 3], spare_blocks=2, num_kv_heads=2)
+    elif what == "ids":
+        # B = 1: 3 members x 2100 ids > 4096.
+        case = wl.random_case(82, 6, 2, 64, 1, "f16", ctx=[5, 40, 41, 9, 2100, 3], spare_blocks=2)
     else:
         case = wl.random_case(83, 6, 2, 32, 16, "bf16", ctx=[5, 40, 41, 9, 100, 3], spare_blocks=2)
     g = GpuCase(case)

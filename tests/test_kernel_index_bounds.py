@@ -605,36 +605,39 @@ SIB_MAX, SIB_MAX_IDS, SIB_TILE = 16, 4096, 16
 
 
 def check_siblings_bounds(case, group):
-    """Grid (H, ceil(S / group)); members m < n of group k are sequences
-    group * k + m.  Staged ids s_blk[m * ids + j] for j <= (ctx_m - 1) / B;
-    the shared prefix covers the leading entries all usable members hold in
-    common, capped at the shortest context; tiles of 16 tokens per segment
-    (shared, then each member's own tokens) load token min(t, end - 1) from
-    the segment's member's ids.  Every staged, loaded and written index is
-    in bounds, and each usable member's tokens 0 .. ctx - 1 are each read
-    exactly once, from the physical block its own table names."""
+    """Grid (H, ceil(S / group) * ceil(group / sub)), sub = min(group,
+    16 // G) members per workgroup: grid row y is sub-group y % per_group
+    of group y // per_group, members m < n are sequences s0 + m.  Staged
+    ids s_blk[m * ids + j] for j <= (ctx_m - 1) / B; the shared prefix
+    covers the leading entries all usable members hold in common, capped at
+    the shortest context; tiles of 16 tokens per segment (shared, then each
+    member's own tokens) load token min(t, end - 1) from the segment's
+    member's ids.  Every staged, loaded and written index is in bounds, every
+    sequence is in exactly one workgroup, and each usable member's tokens
+    0 .. ctx - 1 are each read exactly once, from the physical block its own
+    table names."""
     S, H, D = case.q.shape
     N, Hk, B, _ = case.k_cache.shape
     G = H // Hk
-    assert H % Hk == 0 and 2 <= group and group * G <= SIB_MAX  # matrix columns: members x query heads
+    sub = min(group, SIB_MAX // G)
+    assert H % Hk == 0 and 2 <= group and sub >= 2  # matrix columns: members x query heads <= 16
     W = case.block_tables.shape[1]
     maxc = case.max_context_len
     assert maxc <= W * B
     ids = max(1, -(-maxc // B))
-    assert group * ids <= SIB_MAX_IDS
+    assert sub * ids <= SIB_MAX_IDS
     cache_elems = N * Hk * B * D
     RPI = 64 * 8 // D
-    # Longest-first dispatch: grid row r takes the group of rank r in
-    # decreasing total usable context (ties by index): a permutation.
-    G_n = -(-S // group)
-    tot = [sum(int(c) for c in case.context_lens[k * group:(k + 1) * group] if 0 < int(c) <= maxc)
-           for k in range(G_n)]
-    if G_n <= 512:
-        ranks = [sum((tot[j] > tot[k]) or (tot[j] == tot[k] and j < k) for j in range(G_n)) for k in range(G_n)]
-        assert sorted(ranks) == list(range(G_n))
-    for k in range(G_n):
-        s0 = k * group
-        n = min(group, S - s0)
+    per_group = -(-group // sub)
+    rows = -(-S // group) * per_group
+    covered = np.zeros(S, dtype=np.int64)
+    for y in range(rows):
+        gi, si = divmod(y, per_group)
+        s0 = gi * group + si * sub
+        n = min(sub, group - si * sub, S - s0)
+        if n <= 0:
+            continue
+        covered[s0:s0 + n] += 1
         ctx = [int(case.context_lens[s0 + m]) for m in range(n)]
         usable = [0 < c <= maxc for c in ctx]
         blk = np.full((n, ids), -1, dtype=np.int64)
@@ -674,12 +677,14 @@ def check_siblings_bounds(case, group):
                         # the block read is the member's own block for t
                         assert blk[mid, t // B] == blk[m, t // B]
         for m in members:
-            assert (seen[m] == 1).all(), (k, m)
+            assert (seen[m] == 1).all(), (y, m)
         # query operands and output rows: member c // G, query head hk G + c % G
+        assert n * G <= SIB_MAX
         for col in range(n * G):
             row = (s0 + col // G) * H + (Hk - 1) * G + col % G
             assert row < S * H
         assert s0 + n - 1 < S
+    assert (covered == 1).all()
 
 
 @pytest.mark.parametrize("B", [8, 16, 32])
@@ -702,6 +707,14 @@ SIB_CASES = [
 def test_siblings_forked_bounds(seed, group, dtype, D, B, prompts, samples, plen, msuf):
     case = wl.parallel_sampling(block_size=B, num_prompts=prompts, samples=samples, prompt_len=plen, num_heads=2,
                                 head_dim=D, pool_tokens=max(4096, 64 * B), dtype=dtype, max_suffix=msuf)
+    check_siblings_bounds(case, group)
+
+
+@pytest.mark.parametrize("G,group", [(8, 4), (8, 3), (4, 8), (2, 16), (8, 16), (4, 5)])
+def test_siblings_subgroup_bounds(G, group):
+    """Groups cut into sub-groups of min(n, 16 // G) members."""
+    case = wl.parallel_sampling(block_size=16, num_prompts=3, samples=max(group, 4), prompt_len=90,
+                                num_heads=2 * G, head_dim=128, pool_tokens=16384, max_suffix=40, num_kv_heads=2)
     check_siblings_bounds(case, group)
 
 
