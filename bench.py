@@ -162,7 +162,8 @@ def unique_kv_bytes(case):
 # by a copy kernel of known size), per workload at its default plan.
 COUNTER_FILES = {"llama7b": "decode_llama7b_counters.txt", "opt13b": "decode_opt13b_counters.txt",
                  "sampling": "decode_parallel_sampling_b16_counters.txt",
-                 "sampling-gqa": "decode_parallel_sampling_gqa_counters.txt", "opt175b": "decode_opt175b_counters.txt",
+                 "sampling-gqa": "decode_parallel_sampling_gqa_counters.txt",
+                 "sampling-70b": "decode_parallel_sampling_70b_counters.txt", "opt175b": "decode_opt175b_counters.txt",
                  "gqa8b": "decode_gqa_llama3_8b_counters.txt", "gqa70b": "decode_gqa_llama2_70b_tp8_counters.txt",
                  "prefill-llama7b": "prefill_llama7b_counters.txt", "prefill-gqa8b": "prefill_gqa_llama3_8b_counters.txt",
                  "prefill-prompts": "prefill_prompts_bf16_counters.txt"}
