@@ -63,6 +63,26 @@ def test_opt175b_shape():
     full_parity(wl.opt175b_decode(), partitions=(0, 512))
 
 
+@pytest.mark.parametrize("kind", ["mha", "gqa"])
+def test_wide_batch_of_short_contexts(kind):
+    """12000 sequences of 0-96 tokens (some empty): tens of thousands of
+    workgroups in batch order, every sequence against the oracle, at the
+    default plan and split into 32-token partitions (the merge over 24000 or
+    96000 (sequence, head) rows); for the grouped-query batch also as
+    sibling groups of 4 unrelated sequences (nothing shared)."""
+    if kind == "mha":
+        case = wl.random_case(92, 12000, 2, 64, 16, "f16", ctx_range=(0, 96))
+    else:
+        case = wl.random_case(91, 12000, 8, 64, 16, "bf16", ctx_range=(0, 96), num_kv_heads=2)
+    # bf16 rows that see a few keys reach |out| ~ 3, where one output ulp exceeds 2e-3.
+    g, ref = full_parity(case, partitions=(0, 32), strict=case.dtype == "f16")
+    if kind == "gqa":
+        out = torch.full_like(g.q, float("nan"))
+        pa().decode(out, g.q, g.kc, g.vc, g.bt, g.ctx, case.scale, case.max_context_len, siblings=4)
+        torch.cuda.synchronize()
+        assert_close(out, ref, case.dtype, f"{case.name} siblings=4", strict=False)
+
+
 def test_opt175b_tp8_share():
     # One tensor-parallel rank's share of the OPT-175B-shaped layer: 96 heads
     # over 8 GPUs leave 12 per GPU, with the same block tables and lengths.

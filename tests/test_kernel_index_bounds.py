@@ -252,6 +252,10 @@ CASES = [
     ("opt175b-decode", functools.lru_cache(None)(lambda: wl.opt175b_decode(num_heads=2))),
     ("edge", functools.lru_cache(None)(lambda: wl.random_case(21, 5, 2, 64, 1, "bf16", ctx=[0, 1, 2, 513, 700]))),
     ("gqa-llama3-8b", functools.lru_cache(None)(lambda: wl.gqa_config("llama3-8b"))),
+    # 12000 short contexts (some empty): tens of thousands of workgroups in batch order
+    ("wide-mha", functools.lru_cache(None)(lambda: wl.random_case(92, 12000, 2, 64, 16, "f16", ctx_range=(0, 96)))),
+    ("wide-gqa", functools.lru_cache(None)(lambda: wl.random_case(91, 12000, 8, 64, 16, "bf16", ctx_range=(0, 96),
+                                                                  num_kv_heads=2))),
 ]
 
 
@@ -284,7 +288,7 @@ def test_invalid_ids_are_clamped_in_the_model():
 
 
 MFMA_CASES = [c for c in CASES if c[0] in ("llama7b-decode", "opt13b-decode", "opt175b-decode", "edge", "gqa-llama3-8b",
-                                            "sampling-B8", "sampling-B32")]
+                                            "sampling-B8", "sampling-B32", "wide-mha", "wide-gqa")]
 
 
 @pytest.mark.parametrize("name,make", MFMA_CASES, ids=[c[0] for c in MFMA_CASES])
@@ -716,6 +720,12 @@ def test_siblings_subgroup_bounds(G, group):
     case = wl.parallel_sampling(block_size=16, num_prompts=3, samples=max(group, 4), prompt_len=90,
                                 num_heads=2 * G, head_dim=128, pool_tokens=16384, max_suffix=40, num_kv_heads=2)
     check_siblings_bounds(case, group)
+
+
+def test_siblings_wide_batch_bounds():
+    """12000 unrelated short contexts in groups of 4 (G = 4: the 16 columns)."""
+    case = dict(CASES)["wide-gqa"]()
+    check_siblings_bounds(case, 4)
 
 
 def test_siblings_unrelated_and_guarded_bounds():
