@@ -83,6 +83,20 @@ def test_wide_batch_of_short_contexts(kind):
         assert_close(out, ref, case.dtype, f"{case.name} siblings=4", strict=False)
 
 
+@pytest.mark.parametrize("kind", ["mha", "gqa"])
+def test_128k_token_contexts(kind):
+    """Contexts of 131072, 70001, 1 and 0 tokens.  The default plan cuts the
+    longest into 512 partitions of 256 tokens (multi-head: more than the
+    merge kernel's 256 cached weights) or, for one K/V head of 8 query heads,
+    into a balanced split of a few hundred pieces; also 4096-token
+    partitions."""
+    if kind == "mha":
+        case = wl.random_case(93, 4, 4, 128, 16, "f16", ctx=[131072, 70001, 1, 0])
+    else:
+        case = wl.random_case(94, 4, 8, 128, 16, "bf16", ctx=[131072, 70001, 1, 0], num_kv_heads=1)
+    full_parity(case, partitions=(0, 4096))
+
+
 def test_opt175b_tp8_share():
     # One tensor-parallel rank's share of the OPT-175B-shaped layer: 96 heads
     # over 8 GPUs leave 12 per GPU, with the same block tables and lengths.

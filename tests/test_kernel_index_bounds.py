@@ -256,6 +256,11 @@ CASES = [
     ("wide-mha", functools.lru_cache(None)(lambda: wl.random_case(92, 12000, 2, 64, 16, "f16", ctx_range=(0, 96)))),
     ("wide-gqa", functools.lru_cache(None)(lambda: wl.random_case(91, 12000, 8, 64, 16, "bf16", ctx_range=(0, 96),
                                                                   num_kv_heads=2))),
+    # 128k-token contexts: hundreds of partitions or pieces per context
+    ("long-mha", functools.lru_cache(None)(lambda: wl.random_case(93, 4, 4, 128, 16, "f16",
+                                                                  ctx=[131072, 70001, 1, 0]))),
+    ("long-gqa", functools.lru_cache(None)(lambda: wl.random_case(94, 4, 8, 128, 16, "bf16",
+                                                                  ctx=[131072, 70001, 1, 0], num_kv_heads=1))),
 ]
 
 
@@ -288,7 +293,8 @@ def test_invalid_ids_are_clamped_in_the_model():
 
 
 MFMA_CASES = [c for c in CASES if c[0] in ("llama7b-decode", "opt13b-decode", "opt175b-decode", "edge", "gqa-llama3-8b",
-                                            "sampling-B8", "sampling-B32", "wide-mha", "wide-gqa")]
+                                            "sampling-B8", "sampling-B32", "wide-mha", "wide-gqa", "long-mha",
+                                            "long-gqa")]
 
 
 @pytest.mark.parametrize("name,make", MFMA_CASES, ids=[c[0] for c in MFMA_CASES])
