@@ -73,6 +73,19 @@ def check(case, seqs=None, strict=True, max_query_len=None):
     return run
 
 
+@pytest.mark.parametrize("which", ["f16-gqa", "bf16"])
+def test_prefill_long_cached_prefix(which):
+    """Chunks over cached prefixes of 60000 and 65000 tokens (about 1900 and
+    2000 key tiles per workgroup, 3763 and 4094 staged block ids against the
+    limit of 4096), beside a whole prompt, a 129-row chunk (a 128-row tile
+    plus one row) and a 28-row chunk."""
+    if which == "f16-gqa":
+        case = wl.random_prefill_case(501, [60000, 0, 3000], [200, 300, 129], 4, 128, 16, "f16", num_kv_heads=2)
+    else:
+        case = wl.random_prefill_case(502, [65000, 100], [500, 28], 2, 64, 16, "bf16")
+    check(case, strict=case.dtype == "f16")
+
+
 def test_prefill_llama7b_chunked():
     check(wl.prefill_config("llama7b"))
 

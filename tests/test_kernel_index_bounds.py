@@ -560,6 +560,11 @@ PF_CASES = [
     ("prefill-prompts", functools.lru_cache(None)(lambda: wl.prefill_config("prompts"))),
     ("prefill-ragged", functools.lru_cache(None)(
         lambda: wl.random_prefill_case(31, [0, 1, 63, 200, 5], [1, 64, 65, 130, 3], 4, 64, 1, "bf16", num_kv_heads=2))),
+    # cached prefixes of 60000 and 65000 tokens: up to 4094 staged block ids
+    ("prefill-long-f16", functools.lru_cache(None)(
+        lambda: wl.random_prefill_case(501, [60000, 0, 3000], [200, 300, 129], 4, 128, 16, "f16", num_kv_heads=2))),
+    ("prefill-long-bf16", functools.lru_cache(None)(
+        lambda: wl.random_prefill_case(502, [65000, 100], [500, 28], 2, 64, 16, "bf16"))),
 ]
 
 
