@@ -318,8 +318,12 @@ def main():
     result["hbm_read_probe"] = probe
     best = probe["best_GB/s"]
     result["roofline"]["frac_of_read_probe"] = round(result["roofline"]["achieved"] / best, 4)
+    result["roofline"]["frac_of_scattered_read_probe"] = round(
+        result["roofline"]["achieved"] / probe["scattered_best_GB/s"], 4)
     for extra in result.get("configs", {}).values():
         extra["roofline_frac_of_read_probe"] = round(extra["roofline_achieved"] / best, 4)
+        extra["roofline_frac_of_scattered_read_probe"] = round(
+            extra["roofline_achieved"] / probe["scattered_best_GB/s"], 4)
     print(json.dumps(result), flush=True)
 
 
@@ -333,30 +337,35 @@ def hbm_read_probe(pa, torch, dev, gib=4, reps=10):
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     sink = torch.zeros(cus * 8, dtype=torch.int32, device=dev)
     runs = []
-    # (non-temporal, workgroups per CU, contiguous run bytes; 0 = grid-stride)
-    shapes = [(True, 8, 0), (False, 8, 0), (True, 2, 65536), (True, 4, 65536), (True, 8, 65536),
-              (True, 4, 8192), (True, 8, 8192), (True, 4, 262144), (False, 4, 65536)]
-    for nt, per_cu, run in shapes:
+    # (non-temporal, workgroups per CU, contiguous run bytes (0 = grid-stride), runs in a scattered order)
+    shapes = [(True, 8, 0, False), (False, 8, 0, False), (True, 2, 65536, False), (True, 4, 65536, False),
+              (True, 8, 65536, False), (True, 4, 8192, False), (True, 8, 8192, False), (True, 4, 262144, False),
+              (False, 4, 65536, False), (True, 4, 8192, True), (True, 8, 8192, True), (True, 4, 16384, True)]
+    for nt, per_cu, run, sc in shapes:
         wgs = cus * per_cu
         for _ in range(3):
-            pa.hbm_read_probe(buf, sink, wgs, nontemporal=nt, run_bytes=run)
+            pa.hbm_read_probe(buf, sink, wgs, nontemporal=nt, run_bytes=run, scattered=sc)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         a.record()
         for _ in range(reps):
-            pa.hbm_read_probe(buf, sink, wgs, nontemporal=nt, run_bytes=run)
+            pa.hbm_read_probe(buf, sink, wgs, nontemporal=nt, run_bytes=run, scattered=sc)
         b.record()
         torch.cuda.synchronize()
         us = a.elapsed_time(b) / reps * 1e3
-        runs.append({"nontemporal": nt, "workgroups": wgs, "run_bytes": run, "us": round(us, 1),
+        runs.append({"nontemporal": nt, "workgroups": wgs, "run_bytes": run, "scattered": sc, "us": round(us, 1),
                      "GB/s": round(buf.numel() / us / 1e3, 1)})
     del buf
     best = max(runs, key=lambda r: r["GB/s"])
-    log(f"HBM read probe: best {best}")
-    return {"bytes": gib << 30, "best_GB/s": best["GB/s"], "best": best, "runs": runs,
+    best_sc = max((r for r in runs if r["scattered"]), key=lambda r: r["GB/s"])
+    log(f"HBM read probe: best {best}; scattered 8-16 KB runs {best_sc}")
+    return {"bytes": gib << 30, "best_GB/s": best["GB/s"], "best": best,
+            "scattered_best_GB/s": best_sc["GB/s"], "scattered_best": best_sc, "runs": runs,
             "note": "pa_hbm_read_probe: every byte of a 4 GiB buffer read once per launch (512-thread "
                     "workgroups, 16-byte loads, four in flight per lane; grid-stride or contiguous runs per "
-                    "workgroup); HIP events around 10 launches; the best shape is the ceiling"}
+                    "workgroup, in order or scattered as paged blocks are); HIP events around 10 launches; the best "
+                    "shape is the ceiling, and the best scattered 8-16 KB-run shape the ceiling for decode's "
+                    "access pattern"}
 
 
 def bench_decode(args, config, case, pa, torch, dev, full=True):

@@ -20,6 +20,10 @@ extern "C" {
 #endif
 
 #define PA_PROBE_NONTEMPORAL 1u /* non-temporal loads (the decode kernels' streaming loads) */
+#define PA_PROBE_SCATTERED 2u   /* runs visited in a scattered order, as paged blocks lie in the
+                                   pool: run r read in place of run (r * 0x9E3779B1) mod (number
+                                   of runs); needs run_bytes > 0 dividing bytes into a power-of-two
+                                   number of runs */
 
 /*
  * pa_hbm_read_probe - read `bytes` bytes of device memory once.
@@ -37,7 +41,9 @@ extern "C" {
  *                  bytes and workgroup w reads runs w, w + num_workgroups, ...
  *                  each from start to end, as a decode workgroup reads whole
  *                  K/V blocks
- *   flags          0 or PA_PROBE_NONTEMPORAL (other bits: PA_ERR_INVALID)
+ *   flags          PA_PROBE_NONTEMPORAL and/or PA_PROBE_SCATTERED (other bits:
+ *                  PA_ERR_INVALID; SCATTERED with run_bytes 0, or with a run
+ *                  count that is not a power of two: PA_ERR_INVALID)
  *
  * Enqueued on `stream` (a hipStream_t); nothing allocated or synchronised.
  * Returns PA_OK, PA_ERR_NULL, PA_ERR_INVALID (sizes, alignment, run length, flags) or

@@ -356,11 +356,12 @@ def swap_blocks(dst_k: torch.Tensor, dst_v: torch.Tensor, src_k: torch.Tensor, s
 
 
 def hbm_read_probe(buf: torch.Tensor, sink: torch.Tensor, num_workgroups: int, nontemporal: bool = True,
-                   run_bytes: int = 0, magic: int = 0x5A17C0DE, stream=None) -> None:
+                   run_bytes: int = 0, magic: int = 0x5A17C0DE, stream=None, scattered: bool = False) -> None:
     """Read every byte of ``buf`` once (``pa_hbm_read_probe``, a measurement
     aid): the achievable streaming-read rate.  ``run_bytes`` 0 strides the
     workgroups over the whole buffer; a multiple of 8192 gives each workgroup
-    whole contiguous runs of that size.  ``sink`` is a uint32-sized device
+    whole contiguous runs of that size (``scattered``: visited in a scattered
+    order, as paged blocks lie in the pool).  ``sink`` is a uint32-sized device
     tensor of ``num_workgroups`` elements, written only where a workgroup's
     data XOR to ``magic``."""
     _dev(buf, "buf")
@@ -368,6 +369,7 @@ def hbm_read_probe(buf: torch.Tensor, sink: torch.Tensor, num_workgroups: int, n
     if sink.numel() * sink.element_size() < 4 * num_workgroups:
         raise ValueError("sink must hold num_workgroups uint32 values")
     st = lib.pa_hbm_read_probe(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(),
-                               int(num_workgroups), int(run_bytes), int(magic) & 0xFFFFFFFF, 1 if nontemporal else 0,
+                               int(num_workgroups), int(run_bytes), int(magic) & 0xFFFFFFFF,
+                               (1 if nontemporal else 0) | (2 if scattered else 0),
                                _stream_handle(buf.device, stream))
     _check(st, "pa_hbm_read_probe")

@@ -15,7 +15,7 @@ constexpr int kProbeUnroll = 4;  // independent 16-byte loads in flight per lane
 template <int NT>
 __global__ __launch_bounds__(kProbeThreads) void hbm_read_probe_kernel(const uint4* __restrict__ src, int64_t n16,
                                                                        int64_t chunk16, uint32_t* __restrict__ sink,
-                                                                       uint32_t magic) {
+                                                                       uint32_t magic, int scattered) {
     uint32_t acc = 0;
     if (chunk16 == 0) {
         // Grid-stride over 16-byte chunks: consecutive lanes read consecutive
@@ -38,10 +38,15 @@ __global__ __launch_bounds__(kProbeThreads) void hbm_read_probe_kernel(const uin
         // workgroup w reads runs w, w + grid, w + 2 grid, ... of chunk16
         // 16-byte chunks each (a multiple of the workgroup's 512), lanes on
         // consecutive chunks, kProbeUnroll loads in flight per lane.
+        // Scattered: the run index goes through the bijection r -> r *
+        // 0x9E3779B1 mod nruns (an odd multiplier; nruns a power of two, host
+        // check), so consecutive runs of a workgroup, and the runs read at
+        // one time, lie at scattered addresses, as paged blocks do.
         const int64_t nruns = (n16 + chunk16 - 1) / chunk16;
         for (int64_t r = blockIdx.x; r < nruns; r += gridDim.x) {
-            const int64_t end = min(n16, (r + 1) * chunk16);
-            int64_t i = r * chunk16 + threadIdx.x;
+            const int64_t rr = scattered ? ((r * int64_t{0x9E3779B1}) & (nruns - 1)) : r;
+            const int64_t end = min(n16, (rr + 1) * chunk16);
+            int64_t i = rr * chunk16 + threadIdx.x;
             for (; i + (kProbeUnroll - 1) * kProbeThreads < end; i += kProbeUnroll * kProbeThreads) {
                 uint4 v[kProbeUnroll];
 #pragma unroll
@@ -67,16 +72,23 @@ extern "C" int pa_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, 
     if (!src || !sink) return PA_ERR_NULL;
     if (bytes == 0 || bytes % 16 || (reinterpret_cast<uintptr_t>(src) & 15u) || num_workgroups <= 0 ||
         num_workgroups > 65535 || run_bytes % (16 * kProbeThreads) ||
-        (flags & ~static_cast<uint32_t>(PA_PROBE_NONTEMPORAL)))
+        (flags & ~static_cast<uint32_t>(PA_PROBE_NONTEMPORAL | PA_PROBE_SCATTERED)))
         return PA_ERR_INVALID;
     const int64_t n16 = static_cast<int64_t>(bytes / 16);
     const int64_t run16 = static_cast<int64_t>(run_bytes / 16);
+    const int scattered = (flags & PA_PROBE_SCATTERED) ? 1 : 0;
+    if (scattered) {
+        // Whole runs only, and a power-of-two count of them (the bijection).
+        if (run16 == 0 || n16 % run16) return PA_ERR_INVALID;
+        const int64_t nruns = n16 / run16;
+        if (nruns & (nruns - 1)) return PA_ERR_INVALID;
+    }
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (flags & PA_PROBE_NONTEMPORAL)
         hipLaunchKernelGGL(hbm_read_probe_kernel<1>, dim3(num_workgroups), dim3(kProbeThreads), 0, s,
-                           static_cast<const uint4*>(src), n16, run16, sink, magic);
+                           static_cast<const uint4*>(src), n16, run16, sink, magic, scattered);
     else
         hipLaunchKernelGGL(hbm_read_probe_kernel<0>, dim3(num_workgroups), dim3(kProbeThreads), 0, s,
-                           static_cast<const uint4*>(src), n16, run16, sink, magic);
+                           static_cast<const uint4*>(src), n16, run16, sink, magic, scattered);
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }

@@ -284,7 +284,10 @@ def test_hbm_read_probe_host_checks():
     assert f(P, 64, P, 0, 0, 0, 0, None) == INVALID
     assert f(P, 64, P, 65536, 0, 0, 0, None) == INVALID
     assert f(P, 64, P, 4, 4096, 0, 0, None) == INVALID  # runs not a multiple of 8192 bytes
-    assert f(P, 64, P, 4, 0, 0, 2, None) == INVALID  # unknown flag
+    assert f(P, 64, P, 4, 0, 0, 4, None) == INVALID  # unknown flag
+    assert f(P, 3 * 8192, P, 4, 8192, 0, 2, None) == INVALID  # scattered: 3 runs, not a power of two
+    assert f(P, 8192 + 16, P, 4, 8192, 0, 2, None) == INVALID  # scattered: a partial run
+    assert f(P, 4 * 8192, P, 4, 0, 0, 2, None) == INVALID  # scattered needs runs
 
 
 def test_decode_static_rejects_what_the_scratch_cannot_hold():
