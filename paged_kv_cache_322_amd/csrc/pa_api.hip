@@ -46,33 +46,42 @@ size_t workspace_bytes_for(int64_t num_seqs, int64_t num_heads, int64_t head_dim
            (balanced ? sizeof(int32_t) : 0);
 }
 
-// Compute units of the current device, queried once per device (256 if the
-// query fails).
-int device_cus() {
-    static std::atomic<int> cached_cus[64];
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
-        int n = cached_cus[dev].load(std::memory_order_relaxed);
-        if (n == 0) {
-            if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
-                (void)hipGetLastError();
-                n = 256;
-            }
-            cached_cus[dev].store(n, std::memory_order_relaxed);
-        }
-        cus = n;
-    } else {
+// The device a call's kernels run on: the stream's, or the current device
+// for the null stream (or a handle the query does not take); -1 if neither
+// can be found.
+int launch_device(void* stream) {
+    int dev = -1;
+    if (stream && hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev) == hipSuccess) return dev;
+    if (stream) (void)hipGetLastError();
+    if (hipGetDevice(&dev) != hipSuccess) {
         (void)hipGetLastError();
+        return -1;
     }
-    return cus;
+    return dev;
 }
 
-// Workgroups of a balanced split on the current device: kBalancedWgsPerCu
-// per compute unit, half that for head_dim 256 (whose kernel fits 2
-// wavefronts per SIMD, not 4).
-int balanced_workgroups(int32_t head_dim) {
+// Compute units of device `dev`, queried once per device (256 if the query
+// fails).
+int device_cus(int dev) {
+    static std::atomic<int> cached_cus[64];
+    if (dev < 0 || dev >= 64) return 256;
+    int n = cached_cus[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+            (void)hipGetLastError();
+            n = 256;
+        }
+        cached_cus[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// Workgroups of a balanced split on device `dev`: kBalancedWgsPerCu per
+// compute unit, half that for head_dim 256 (whose kernel fits 2 wavefronts
+// per SIMD, not 4).
+int balanced_workgroups(int32_t head_dim, int dev) {
     const int per_cu = head_dim <= 128 ? pa::kBalancedWgsPerCu : (pa::kBalancedWgsPerCu + 1) / 2;
-    return device_cus() * per_cu;
+    return device_cus(dev) * per_cu;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
@@ -145,20 +154,28 @@ constexpr int kMaxDevices = 64;
 std::atomic<void*> g_scratch_ptr[kMaxDevices];
 std::mutex g_scratch_mutex;
 
-// Device address of the current device's scratch, looked up once per device
-// (with that device current); NULL if the lookup fails.
-void* device_scratch() {
-    int dev = -1;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
-        (void)hipGetLastError();
-        return nullptr;
-    }
+// Device address of device `dev`'s scratch (the device the call's stream
+// runs on), looked up once per device with that device current (the
+// caller's current device is restored); NULL if the lookup fails.
+void* device_scratch(int dev) {
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
     void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
     if (p) return p;
     std::lock_guard<std::mutex> lock(g_scratch_mutex);
     p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
     if (!p) {
-        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) (void)hipSetDevice(cur);
+        if (e != hipSuccess || !p) {
             (void)hipGetLastError();
             return nullptr;
         }
@@ -213,7 +230,7 @@ int decode_common(void* out, const void* query, const void* key, const void* val
     if (need && static_scratch) {
         // pa_decode_static: the library's per-GPU scratch stands in for the workspace.
         if (need > static_cast<size_t>(PA_STATIC_SCRATCH_BYTES)) return PA_ERR_SCRATCH;
-        workspace = device_scratch();
+        workspace = device_scratch(launch_device(stream));
         if (!workspace) return PA_ERR_HIP;
         workspace_bytes = PA_STATIC_SCRATCH_BYTES;
     }
@@ -248,14 +265,16 @@ int decode_common(void* out, const void* query, const void* key, const void* val
     // Grouped heads under longest-first order: pair long and short contexts
     // in the CUs' first two workgroup slots (grid rows hold num_kv_heads
     // workgroups each).
-    a.pair_rows = (plan.longest_first && num_heads > num_kv_heads) ? std::max(1, device_cus() / num_kv_heads) : 0;
+    const int dev = launch_device(stream);
+    a.pair_rows =
+        (plan.longest_first && num_heads > num_kv_heads) ? std::max(1, device_cus(dev) / num_kv_heads) : 0;
     a.balanced = plan.balanced;
     a.balanced_wgs = 0;
     a.staged_balanced = 0;
     if (plan.balanced) {
         // A workgroup's piece has at most min(C, the context) tokens, C as
         // the kernel computes it (its total is at most pairs * max_context_len).
-        a.balanced_wgs = balanced_workgroups(head_dim);
+        a.balanced_wgs = balanced_workgroups(head_dim, dev);
         const int64_t pairs = static_cast<int64_t>(num_seqs) * num_kv_heads;
         const int64_t slots = std::max<int64_t>(1, a.balanced_wgs - pairs / 2);
         int64_t share = (pairs * max_context_len + slots - 1) / slots;
