@@ -240,8 +240,7 @@ int pa_append_decode(void* out, const void* query, const void* key, const void* 
  * device memory: a file-scope array of PA_STATIC_SCRATCH_BYTES, one copy per
  * GPU the library runs on, kept until the process ends (the copy of the GPU
  * that `stream` belongs to, or of the current GPU for the null stream).
- * Nothing is
- * allocated or freed by the call.  A call whose plan needs more than
+ * Nothing is allocated or freed by the call.  A call whose plan needs more than
  * PA_STATIC_SCRATCH_BYTES (pa_decode_workspace_size of the same arguments)
  * returns PA_ERR_SCRATCH before anything is enqueued.  The scratch needs no
  * initialisation (every partial is written before it is read).
