@@ -131,14 +131,15 @@ def test_siblings_grouped_query_llama3_8b_shape():
     run_case(case, 4)
 
 
-@pytest.mark.parametrize("G,group,dtype", [(8, 4, "f16"), (8, 3, "bf16"), (4, 8, "f16"), (2, 16, "bf16"),
-                                           (8, 16, "f16")])
-def test_siblings_subgroups(G, group, dtype):
+@pytest.mark.parametrize("G,group,dtype,D", [(8, 4, "f16", 128), (8, 3, "bf16", 128), (4, 8, "f16", 128),
+                                             (2, 16, "bf16", 128), (8, 16, "f16", 128), (8, 4, "bf16", 256),
+                                             (4, 6, "f16", 64)])
+def test_siblings_subgroups(G, group, dtype, D):
     """Members x query heads above the 16 matrix columns: each group is cut
     into consecutive sub-groups of min(n, 16 // G) members, one workgroup
     each (a group's last sub-group may be smaller, down to one member)."""
     case = wl.parallel_sampling(block_size=16, num_prompts=3, samples=max(group, 4), prompt_len=90,
-                                num_heads=2 * G, head_dim=128, pool_tokens=16384, max_suffix=40, num_kv_heads=2,
+                                num_heads=2 * G, head_dim=D, pool_tokens=16384, max_suffix=40, num_kv_heads=2,
                                 dtype=dtype)
     g, out, ref = run_case(case, group, strict=False)
     sub = 16 // G

@@ -725,11 +725,12 @@ def test_siblings_forked_bounds(seed, group, dtype, D, B, prompts, samples, plen
     check_siblings_bounds(case, group)
 
 
-@pytest.mark.parametrize("G,group", [(8, 4), (8, 3), (4, 8), (2, 16), (8, 16), (4, 5)])
-def test_siblings_subgroup_bounds(G, group):
+@pytest.mark.parametrize("G,group,D", [(8, 4, 128), (8, 3, 128), (4, 8, 128), (2, 16, 128), (8, 16, 128),
+                                       (4, 5, 128), (8, 4, 256), (4, 6, 64)])
+def test_siblings_subgroup_bounds(G, group, D):
     """Groups cut into sub-groups of min(n, 16 // G) members."""
     case = wl.parallel_sampling(block_size=16, num_prompts=3, samples=max(group, 4), prompt_len=90,
-                                num_heads=2 * G, head_dim=128, pool_tokens=16384, max_suffix=40, num_kv_heads=2)
+                                num_heads=2 * G, head_dim=D, pool_tokens=16384, max_suffix=40, num_kv_heads=2)
     check_siblings_bounds(case, group)
 
 
