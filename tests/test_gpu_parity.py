@@ -4,15 +4,12 @@ Tolerances: max-abs 2e-3 for f16/bf16 inputs and 1e-5 for f32 inputs on the
 attention output; cache writes and block copies bit-exact over the whole
 pool (compared as integers, so NaN canaries compare too).
 """
-import math
-
 import numpy as np
 import pytest
 import torch
 
 import workloads as wl
-from gpu_helpers import (GpuCase, assert_close, assert_pool_equal, log, oracle_decode, oracle_steps, pa,
-                         to_gpu)
+from gpu_helpers import GpuCase, assert_close, assert_pool_equal, log, oracle_decode, oracle_steps, pa
 
 pytestmark = pytest.mark.gpu
 

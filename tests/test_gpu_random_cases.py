@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import workloads as wl
-from gpu_helpers import GpuCase, assert_close, assert_pool_equal, log, oracle_decode, oracle_steps, pa, to_gpu
+from gpu_helpers import GpuCase, assert_close, assert_pool_equal, log, oracle_decode, oracle_steps, pa
 
 pytestmark = pytest.mark.gpu
 

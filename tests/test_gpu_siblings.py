@@ -5,7 +5,6 @@ differ by fp32 rounding only).  Multi-head and grouped-query heads,
 groups cut into sub-groups where members x query heads exceed the 16
 matrix columns, unrelated sequences, empty, impossible and out-of-pool
 entries, and the cases where the hint is not taken."""
-import numpy as np
 import pytest
 import torch
 
