@@ -342,7 +342,7 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pairs, int
  *   max_context_len  host upper bound of every ctx_s; <= max_blocks_per_seq *
  *                  block_size and ceil(max_context_len / block_size) <= 4096
  *
- * Built for dtype PA_F16 and PA_BF16 with head_dim 64 or 128 (others:
+ * Built for dtype PA_F16 and PA_BF16 with head_dim 64, 128 or 256 (others:
  * PA_ERR_UNSUPPORTED).  query, out and the caches 16-byte aligned.  Ownership,
  * streams and host-side errors as for pa_decode.  Device-side guards (the
  * kernel checks what it reads from device memory, nothing faults):
@@ -353,7 +353,8 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pairs, int
  *   - n_s > ctx_s, ctx_s > max_context_len or n_s > max_query_len gives NaN
  *     in every row of that chunk;
  *   - a needed block id outside [0, num_blocks) gives NaN for the rows of
- *     that (128-row tile, head) without reading outside the caches.
+ *     that (row tile, head) without reading outside the caches (tiles of
+ *     128 rows, 64 at head_dim 256).
  * Chunks of a query_start that is not non-decreasing may overlap; their
  * rows are then undefined (some may be left unwritten).
  */

@@ -279,7 +279,7 @@ def prefill(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor, val
             max_query_len: int, max_context_len: int, stream=None) -> torch.Tensor:
     """Causal attention of packed query chunks over the paged context (``pa_prefill``).
 
-    out, query [T, H, D] (f16/bf16, D in {64, 128}); key_cache, value_cache
+    out, query [T, H, D] (f16/bf16, D in {64, 128, 256}); key_cache, value_cache
     [N, Hk, B, D] with the chunks' K/V already written; block_tables int32
     [S, W]; context_lens int32 [S] (chunks included); query_start int32
     [S + 1] (sequence s owns query rows query_start[s] .. query_start[s+1]-1,

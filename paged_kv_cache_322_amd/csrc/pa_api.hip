@@ -392,7 +392,7 @@ extern "C" int pa_prefill(void* out, const void* query, const void* k_cache, con
                           int32_t num_seqs, int32_t num_tokens, int32_t num_heads, int32_t num_kv_heads,
                           int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int32_t max_query_len,
                           int32_t max_context_len, int64_t num_blocks, float scale, int32_t dtype, void* stream) {
-    if ((dtype != PA_F16 && dtype != PA_BF16) || (head_dim != 64 && head_dim != 128) ||
+    if ((dtype != PA_F16 && dtype != PA_BF16) || (head_dim != 64 && head_dim != 128 && head_dim != 256) ||
         !supported_block_size(block_size))
         return PA_ERR_UNSUPPORTED;
     if (num_seqs == 0 || num_tokens == 0) return PA_OK;  // nothing to compute
@@ -412,9 +412,12 @@ extern "C" int pa_prefill(void* out, const void* query, const void* k_cache, con
     const int64_t ids = (static_cast<int64_t>(max_context_len) + block_size - 1) / block_size;
     if (ids > pa::kMaxPrefillIds) return PA_ERR_INVALID;
     if (max_query_len == 0) return PA_OK;
-    // One workgroup per (sequence, query head, 128-row tile), units padded to a multiple of 8.
+    // One workgroup per (sequence, query head, row tile: 128 rows, 64 at
+    // head_dim 256), units padded to a multiple of 8.
+    const int64_t tile_rows = head_dim <= 128 ? 128 : 64;
     const int64_t units = (static_cast<int64_t>(num_seqs) * num_kv_heads + 7) / 8 * 8;
-    if (units * (num_heads / num_kv_heads) * ((static_cast<int64_t>(max_query_len) + 127) / 128) > 0x7FFFFFFF)
+    if (units * (num_heads / num_kv_heads) * ((static_cast<int64_t>(max_query_len) + tile_rows - 1) / tile_rows) >
+        0x7FFFFFFF)
         return PA_ERR_INVALID;
 
     pa::PrefillArgs a;

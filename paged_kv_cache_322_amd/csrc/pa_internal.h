@@ -159,7 +159,7 @@ constexpr int kMaxSiblingIds = 4096;
 inline bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
 
 // Prefill (pa_prefill): causal attention of packed query chunks over the
-// paged context.  16-bit caches, head_dim 64 or 128.
+// paged context.  16-bit caches, head_dim 64, 128 or 256.
 constexpr int kMaxPrefillIds = 4096;  // block ids of one context staged in LDS (16 KB)
 
 struct PrefillArgs {

@@ -15,7 +15,9 @@
 // against N keys is M*N*D multiply-adds for (M + N)*D loaded elements, so the
 // kernel is matrix-core bound.  Design (one workgroup = 4 wavefronts = 128
 // query rows of one sequence and one query head; a wavefront owns two blocks
-// of 16 rows, so every K and V operand it reads from LDS feeds two products):
+// of 16 rows, so every K and V operand it reads from LDS feeds two products;
+// at head_dim 256 one block, 64 rows per workgroup, as the accumulators and
+// query operands per row are twice as large):
 //
 //   * the K and V rows of a 32-key tile are gathered through the block table
 //     (ids staged in LDS once) into double-buffered LDS, the next tile's
@@ -79,8 +81,11 @@ namespace {
 
 constexpr int kPfWaves = 4;
 constexpr int kPfThreads = kPfWaves * kWave;
-constexpr int kPfBlocks = 2;                        // 16-row blocks per wavefront
-constexpr int kPfRows = 16 * kPfBlocks * kPfWaves;  // query rows per workgroup
+// 16-row blocks per wavefront: two up to head_dim 128, so every K/V operand
+// read from LDS feeds two products; one at head_dim 256, whose accumulators
+// and query operands are twice as large per row.
+constexpr int pf_blocks(int D) { return D <= 128 ? 2 : 1; }
+constexpr int pf_rows(int D) { return 16 * pf_blocks(D) * kPfWaves; }  // query rows per workgroup
 constexpr int kPfKeys = 32;                         // keys per tile
 constexpr int kXcds = 8;                            // MI355X: XCDs, each with its own L2
 constexpr int kPfPad = 16;                          // LDS row padding (elements): 32 bytes
@@ -146,7 +151,9 @@ __device__ __forceinline__ float dot2_f16_ones(uint32_t x, float acc) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, x), one, acc, false);
 }
 
-constexpr int kPfWavesPerSimd = 3;  // register budget: <= 168 VGPRs, 3 workgroups per CU
+// Register budget: <= 168 VGPRs for 3 workgroups per CU up to head_dim 128;
+// at 256 the tiles' 70 KB of LDS allow two workgroups per CU, so <= 256.
+constexpr int pf_waves_per_simd(int D) { return D <= 128 ? 3 : 2; }
 
 // gfx950 transposing LDS read (ds_read_b64_tr_b16).  In each group of 16
 // lanes, lanes 4r .. 4r + 3 each point at 4 consecutive 16-bit elements, the
@@ -165,7 +172,7 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
 constexpr int kPfOrderTileMajor = 0;  // query tiles last first, every unit's tiles launched (padded)
 constexpr int kPfOrderUnitMajor = 1;  // units by decreasing context, all of a unit's tiles adjacent
 constexpr int kPfOrderPacked = 2;     // tile levels last first, only tiles that hold rows
-constexpr int kPfMaxLevels = 64;      // packed order: at most this many 128-row tiles per chunk
+constexpr int kPfMaxLevels = 64;      // packed order: at most this many row tiles per chunk
 static_assert(kPfMaxLevels <= kPfThreads, "one thread counts one tile level");
 
 // Rows of sequence s whose chunk lies inside the call's rows [0, num_tokens):
@@ -176,7 +183,7 @@ __device__ __forceinline__ int chunk_rows(const int32_t* __restrict__ query_star
 }
 
 template <class T, int D>
-__global__ __launch_bounds__(kPfThreads, kPfWavesPerSimd) void prefill_kernel(
+__global__ __launch_bounds__(kPfThreads, pf_waves_per_simd(D)) void prefill_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ query_start, int num_heads,
@@ -184,7 +191,8 @@ __global__ __launch_bounds__(kPfThreads, kPfWavesPerSimd) void prefill_kernel(
     int num_units, int num_tokens, int max_query_len, int order, float qscale) {
     using Sh = PfShape<D>;
     constexpr int KS = Sh::KS, E = Sh::E, LD = Sh::LD, CPR = Sh::CPR, CPT = Sh::CPT;
-    constexpr int RB = kPfBlocks;
+    constexpr int RB = pf_blocks(D);
+    constexpr int kPfRows = pf_rows(D);
     using Ops = MfmaOps<T>;
 
     extern __shared__ int s_ids[];  // block ids of keys 0 .. kv_end - 1 (dynamic size)
@@ -536,6 +544,7 @@ __global__ __launch_bounds__(kPfThreads, kPfWavesPerSimd) void prefill_kernel(
 
 template <class T, int D>
 hipError_t launch_prefill_t(const PrefillArgs& a) {
+    constexpr int kPfRows = pf_rows(D);
     const int log2_bs = __builtin_ctz(static_cast<unsigned>(a.block_size));
     const float qscale = a.scale * 1.4426950408889634f;  // log2(e)
     const int n_qtiles = (a.max_query_len + kPfRows - 1) / kPfRows;
@@ -577,6 +586,7 @@ hipError_t launch_prefill_dim(const PrefillArgs& a) {
     switch (a.head_dim) {
         case 64: return launch_prefill_t<T, 64>(a);
         case 128: return launch_prefill_t<T, 128>(a);
+        case 256: return launch_prefill_t<T, 256>(a);
         default: return hipErrorInvalidValue;
     }
 }

@@ -220,7 +220,8 @@ def test_prefill_host_checks():
     assert pf(mq=0) == OK  # no query rows anywhere
     assert pf(dtype=0) == UNSUP  # fp32 prefill not built
     assert pf(dtype=3) == UNSUP
-    assert pf(D=256) == UNSUP
+    assert pf(D=256, out=0) == NULL  # head_dim 256 is built: validation goes on
+    assert pf(D=512) == UNSUP
     assert pf(D=32) == UNSUP
     assert pf(B=12) == UNSUP
     assert pf(out=0) == NULL

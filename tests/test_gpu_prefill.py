@@ -110,6 +110,9 @@ SWEEP = [
     ("f16", 6, 3, 128, 4, [0], [257]),
     ("bf16", 8, 8, 64, 256, [300, 0], [20, 300]),
     ("f16", 16, 2, 128, 16, [1000, 0, 7], [63, 129, 1]),
+    # head_dim 256: 64-row tiles (one 16-row block per wavefront)
+    ("f16", 4, 2, 256, 16, [0, 40, 100], [130, 64, 65]),
+    ("bf16", 8, 8, 256, 8, [200, 0], [1, 200]),
 ]
 
 

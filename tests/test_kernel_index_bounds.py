@@ -367,9 +367,15 @@ def test_mfma_bounds_all_shapes(D, G):
 PF_ROWS, PF_KEYS, PF_THREADS, PF_MAX_IDS = 128, 32, 256, 4096
 
 
+def pf_rows(D):
+    """Query rows per workgroup: 4 wavefronts x two 16-row blocks, one block at head_dim 256."""
+    return PF_ROWS if D <= 128 else PF_ROWS // 2
+
+
 def check_prefill_bounds(case, max_query_len=None):
-    """Grid (H, S, ceil(max_query_len / 128)); wavefront w of a workgroup owns
-    chunk rows r0 + 32 w + 16 rb + c (rb = 0, 1); query loads read row min(row, n - 1), channels
+    """Grid (H, S, ceil(max_query_len / R)), R = 128 query rows per workgroup
+    (64 at head_dim 256); wavefront w of a workgroup owns chunk rows
+    r0 + R/4 w + 16 rb + c (rb < R/64); query loads read row min(row, n - 1), channels
     32 ks + 8 g .. +7; block ids of keys 0 .. kv_end - 1 are staged; tile
     loads read key min(kp, kv_end - 1), CPT 16-byte chunks of one row per
     thread (CPR / CPT apart); LDS reads stay in
@@ -387,7 +393,8 @@ def check_prefill_bounds(case, max_query_len=None):
     maxc = case.max_context_len
     ids_cap = -(-maxc // B)
     assert ids_cap <= PF_MAX_IDS and maxc <= W * B
-    n_qt = -(-mq // PF_ROWS)
+    R = pf_rows(D)
+    n_qt = -(-mq // R)
     KS, E, CPR = D // 32, D // 16, D // 8
     assert (PF_KEYS * CPR) % PF_THREADS == 0
     cpt = PF_KEYS * CPR // PF_THREADS
@@ -407,18 +414,18 @@ def check_prefill_bounds(case, max_query_len=None):
         n, ctx = int(n_all[s]), int(case.context_lens[s])
         assert 1 <= n <= ctx <= maxc
         for qt in range(n_qt):
-            r0 = qt * PF_ROWS
+            r0 = qt * R
             if r0 >= n:
                 continue
             first = ctx - n
-            last_row = min(r0 + PF_ROWS, n) - 1
+            last_row = min(r0 + R, n) - 1
             kv_end = first + last_row + 1
             assert kv_end <= ctx
             nids = ((kv_end - 1) // B) + 1
             assert nids <= ids_cap and nids <= W
             ntiles = -(-kv_end // PF_KEYS)
             # query rows read
-            rows = np.minimum(r0 + np.arange(PF_ROWS), n - 1)
+            rows = np.minimum(r0 + np.arange(R), n - 1)
             assert int(qs[s]) + rows.max() < T
             # tile loads
             tid = np.arange(PF_THREADS)
@@ -445,16 +452,16 @@ def check_prefill_bounds(case, max_query_len=None):
     # Every order's linear id -> (sequence, head, query tile) map covers each
     # tile that holds rows exactly once; padding ids exit.
     rows = [prefill_chunk_rows(qs, s, T) for s in range(S)]
-    want = {(s_, h, qt) for s_ in range(S) for h in range(H) for qt in range(min(-(-rows[s_] // PF_ROWS), n_qt))}
+    want = {(s_, h, qt) for s_ in range(S) for h in range(H) for qt in range(min(-(-rows[s_] // R), n_qt))}
     for order in ("tile", "unit", "packed"):
         if order != "tile" and S > PF_MAX_RANKED:
             continue
         if order == "packed" and n_qt > PF_MAX_LEVELS:
             continue
-        grid = prefill_grid(S, Hk, G, n_qt, T, order)
+        grid = prefill_grid(S, Hk, G, n_qt, T, order, R)
         assert grid <= 0x7FFFFFFF
-        got = [w for w in prefill_items(qs, case.context_lens, S, Hk, G, n_qt, T, grid, order)]
-        got = [w for w in got if w[2] * PF_ROWS < rows[w[0]]]  # tiles past a chunk exit
+        got = [w for w in prefill_items(qs, case.context_lens, S, Hk, G, n_qt, T, grid, order, R)]
+        got = [w for w in got if w[2] * R < rows[w[0]]]  # tiles past a chunk exit
         assert len(got) == len(set(got)), order
         assert set(got) == want, order
 
@@ -468,34 +475,34 @@ def prefill_chunk_rows(qs, s, T):
     return q1 - q0 if (q0 >= 0 and q1 > q0 and q1 <= T) else 0
 
 
-def prefill_order(S, n_qt, T):
+def prefill_order(S, n_qt, T, rows=PF_ROWS):
     """The host's choice of dispatch order (launch_prefill_t)."""
-    if S <= PF_MAX_RANKED and 2 * T >= S * n_qt * PF_ROWS:
+    if S <= PF_MAX_RANKED and 2 * T >= S * n_qt * rows:
         return "unit"
     if S <= PF_MAX_RANKED and n_qt <= PF_MAX_LEVELS:
         return "packed"
     return "tile"
 
 
-def prefill_grid(S, Hk, G, n_qt, T, order):
+def prefill_grid(S, Hk, G, n_qt, T, order, rows=PF_ROWS):
     padded = -(-(S * Hk) // 8) * 8 * G * n_qt
     if order != "packed":
         return padded
-    tiles = (T + (PF_ROWS - 1) * S) // PF_ROWS
+    tiles = (T + (rows - 1) * S) // rows
     per_xcd = -(-(tiles * Hk) // 8) + n_qt
     return min(padded, per_xcd * 8 * G)
 
 
-def prefill_items(qs, ctx, S, Hk, G, n_qt, T, grid, order):
+def prefill_items(qs, ctx, S, Hk, G, n_qt, T, grid, order, rows=PF_ROWS):
     """(sequence, head, query tile) of every workgroup that does not exit at
     once, as the kernel maps linear ids (XCD = lin % 8 = unit % 8)."""
     units = S * Hk
     if order == "unit":
         rank_to_seq = sorted(range(S), key=lambda i: (-int(ctx[i]), i))
     if order == "packed":
-        key = [min(prefill_chunk_rows(qs, i, T), n_qt * PF_ROWS) for i in range(S)]
+        key = [min(prefill_chunk_rows(qs, i, T), n_qt * rows) for i in range(S)]
         rank_to_seq = sorted(range(S), key=lambda i: (-key[i], i))
-        cnt = [sum(k > (n_qt - 1 - j) * PF_ROWS for k in key) for j in range(n_qt)]  # level j = tile n_qt-1-j
+        cnt = [sum(k > (n_qt - 1 - j) * rows for k in key) for j in range(n_qt)]  # level j = tile n_qt-1-j
     for lin in range(grid):
         xcd, r8 = lin % 8, lin // 8
         if order == "tile":
@@ -526,7 +533,7 @@ def prefill_items(qs, ctx, S, Hk, G, n_qt, T, grid, order):
             s_ = rank_to_seq[unit // Hk]
             hk, h = unit % Hk, (unit % Hk) * G + off % G
             qt = n_qt - 1 - j
-            assert qt >= 0 and key[s_] > qt * PF_ROWS
+            assert qt >= 0 and key[s_] > qt * rows
         assert 0 <= s_ < S and 0 <= h < H_of(Hk, G) and 0 <= qt < n_qt and h // G == hk
         assert unit % 8 == lin % 8  # a unit's workgroups share one XCD
         yield (s_, h, qt)
@@ -565,6 +572,11 @@ PF_CASES = [
         lambda: wl.random_prefill_case(501, [60000, 0, 3000], [200, 300, 129], 4, 128, 16, "f16", num_kv_heads=2))),
     ("prefill-long-bf16", functools.lru_cache(None)(
         lambda: wl.random_prefill_case(502, [65000, 100], [500, 28], 2, 64, 16, "bf16"))),
+    # head_dim 256: 64-row tiles
+    ("prefill-d256", functools.lru_cache(None)(
+        lambda: wl.random_prefill_case(503, [0, 40, 100], [130, 64, 65], 4, 256, 16, "f16", num_kv_heads=2))),
+    ("prefill-d256-prompts", functools.lru_cache(None)(
+        lambda: wl.random_prefill_case(504, [200, 0, 0, 3], [1, 200, 333, 64], 8, 256, 8, "bf16"))),
 ]
 
 
