@@ -31,7 +31,8 @@
  * memory.  The library allocates nothing, frees
  * nothing and never synchronises: each call validates its arguments on the
  * host, enqueues its kernels on `stream` (a hipStream_t; NULL is the null
- * stream) and returns.  The library keeps no global state, so calls are
+ * stream) and returns.  Apart from the scratch array of pa_decode_static
+ * (one per GPU, see there) the library keeps no global state, so calls are
  * re-entrant; calls on one stream execute in order.
  *
  * Errors: the return value is a pa_status.  Argument errors are detected on
