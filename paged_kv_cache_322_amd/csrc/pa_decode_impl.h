@@ -34,7 +34,13 @@
 //     exponentials taken base 2 with log2(e) folded into the query), so the
 //     loop needs no exchange between rows; rows are merged once at the end;
 //   * wavefronts interleave steps, then merge their (max, sum, accumulators)
-//     through LDS, one query head at a time.
+//     through LDS, one query head at a time;
+//   * the workgroups of one sequence's K/V heads run together (adjacent
+//     grid ids) and read the same blocks (head hk's rows of a block are one
+//     contiguous run beside head hk + 1's), so each starts its walk at a
+//     different step (head hk at step hk * niter / Hk, wrapping around):
+//     at any moment they read different blocks.  (The softmax is
+//     order-independent; only fp32 rounding depends on the order.)
 //
 // Grid order: the hardware dispatches workgroups in linear-id order, so the
 // partition index is the slowest grid dimension, and for mid-sized batches
@@ -195,8 +201,12 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(
     int bad = 0;
 
     const int niter = (t_end - t_begin + U - 1) / U;
+    // Step order of this K/V head: logical step (it + rot) mod niter.
+    const int rot = static_cast<int>((static_cast<int64_t>(hk) * niter) / num_kv_heads);
+    auto rotated = [&](int it) { const int r = it + rot; return r >= niter ? r - niter : r; };
 
-    auto load_step = [&](int it, uint4 (&kr)[NL], uint4 (&vr)[NL]) {
+    auto load_step = [&](int it0, uint4 (&kr)[NL], uint4 (&vr)[NL]) {
+        const int it = rotated(it0);
         const int tb = t_begin + it * U;
         const bool newest = APPEND && newest_here && it == niter - 1;  // wave-uniform
 #pragma unroll
@@ -220,7 +230,8 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(
         }
     };
 
-    auto compute_step = [&](int it, const uint4 (&kr)[NL], const uint4 (&vr)[NL]) {
+    auto compute_step = [&](int it0, const uint4 (&kr)[NL], const uint4 (&vr)[NL]) {
+        const int it = rotated(it0);
         const int tb = t_begin + it * U;
         if constexpr (APPEND) {
             if (newest_here && it == niter - 1) {

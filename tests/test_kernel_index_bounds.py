@@ -79,6 +79,11 @@ def check_decode_bounds(S, H, D, B, N, W, elem, ctx, bt, max_ctx, part, G=1):
             assert 1 <= nblk <= staged
             assert 0 <= j0 and j0 + nblk - 1 < W  # block-table row reads
             niter = (t_end - t_begin + U - 1) // U
+            # K/V head hk walks the steps from hk * niter // H on, wrapping
+            # around: every step exactly once, whatever the head.
+            for hk in {0, H // 2, H - 1}:
+                order = (np.arange(niter) + hk * niter // H) % niter
+                assert np.array_equal(np.sort(order), np.arange(niter))
             ts = np.arange(niter)[:, None, None] * U + np.arange(nl)[None, :, None] * tpl + np.arange(tpl)[None, None, :]
             t = np.minimum(t_begin + ts, t_end - 1).ravel()
             assert t.min() >= t_begin
