@@ -86,6 +86,10 @@ int balanced_workgroups(int32_t head_dim, int dev) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
 
+// Contexts from this length on make a thin sibling grid (see decode_common)
+// slower than the ungrouped plan.
+constexpr int32_t kSiblingLongContext = 1024;
+
 // True when a kernel may dereference p: device memory, or host memory
 // allocated pinned and mapped (hipHostMalloc, torch's pin_memory).  Pageable
 // host memory (or an unknown pointer) would fault on the device.
@@ -286,20 +290,30 @@ int decode_common(void* out, const void* query, const void* key, const void* val
     // Sibling groups: a hint the sibling-group kernel takes where it is built
     // (16-bit caches, head_dim 64..256, plain decode), its matrix columns hold
     // at least two members (members x query heads per K/V head <= 16; a
-    // larger group is cut into sub-groups of 16 / G members) and the
-    // members' block ids fit its LDS; otherwise ignored.
+    // larger group is cut into sub-groups of 16 / G members), the members'
+    // block ids fit its LDS, and its grid is not a single thin round over
+    // long contexts; otherwise ignored.
     a.siblings = 0;
     a.sibling_sub = 0;
     a.sibling_ids = 0;
     const int sub = std::min(siblings, pa::kMaxSiblings / (num_heads / num_kv_heads));
     if (siblings >= 2 && sub >= 2 && !append && (dtype == PA_F16 || dtype == PA_BF16) && head_dim >= 64) {
         const int64_t ids = std::max<int64_t>(1, (static_cast<int64_t>(max_context_len) + block_size - 1) / block_size);
-        if (sub * ids <= pa::kMaxSiblingIds) {
+        // One workgroup per (sub-group, K/V head) in a single round: with
+        // fewer of them than half the compute units and long contexts, most
+        // of the GPU would idle while the ungrouped plan spreads (or splits)
+        // the same contexts over all of it.
+        const int64_t rows = (static_cast<int64_t>(num_seqs) + siblings - 1) / siblings * ((siblings + sub - 1) / sub);
+        const bool thin = 2 * rows * num_kv_heads < device_cus(dev) && max_context_len >= kSiblingLongContext;
+        if (sub * ids <= pa::kMaxSiblingIds && !thin) {
             a.siblings = siblings;
             a.sibling_sub = sub;
             a.sibling_ids = static_cast<int>(ids);
         }
     }
+    // A sibling hint not taken still says that the sequences share blocks:
+    // load them through the caches (as PA_DECODE_SHARED_BLOCKS; same bits).
+    if (siblings >= 2 && !append && a.siblings == 0) a.cached_loads = true;
     a.workspace = need ? workspace : nullptr;
     a.stream = static_cast<hipStream_t>(stream);
     return hip_status(pa::launch_decode(a));

@@ -171,3 +171,24 @@ def test_siblings_hint_ignored_where_not_built(what):
     torch.cuda.synchronize()
     iv = torch.int32 if case.dtype == "f32" else torch.int16
     assert torch.equal(a.view(iv), b.view(iv))
+
+
+@pytest.mark.parametrize("Hk", [8, 32])
+def test_siblings_thin_grid_over_long_contexts_declined(Hk):
+    """One prompt of 1200 tokens forked into 16 samples: one workgroup per
+    (sub-group, K/V head) would be 32 workgroups in a single round, most of
+    the GPU idle, so the hint is declined and the call runs the ungrouped
+    plan with cached loads: that plan's bits, and the oracle's values."""
+    case = wl.parallel_sampling(block_size=16, num_prompts=1, samples=16, prompt_len=1200, num_heads=32,
+                                head_dim=128, pool_tokens=16384, max_suffix=64, num_kv_heads=Hk)
+    g = GpuCase(case)
+    g.run_steps()
+    for kc, vc in oracle_steps(case):
+        pass
+    ref = oracle_decode(case, kc, vc)
+    out = torch.full_like(g.q, float("nan"))
+    pa().decode(out, g.q, g.kc, g.vc, g.bt, g.ctx, case.scale, case.max_context_len, siblings=16)
+    plain = g.decode(out=torch.empty_like(g.q), shared_blocks=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), plain.view(torch.int16))
+    assert_close(out, ref, case.dtype, f"{case.name} siblings=16 (declined)")
