@@ -87,14 +87,18 @@ typedef enum {
                                       each reading the blocks its members share once.  Taken for
                                       16-bit caches, head_dim 64, 128 or 256, u >= 2 (G <= 8) and
                                       u * ceil(max_context_len / B) <= 4096, over whole contexts
-                                      (partition_size is then not used), unless its workgroups
+                                      (partition_size is then not used).  Where its workgroups
                                       (sub-groups x num_kv_heads) are fewer than half the GPU's
-                                      compute units while max_context_len >= 1024: that single
-                                      thin round would leave most of the GPU idle, where the
-                                      ungrouped plan spreads or splits the contexts over all of
-                                      it.  Not taken, the hint still makes K/V load through the
-                                      caches, as PA_DECODE_SHARED_BLOCKS does (the results do not
-                                      depend on the load policy).  Taken, the arithmetic (fp32
+                                      compute units and max_context_len >= 1024, one round of
+                                      them would leave most of the GPU idle: each sub-group's
+                                      tiles are then split over several workgroups (about one
+                                      per compute unit), whose partial results a second kernel
+                                      merges, as many as the workspace the call needs without
+                                      the hint (pa_decode_workspace_size) holds; with room for
+                                      fewer than two the hint is declined.  Not taken, the hint
+                                      still makes K/V load through the caches, as
+                                      PA_DECODE_SHARED_BLOCKS does (the results do not depend on
+                                      the load policy).  Taken, the arithmetic (fp32
                                       products and softmax, probabilities as hi and lo 16-bit
                                       parts) differs from the multi-head kernel's only by fp32
                                       rounding.  Each block shared within a group is then

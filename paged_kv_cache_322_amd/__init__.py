@@ -198,15 +198,18 @@ def decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor, valu
 
 def decode_static(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
                   block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float, max_context_len: int,
-                  partition_size: int = 0, stream=None, shared_blocks: bool = False) -> torch.Tensor:
+                  partition_size: int = 0, stream=None, shared_blocks: bool = False,
+                  siblings: int = 0) -> torch.Tensor:
     """``decode`` through ``pa_decode_static``: no workspace, none allocated;
     split-K partials go to the library's static per-GPU scratch
-    (``STATIC_SCRATCH_BYTES``).  Calls overlapping on one GPU race on it."""
+    (``STATIC_SCRATCH_BYTES``).  Calls overlapping on one GPU race on it.
+    ``shared_blocks`` and ``siblings`` as for ``decode``."""
     dt, tail, _, _ = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, max_context_len,
                                   partition_size, None, stream, allocate=False)
     st = lib.pa_decode_static(out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
                               *tail, float(scale), _code(dt), int(partition_size),
-                              SHARED_BLOCKS if shared_blocks else 0, _stream_handle(query.device, stream))
+                              (SHARED_BLOCKS if shared_blocks else 0) | (int(siblings) << 8),
+                              _stream_handle(query.device, stream))
     _check(st, "pa_decode_static")
     return out
 

@@ -87,7 +87,7 @@ int balanced_workgroups(int32_t head_dim, int dev) {
 int hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
 
 // Contexts from this length on make a thin sibling grid (see decode_common)
-// slower than the ungrouped plan.
+// slower than the ungrouped plan, unless its tile lists are split.
 constexpr int32_t kSiblingLongContext = 1024;
 
 // True when a kernel may dereference p: device memory, or host memory
@@ -290,12 +290,14 @@ int decode_common(void* out, const void* query, const void* key, const void* val
     // Sibling groups: a hint the sibling-group kernel takes where it is built
     // (16-bit caches, head_dim 64..256, plain decode), its matrix columns hold
     // at least two members (members x query heads per K/V head <= 16; a
-    // larger group is cut into sub-groups of 16 / G members), the members'
-    // block ids fit its LDS, and its grid is not a single thin round over
-    // long contexts; otherwise ignored.
+    // larger group is cut into sub-groups of 16 / G members) and the
+    // members' block ids fit its LDS; otherwise ignored.  A thin grid over
+    // long contexts is split, or declined where the workspace cannot hold
+    // the split's partials.
     a.siblings = 0;
     a.sibling_sub = 0;
     a.sibling_ids = 0;
+    a.sibling_parts = 1;
     const int sub = std::min(siblings, pa::kMaxSiblings / (num_heads / num_kv_heads));
     if (siblings >= 2 && sub >= 2 && !append && (dtype == PA_F16 || dtype == PA_BF16) && head_dim >= 64) {
         const int64_t ids = std::max<int64_t>(1, (static_cast<int64_t>(max_context_len) + block_size - 1) / block_size);
@@ -303,12 +305,28 @@ int decode_common(void* out, const void* query, const void* key, const void* val
         // fewer of them than half the compute units and long contexts, most
         // of the GPU would idle while the ungrouped plan spreads (or splits)
         // the same contexts over all of it.
+        // Such a grid is split instead: each tile list over `parts`
+        // workgroups (about one per compute unit, at least 8 tiles of the
+        // longest context each), whose partials go to the workspace; as
+        // many as the ungrouped plan's workspace size holds, so that the
+        // choice (and the rounding) depends on the shapes only.
         const int64_t rows = (static_cast<int64_t>(num_seqs) + siblings - 1) / siblings * ((siblings + sub - 1) / sub);
-        const bool thin = 2 * rows * num_kv_heads < device_cus(dev) && max_context_len >= kSiblingLongContext;
-        if (sub * ids <= pa::kMaxSiblingIds && !thin) {
+        const int64_t wgs = rows * num_kv_heads;
+        const bool thin = 2 * wgs < device_cus(dev) && max_context_len >= kSiblingLongContext;
+        const bool fits = sub * ids <= pa::kMaxSiblingIds;
+        int64_t parts = 1;
+        if (fits && thin) {
+            const int64_t per_part = static_cast<int64_t>(num_seqs) * num_heads * (head_dim + 2) * sizeof(float);
+            const int64_t have = static_cast<int64_t>(need) / per_part;
+            const int64_t want = (device_cus(dev) + wgs - 1) / wgs;
+            const int64_t by_len = (static_cast<int64_t>(max_context_len) + 127) / 128;
+            parts = std::min(std::min(want, have), std::min(by_len, static_cast<int64_t>(pa::kMaxSiblingParts)));
+        }
+        if (fits && (!thin || parts >= 2)) {
             a.siblings = siblings;
             a.sibling_sub = sub;
             a.sibling_ids = static_cast<int>(ids);
+            a.sibling_parts = thin ? static_cast<int>(parts) : 1;
         }
     }
     // A sibling hint not taken still says that the sequences share blocks:

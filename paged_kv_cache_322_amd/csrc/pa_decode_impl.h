@@ -390,7 +390,17 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(
     const int64_t sh = static_cast<int64_t>(s) * num_heads + h;
     const int lane = threadIdx.x;
     int np;
-    if (meta) {
+    if (part_tokens == 0) {
+        // Sibling groups split over max_parts workgroups each: every
+        // (sequence, head) has max_parts partials (empty ones weigh 0); the
+        // sibling kernel skipped empty and impossible contexts.
+        if (ctx <= 0 || ctx > max_context_len) {
+            const float v = (ctx == 0) ? 0.0f : __builtin_nanf("");
+            for (int d = lane; d < D; d += kWave) out[sh * D + d] = narrow<T>(v);
+            return;
+        }
+        np = max_parts;
+    } else if (meta) {
         // Balanced split: the decode kernel skipped empty and invalid
         // contexts, and wrote whole (sequence, K/V head) runs itself.
         if (ctx <= 0 || ctx > max_context_len) {
@@ -490,13 +500,25 @@ hipError_t launch_decode_t(const DecodeArgs& a) {
             const int64_t groups = (a.num_seqs + a.siblings - 1) / a.siblings;
             const int64_t per_group = (a.siblings + a.sibling_sub - 1) / a.sibling_sub;
             const unsigned rows = static_cast<unsigned>(groups * per_group);
-            hipLaunchKernelGGL((decode_siblings_kernel<T, D, NT>), dim3(a.num_kv_heads, rows), dim3(kMfmaThreads),
-                               static_cast<size_t>(a.sibling_sub) * a.sibling_ids * sizeof(int), a.stream, out,
-                               static_cast<const bits*>(a.query), static_cast<const bits*>(a.k_cache),
+            // Split tile lists: partials laid out with max_parts = parts.
+            const int parts = a.sibling_parts;
+            const size_t n_sp = static_cast<size_t>(a.num_seqs) * a.num_heads * parts;
+            float* sp_o = parts > 1 ? static_cast<float*>(a.workspace) : nullptr;
+            float* sp_m = parts > 1 ? sp_o + n_sp * D : nullptr;
+            float* sp_l = parts > 1 ? sp_m + n_sp : nullptr;
+            hipLaunchKernelGGL((decode_siblings_kernel<T, D, NT>), dim3(a.num_kv_heads, rows, parts),
+                               dim3(kMfmaThreads), static_cast<size_t>(a.sibling_sub) * a.sibling_ids * sizeof(int),
+                               a.stream, out, static_cast<const bits*>(a.query), static_cast<const bits*>(a.k_cache),
                                static_cast<const bits*>(a.v_cache), a.block_tables, a.context_lens, a.num_seqs,
                                a.num_kv_heads, G, a.siblings, a.sibling_sub, a.sibling_ids, log2_bs,
-                               a.max_blocks_per_seq,
-                               a.max_context_len, a.num_blocks, qscale);
+                               a.max_blocks_per_seq, a.max_context_len, a.num_blocks, qscale, parts, sp_o, sp_m,
+                               sp_l);
+            hipError_t err = hipGetLastError();
+            if (err != hipSuccess || parts <= 1) return err;
+            hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(a.num_heads, a.num_seqs), dim3(kWave), 0, a.stream,
+                               out, static_cast<const float*>(sp_o), static_cast<const float*>(sp_m),
+                               static_cast<const float*>(sp_l), a.context_lens, a.num_heads, a.max_context_len, 0,
+                               parts, a.num_kv_heads, static_cast<const int32_t*>(nullptr));
             return hipGetLastError();
         }
     }

@@ -30,7 +30,12 @@
 // the same result), and the arithmetic is decode_mfma_kernel's (fp32
 // products and softmax, probabilities split into hi and lo 16-bit parts).
 // Each member's softmax state is per column; the 8 wavefronts split the
-// tiles of the whole token list and merge through LDS.
+// tiles of the whole token list and merge through LDS.  A batch with few
+// (sub-group, K/V head) pairs can also split each tile list over `parts`
+// workgroups (grid z): workgroup z takes tiles [z n / parts, (z + 1) n /
+// parts) of the n and writes, per member and query head, its unnormalised
+// partial result (accumulator, maximum, sum) to the workspace, which
+// decode_merge_kernel combines as it does the partitions of one context.
 // The members' K/V values must be finite: a masked column still multiplies
 // its zero probabilities with the tile's V rows, so a non-finite value in
 // one member's own tokens can reach its siblings' results.
@@ -51,7 +56,8 @@ __global__ __launch_bounds__(kMfmaThreads, mfma_waves_per_simd(D)) void decode_s
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens, int num_seqs,
     int num_kv_heads, int gq, int group, int sub, int ids_per_seq, int log2_bs, int max_blocks_per_seq,
     int max_context_len,
-    int64_t num_blocks, float qscale) {
+    int64_t num_blocks, float qscale, int parts, float* __restrict__ ws_o, float* __restrict__ ws_m,
+    float* __restrict__ ws_l) {
     static_assert(sizeof(typename T::bits) == 2, "16-bit caches only");
     static_assert(D == 64 || D == 128 || D == 256, "head_dim");
     constexpr int KS = D / 32;  // q.k k-steps (8 channels per lane each)
@@ -161,6 +167,10 @@ __global__ __launch_bounds__(kMfmaThreads, mfma_waves_per_simd(D)) void decode_s
         qv[ks] = (c < ncols) ? as_u32x4(load16(q + q_row * D + 32 * ks + 8 * g)) : u32x4{0u, 0u, 0u, 0u};
     __syncthreads();  // s_seg published
     const int ntile = __builtin_amdgcn_readfirstlane(s_seg[n + 1]);
+    // This workgroup's tiles [it_begin, it_end) of the list.
+    const int part = blockIdx.z;
+    const int it_begin = static_cast<int>(static_cast<int64_t>(ntile) * part / parts);
+    const int it_end = static_cast<int>(static_cast<int64_t>(ntile) * (part + 1) / parts);
 
     const uint32_t blk_stride = static_cast<uint32_t>(num_kv_heads << log2_bs) * D;
     const uint32_t head_off = (static_cast<uint32_t>(hk) << log2_bs) * D;
@@ -286,20 +296,20 @@ __global__ __launch_bounds__(kMfmaThreads, mfma_waves_per_simd(D)) void decode_s
 
     // Software pipeline: the next tile's loads in flight while the current
     // one is computed.
-    int it = wave;
-    if (it < ntile) {
+    int it = it_begin + wave;
+    if (it < it_end) {
         TileInfo cur = tile_info(it);
         load_tile(cur);
         while (true) {
             store_tile();
             const int nx = it + kMfmaWaves;
             TileInfo nxt = cur;
-            if (nx < ntile) {
+            if (nx < it_end) {
                 nxt = tile_info(nx);
                 load_tile(nxt);
             }
             compute_tile(cur);
-            if (nx >= ntile) break;
+            if (nx >= it_end) break;
             it = nx;
             cur = nxt;
         }
@@ -311,7 +321,10 @@ __global__ __launch_bounds__(kMfmaThreads, mfma_waves_per_simd(D)) void decode_s
     const uint32_t bad_all = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(s_bad));
 
     // Merge the wavefronts through LDS, HC columns per pass; one output row
-    // per member.
+    // per member, or (parts > 1) one partial per member and query head: the
+    // empty and impossible members' rows are then the merge kernel's, and a
+    // flagged segment makes the partial NaN (sum and accumulator), which the
+    // merge carries into the row whatever the partial's weight.
     if (g == 0) {
         s_m[wave][c] = m;
         s_l[wave][c] = l;
@@ -329,6 +342,27 @@ __global__ __launch_bounds__(kMfmaThreads, mfma_waves_per_simd(D)) void decode_s
             if (col >= ncols) continue;
             const int mem = col / gq;
             const int cm = s_ctx[mem];
+            if (parts > 1) {
+                if (!((vmask >> mem) & 1)) continue;
+                float M = s_m[0][col];
+#pragma unroll
+                for (int w = 1; w < kMfmaWaves; ++w) M = fmaxf(M, s_m[w][col]);
+                float L = 0.0f, O = 0.0f;
+#pragma unroll
+                for (int w = 0; w < kMfmaWaves; ++w) {
+                    const float f = (s_m[w][col] == -INFINITY) ? 0.0f : fast_exp2(s_m[w][col] - M);
+                    L = fmaf(f, s_l[w][col], L);
+                    O = fmaf(f, s_o[w][hl][d], O);
+                }
+                if ((bad_all & 1u) || ((bad_all >> (mem + 1)) & 1u)) L = O = __builtin_nanf("");
+                const int64_t slot = (static_cast<int64_t>(s0 + mem) * num_heads + hk * gq + col % gq) * parts + part;
+                ws_o[slot * D + d] = O;
+                if (d == 0) {
+                    ws_m[slot] = M;
+                    ws_l[slot] = L;
+                }
+                continue;
+            }
             float v;
             if (cm == 0) {
                 v = 0.0f;

@@ -139,6 +139,10 @@ struct DecodeArgs {
     int siblings;
     int sibling_sub;  // members per workgroup: min(siblings, 16 / G)
     int sibling_ids;
+    // > 1: a sub-group's tiles are split over this many workgroups, whose
+    // partial results (workspace laid out as below with max_parts =
+    // sibling_parts) decode_merge_kernel combines; 1: whole tile lists.
+    int sibling_parts;
     // float [S*H*max_parts*D] then [S*H*max_parts] x 2, then (balanced plan)
     // int32 [S + 2]; NULL when max_parts == 1
     void* workspace;
@@ -154,6 +158,7 @@ hipError_t launch_decode_bf16(const DecodeArgs& a);
 // one 16x16 matrix product) and staged block ids per workgroup.
 constexpr int kMaxSiblings = 16;
 constexpr int kMaxSiblingIds = 4096;
+constexpr int kMaxSiblingParts = 64;  // workgroups one sub-group's tiles are split over, at most
 
 // Query heads per K/V head with built kernels.
 inline bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }

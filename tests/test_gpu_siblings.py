@@ -173,16 +173,80 @@ def test_siblings_hint_ignored_where_not_built(what):
     assert torch.equal(a.view(iv), b.view(iv))
 
 
+def _thin_case(Hk, prompts=1):
+    # One (or two) 1200-token prompts forked into 16 samples each: a single
+    # round of one workgroup per (sub-group, K/V head) would be 32 or 64
+    # workgroups for the whole GPU.
+    return wl.parallel_sampling(block_size=16, num_prompts=prompts, samples=16, prompt_len=1200, num_heads=32,
+                                head_dim=128, pool_tokens=32768, max_suffix=64, num_kv_heads=Hk)
+
+
 @pytest.mark.parametrize("Hk", [8, 32])
-def test_siblings_thin_grid_over_long_contexts_declined(Hk):
-    """One prompt of 1200 tokens forked into 16 samples: one workgroup per
-    (sub-group, K/V head) would be 32 workgroups in a single round, most of
-    the GPU idle, so the hint is declined and the call runs the ungrouped
-    plan with cached loads: that plan's bits, and the oracle's values."""
-    case = wl.parallel_sampling(block_size=16, num_prompts=1, samples=16, prompt_len=1200, num_heads=32,
-                                head_dim=128, pool_tokens=16384, max_suffix=64, num_kv_heads=Hk)
+def test_siblings_thin_grid_split(Hk):
+    """A thin grid over long contexts splits each tile list over several
+    workgroups (their partials merged as split contexts are): the oracle's
+    values, every member, and the same bits from pa_decode_static (the
+    same kernels with the library's scratch as workspace)."""
+    case = _thin_case(Hk)
     g = GpuCase(case)
     g.run_steps()
+    for kc, vc in oracle_steps(case):
+        pass
+    ref = oracle_decode(case, kc, vc)
+    out = torch.full_like(g.q, float("nan"))
+    pa().decode(out, g.q, g.kc, g.vc, g.bt, g.ctx, case.scale, case.max_context_len, siblings=16)
+    st = torch.full_like(g.q, float("nan"))
+    pa().decode_static(st, g.q, g.kc, g.vc, g.bt, g.ctx, case.scale, case.max_context_len, siblings=16)
+    plain = g.decode(out=torch.empty_like(g.q), shared_blocks=True)
+    torch.cuda.synchronize()
+    assert_close(out, ref, case.dtype, f"{case.name} siblings=16 (split)")
+    assert torch.equal(out.view(torch.int16), st.view(torch.int16))
+    log(f"{case.name}: max |split siblings - ungrouped| = {(out.float() - plain.float()).abs().max().item():.3e}")
+
+
+def test_siblings_thin_grid_split_guards():
+    """Split tile lists keep the guards: an empty member gives zeros, an
+    impossible one NaN, an out-of-pool id in one member's own blocks NaN for
+    that member, one in the shared prompt NaN for the whole group; the other
+    members match the oracle."""
+    case = _thin_case(8)
+    g = GpuCase(case)
+    g.run_steps()
+    for kc, vc in oracle_steps(case):
+        pass
+    ref = oracle_decode(case, kc, vc)
+    ctx = case.context_lens.copy()
+    ctx[3] = 0
+    ctx[5] = case.max_context_len + 7
+    bt = case.block_tables.copy()
+    bt[9, (int(ctx[9]) - 1) // case.block_size] = case.num_blocks + 2  # member 9's last (own) block
+    out = torch.full_like(g.q, 1.0)
+    pa().decode(out, g.q, g.kc, g.vc, torch.from_numpy(bt).cuda(), torch.from_numpy(ctx).cuda(), case.scale,
+                case.max_context_len, siblings=16)
+    torch.cuda.synchronize()
+    assert (out[3].float() == 0).all()
+    assert torch.isnan(out[5].float()).all() and torch.isnan(out[9].float()).all()
+    keep = [i for i in range(16) if i not in (3, 5, 9)]
+    assert_close(out[keep], ref[keep], case.dtype, "split siblings: other members")
+    bt = case.block_tables.copy()
+    bt[:, 2] = case.num_blocks + 1  # a shared prompt block of the one group
+    out = torch.full_like(g.q, 0.0)
+    pa().decode(out, g.q, g.kc, g.vc, torch.from_numpy(bt).cuda(), g.ctx, case.scale, case.max_context_len,
+                siblings=16)
+    torch.cuda.synchronize()
+    assert torch.isnan(out.float()).all()
+
+
+def test_siblings_thin_grid_declined_without_workspace():
+    """Where the ungrouped plan needs no workspace (two prompts x 16 samples,
+    multi-head: whole contexts) a thin sibling grid has nowhere to put split
+    partials: the hint is declined and the call runs the ungrouped plan with
+    cached loads, bit for bit."""
+    case = _thin_case(32, prompts=2)
+    g = GpuCase(case)
+    g.run_steps()
+    S, H, D = case.q.shape
+    assert pa().decode_workspace_size(S, H, D, case.max_context_len) == 0
     for kc, vc in oracle_steps(case):
         pass
     ref = oracle_decode(case, kc, vc)

@@ -636,7 +636,7 @@ def test_random_prefill_case_bounds(seed):
 SIB_MAX, SIB_MAX_IDS, SIB_TILE = 16, 4096, 16
 
 
-def check_siblings_bounds(case, group):
+def check_siblings_bounds(case, group, parts=1):
     """Grid (H, ceil(S / group) * ceil(group / sub)), sub = min(group,
     16 // G) members per workgroup: grid row y is sub-group y % per_group
     of group y // per_group, members m < n are sequences s0 + m.  Staged
@@ -647,7 +647,9 @@ def check_siblings_bounds(case, group):
     member's ids.  Every staged, loaded and written index is in bounds, every
     sequence is in exactly one workgroup, and each usable member's tokens
     0 .. ctx - 1 are each read exactly once, from the physical block its own
-    table names."""
+    table names.  With parts > 1 (grid z) each tile list is cut into `parts`
+    contiguous ranges, one workgroup each, and every usable member's partial
+    for each query head goes to workspace slot ((s * H + h) * parts + z)."""
     S, H, D = case.q.shape
     N, Hk, B, _ = case.k_cache.shape
     G = H // Hk
@@ -694,20 +696,29 @@ def check_siblings_bounds(case, group):
         segs = [(0, shared_end, members[0] if members else 0, set(members))]
         segs += [(shared_end, ctx[m], m, {m}) for m in members]
         seen = {m: np.zeros(ctx[m], dtype=np.int64) for m in members}
-        for tb0, tend, mid, cols in segs:
-            for tb in range(tb0, tend, SIB_TILE):
-                for i in range(SIB_TILE // RPI):
-                    t = np.minimum(tb + RPI * i + np.arange(RPI), tend - 1)
-                    assert (t >> int(np.log2(B))).max() < ids
-                    b = np.maximum(blk[mid, t // B], 0)
-                    e = b * Hk * B * D + (Hk - 1) * B * D + (t % B) * D + D - 8
-                    assert e.max() + 8 <= cache_elems
-                # tokens this tile weighs (unmasked: tb + 4 g + j < tend)
-                for t in range(tb, min(tb + SIB_TILE, tend)):
-                    for m in cols:
-                        seen[m][t] += 1
-                        # the block read is the member's own block for t
-                        assert blk[mid, t // B] == blk[m, t // B]
+        # the tile list, segment after segment, cut into `parts` ranges
+        tiles = [(tb, tend, mid, cols) for tb0, tend, mid, cols in segs for tb in range(tb0, tend, SIB_TILE)]
+        ntile = len(tiles)
+        ranges = [(ntile * z // parts, ntile * (z + 1) // parts) for z in range(parts)]
+        assert sum(hi - lo for lo, hi in ranges) == ntile and all(lo <= hi for lo, hi in ranges)
+        for z in range(parts if parts > 1 else 0):
+            for m in members:
+                for hk in (0, Hk - 1):
+                    slot = ((s0 + m) * H + hk * G + G - 1) * parts + z
+                    assert slot < S * H * parts and (slot + 1) * D <= S * H * parts * D
+        for tb, tend, mid, cols in (tiles[k] for lo, hi in ranges for k in range(lo, hi)):
+            for i in range(SIB_TILE // RPI):
+                t = np.minimum(tb + RPI * i + np.arange(RPI), tend - 1)
+                assert (t >> int(np.log2(B))).max() < ids
+                b = np.maximum(blk[mid, t // B], 0)
+                e = b * Hk * B * D + (Hk - 1) * B * D + (t % B) * D + D - 8
+                assert e.max() + 8 <= cache_elems
+            # tokens this tile weighs (unmasked: tb + 4 g + j < tend)
+            for t in range(tb, min(tb + SIB_TILE, tend)):
+                for m in cols:
+                    seen[m][t] += 1
+                    # the block read is the member's own block for t
+                    assert blk[mid, t // B] == blk[m, t // B]
         for m in members:
             assert (seen[m] == 1).all(), (y, m)
         # query operands and output rows: member c // G, query head hk G + c % G
@@ -781,3 +792,54 @@ def test_siblings_grouped_query_bounds(G, group):
     case = wl.parallel_sampling(block_size=16, num_prompts=3, samples=4, prompt_len=90, num_heads=2 * G, head_dim=128,
                                 pool_tokens=8192, max_suffix=40, num_kv_heads=2)
     check_siblings_bounds(case, group)
+
+
+def sibling_plan(S, H, Hk, D, B, group, maxc, ws_bytes, cus=256):
+    """The host's choice for PA_DECODE_SIBLINGS(group): 0 = not taken,
+    otherwise the number of workgroups each tile list is split over (1 =
+    whole lists).  A thin grid (fewer workgroups than half the CUs) over
+    contexts of 1024 tokens or more is split into about one workgroup per
+    CU, at least 8 tiles of the longest context each, as many as the
+    ungrouped plan's workspace holds (at least two); otherwise declined."""
+    G = H // Hk
+    sub = min(group, SIB_MAX // G)
+    if group < 2 or sub < 2 or D < 64:
+        return 0
+    ids = max(1, -(-maxc // B))
+    fits = sub * ids <= SIB_MAX_IDS
+    rows = -(-S // group) * -(-group // sub)
+    wgs = rows * Hk
+    thin = 2 * wgs < cus and maxc >= 1024
+    parts = 1
+    if fits and thin:
+        have = ws_bytes // (S * H * (D + 2) * 4)
+        parts = min(-(-cus // wgs), have, -(-maxc // 128), 64)
+    return (1 if not thin else parts) if fits and (not thin or parts >= 2) else 0
+
+
+@pytest.mark.parametrize("Hk,samples,plen", [(8, 16, 1200), (32, 16, 1200), (8, 8, 4000), (2, 4, 2000)])
+def test_siblings_split_bounds(Hk, samples, plen):
+    """One prompt forked into samples, long enough for a thin grid: the tile
+    lists are split over the workgroups the plain plan's workspace allows,
+    every token of every member still read exactly once."""
+    import paged_kv_cache_322_amd as pa
+
+    H = 32 if Hk != 2 else 16
+    case = wl.parallel_sampling(block_size=16, num_prompts=1, samples=samples, prompt_len=plen, num_heads=H,
+                                head_dim=128, pool_tokens=32768, max_suffix=64, num_kv_heads=Hk)
+    S, D = case.q.shape[0], case.q.shape[2]
+    ws = pa.decode_workspace_size(S, H, D, case.max_context_len, num_kv_heads=Hk)
+    parts = sibling_plan(S, H, Hk, D, 16, samples, case.max_context_len, ws)
+    assert parts >= 2
+    assert S * H * parts * (D + 2) * 4 <= ws
+    check_siblings_bounds(case, samples, parts)
+
+
+def test_sibling_plan_rule():
+    """Not thin: whole lists; thin without a workspace: declined."""
+    assert sibling_plan(256, 40, 40, 128, 16, 4, 756, 0) == 1  # config 4
+    assert sibling_plan(16, 32, 8, 128, 16, 16, 4225, 0) == 0  # no room for partials
+    assert sibling_plan(16, 32, 8, 128, 16, 16, 900, 0) == 1  # short contexts: whole lists
+    assert sibling_plan(16, 32, 8, 128, 16, 16, 4225, 1 << 30) == 8  # 32 workgroups -> 1 per CU
+    assert sibling_plan(16, 32, 8, 128, 16, 16, 4225, 3 * 16 * 32 * 130 * 4) == 3  # as the workspace holds
+    assert sibling_plan(16, 32, 8, 128, 16, 16, 4225, 16 * 32 * 130 * 4) == 0  # room for one: declined
