@@ -204,6 +204,26 @@ def test_siblings_thin_grid_split(Hk):
     log(f"{case.name}: max |split siblings - ungrouped| = {(out.float() - plain.float()).abs().max().item():.3e}")
 
 
+THIN_SHAPES = [
+    # dtype, D, B, query heads, K/V heads, prompts, samples, prompt tokens
+    ("bf16", 256, 32, 4, 2, 1, 8, 1500),
+    ("f16", 64, 8, 16, 4, 2, 8, 1100),
+    ("bf16", 128, 16, 16, 2, 1, 4, 2100),  # G = 8: sub-groups of 2
+    ("f16", 128, 64, 4, 4, 3, 5, 1300),  # groups cut across prompts
+]
+
+
+@pytest.mark.parametrize("dtype,D,B,H,Hk,prompts,samples,plen", THIN_SHAPES,
+                         ids=[f"{t[0]}-D{t[1]}-B{t[2]}-G{t[3] // t[4]}" for t in THIN_SHAPES])
+def test_siblings_thin_grid_split_shapes(dtype, D, B, H, Hk, prompts, samples, plen):
+    """Split tile lists at other head sizes, block sizes, group sizes and
+    dtypes, and with groups that straddle prompts: the oracle's values."""
+    case = wl.parallel_sampling(block_size=B, num_prompts=prompts, samples=samples, prompt_len=plen, num_heads=H,
+                                head_dim=D, pool_tokens=65536, max_suffix=48, num_kv_heads=Hk, dtype=dtype)
+    group = 4 if samples == 5 else samples
+    run_case(case, group)
+
+
 def test_siblings_thin_grid_split_guards():
     """Split tile lists keep the guards: an empty member gives zeros, an
     impossible one NaN, an out-of-pool id in one member's own blocks NaN for

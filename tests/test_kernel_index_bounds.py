@@ -843,3 +843,20 @@ def test_sibling_plan_rule():
     assert sibling_plan(16, 32, 8, 128, 16, 16, 4225, 1 << 30) == 8  # 32 workgroups -> 1 per CU
     assert sibling_plan(16, 32, 8, 128, 16, 16, 4225, 3 * 16 * 32 * 130 * 4) == 3  # as the workspace holds
     assert sibling_plan(16, 32, 8, 128, 16, 16, 4225, 16 * 32 * 130 * 4) == 0  # room for one: declined
+
+
+@pytest.mark.parametrize("dtype,D,B,H,Hk,prompts,samples,plen", [
+    ("bf16", 256, 32, 4, 2, 1, 8, 1500), ("f16", 64, 8, 16, 4, 2, 8, 1100), ("bf16", 128, 16, 16, 2, 1, 4, 2100),
+    ("f16", 128, 64, 4, 4, 3, 5, 1300)])
+def test_siblings_split_shapes_bounds(dtype, D, B, H, Hk, prompts, samples, plen):
+    """The split GPU cases at other head, block and group sizes."""
+    import paged_kv_cache_322_amd as pa
+
+    case = wl.parallel_sampling(block_size=B, num_prompts=prompts, samples=samples, prompt_len=plen, num_heads=H,
+                                head_dim=D, pool_tokens=65536, max_suffix=48, num_kv_heads=Hk, dtype=dtype)
+    S = case.q.shape[0]
+    group = 4 if samples == 5 else samples
+    ws = pa.decode_workspace_size(S, H, D, case.max_context_len, num_kv_heads=Hk)
+    parts = sibling_plan(S, H, Hk, D, B, group, case.max_context_len, ws)
+    assert parts >= 2, parts
+    check_siblings_bounds(case, group, parts)
