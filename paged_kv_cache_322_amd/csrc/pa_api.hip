@@ -301,15 +301,14 @@ int decode_common(void* out, const void* query, const void* key, const void* val
     const int sub = std::min(siblings, pa::kMaxSiblings / (num_heads / num_kv_heads));
     if (siblings >= 2 && sub >= 2 && !append && (dtype == PA_F16 || dtype == PA_BF16) && head_dim >= 64) {
         const int64_t ids = std::max<int64_t>(1, (static_cast<int64_t>(max_context_len) + block_size - 1) / block_size);
-        // One workgroup per (sub-group, K/V head) in a single round: with
-        // fewer of them than half the compute units and long contexts, most
-        // of the GPU would idle while the ungrouped plan spreads (or splits)
-        // the same contexts over all of it.
-        // Such a grid is split instead: each tile list over `parts`
-        // workgroups (about one per compute unit, at least 8 tiles of the
-        // longest context each), whose partials go to the workspace; as
-        // many as the ungrouped plan's workspace size holds, so that the
-        // choice (and the rounding) depends on the shapes only.
+        // The kernel runs one round of one workgroup per (sub-group, K/V
+        // head).  With fewer of them than half the compute units over long
+        // contexts (a thin grid) most of the GPU would idle, so each tile
+        // list is split over `parts` workgroups: about one workgroup per
+        // compute unit in all, at least 8 tiles of the longest context each,
+        // and no more partials than the workspace of the same call without
+        // the hint holds (so the choice, and the rounding, depend on the
+        // shapes only).  Fewer than two: declined.
         const int64_t rows = (static_cast<int64_t>(num_seqs) + siblings - 1) / siblings * ((siblings + sub - 1) / sub);
         const int64_t wgs = rows * num_kv_heads;
         const bool thin = 2 * wgs < device_cus(dev) && max_context_len >= kSiblingLongContext;
