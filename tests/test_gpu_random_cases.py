@@ -118,3 +118,43 @@ def test_random_siblings(seed):
     pa().decode(out, g.q, g.kc, g.vc, g.bt, g.ctx, case.scale, case.max_context_len, siblings=group)
     torch.cuda.synchronize()
     assert_close(out, ref, case.dtype, f"seed {seed} siblings", strict=False)
+
+
+def random_thin_siblings_case(seed: int) -> tuple:
+    """(case, group size) of random thin-grid seed `seed`: one or two long
+    prompts (1024 tokens or more) forked into up to 16 samples, so that the
+    sibling grid is thin and its tile lists are split (or, where the ids do
+    not fit or the ungrouped plan has no workspace, the hint is not taken)."""
+    rng = np.random.default_rng([322, 9004, seed])
+    dtype = ["f16", "bf16"][seed % 2]
+    D = int(rng.choice([64, 128, 256]))
+    B = int(rng.choice([8, 16, 32, 64]))
+    samples = int(rng.integers(2, 17))
+    prompts = int(rng.integers(1, 3))
+    prompt_len = int(rng.integers(1024, 3000))
+    max_suffix = int(rng.integers(0, 200))
+    Hk = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    group = max(2, min(16, samples))
+    need = prompts * samples * ((prompt_len + max_suffix) // B + 3)
+    case = wl.parallel_sampling(block_size=B, num_prompts=prompts, samples=samples, prompt_len=prompt_len,
+                                num_heads=Hk * G, head_dim=D, pool_tokens=max(4096, 2 * need * B), dtype=dtype,
+                                max_suffix=max_suffix, num_kv_heads=Hk)
+    return case, group
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_thin_siblings(seed):
+    case, group = random_thin_siblings_case(seed)
+    log(f"thin seed {seed}: {case.dtype} D={case.head_dim} B={case.block_size} H={case.num_heads} "
+        f"Hk={case.num_kv_heads} group={group} S={case.q.shape[0]} max_ctx={case.max_context_len}")
+    g = GpuCase(case)
+    g.run_steps()
+    kc, vc = case.k_cache, case.v_cache
+    for kc, vc in oracle_steps(case):
+        pass
+    ref = oracle_decode(case, kc, vc)
+    out = torch.empty_like(g.q)
+    pa().decode(out, g.q, g.kc, g.vc, g.bt, g.ctx, case.scale, case.max_context_len, siblings=group)
+    torch.cuda.synchronize()
+    assert_close(out, ref, case.dtype, f"thin seed {seed} siblings", strict=False)

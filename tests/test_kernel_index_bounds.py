@@ -860,3 +860,18 @@ def test_siblings_split_shapes_bounds(dtype, D, B, H, Hk, prompts, samples, plen
     parts = sibling_plan(S, H, Hk, D, B, group, case.max_context_len, ws)
     assert parts >= 2, parts
     check_siblings_bounds(case, group, parts)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_thin_siblings_bounds(seed):
+    """The random thin-grid GPU cases, with the split count the host picks."""
+    import paged_kv_cache_322_amd as pa
+    from test_gpu_random_cases import random_thin_siblings_case
+
+    case, group = random_thin_siblings_case(seed)
+    S, H, D = case.q.shape
+    Hk = case.k_cache.shape[1]
+    ws = pa.decode_workspace_size(S, H, D, case.max_context_len, num_kv_heads=Hk)
+    parts = sibling_plan(S, H, Hk, D, case.block_size, group, case.max_context_len, ws)
+    if parts:
+        check_siblings_bounds(case, group, parts)
