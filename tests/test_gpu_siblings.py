@@ -257,6 +257,14 @@ def test_siblings_thin_grid_split_guards():
     assert torch.isnan(out.float()).all()
 
 
+def test_siblings_thin_grid_split_unrelated():
+    """A thin split grid whose members share nothing (every token read
+    privately), with an empty and a one-token context among them."""
+    case = wl.random_case(91, 8, 4, 128, 16, "bf16", ctx=[1500, 1200, 0, 1100, 2000, 1, 1300, 1700], spare_blocks=4)
+    g, out, ref = run_case(case, 8, strict=False)
+    assert (out[2].float() == 0).all()
+
+
 def test_siblings_thin_grid_declined_without_workspace():
     """Where the ungrouped plan needs no workspace (two prompts x 16 samples,
     multi-head: whole contexts) a thin sibling grid has nowhere to put split

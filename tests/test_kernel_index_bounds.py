@@ -875,3 +875,15 @@ def test_random_thin_siblings_bounds(seed):
     parts = sibling_plan(S, H, Hk, D, case.block_size, group, case.max_context_len, ws)
     if parts:
         check_siblings_bounds(case, group, parts)
+
+
+def test_siblings_split_unrelated_bounds():
+    """The thin split grid of unrelated sequences (empty and one-token
+    contexts among them) that the GPU test runs."""
+    import paged_kv_cache_322_amd as pa
+
+    case = wl.random_case(91, 8, 4, 128, 16, "bf16", ctx=[1500, 1200, 0, 1100, 2000, 1, 1300, 1700], spare_blocks=4)
+    ws = pa.decode_workspace_size(8, 4, 128, case.max_context_len)
+    parts = sibling_plan(8, 4, 4, 128, 16, 8, case.max_context_len, ws)
+    assert parts >= 2
+    check_siblings_bounds(case, 8, parts)
