@@ -49,6 +49,8 @@ WORKLOADS = {
                     "heads (LLaMA-3-8B-shaped), D=128, f16",
     "sampling-70b": "parallel-sampling-cow-70b: 64 prompts x 4 samples, prompt 500, suffix U[0,256], 64 query / 8 K/V "
                     "heads (LLaMA-2-70B-shaped), D=128, f16",
+    "sampling-one": "parallel-sampling-one-prompt: 1 prompt x 16 samples, prompt 4000, suffix U[0,64], 32 query / 8 K/V "
+                    "heads (LLaMA-3-8B-shaped), D=128, f16",
     "opt175b": "opt175b-decode-layer: 128 seqs, ctx U[1024,2048], H=96, D=128, bf16, B=16, 16384-block pool",
     "opt175b-tp8": "opt175b-decode-tp8-share: the OPT-175B-shaped layer with the 12 of its 96 heads one of 8 tensor-parallel GPUs holds; "
             "128 seqs, ctx U[1024,2048], D=128, bf16, B=16, 16384-block pool",
@@ -65,7 +67,7 @@ WORKLOADS = {
                      "(lognormal(300, 0.9) contexts, B=16) and prefix-cached admission of 256 prompts sharing a "
                      "512-token system prompt",
 }
-SAMPLING_KINDS = ("sampling", "sampling-gqa", "sampling-70b")  # forked samples sharing prompt blocks
+SAMPLING_KINDS = ("sampling", "sampling-gqa", "sampling-70b", "sampling-one")  # forked samples sharing prompt blocks
 PREFILL_KINDS = {"prefill-llama7b": "llama7b", "prefill-gqa8b": "llama3-8b", "prefill-prompts": "prompts"}
 MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak, vendor figure
 PREFILL_METRIC = "paged prefill attention: TFLOP/s and % of MFMA peak"
@@ -86,8 +88,8 @@ def parse():
                     help="PA_DECODE_SHARED_BLOCKS (cached K/V loads); auto = on for the parallel-sampling workload "
                          "decoded without sibling groups (its samples then re-read the shared prompt blocks)")
     ap.add_argument("--siblings", default="auto",
-                    help="PA_DECODE_SIBLINGS group size (0 = off); auto = the samples per prompt (4) for the "
-                         "parallel-sampling workload, off otherwise")
+                    help="PA_DECODE_SIBLINGS group size (0 = off); auto = the samples per prompt (4, or 16 for "
+                         "sampling-one) for the parallel-sampling workloads, off otherwise")
     ap.add_argument("--rotate", type=int, default=2, help="independent pool copies cycled across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-second-config", action="store_true",
@@ -113,6 +115,9 @@ def make_case(cfg, block_size=16):
         return wl.parallel_sampling(block_size=block_size, num_heads=32, num_kv_heads=8)
     if cfg == "sampling-70b":
         return wl.parallel_sampling(block_size=block_size, num_heads=64, num_kv_heads=8)
+    if cfg == "sampling-one":
+        return wl.parallel_sampling(block_size=block_size, num_prompts=1, samples=16, prompt_len=4000, num_heads=32,
+                                    num_kv_heads=8, max_suffix=64)
     if cfg == "gqa8b":
         return wl.gqa_config("llama3-8b", n_append=1)
     if cfg == "gqa70b":
@@ -406,7 +411,8 @@ def bench_decode(args, config, case, pa, torch, dev, full=True):
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
-    siblings = (4 if config in SAMPLING_KINDS else 0) if args.siblings == "auto" else int(args.siblings)
+    siblings = (int(case.meta["samples"]) if config in SAMPLING_KINDS else 0) if args.siblings == "auto" \
+        else int(args.siblings)
     # Cached K/V loads pay off when several workgroups read the same blocks:
     # the parallel-sampling workload decoded without sibling groups.  With
     # them, each shared block is read once per (group, head) and the
