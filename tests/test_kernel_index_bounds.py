@@ -887,3 +887,22 @@ def test_siblings_split_unrelated_bounds():
     parts = sibling_plan(8, 4, 4, 128, 16, 8, case.max_context_len, ws)
     assert parts >= 2
     check_siblings_bounds(case, 8, parts)
+
+
+def test_bench_sampling_one_bounds():
+    """The benchmark's one-prompt workload (4000 tokens x 16 samples, 32 query
+    over 8 K/V heads) under the split sibling grid the host picks, and under
+    the ungrouped plan."""
+    import paged_kv_cache_322_amd as pa
+
+    case = wl.parallel_sampling(block_size=16, num_prompts=1, samples=16, prompt_len=4000, num_heads=32,
+                                num_kv_heads=8, max_suffix=64)
+    S, H, D = case.q.shape
+    ws = pa.decode_workspace_size(S, H, D, case.max_context_len, num_kv_heads=8)
+    parts = sibling_plan(S, H, 8, D, 16, 16, case.max_context_len, ws)
+    assert parts == 8
+    check_siblings_bounds(case, 16, parts)
+    assert balanced_plan(S, 8, case.max_context_len, 4)  # the ungrouped plan (--siblings 0)
+    for wgs in (512, 64):
+        check_balanced_bounds(S, 8, 4, D, 16, case.k_cache.shape[0], case.block_tables.shape[1], case.context_lens,
+                              case.block_tables, case.max_context_len, wgs)
