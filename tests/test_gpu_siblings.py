@@ -265,6 +265,26 @@ def test_siblings_thin_grid_split_unrelated():
     assert (out[2].float() == 0).all()
 
 
+@pytest.mark.parametrize("scale", [0.0, -0.3])
+def test_siblings_scale_zero_and_negative(scale):
+    """Scale 0 (every weight equal: the mean of the V rows) and a negative
+    scale, through whole sibling tile lists (config 4's shape at 16 prompts)
+    and through a split thin grid."""
+    for case, group in ((wl.parallel_sampling(block_size=16, num_prompts=16, samples=4, prompt_len=300,
+                                              num_heads=8, head_dim=128, pool_tokens=16384, max_suffix=64), 4),
+                        (_thin_case(8), 16)):
+        case.scale = scale
+        g = GpuCase(case)
+        g.run_steps()
+        for kc, vc in oracle_steps(case):
+            pass
+        ref = oracle_decode(case, kc, vc)
+        out = torch.full_like(g.q, float("nan"))
+        pa().decode(out, g.q, g.kc, g.vc, g.bt, g.ctx, scale, case.max_context_len, siblings=group)
+        torch.cuda.synchronize()
+        assert_close(out, ref, case.dtype, f"{case.name} siblings={group} scale={scale}")
+
+
 def test_siblings_thin_grid_declined_without_workspace():
     """Where the ungrouped plan needs no workspace (two prompts x 16 samples,
     multi-head: whole contexts) a thin sibling grid has nowhere to put split
