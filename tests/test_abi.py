@@ -310,3 +310,16 @@ def test_decode_sibling_flag_host_checks():
     args = (P, P, P, P, P, P, 4, 2, 2, 128, 16, 8, 100, 64, 0.1, 1, 0)
     assert f(*args, 17 << 8, P, 0, None) == INVALID  # more than 16 members
     assert f(*args, 1 << 16, P, 0, None) == INVALID  # unknown bit
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus 2 exits non-zero with a message,
+    before touching a GPU."""
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300, cwd=root)
+    assert r.returncode != 0
+    assert "one GPU" in r.stderr
