@@ -91,6 +91,13 @@ struct DecodeShape {
     static_assert(LPR >= 1 && LPR <= kWave && (kWave % LPR) == 0, "unsupported head_dim");
 };
 
+// 16-byte non-temporal store of an appended row.  These rows are scattered
+// over the pool and written while the kernel streams the cache: on 256
+// sequences x 40 heads ordinary stores added 20 us to the call, these add 10.
+__device__ __forceinline__ void store16_nt(void* p, const uint4& v) {
+    __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(p));
+}
+
 // APPEND: the newest token of every sequence (position ctx - 1) arrives in
 // knew/vnew [S, Hk, D]; the workgroup whose partition holds it reads that
 // token's rows from there and stores them into the caches.
@@ -243,8 +250,8 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(
 #pragma unroll
                 for (int i = 0; i < NL; ++i) {
                     if (b >= 0 && tb + i * TPL + row == t) {
-                        *reinterpret_cast<uint4*>(kc + e) = kr[i];
-                        *reinterpret_cast<uint4*>(vc + e) = vr[i];
+                        store16_nt(kc + e, kr[i]);
+                        store16_nt(vc + e, vr[i]);
                     }
                 }
             }
